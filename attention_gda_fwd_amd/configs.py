@@ -1,0 +1,89 @@
+"""The five workloads of the GDA forward path (shapes only; no arithmetic).
+
+Head layouts follow the pages: Motif-2-12.7B has 32 signal + 8 noise query heads
+over 16 KV heads (overview page, sections 2.1-2.2); Motif 3 has 64 signal + 16
+noise query heads over 16 shared KV heads with a 1:3 full:sliding-window (W=128)
+layer schedule (Motif 3 release post, architecture and pretraining paragraphs).
+Head dims for the Motif 3 layout (dqk = 128 + 64 shared rotary, dv = 128) are
+not printed on the pages and are taken as stated by the workload list.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+
+@dataclass(frozen=True)
+class Case:
+    name: str
+    kind: str          # "fwd" (prefill) or "decode"
+    dtype: str         # "bf16" or "f32"
+    B: int
+    L: int             # prefill sequence length, or decode cache length Lmax
+    S: int
+    N: int
+    Hkv: int
+    dqk: int
+    dv: int
+    window: int        # 0 = full causal
+    rope_dims: int = 0
+    case_id: int = 0   # seed key
+
+    @property
+    def g(self) -> int:
+        return self.S // self.N
+
+    def with_(self, **kw) -> "Case":
+        return replace(self, **kw)
+
+    # Algorithmic work, as the bench reports it -----------------------------------------
+    def visible_pairs(self, lens=None) -> int:
+        """Visible (query, key) pairs per query head, summed over the batch."""
+        W = self.window
+        if self.kind == "fwd":
+            L = self.L
+            if W == 0 or W >= L:
+                per = L * (L + 1) // 2
+            else:
+                per = W * (W + 1) // 2 + (L - W) * W
+            return per * self.B
+        tot = 0
+        for b in range(self.B):
+            n = self.L if lens is None else int(min(max(int(lens[b]), 0), self.L))
+            tot += n if W == 0 else min(n, W)
+        return tot
+
+    def flops(self, lens=None) -> int:
+        return 2 * (self.dqk + self.dv) * self.visible_pairs(lens) * (self.S + self.N)
+
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self, lens=None) -> int:
+        """Every input read once and the output written once, at the stored dtype.
+        Decode counts only the cache rows that are visible."""
+        e = self.elem_bytes()
+        B, L, S, N, H, dqk, dv = self.B, self.L, self.S, self.N, self.Hkv, self.dqk, self.dv
+        if self.kind == "fwd":
+            n = B * L * (S * dqk + N * dqk + H * dqk + H * dv + S + 2 * S * dv)
+            return n * e
+        keys = self.visible_pairs(lens)
+        n = B * (S * dqk + N * dqk + S + 2 * S * dv) + keys * H * (dqk + dv)
+        return n * e + (4 * B if lens is not None else 0)
+
+    def tokens(self) -> int:
+        return self.B * self.L if self.kind == "fwd" else self.B
+
+
+CFG0 = Case("cfg0_f32_tiny", "fwd", "f32", B=1, L=256, S=8, N=2, Hkv=2, dqk=64, dv=64,
+            window=0, case_id=0)
+CFG1 = Case("cfg1_motif2_L4096", "fwd", "bf16", B=1, L=4096, S=32, N=8, Hkv=16, dqk=128,
+            dv=128, window=0, case_id=1)
+CFG2 = Case("cfg2_motif3_full_B2_L8192", "fwd", "bf16", B=2, L=8192, S=64, N=16, Hkv=16,
+            dqk=192, dv=128, window=0, rope_dims=64, case_id=2)
+CFG3 = Case("cfg3_motif3_swa128_L32768", "fwd", "bf16", B=1, L=32768, S=64, N=16, Hkv=16,
+            dqk=192, dv=128, window=128, rope_dims=64, case_id=3)
+CFG4 = Case("cfg4_motif3_decode_B64_Lk32768", "decode", "bf16", B=64, L=32768, S=64, N=16,
+            Hkv=16, dqk=192, dv=128, window=0, rope_dims=64, case_id=4)
+CFG4W = CFG4.with_(name="cfg4w_motif3_decode_B64_Lk32768_swa128", window=128)
+
+CONFIGS = {c.name: c for c in (CFG0, CFG1, CFG2, CFG3, CFG4, CFG4W)}

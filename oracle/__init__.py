@@ -1,0 +1,135 @@
+"""fp64 CPU oracle for the GDA/GDLA attention core (ctypes front end of ``gda_ref.c``).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's
+CPU-baseline leg may import this package. It imports nothing from the product
+package and the product package imports nothing from it.
+
+Inputs are numpy arrays at their storage type: ``uint16`` bf16 bit patterns or
+``float32``. Outputs are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgda_ref.so")
+SRC = os.path.join(_HERE, "gda_ref.c")
+
+BF16, F32 = 0, 1
+(EXACT, MUT_DROP_LAMBDA, MUT_PLUS_LAMBDA, MUT_TILED_REPEAT, MUT_KV_INTERLEAVE, MUT_WINDOW_OBO,
+ MUT_SCALE_DV, MUT_NO_GATE, MUT_NO_CAUSAL, MUT_K_TRANSPOSED, MUT_LAMBDA_BY_GROUP,
+ MUT_NO_NORMALIZE, MUT_DECODE_POS, MUT_SKIP_FIRST_KEY) = range(14)
+MUTANTS = {
+    "drop_lambda": MUT_DROP_LAMBDA, "plus_lambda": MUT_PLUS_LAMBDA,
+    "tiled_repeat": MUT_TILED_REPEAT, "kv_interleave": MUT_KV_INTERLEAVE,
+    "window_off_by_one": MUT_WINDOW_OBO, "scale_dv": MUT_SCALE_DV, "no_gate": MUT_NO_GATE,
+    "no_causal": MUT_NO_CAUSAL, "k_transposed": MUT_K_TRANSPOSED,
+    "lambda_by_group": MUT_LAMBDA_BY_GROUP, "no_normalize": MUT_NO_NORMALIZE,
+    "decode_position": MUT_DECODE_POS, "skip_first_key": MUT_SKIP_FIRST_KEY,
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile ``gda_ref.c`` with gcc (fp64, OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.gda_ref_fwd.restype = ctypes.c_int
+        lib.gda_ref_fwd.argtypes = [vp] * 7 + [i64] * 8 + [ctypes.c_int, vp, i64, ctypes.c_int]
+        lib.gda_ref_decode.restype = ctypes.c_int
+        lib.gda_ref_decode.argtypes = [vp] * 8 + [i64] * 8 + [ctypes.c_int, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle inputs must be uint16 (bf16 bits) or float32, got {a.dtype}")
+
+
+def _c(a: np.ndarray, code: int) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if _dtype_code(a) != code:
+        raise TypeError("all oracle inputs must share one storage type")
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def ref_fwd(q_sig, q_noise, k, v, lam, gate, *, window: int, rows=None,
+            mutant: int = EXACT) -> np.ndarray:
+    """Prefill oracle. Shapes: q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk],
+    v [B,L,Hkv,dv], lam [B,L,S], gate [B,L,S,dv]. ``rows`` selects flat (b*L + t) rows;
+    the result is [B,L,S,dv] when ``rows`` is None, else [len(rows),S,dv] (float64)."""
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, k, v, lam, gate = (_c(x, code) for x in (q_sig, q_noise, k, v, lam, gate))
+    B, L, S, dqk = q_sig.shape
+    N = q_noise.shape[2]
+    Hkv, dv = v.shape[2], v.shape[3]
+    assert q_noise.shape == (B, L, N, dqk) and k.shape == (B, L, Hkv, dqk)
+    assert v.shape == (B, L, Hkv, dv) and lam.shape == (B, L, S) and gate.shape == (B, L, S, dv)
+    if rows is None:
+        out = np.empty((B, L, S, dv), dtype=np.float64)
+        rows_arr, n_rows, rp = None, 0, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        n_rows = rows_arr.size
+        out = np.empty((n_rows, S, dv), dtype=np.float64)
+        rp = _ptr(rows_arr)
+    rc = _load().gda_ref_fwd(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam), _ptr(gate),
+                             _ptr(out), B, L, S, N, Hkv, dqk, dv, int(window), code, rp, n_rows,
+                             int(mutant))
+    if rc != 0:
+        raise ValueError(f"gda_ref_fwd rejected its arguments (code {rc})")
+    return out
+
+
+def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window: int,
+               mutant: int = EXACT) -> np.ndarray:
+    """Decode oracle. Shapes: q_sig [B,S,dqk], q_noise [B,N,dqk], k_cache [B,Lmax,Hkv,dqk],
+    v_cache [B,Lmax,Hkv,dv], lam [B,S], gate [B,S,dv], lens int32 [B] or None (= Lmax).
+    Returns [B,S,dv] float64."""
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, k_cache, v_cache, lam, gate = (
+        _c(x, code) for x in (q_sig, q_noise, k_cache, v_cache, lam, gate))
+    B, S, dqk = q_sig.shape
+    N = q_noise.shape[1]
+    Lmax, Hkv, dv = v_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
+    assert q_noise.shape == (B, N, dqk) and k_cache.shape == (B, Lmax, Hkv, dqk)
+    assert lam.shape == (B, S) and gate.shape == (B, S, dv)
+    lp = None
+    if lens is not None:
+        lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32).reshape(-1))
+        assert lens.size == B
+        lp = _ptr(lens)
+    out = np.empty((B, S, dv), dtype=np.float64)
+    rc = _load().gda_ref_decode(_ptr(q_sig), _ptr(q_noise), _ptr(k_cache), _ptr(v_cache), lp,
+                                _ptr(lam), _ptr(gate), _ptr(out), B, Lmax, S, N, Hkv, dqk, dv,
+                                int(window), code, int(mutant))
+    if rc != 0:
+        raise ValueError(f"gda_ref_decode rejected its arguments (code {rc})")
+    return out

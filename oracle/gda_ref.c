@@ -1,0 +1,229 @@
+/* gda_ref.c - fp64 CPU oracle for the Grouped Differential (Latent) Attention core.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * bench's CPU-baseline leg, never by the product path. Shares no code with it.
+ *
+ * It is the definition written out, in the order the Motif 3 technical-report
+ * walk-through (paper.rainbus.top, step 2 "GDLA forward") states it:
+ *   1. signal and noise query paths share the expanded KV heads and each
+ *      computes its own softmax attention over the visible keys;
+ *   2. the noise output is repeated g = S/N times by group;
+ *   3. D_t = H_S,t - lambda_t (.) Repeat_g(H_N,t)      (equation D_t);
+ *   4. the sigmoid gate G_t multiplies D_t elementwise (before W^O).
+ * Readings taken where the pages are silent (each listed in the design notes):
+ *   - softmax scale 1/sqrt(dqk), dqk the contraction length;
+ *   - signal head i reads KV head floor(i*Hkv/S), noise head j reads KV head
+ *     floor(j*Hkv/N), and noise head j serves signal heads g*j .. g*j+g-1
+ *     (block order of "repeated g times by group");
+ *   - lambda is one value per (token, signal head), broadcast over dv; lambda
+ *     and gate arrive as values in (0,1) (the sigmoid is upstream);
+ *   - key s is visible from query t iff s <= t and, for a window W >= 1,
+ *     t - s <= W - 1 (W keys including the query's own); W = 0 is full causal;
+ *   - decode attends from position len-1 of a cache that already holds it.
+ * Built with -ffp-contract=off so no fused multiply-add changes a rounding.
+ */
+#include "gda_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t Lk, Hkv, dqk, dv;
+  int dtype;
+  int mutant;
+} kv_view;
+
+/* Stored value -> double. bf16 is the upper half of a float32, so the
+ * widening is exact. */
+static double rd(const void* base, int64_t i, int dtype) {
+  if (dtype == GDA_REF_F32) return (double)((const float*)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static int64_t k_index(const kv_view* kv, int64_t b, int64_t s, int64_t h, int64_t d) {
+  if (kv->mutant == GDA_REF_MUT_K_TRANSPOSED)
+    return ((b * kv->Hkv + h) * kv->Lk + s) * kv->dqk + d;
+  return ((b * kv->Lk + s) * kv->Hkv + h) * kv->dqk + d;
+}
+
+static int64_t v_index(const kv_view* kv, int64_t b, int64_t s, int64_t h, int64_t e) {
+  return ((b * kv->Lk + s) * kv->Hkv + h) * kv->dv + e;
+}
+
+/* Visible keys of query position t: [lo, hi]. */
+static void visible_range(int64_t t, int64_t W, int64_t Lk, int mutant, int64_t* lo,
+                          int64_t* hi) {
+  int64_t h = t, l;
+  if (mutant == GDA_REF_MUT_NO_CAUSAL) h = Lk - 1;
+  if (W == 0)
+    l = 0;
+  else if (mutant == GDA_REF_MUT_WINDOW_OBO)
+    l = t - W;
+  else
+    l = t - W + 1;
+  if (l < 0) l = 0;
+  if (mutant == GDA_REF_MUT_SKIP_FIRST_KEY && l == 0) l = 1;
+  *lo = l;
+  *hi = h;
+}
+
+/* One path's attention for one query row over KV head h of batch row b:
+ *   z_s = scale * sum_d q[d] k[b,s,h,d]           for s in [lo, hi]
+ *   w_s = exp(z_s - max_s z_s),  l = sum_s w_s
+ *   H[e] = (sum_s w_s v[b,s,h,e]) / l
+ * z is scratch of at least hi-lo+1 doubles. */
+static void attend(const void* q, int64_t q_off, const kv_view* kv, int64_t b, int64_t h,
+                   int64_t lo, int64_t hi, double scale, double* z, double* H) {
+  for (int64_t e = 0; e < kv->dv; ++e) H[e] = 0.0;
+  if (hi < lo) return;
+  double m = -INFINITY;
+  for (int64_t s = lo; s <= hi; ++s) {
+    double acc = 0.0;
+    for (int64_t d = 0; d < kv->dqk; ++d)
+      acc += rd(q, q_off + d, kv->dtype) * rd(kv->k, k_index(kv, b, s, h, d), kv->dtype);
+    z[s - lo] = scale * acc;
+    if (z[s - lo] > m) m = z[s - lo];
+  }
+  double l = 0.0;
+  for (int64_t s = lo; s <= hi; ++s) {
+    z[s - lo] = exp(z[s - lo] - m);
+    l += z[s - lo];
+  }
+  for (int64_t s = lo; s <= hi; ++s)
+    for (int64_t e = 0; e < kv->dv; ++e)
+      H[e] += z[s - lo] * rd(kv->v, v_index(kv, b, s, h, e), kv->dtype);
+  if (kv->mutant != GDA_REF_MUT_NO_NORMALIZE)
+    for (int64_t e = 0; e < kv->dv; ++e) H[e] /= l;
+}
+
+/* Every output of one query row: out[i][e] for signal heads i, dv channels e. */
+static void gda_row(const void* q_sig, int64_t qs_off, const void* q_noise, int64_t qn_off,
+                    const void* lambda, int64_t lam_off, const void* gate, int64_t gate_off,
+                    const kv_view* kv, int64_t b, int64_t t, int64_t S, int64_t N,
+                    int64_t window, double* z, double* Hn, double* Hs, double* out) {
+  const int64_t Hkv = kv->Hkv, dqk = kv->dqk, dv = kv->dv;
+  const int mut = kv->mutant;
+  const int64_t g = S / N;
+  const double scale = 1.0 / sqrt((double)(mut == GDA_REF_MUT_SCALE_DV ? dv : dqk));
+  int64_t lo, hi;
+  visible_range(t, window, kv->Lk, mut, &lo, &hi);
+
+  /* Noise path: noise head j on KV head floor(j*Hkv/N). */
+  for (int64_t j = 0; j < N; ++j)
+    attend(q_noise, qn_off + j * dqk, kv, b, (j * Hkv) / N, lo, hi, scale, z, Hn + j * dv);
+
+  /* Signal path, then D = H_S - lambda * Repeat_g(H_N), then the gate. */
+  for (int64_t i = 0; i < S; ++i) {
+    const int64_t kvs = (mut == GDA_REF_MUT_KV_INTERLEAVE) ? i % Hkv : (i * Hkv) / S;
+    attend(q_sig, qs_off + i * dqk, kv, b, kvs, lo, hi, scale, z, Hs);
+    const int64_t j = (mut == GDA_REF_MUT_TILED_REPEAT) ? i % N : i / g;
+    const double lam = rd(lambda, lam_off + (mut == GDA_REF_MUT_LAMBDA_BY_GROUP ? j : i),
+                          kv->dtype);
+    for (int64_t e = 0; e < dv; ++e) {
+      double D;
+      if (mut == GDA_REF_MUT_DROP_LAMBDA)
+        D = Hs[e];
+      else if (mut == GDA_REF_MUT_PLUS_LAMBDA)
+        D = Hs[e] + lam * Hn[j * dv + e];
+      else
+        D = Hs[e] - lam * Hn[j * dv + e];
+      const double G = rd(gate, gate_off + i * dv + e, kv->dtype);
+      out[i * dv + e] = (mut == GDA_REF_MUT_NO_GATE) ? D : G * D;
+    }
+  }
+}
+
+static int check_common(int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv, int64_t dqk,
+                        int64_t dv, int64_t window, int dtype) {
+  if (B < 1 || L < 1 || S < 1 || N < 1 || Hkv < 1 || dqk < 1 || dv < 1) return -1;
+  if (S % N != 0 || S % Hkv != 0) return -2;
+  if (N % Hkv != 0 && Hkv % N != 0) return -3;
+  if (window < 0) return -4;
+  if (dtype != GDA_REF_BF16 && dtype != GDA_REF_F32) return -5;
+  return 0;
+}
+
+int gda_ref_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                const void* lambda, const void* gate, double* out, int64_t B, int64_t L,
+                int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
+                int dtype, const int64_t* rows, int64_t n_rows, int mutant) {
+  int rc = check_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
+  if (rc) return rc;
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out) return -6;
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, mutant};
+  const int64_t total = rows ? n_rows : B * L;
+  for (int64_t r = 0; r < total; ++r) {
+    const int64_t flat = rows ? rows[r] : r;
+    if (flat < 0 || flat >= B * L) return -7;
+  }
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    double* Hn = (double*)malloc(sizeof(double) * (size_t)(N * dv));
+    double* Hs = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!z || !Hn || !Hs) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < total; ++r) {
+        const int64_t flat = rows ? rows[r] : r;
+        const int64_t b = flat / L, t = flat % L;
+        gda_row(q_sig, flat * S * dqk, q_noise, flat * N * dqk, lambda, flat * S, gate,
+                flat * S * dv, &kv, b, t, S, N, window, z, Hn, Hs, out + r * S * dv);
+      }
+    }
+    free(z);
+    free(Hn);
+    free(Hs);
+  }
+  return failed ? -8 : 0;
+}
+
+int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
+                   const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                   const void* gate, double* out, int64_t B, int64_t Lmax, int64_t S,
+                   int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window, int dtype,
+                   int mutant) {
+  int rc = check_common(B, Lmax, S, N, Hkv, dqk, dv, window, dtype);
+  if (rc) return rc;
+  if (!q_sig || !q_noise || !k_cache || !v_cache || !lambda || !gate || !out) return -6;
+  const kv_view kv = {k_cache, v_cache, Lmax, Hkv, dqk, dv, dtype, mutant};
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    double* Hn = (double*)malloc(sizeof(double) * (size_t)(N * dv));
+    double* Hs = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!z || !Hn || !Hs) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t b = 0; b < B; ++b) {
+        int64_t len = cache_lens ? (int64_t)cache_lens[b] : Lmax;
+        if (len > Lmax) len = Lmax;
+        double* o = out + b * S * dv;
+        if (len < 1) {
+          for (int64_t x = 0; x < S * dv; ++x) o[x] = 0.0;
+          continue;
+        }
+        int64_t p = len - 1;
+        if (mutant == GDA_REF_MUT_DECODE_POS) p = len < Lmax ? len : Lmax - 1;
+        gda_row(q_sig, b * S * dqk, q_noise, b * N * dqk, lambda, b * S, gate, b * S * dv, &kv,
+                b, p, S, N, window, z, Hn, Hs, o);
+      }
+    }
+    free(z);
+    free(Hn);
+    free(Hs);
+  }
+  return failed ? -8 : 0;
+}

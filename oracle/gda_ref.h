@@ -1,0 +1,74 @@
+/* gda_ref.h - fp64 CPU oracle for the Grouped Differential (Latent) Attention core.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg may load this library. The product path (libgda) neither
+ * includes this header nor links this code, and this code includes nothing
+ * from the product path.
+ *
+ * The operation is the one the Motif 3 technical-report walk-through
+ * (paper.rainbus.top, step 2 "GDLA forward", equation D_t) writes out: signal
+ * and noise query heads attend over the same expanded KV heads, each path with
+ * its own softmax attention; the noise output is repeated g times by group;
+ * D = H_S - lambda (.) Repeat_g(H_N); a sigmoid gate G multiplies D elementwise.
+ *
+ * All inputs are read at their stored values (bf16 bit patterns or float32,
+ * widened exactly to double); every sum, exponential and quotient is in double.
+ */
+#ifndef GDA_REF_H
+#define GDA_REF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { GDA_REF_BF16 = 0, GDA_REF_F32 = 1 };
+
+/* Deliberate mistakes, used only by tests that show the pins catch them. */
+enum {
+  GDA_REF_EXACT = 0,
+  GDA_REF_MUT_DROP_LAMBDA = 1,   /* D = H_S                                  */
+  GDA_REF_MUT_PLUS_LAMBDA = 2,   /* D = H_S + lambda H_N                     */
+  GDA_REF_MUT_TILED_REPEAT = 3,  /* noise head of signal i taken as i mod N  */
+  GDA_REF_MUT_KV_INTERLEAVE = 4, /* signal i reads KV head i mod Hkv         */
+  GDA_REF_MUT_WINDOW_OBO = 5,    /* window keeps t-s <= W (W+1 keys)         */
+  GDA_REF_MUT_SCALE_DV = 6,      /* softmax scale 1/sqrt(dv)                 */
+  GDA_REF_MUT_NO_GATE = 7,       /* gate not applied                         */
+  GDA_REF_MUT_NO_CAUSAL = 8,     /* prefill keys up to L-1 visible           */
+  GDA_REF_MUT_K_TRANSPOSED = 9,  /* K read as [B, Hkv, L, dqk]               */
+  GDA_REF_MUT_LAMBDA_BY_GROUP = 10, /* lambda read at the noise index        */
+  GDA_REF_MUT_NO_NORMALIZE = 11, /* softmax weights not divided by their sum */
+  GDA_REF_MUT_DECODE_POS = 12,   /* decode query at position len, not len-1  */
+  GDA_REF_MUT_SKIP_FIRST_KEY = 13, /* key 0 never visible                    */
+  GDA_REF_MUT_COUNT = 14
+};
+
+/* Prefill. Layouts (row-major, innermost contiguous):
+ *   q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk], v [B,L,Hkv,dv],
+ *   lambda [B,L,S], gate [B,L,S,dv]; all of storage type `dtype`.
+ * rows: NULL for every (b,t) (out is [B,L,S,dv]), else n_rows flat indices
+ *   r = b*L + t (out is [n_rows,S,dv]).
+ * Returns 0, or a negative value for arguments it cannot take. */
+int gda_ref_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                const void* lambda, const void* gate, double* out,
+                int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
+                int64_t dqk, int64_t dv, int64_t window, int dtype,
+                const int64_t* rows, int64_t n_rows, int mutant);
+
+/* Decode: one query token per sequence at position len_b - 1 over a cache that
+ * already holds that token's K/V.
+ *   q_sig [B,S,dqk], q_noise [B,N,dqk], k_cache [B,Lmax,Hkv,dqk],
+ *   v_cache [B,Lmax,Hkv,dv], lambda [B,S], gate [B,S,dv]; cache_lens host
+ *   int32 [B] or NULL (= Lmax). A length above Lmax is clamped to Lmax; a
+ *   length below 1 gives an all-zero output row. out is [B,S,dv]. */
+int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
+                   const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                   const void* gate, double* out,
+                   int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
+                   int64_t dqk, int64_t dv, int64_t window, int dtype, int mutant);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,324 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each ``pin_*`` function takes the oracle entry points (possibly with a planted
+mistake) and returns a list of failure messages (empty = the pin holds). The
+tests run them on the exact oracle (all must hold) and on each planted mistake
+(at least one must fail).
+
+What each pin rests on:
+  * head maps stated by the workload descriptions themselves (layouts A, B, C
+    below: "signal head i uses KV head i//4", "noise head j uses KV head 2j and
+    is repeated onto signal heads 4j..4j+3", ...), never by the oracle's formula;
+  * torch's CPU float64 ``scaled_dot_product_attention`` (a library routine)
+    with its default scale;
+  * closed forms: uniform weights give the mean of the visible values, a single
+    visible key gives that key's value, two visible keys give a logistic mix;
+  * invariants of softmax attention: a per-row logit shift, scaling of V or G;
+  * a pure-Python brute force on tiny inputs.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from attention_gda_fwd_amd import inputs as gin
+
+from . import brute
+
+# Head layouts as the workload descriptions state them.
+LAYOUTS = {
+    # S=8, N=2, Hkv=2: signal i -> KV i//4; noise j -> KV j; noise j serves signals 4j..4j+3.
+    "A": dict(S=8, N=2, Hkv=2, kv_sig=lambda i: i // 4, kv_noise=lambda j: j,
+              group=lambda i: i // 4),
+    # S=32, N=8, Hkv=16: signal i -> KV i//2; noise j -> KV 2j; noise j serves 4j..4j+3.
+    "B": dict(S=32, N=8, Hkv=16, kv_sig=lambda i: i // 2, kv_noise=lambda j: 2 * j,
+              group=lambda i: i // 4),
+    # S=64, N=16, Hkv=16: signal i -> KV i//4; noise j -> KV j (g=4).
+    "C": dict(S=64, N=16, Hkv=16, kv_sig=lambda i: i // 4, kv_noise=lambda j: j,
+              group=lambda i: i // 4),
+}
+
+
+def make(layout, *, B=2, L=9, dqk=8, dv=4, dtype="f32", case_id=1000):
+    lay = LAYOUTS[layout]
+    return gin.fwd_inputs(case_id, B=B, L=L, S=lay["S"], N=lay["N"], Hkv=lay["Hkv"], dqk=dqk,
+                          dv=dv, dtype=dtype)
+
+
+def f64(a, dtype="f32"):
+    return gin.storage_to_f64(a, "bf16" if a.dtype == np.uint16 else "f32")
+
+
+def ones_like_storage(a):
+    return gin.to_storage(np.ones(a.shape, dtype=np.float32), "bf16" if a.dtype == np.uint16 else "f32")
+
+
+def zeros_like_storage(a):
+    return gin.to_storage(np.zeros(a.shape, dtype=np.float32), "bf16" if a.dtype == np.uint16 else "f32")
+
+
+def band_mask(L, window):
+    t = torch.arange(L)[:, None]
+    s = torch.arange(L)[None, :]
+    m = s <= t
+    if window:
+        m &= (t - s) <= window - 1
+    return m
+
+
+def sdpa(q, k, v, window):
+    """torch CPU float64 SDPA. q [B,L,d], k [B,L,d], v [B,L,e] -> [B,L,e]."""
+    qt = torch.from_numpy(q)[:, None]
+    kt = torch.from_numpy(k)[:, None]
+    vt = torch.from_numpy(v)[:, None]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=band_mask(q.shape[1], window))
+    return out[:, 0].numpy()
+
+
+def _fail(msgs, name, err, tol):
+    if not (err <= tol):
+        msgs.append(f"{name}: err {err:.3e} > {tol:.1e}")
+
+
+# ---------------------------------------------------------------------------------------
+def pin_library_sdpa(fwd, layouts=("A", "B", "C"), windows=(0, 3)):
+    """lambda = 0, gate = 1 -> out_i is plain attention of signal head i over KV kv_sig(i);
+    lambda = 1, gate = 1 -> out_i = attn(signal i) - attn(noise group(i)); random lambda and
+    gate compose the same two library attentions. dqk != dv so the scale is exercised."""
+    msgs = []
+    for lay_name in layouts:
+        lay = LAYOUTS[lay_name]
+        for W in windows:
+            x = make(lay_name, dqk=6, dv=4, L=7, case_id=1100)
+            qs, qn, k, v = (f64(x[n]) for n in ("q_sig", "q_noise", "k", "v"))
+            lamv, gatev = f64(x["lam"]), f64(x["gate"])
+            HS = np.stack([sdpa(qs[:, :, i], k[:, :, lay["kv_sig"](i)], v[:, :, lay["kv_sig"](i)], W)
+                           for i in range(lay["S"])], axis=2)
+            HN = np.stack([sdpa(qn[:, :, j], k[:, :, lay["kv_noise"](j)],
+                                v[:, :, lay["kv_noise"](j)], W) for j in range(lay["N"])], axis=2)
+            rep = HN[:, :, [lay["group"](i) for i in range(lay["S"])]]
+            # lambda = 0, gate = 1
+            o0 = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], zeros_like_storage(x["lam"]),
+                     ones_like_storage(x["gate"]), window=W)
+            _fail(msgs, f"sdpa lam=0 layout {lay_name} W={W}", np.abs(o0 - HS).max(), 1e-12)
+            o1 = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], ones_like_storage(x["lam"]),
+                     ones_like_storage(x["gate"]), window=W)
+            _fail(msgs, f"sdpa lam=1 layout {lay_name} W={W}", np.abs(o1 - (HS - rep)).max(), 1e-12)
+            o2 = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], window=W)
+            exp2 = gatev * (HS - lamv[..., None] * rep)
+            _fail(msgs, f"sdpa random layout {lay_name} W={W}", np.abs(o2 - exp2).max(), 1e-12)
+    return msgs
+
+
+def pin_noise_one_hot(fwd):
+    """lambda one-hot on signal head i: only out_i moves, by exactly -attn(noise group(i))."""
+    msgs = []
+    for lay_name in ("A", "B"):
+        lay = LAYOUTS[lay_name]
+        x = make(lay_name, L=6, case_id=1200)
+        qn, k, v = f64(x["q_noise"]), f64(x["k"]), f64(x["v"])
+        zero = zeros_like_storage(x["lam"])
+        ones_g = ones_like_storage(x["gate"])
+        base = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], zero, ones_g, window=0)
+        for i in (0, 3, 5, lay["S"] - 1):
+            lam = np.zeros(x["lam"].shape, dtype=np.float32)
+            lam[:, :, i] = 1.0
+            o = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], gin.to_storage(lam, "f32"), ones_g,
+                    window=0)
+            j = lay["group"](i)
+            hn = sdpa(qn[:, :, j], k[:, :, lay["kv_noise"](j)], v[:, :, lay["kv_noise"](j)], 0)
+            _fail(msgs, f"one-hot lambda layout {lay_name} head {i}",
+                  np.abs((o[:, :, i] - base[:, :, i]) + hn).max(), 1e-12)
+            others = [h for h in range(lay["S"]) if h != i]
+            _fail(msgs, f"one-hot lambda leaks, layout {lay_name} head {i}",
+                  np.abs(o[:, :, others] - base[:, :, others]).max(), 0.0)
+    return msgs
+
+
+def pin_identical_queries_zero(fwd):
+    """q_sig[i] := q_noise[group(i)], lambda = 1: out_i is exactly 0 wherever signal i and
+    noise group(i) read the same KV head; nonzero where they do not (layout B, heads 4j+2, 4j+3)."""
+    msgs = []
+    for lay_name in ("A", "B", "C"):
+        lay = LAYOUTS[lay_name]
+        x = make(lay_name, L=8, case_id=1300)
+        qs = x["q_sig"].copy()
+        for i in range(lay["S"]):
+            qs[:, :, i] = x["q_noise"][:, :, lay["group"](i)]
+        o = fwd(qs, x["q_noise"], x["k"], x["v"], ones_like_storage(x["lam"]), x["gate"], window=0)
+        for i in range(lay["S"]):
+            same = lay["kv_sig"](i) == lay["kv_noise"](lay["group"](i))
+            mx = np.abs(o[:, :, i]).max()
+            if same and mx != 0.0:
+                msgs.append(f"zero pin layout {lay_name} head {i}: max |out| {mx:.3e} != 0")
+            if not same and not (mx > 1e-6):
+                msgs.append(f"zero pin layout {lay_name} head {i}: expected nonzero, got {mx:.3e}")
+    return msgs
+
+
+def pin_constant_keys(fwd):
+    """All keys of a KV head equal -> uniform weights -> H = mean of the visible V rows."""
+    msgs = []
+    for lay_name in ("A", "B"):
+        lay = LAYOUTS[lay_name]
+        for W in (0, 1, 3, 50):
+            x = make(lay_name, L=10, case_id=1400)
+            k = x["k"].copy()
+            k[:] = k[:, :1]  # every key row equal to row 0 of its (b, head)
+            vv = f64(x["v"])
+            L = vv.shape[1]
+            mean = np.zeros_like(vv)
+            for t in range(L):
+                lo = 0 if W == 0 else max(0, t - W + 1)
+                mean[:, t] = vv[:, lo:t + 1].mean(axis=1)
+            HS = mean[:, :, [lay["kv_sig"](i) for i in range(lay["S"])]]
+            HN = mean[:, :, [lay["kv_noise"](lay["group"](i)) for i in range(lay["S"])]]
+            exp = f64(x["gate"]) * (HS - f64(x["lam"])[..., None] * HN)
+            o = fwd(x["q_sig"], x["q_noise"], k, x["v"], x["lam"], x["gate"], window=W)
+            _fail(msgs, f"constant keys layout {lay_name} W={W}", np.abs(o - exp).max(), 1e-13)
+    return msgs
+
+
+def pin_window(fwd):
+    """L <= W equals full causal; W = 1 is the own row's value; W = 2 is a logistic mix of
+    two rows; W = L-1 differs from full only at the last query."""
+    msgs = []
+    x = make("A", L=9, case_id=1500)
+    args = (x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"])
+    full = fwd(*args, window=0)
+    for W in (9, 10, 300):
+        o = fwd(*args, window=W)
+        _fail(msgs, f"L<=W equality W={W}", np.abs(o - full).max(), 0.0)
+    lay = LAYOUTS["A"]
+    qs, qn, k, v = (f64(x[n]) for n in ("q_sig", "q_noise", "k", "v"))
+    lam, gate = f64(x["lam"]), f64(x["gate"])
+    S = lay["S"]
+    hs_idx = [lay["kv_sig"](i) for i in range(S)]
+    hn_idx = [lay["kv_noise"](lay["group"](i)) for i in range(S)]
+    # W = 1: only key t is visible, its weight is exactly 1.
+    o1 = fwd(*args, window=1)
+    exp1 = gate * (v[:, :, hs_idx] - lam[..., None] * v[:, :, hn_idx])
+    _fail(msgs, "W=1 closed form", np.abs(o1 - exp1).max(), 1e-15)
+    # W = 2: H = v_t + (v_{t-1} - v_t) * logistic(z_{t-1} - z_t), z = q.k / sqrt(dqk).
+    o2 = fwd(*args, window=2)
+    dqk = qs.shape[-1]
+    exp2 = np.empty_like(o2)
+    Bn, L = qs.shape[0], qs.shape[1]
+    for b in range(Bn):
+        for t in range(L):
+            for i in range(S):
+                j = lay["group"](i)
+                def mix(q, h):
+                    if t == 0:
+                        return v[b, 0, h]
+                    dz = (q @ k[b, t - 1, h] - q @ k[b, t, h]) / math.sqrt(dqk)
+                    p = 1.0 / (1.0 + math.exp(-dz))
+                    return v[b, t, h] + (v[b, t - 1, h] - v[b, t, h]) * p
+                hs = mix(qs[b, t, i], hs_idx[i])
+                hn = mix(qn[b, t, j], hn_idx[i])
+                exp2[b, t, i] = gate[b, t, i] * (hs - lam[b, t, i] * hn)
+    _fail(msgs, "W=2 closed form", np.abs(o2 - exp2).max(), 1e-12)
+    # W = L-1: only the last query row loses a key (key 0).
+    o8 = fwd(*args, window=8)
+    _fail(msgs, "W=L-1 equal before last row", np.abs(o8[:, :8] - full[:, :8]).max(), 0.0)
+    if not np.abs(o8[:, 8] - full[:, 8]).max() > 1e-9:
+        msgs.append("W=L-1 last row should differ from full attention")
+    return msgs
+
+
+def pin_invariances(fwd):
+    """A per-KV-head shift c_h added to every key changes each row's logits by a constant
+    (output unchanged); V -> 2V and G -> 2G each double the output exactly."""
+    msgs = []
+    g = np.random.default_rng(7)
+    x = make("B", L=8, case_id=1600)
+    # dyadic keys and shifts so that k + c is exact in float32
+    k = (g.integers(-16, 17, size=x["k"].shape) / 8.0).astype(np.float32)
+    c = (g.integers(-16, 17, size=(1, 1, x["k"].shape[2], x["k"].shape[3])) / 8.0).astype(np.float32)
+    c = np.broadcast_to(c, (k.shape[0], 1) + c.shape[2:])
+    base_args = [x["q_sig"], x["q_noise"], k, x["v"], x["lam"], x["gate"]]
+    for W in (0, 3):
+        o = fwd(*base_args, window=W)
+        shifted = fwd(x["q_sig"], x["q_noise"], (k + c).astype(np.float32), x["v"], x["lam"],
+                      x["gate"], window=W)
+        _fail(msgs, f"key shift invariance W={W}", np.abs(shifted - o).max() / np.abs(o).max(),
+              1e-12)
+        o_v = fwd(x["q_sig"], x["q_noise"], k, (2 * x["v"]).astype(np.float32), x["lam"],
+                  x["gate"], window=W)
+        _fail(msgs, f"V scaling W={W}", np.abs(o_v - 2 * o).max(), 0.0)
+        o_g = fwd(x["q_sig"], x["q_noise"], k, x["v"], x["lam"], (2 * x["gate"]).astype(np.float32),
+                  window=W)
+        _fail(msgs, f"G scaling W={W}", np.abs(o_g - 2 * o).max(), 0.0)
+    return msgs
+
+
+def pin_decode_is_last_row(fwd, decode):
+    """Decode over a cache of length n equals prefill row n-1 over the same K/V."""
+    msgs = []
+    for lay_name in ("A", "B"):
+        for W in (0, 3):
+            x = make(lay_name, B=3, L=11, case_id=1700)
+            lens = np.array([11, 1, 6], dtype=np.int32)
+            full = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], window=W)
+            bi = np.arange(3)
+            ti = lens - 1
+            dec = decode(x["q_sig"][bi, ti], x["q_noise"][bi, ti], x["k"], x["v"], x["lam"][bi, ti],
+                         x["gate"][bi, ti], lens, window=W)
+            _fail(msgs, f"decode == last prefill row, layout {lay_name} W={W}",
+                  np.abs(dec - full[bi, ti]).max(), 0.0)
+            # lens above the cache are clamped; lens below 1 give zeros
+            dec2 = decode(x["q_sig"][bi, ti], x["q_noise"][bi, ti], x["k"], x["v"],
+                          x["lam"][bi, ti], x["gate"][bi, ti], np.array([99, 0, -3], np.int32),
+                          window=W)
+            _fail(msgs, f"decode clamp, layout {lay_name} W={W}",
+                  np.abs(dec2[0] - full[0, 10]).max(), 0.0)
+            _fail(msgs, f"decode empty rows, layout {lay_name} W={W}", np.abs(dec2[1:]).max(), 0.0)
+    return msgs
+
+
+def pin_brute_force(fwd):
+    """Pure-Python enumeration on tiny shapes, including an N > Hkv layout."""
+    msgs = []
+    shapes = [
+        ("A", LAYOUTS["A"]),
+        ("N>Hkv", dict(S=8, N=4, Hkv=2, kv_sig=lambda i: i // 4, kv_noise=lambda j: j // 2,
+                       group=lambda i: i // 2)),
+        ("g=1", dict(S=2, N=2, Hkv=1, kv_sig=lambda i: 0, kv_noise=lambda j: 0,
+                     group=lambda i: i)),
+    ]
+    for name, lay in shapes:
+        for L, W in ((1, 0), (2, 0), (5, 0), (9, 3), (9, 1), (5, 100)):
+            for dtype in ("f32", "bf16"):
+                x = gin.fwd_inputs(1800 + L, B=2, L=L, S=lay["S"], N=lay["N"], Hkv=lay["Hkv"],
+                                   dqk=3, dv=2, dtype=dtype)
+                o = fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], window=W)
+                ref = brute.gda_fwd(*(f64(x[n]).tolist() for n in
+                                      ("q_sig", "q_noise", "k", "v", "lam", "gate")), W,
+                                    lay["kv_sig"], lay["kv_noise"], lay["group"])
+                ref = np.array(ref)
+                err = np.abs(o - ref).max() / max(1e-300, np.abs(ref).max())
+                _fail(msgs, f"brute force {name} L={L} W={W} {dtype}", err, 1e-12)
+    return msgs
+
+
+def all_pins(fwd, decode):
+    msgs = []
+    for p in (pin_library_sdpa, pin_noise_one_hot, pin_identical_queries_zero,
+              pin_constant_keys, pin_window, pin_invariances, pin_brute_force):
+        msgs += p(fwd)
+    msgs += pin_decode_is_last_row(fwd, decode)
+    return msgs
+
+
+def oracle_entry_points(mutant=oracle.EXACT):
+    def fwd(*a, window, rows=None):
+        return oracle.ref_fwd(*a, window=window, rows=rows, mutant=mutant)
+
+    def decode(*a, window):
+        return oracle.ref_decode(*a, window=window, mutant=mutant)
+
+    return fwd, decode

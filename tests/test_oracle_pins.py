@@ -1,0 +1,71 @@
+"""The fp64 oracle against things other than itself (no GPU needed).
+
+Each pin from ``tests/pins.py`` must hold for the exact oracle, and every planted
+mistake (a dropped or flipped term, a wrong index map, an off-by-one window, a
+transposed operand, ...) must break at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+from . import pins
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+EXACT_FWD, EXACT_DEC = pins.oracle_entry_points()
+
+PINS_FWD = [pins.pin_library_sdpa, pins.pin_noise_one_hot, pins.pin_identical_queries_zero,
+            pins.pin_constant_keys, pins.pin_window, pins.pin_invariances, pins.pin_brute_force]
+
+
+@pytest.mark.parametrize("pin", PINS_FWD, ids=lambda p: p.__name__)
+def test_exact_oracle_pin(pin):
+    assert pin(EXACT_FWD) == []
+
+
+def test_exact_oracle_decode_pin():
+    assert pins.pin_decode_is_last_row(EXACT_FWD, EXACT_DEC) == []
+
+
+@pytest.mark.parametrize("name", sorted(oracle.MUTANTS))
+def test_planted_mistake_is_caught(name):
+    fwd, dec = pins.oracle_entry_points(oracle.MUTANTS[name])
+    assert pins.all_pins(fwd, dec), f"no pin catches the planted mistake {name!r}"
+
+
+def test_hand_worked_example():
+    with open(os.path.join(HERE, "golden", "hand_worked_example.json")) as f:
+        ex = json.load(f)
+    x = {k: np.array(v, dtype=np.float32) for k, v in ex["inputs"].items()}
+    args = (x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"])
+    for key, W in (("window_0", 0), ("window_2", 2)):
+        expected = np.array([[eval(s, {"__builtins__": {}}, {"e": math.e}) for s in row]
+                             for row in ex["expected"][key]])
+        got = oracle.ref_fwd(*args, window=W)[0, :, :, 0]
+        np.testing.assert_allclose(got, expected, rtol=0, atol=1e-15)
+
+
+def test_rows_subset_matches_full():
+    x = pins.make("B", L=7, case_id=1900)
+    args = (x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"])
+    full = oracle.ref_fwd(*args, window=3)
+    rows = np.array([13, 0, 6, 7])
+    sub = oracle.ref_fwd(*args, window=3, rows=rows)
+    np.testing.assert_array_equal(sub, full.reshape(-1, *full.shape[2:])[rows])
+
+
+def test_rejects_bad_arguments():
+    x = pins.make("A", L=4)
+    with pytest.raises(ValueError):
+        oracle.ref_fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], window=-1)
+    with pytest.raises(ValueError):
+        oracle.ref_fwd(x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"], window=0,
+                       rows=[8])
+    with pytest.raises(TypeError):
+        oracle.ref_fwd(x["q_sig"].astype(np.float64), x["q_noise"], x["k"], x["v"], x["lam"],
+                       x["gate"], window=0)
