@@ -1,0 +1,71 @@
+"""ctypes loader of libgda.so (the C ABI declared in include/gda.h).
+
+Argument marshalling only. Loading fails loudly if the library has not been
+built: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgda.so")
+
+GDA_SUCCESS, GDA_ERROR_INVALID_ARGUMENT, GDA_ERROR_UNSUPPORTED, GDA_ERROR_HIP = range(4)
+GDA_BF16, GDA_F32 = 0, 1
+
+EXPORTED = ("gda_fwd", "gda_decode", "gda_status_string", "gda_last_error")
+
+_lib = None
+
+
+class GdaError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}" if detail else name)
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libgda.so is not built ({LIB_PATH} missing); run "
+            "`python -m attention_gda_fwd_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.gda_fwd.restype = i32
+    lib.gda_fwd.argtypes = [vp] * 7 + [i32] * 8 + [i32, vp]
+    lib.gda_decode.restype = i32
+    lib.gda_decode.argtypes = [vp] * 8 + [i32] * 8 + [i32, vp]
+    lib.gda_status_string.restype = ctypes.c_char_p
+    lib.gda_status_string.argtypes = [i32]
+    lib.gda_last_error.restype = ctypes.c_char_p
+    lib.gda_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != GDA_SUCCESS:
+        lib = load()
+        name = lib.gda_status_string(status).decode()
+        detail = lib.gda_last_error().decode()
+        raise GdaError(status, name, detail)
+
+
+def fwd_raw(q_sig, q_noise, k, v, lam, gate, out, B, L, S, N, Hkv, dqk, dv, window, dtype,
+            stream) -> int:
+    """Direct call of gda_fwd with integer pointers; returns the status code."""
+    return load().gda_fwd(q_sig, q_noise, k, v, lam, gate, out, B, L, S, N, Hkv, dqk, dv,
+                          window, dtype, stream)
+
+
+def decode_raw(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax, S, N, Hkv,
+               dqk, dv, window, dtype, stream) -> int:
+    """Direct call of gda_decode with integer pointers; returns the status code."""
+    return load().gda_decode(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax,
+                             S, N, Hkv, dqk, dv, window, dtype, stream)

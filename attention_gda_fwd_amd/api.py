@@ -1,0 +1,99 @@
+"""PyTorch front end of libgda: tensors in, tensors out, same names as the C ABI.
+
+PyTorch only provides device memory and the stream. Every step of the
+computation runs in the HIP kernels behind ``gda_fwd`` / ``gda_decode``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.GDA_BF16, torch.float32: _lib.GDA_F32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"gda: dtype must be bfloat16 or float32, got {t.dtype}") from None
+
+
+def _check(name: str, t: torch.Tensor, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"gda: {name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"gda: {name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"gda: {name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"gda: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"gda: {name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gda_fwd(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            lam: torch.Tensor, gate: torch.Tensor, window: int = 0,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Prefill. q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk], v [B,L,Hkv,dv],
+    lam [B,L,S], gate [B,L,S,dv] -> out [B,L,S,dv] = gate*(H_S - lam*Repeat_g(H_N))."""
+    if q_sig.dim() != 4 or q_noise.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("gda_fwd: q_sig, q_noise, k, v must be 4-D")
+    B, L, S, dqk = q_sig.shape
+    N, Hkv, dv = q_noise.shape[2], k.shape[2], v.shape[3]
+    dev, dt = q_sig.device, q_sig.dtype
+    code = _dtype_code(q_sig)
+    if dev.type != "cuda":
+        raise ValueError("gda_fwd: tensors must be on a HIP (cuda) device")
+    _check("q_sig", q_sig, (B, L, S, dqk), dt, dev)
+    _check("q_noise", q_noise, (B, L, N, dqk), dt, dev)
+    _check("k", k, (B, L, Hkv, dqk), dt, dev)
+    _check("v", v, (B, L, Hkv, dv), dt, dev)
+    _check("lam", lam, (B, L, S), dt, dev)
+    _check("gate", gate, (B, L, S, dv), dt, dev)
+    if out is None:
+        out = torch.empty((B, L, S, dv), dtype=dt, device=dev)
+    _check("out", out, (B, L, S, dv), dt, dev)
+    _lib.check(_lib.fwd_raw(q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            lam.data_ptr(), gate.data_ptr(), out.data_ptr(), B, L, S, N, Hkv,
+                            dqk, dv, int(window), code, _stream(dev)))
+    return out
+
+
+def gda_decode(q_sig: torch.Tensor, q_noise: torch.Tensor, k_cache: torch.Tensor,
+               v_cache: torch.Tensor, lam: torch.Tensor, gate: torch.Tensor,
+               cache_lens: torch.Tensor | None = None, window: int = 0,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode. q_sig [B,S,dqk], q_noise [B,N,dqk], k_cache [B,Lmax,Hkv,dqk],
+    v_cache [B,Lmax,Hkv,dv], lam [B,S], gate [B,S,dv], cache_lens int32 [B] on the
+    device (or None = Lmax) -> out [B,S,dv]."""
+    if q_sig.dim() != 3 or q_noise.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("gda_decode: q_sig/q_noise must be 3-D and the caches 4-D")
+    B, S, dqk = q_sig.shape
+    N, Lmax, Hkv, dv = q_noise.shape[1], k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    dev, dt = q_sig.device, q_sig.dtype
+    code = _dtype_code(q_sig)
+    if dev.type != "cuda":
+        raise ValueError("gda_decode: tensors must be on a HIP (cuda) device")
+    _check("q_sig", q_sig, (B, S, dqk), dt, dev)
+    _check("q_noise", q_noise, (B, N, dqk), dt, dev)
+    _check("k_cache", k_cache, (B, Lmax, Hkv, dqk), dt, dev)
+    _check("v_cache", v_cache, (B, Lmax, Hkv, dv), dt, dev)
+    _check("lam", lam, (B, S), dt, dev)
+    _check("gate", gate, (B, S, dv), dt, dev)
+    lens_ptr = None
+    if cache_lens is not None:
+        _check("cache_lens", cache_lens, (B,), torch.int32, dev)
+        lens_ptr = cache_lens.data_ptr()
+    if out is None:
+        out = torch.empty((B, S, dv), dtype=dt, device=dev)
+    _check("out", out, (B, S, dv), dt, dev)
+    _lib.check(_lib.decode_raw(q_sig.data_ptr(), q_noise.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), lens_ptr, lam.data_ptr(), gate.data_ptr(),
+                               out.data_ptr(), B, Lmax, S, N, Hkv, dqk, dv, int(window), code,
+                               _stream(dev)))
+    return out

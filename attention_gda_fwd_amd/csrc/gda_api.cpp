@@ -1,0 +1,180 @@
+// gda_api.cpp - host side of libgda: argument validation, head grouping, dispatch.
+//
+// Every argument is checked before the first HIP call, so a rejected call
+// launches nothing and does not touch the device. No device memory is
+// allocated and nothing is synchronised: kernels are enqueued on the caller's
+// stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+
+#include "../../include/gda.h"
+#include "gda_kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+gda_status fail(gda_status st, const char* msg) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+  return st;
+}
+
+// Heads of one batch row grouped into units (the head maps of the Motif 3
+// walk-through's GDLA forward, step 2, as read here: signal head i reads KV head
+// floor(i*Hkv/S), noise head j reads KV head floor(j*Hkv/N), noise head j
+// serves signal heads g*j .. g*j+g-1, g = S/N):
+//  * Hkv >= N: unit j = noise head j, its g signal heads and KV heads
+//    j*R .. j*R+R-1 (R = Hkv/N); phase p attends KV head j*R+p with the
+//    NS = S/Hkv signal heads reading it, and phase 0 also with noise head j;
+//  * N > Hkv: unit h = KV head h with its NS = S/Hkv signal heads and
+//    NN = N/Hkv noise heads (one phase).
+gda::UnitPlan make_plan(int S, int N, int Hkv) {
+  gda::UnitPlan p;
+  p.NS = S / Hkv;
+  if (Hkv >= N) {
+    p.units = N;
+    p.NN = 1;
+    p.R = Hkv / N;
+  } else {
+    p.units = Hkv;
+    p.NN = N / Hkv;
+    p.R = 1;
+  }
+  return p;
+}
+
+gda_status validate_common(int B, int L, int S, int N, int Hkv, int dqk, int dv, int window,
+                           gda_dtype dtype) {
+  if (B < 1 || L < 1 || S < 1 || N < 1 || Hkv < 1 || dqk < 1 || dv < 1)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "every size must be >= 1");
+  if (window < 0) return fail(GDA_ERROR_INVALID_ARGUMENT, "window must be >= 0");
+  if (S % N != 0) return fail(GDA_ERROR_INVALID_ARGUMENT, "S must be a multiple of N");
+  if (S % Hkv != 0) return fail(GDA_ERROR_INVALID_ARGUMENT, "S must be a multiple of Hkv");
+  if (N % Hkv != 0 && Hkv % N != 0)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "one of N, Hkv must divide the other");
+  if (dtype != GDA_BF16 && dtype != GDA_F32)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "unknown dtype");
+  return GDA_SUCCESS;
+}
+
+gda_status check_bf16_dims(int dqk, int dv) {
+  const bool ok = (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+  if (!ok) return fail(GDA_ERROR_UNSUPPORTED, "bf16 needs (dqk, dv) in {(64,64), (128,128), (192,128)}");
+  return GDA_SUCCESS;
+}
+
+gda_status from_hip(hipError_t e) {
+  if (e == hipSuccess) {
+    g_last_error[0] = '\0';
+    return GDA_SUCCESS;
+  }
+  if (e == (hipError_t)-1) return fail(GDA_ERROR_UNSUPPORTED, "no compiled kernel instance");
+  return fail(GDA_ERROR_HIP, hipGetErrorString(e));
+}
+
+// A device must exist before launching; hipGetDeviceCount is the first HIP call
+// of a valid request.
+gda_status require_device() {
+  int n = 0;
+  const hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n < 1) return fail(GDA_ERROR_HIP, "no HIP device available");
+  return GDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                   const void* lambda, const void* gate, void* out, int B, int L, int S, int N,
+                   int Hkv, int dqk, int dv, int window, gda_dtype dtype, void* stream) {
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
+  gda_status st = validate_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  gda::FwdArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.gate = gate;
+  a.out = out;
+  a.B = B;
+  a.L = L;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  a.plan = make_plan(S, N, Hkv);
+  a.scale = (float)(1.0 / std::sqrt((double)dqk));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dqk));
+  if (dtype == GDA_BF16) {
+    if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+    if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
+      return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+  }
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == GDA_BF16 ? gda::launch_fwd_bf16(a, s) : gda::launch_fwd_f32(a, s));
+}
+
+gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cache,
+                      const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                      const void* gate, void* out, int B, int Lmax, int S, int N, int Hkv,
+                      int dqk, int dv, int window, gda_dtype dtype, void* stream) {
+  if (!q_sig || !q_noise || !k_cache || !v_cache || !lambda || !gate || !out)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
+  gda_status st = validate_common(B, Lmax, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  gda::DecodeArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.lens = cache_lens;
+  a.lam = lambda;
+  a.gate = gate;
+  a.out = out;
+  a.B = B;
+  a.Lmax = Lmax;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  a.plan = make_plan(S, N, Hkv);
+  a.scale = (float)(1.0 / std::sqrt((double)dqk));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dqk));
+  if (dtype == GDA_BF16) {
+    if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+    if (!gda::decode_bf16_supported(dqk, dv, a.plan))
+      return fail(GDA_ERROR_UNSUPPORTED, "bf16 decode: more than 16 query heads per unit");
+  }
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == GDA_BF16 ? gda::launch_decode_bf16(a, s) : gda::launch_decode_f32(a, s));
+}
+
+const char* gda_status_string(gda_status s) {
+  switch (s) {
+    case GDA_SUCCESS:
+      return "GDA_SUCCESS";
+    case GDA_ERROR_INVALID_ARGUMENT:
+      return "GDA_ERROR_INVALID_ARGUMENT";
+    case GDA_ERROR_UNSUPPORTED:
+      return "GDA_ERROR_UNSUPPORTED";
+    case GDA_ERROR_HIP:
+      return "GDA_ERROR_HIP";
+  }
+  return "GDA_UNKNOWN_STATUS";
+}
+
+const char* gda_last_error(void) { return g_last_error; }
+
+}  // extern "C"

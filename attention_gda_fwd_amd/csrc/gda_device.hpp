@@ -1,0 +1,79 @@
+// gda_device.hpp - gfx950 device helpers shared by the libgda kernels.
+//
+// Lane layouts below were checked on gfx950 hardware:
+//  * v_mfma_f32_16x16x32_bf16 (D[16x16] += A[16x32] B[32x16]): lane l holds
+//    A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16], D[4*(l/16) .. +4][l%16].
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element
+//    i%4 of the 4-element row addressed by lane 4*j + i/4, for j = 0..3. So if
+//    lanes 4j..4j+3 address the 16 consecutive columns c0..c0+15 of row r_j (4
+//    columns each), lane i receives column c0+i of rows r_0..r_3: a transposed
+//    read of a row-major tile.
+//  * v_permlane16_swap / v_permlane32_swap called with the same register twice
+//    return, in their two results, the values of lanes l and l^16 (l^32).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gda {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ floatx4 mfma_16x16x32(const bf16x8& a, const bf16x8& b,
+                                                  const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// max / sum of a value over lanes l, l^16, l^32, l^48 (the four lane groups that
+// hold one column of a 16x16 MFMA tile).
+__device__ __forceinline__ float col_max4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float col_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Read-only 16-byte global load.
+__device__ __forceinline__ u32x4 ld_g16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+
+__device__ __forceinline__ u32x2 ldg8(const void* p) { return *(const u32x2*)p; }
+
+}  // namespace gda

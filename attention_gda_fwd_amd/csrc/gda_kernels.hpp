@@ -1,0 +1,58 @@
+// gda_kernels.hpp - launch interface between the libgda host API and its kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gda {
+
+// How the heads of one batch row are grouped into units (see gda_api.cpp):
+// a unit is R KV heads u*R .. u*R+R-1; phase p of the unit attends over KV head
+// u*R+p with NS signal heads (and, in phase 0, NN noise heads).
+struct UnitPlan {
+  int units;  // units per batch row
+  int NS;     // signal heads per phase
+  int NN;     // noise heads (all in phase 0)
+  int R;      // phases (KV heads) per unit
+};
+
+struct FwdArgs {
+  const void* q_sig;
+  const void* q_noise;
+  const void* k;
+  const void* v;
+  const void* lam;
+  const void* gate;
+  void* out;
+  int B, L, S, N, Hkv, dqk, dv, window;
+  UnitPlan plan;
+  float scale_log2;  // log2(e) / sqrt(dqk)
+  float scale;       // 1 / sqrt(dqk)
+};
+
+struct DecodeArgs {
+  const void* q_sig;
+  const void* q_noise;
+  const void* k;
+  const void* v;
+  const int32_t* lens;
+  const void* lam;
+  const void* gate;
+  void* out;
+  int B, Lmax, S, N, Hkv, dqk, dv, window;
+  UnitPlan plan;
+  float scale_log2;
+  float scale;
+};
+
+// Each returns hipSuccess or the launch error; -1 cast to hipError_t means no
+// compiled instance matches (the host API checks support first).
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+
+bool fwd_bf16_supported(int dqk, int dv, const UnitPlan& plan);
+bool decode_bf16_supported(int dqk, int dv, const UnitPlan& plan);
+
+}  // namespace gda

@@ -1,0 +1,263 @@
+"""Benchmark of the GDA/GDLA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  * gda_fwd on the Motif 3 full-attention layer (B=2, L=8192, 64 signal + 16 noise
+    query heads over 16 KV heads, dqk=192, dv=128, causal), and
+  * gda_decode on the Motif 3 decode step (B=64 sequences, 32768-token cache,
+    same heads, full causal).
+The headline ``value`` is the prefill's attention TFLOP/s, FLOPs counted as
+2*(dqk+dv) per visible (query, key) pair per query head (signal + noise); the
+decode's HBM GB/s is reported beside it. Inputs are resident in HBM before the
+timed region; times come from HIP events on the stream the kernels run on.
+A breakdown times every other workload (Motif-2 layer, sliding window W=128,
+W=128 decode) outside the step. The CPU baseline is the fp64 oracle timed on a
+bounded sample of the prefill rows. Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--breakdown-reps", type=int, default=20)
+    p.add_argument("--cpu-rows", type=int, default=512,
+                   help="prefill rows of the CPU-baseline sample")
+    return p.parse_args()
+
+
+def host_threads() -> int:
+    """Host threads this process may use (OMP_NUM_THREADS if set, else its CPU affinity)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
+def fill_fwd(cfg, torch, gin):
+    """Device tensors of a prefill workload, generated per batch row on the host."""
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    shapes = dict(q_sig=(cfg.L, cfg.S, cfg.dqk), q_noise=(cfg.L, cfg.N, cfg.dqk),
+                  k=(cfg.L, cfg.Hkv, cfg.dqk), v=(cfg.L, cfg.Hkv, cfg.dv), lam=(cfg.L, cfg.S),
+                  gate=(cfg.L, cfg.S, cfg.dv))
+    dev = {k: torch.empty((cfg.B,) + s, dtype=dt, device="cuda") for k, s in shapes.items()}
+    host0 = None
+    for b in range(cfg.B):
+        row = gin.fwd_row(cfg.case_id, b, L=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk,
+                          dv=cfg.dv, dtype=cfg.dtype, rope_dims=cfg.rope_dims)
+        for k, v in row.items():
+            t = torch.from_numpy(v)
+            dev[k][b].copy_(t.view(torch.bfloat16) if cfg.dtype == "bf16" else t)
+        if b == 0:
+            host0 = row
+    return dev, host0
+
+
+def fill_decode(cfg, torch, gin):
+    shapes = dict(q_sig=(cfg.B, cfg.S, cfg.dqk), q_noise=(cfg.B, cfg.N, cfg.dqk),
+                  k_cache=(cfg.B, cfg.L, cfg.Hkv, cfg.dqk), v_cache=(cfg.B, cfg.L, cfg.Hkv, cfg.dv),
+                  lam=(cfg.B, cfg.S), gate=(cfg.B, cfg.S, cfg.dv))
+    dev = {k: torch.empty(s, dtype=torch.bfloat16, device="cuda") for k, s in shapes.items()}
+    shp = dict(Lmax=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk, dv=cfg.dv,
+               dtype=cfg.dtype, rope_dims=cfg.rope_dims)
+    with ThreadPoolExecutor(host_threads()) as ex:
+        for b0 in range(0, cfg.B, 8):
+            rows = list(ex.map(lambda b: gin.decode_row(cfg.case_id, b, **shp),
+                               range(b0, min(b0 + 8, cfg.B))))
+            for b, row in zip(range(b0, b0 + len(rows)), rows):
+                for k, v in row.items():
+                    dev[k][b].copy_(torch.from_numpy(v).view(torch.bfloat16))
+    return dev
+
+
+def event_times(torch, fn, reps, warmup):
+    """Per-launch milliseconds, HIP events on the current stream around each launch."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def main():
+    args = parse()
+    os.environ.setdefault("OMP_NUM_THREADS", str(host_threads()))
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (batch, unit) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    from attention_gda_fwd_amd import configs as C
+    from attention_gda_fwd_amd import inputs as gin
+    from attention_gda_fwd_amd.api import gda_decode, gda_fwd
+
+    torch.cuda.set_device(0)
+    fwd_cfg, dec_cfg = C.CFG2, C.CFG4
+    log(f"generating {fwd_cfg.name}")
+    fdev, fhost0 = fill_fwd(fwd_cfg, torch, gin)
+    log(f"generating {dec_cfg.name} (21.5 GB cache)")
+    ddev = fill_decode(dec_cfg, torch, gin)
+    fout = torch.empty(fwd_cfg.B, fwd_cfg.L, fwd_cfg.S, fwd_cfg.dv, dtype=torch.bfloat16,
+                       device="cuda")
+    dout = torch.empty(dec_cfg.B, dec_cfg.S, dec_cfg.dv, dtype=torch.bfloat16, device="cuda")
+
+    def run_fwd():
+        gda_fwd(fdev["q_sig"], fdev["q_noise"], fdev["k"], fdev["v"], fdev["lam"], fdev["gate"],
+                window=fwd_cfg.window, out=fout)
+
+    def run_dec(window=0):
+        gda_decode(ddev["q_sig"], ddev["q_noise"], ddev["k_cache"], ddev["v_cache"],
+                   ddev["lam"], ddev["gate"], window=window, out=dout)
+
+    # ---- timed steps: warmup, barrier + sync, K steps, sync -------------------------
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        run_fwd()
+        run_dec()
+    torch.cuda.synchronize()
+    fwd_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fwd_ev[i][0].record()
+        run_fwd()
+        fwd_ev[i][1].record()
+        dec_ev[i][0].record()
+        run_dec()
+        dec_ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [a.elapsed_time(b) for a, b in fwd_ev]
+    dec_ms = [a.elapsed_time(b) for a, b in dec_ev]
+    f_avg = sum(fwd_ms) / len(fwd_ms)
+    d_avg = sum(dec_ms) / len(dec_ms)
+    f_flops = fwd_cfg.flops()
+    f_tflops = f_flops / (f_avg * 1e-3) / 1e12
+    d_bytes = dec_cfg.algorithmic_bytes()
+    d_gbps = d_bytes / (d_avg * 1e-3) / 1e9
+    log(f"prefill {f_avg:.3f} ms = {f_tflops:.1f} TFLOP/s; decode {d_avg:.3f} ms = {d_gbps:.0f} GB/s")
+
+    # ---- sampled parity of the timed outputs ----------------------------------------
+    rows = np.linspace(0, fwd_cfg.L - 1, args.cpu_rows).astype(np.int64)
+    rows = np.unique(np.concatenate([rows, [0, 63, 64, fwd_cfg.L - 1]]))
+    got = fout[0, torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+
+    # ---- CPU baseline: the oracle on a bounded sample of the prefill rows -------------
+    one = {k: v[None] for k, v in fhost0.items()}
+    threads = host_threads()
+    log(f"oracle on {rows.size} prefill rows ({threads} threads)")
+    t1 = time.perf_counter()
+    ref = oracle.ref_fwd(one["q_sig"], one["q_noise"], one["k"], one["v"], one["lam"],
+                         one["gate"], window=fwd_cfg.window, rows=rows)
+    cpu_s = time.perf_counter() - t1
+    cpu_flops = sum(2 * (fwd_cfg.dqk + fwd_cfg.dv) * (int(t) + 1) * (fwd_cfg.S + fwd_cfg.N)
+                    for t in rows)
+    err = np.abs(got - ref)
+    log(f"oracle {cpu_s:.1f} s; sampled parity max|err| {err.max():.3e} mean {err.mean():.3e}")
+
+    # ---- breakdown: every other workload, timed on its own ----------------------------
+    breakdown = {}
+
+    def record(cfg, ms, extra=None):
+        med = float(np.median(ms))
+        fl, by = cfg.flops(), cfg.algorithmic_bytes()
+        d = dict(median_ms=round(med, 4), min_ms=round(min(ms), 4),
+                 tflops=round(fl / (med * 1e-3) / 1e12, 2),
+                 gbps=round(by / (med * 1e-3) / 1e9, 1),
+                 tokens_per_s=round(cfg.tokens() / (med * 1e-3), 1),
+                 mfma_frac=round(fl / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 hbm_frac=round(by / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+        if extra:
+            d.update(extra)
+        breakdown[cfg.name] = d
+
+    record(fwd_cfg, fwd_ms)
+    record(dec_cfg, dec_ms)
+    reps = args.breakdown_reps
+    record(C.CFG4W, event_times(torch, lambda: run_dec(128), reps, 5))
+    del ddev
+    torch.cuda.empty_cache()
+    for cfg in (C.CFG1, C.CFG3, C.CFG0):
+        log(f"breakdown {cfg.name}")
+        dev, _ = fill_fwd(cfg, torch, gin)
+        o = torch.empty_like(dev["gate"])
+        ms = event_times(torch, lambda: gda_fwd(dev["q_sig"], dev["q_noise"], dev["k"], dev["v"],
+                                                dev["lam"], dev["gate"], window=cfg.window,
+                                                out=o), reps, 5)
+        record(cfg, ms)
+        del dev, o
+        torch.cuda.empty_cache()
+
+    result = {
+        "metric": "GDA fwd TFLOP/s (% bf16 MFMA peak) + decode HBM GB/s, 1xMI355X",
+        "value": round(f_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q/K/V (shared 64 rotary key dims), sigmoid(N(0,1)) "
+                "lambda and gate, resident in HBM",
+        "config": {"workload": "gda_fwd Motif-3 full layer B=2 L=8192 S=64 N=16 Hkv=16 "
+                               "dqk=192 dv=128 causal + gda_decode B=64 Lk=32768 same heads",
+                   "prefill": fwd_cfg.name, "decode": dec_cfg.name, "parallelism": "none"},
+        "decode_gbps": round(d_gbps, 1),
+        "decode_hbm_frac": round(d_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(f_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(f_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "fwd_bf16_kernel<192,128,4,1,1>",
+                     "flops_per_launch": f_flops, "avg_launch_ms": round(f_avg, 4)},
+        "decode_roofline": {"bound": "hbm", "achieved": round(d_gbps, 1), "peak": PEAK_HBM_GBPS,
+                            "unit": "GB/s", "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
+                            "traffic": None, "kernel": "decode_bf16_kernel<192,128>",
+                            "bytes_per_launch": d_bytes, "avg_launch_ms": round(d_avg, 4)},
+        "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+                         "cores": threads, "kind": "oracle",
+                         "sample": f"{rows.size} query rows of batch row 0 of the prefill "
+                                   f"workload (all 64 signal + 16 noise heads), "
+                                   f"{cpu_flops / 1e9:.1f} GFLOP in {cpu_s:.1f} s"},
+        "parity_sampled": {"rows": int(rows.size), "max_abs": float(err.max()),
+                           "mean_abs": float(err.mean())},
+        "breakdown": breakdown,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,103 @@
+/* gda.h - C ABI of libgda: the Grouped Differential (Latent) Attention forward on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operation (Motif 3 technical-report walk-through, paper.rainbus.top, step 2
+ * "GDLA forward", equation D_t; head split of the Motif-2-12.7B overview,
+ * section 2.2, and the Motif 3 release post, architecture paragraph):
+ *
+ *   signal heads i < S and noise heads j < N attend over the same expanded KV
+ *   heads h < Hkv, each path with its own softmax attention
+ *       H_x[t] = sum_{s visible from t} softmax_s(q_x[t] . k[s] / sqrt(dqk)) v[s]
+ *   signal head i reads KV head floor(i*Hkv/S), noise head j reads KV head
+ *   floor(j*Hkv/N); noise head j is repeated onto signal heads g*j .. g*j+g-1
+ *   (g = S/N), and
+ *       out[t,i,:] = gate[t,i,:] * (H_S[t,i,:] - lambda[t,i] * H_N[t,floor(i/g),:]).
+ *   Key s is visible from query t iff s <= t and (window == 0 or t-s <= window-1).
+ *   lambda and gate are values in (0,1) (the sigmoid that produces them is
+ *   upstream of this call). W^O is not applied.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensors are dense, row-major, innermost dimension contiguous, device
+ *     memory, 16-byte aligned, of the element type `dtype` (all share it).
+ *   - Ownership: the caller owns every buffer. The library allocates no device
+ *     memory and keeps no mutable global state (only a thread-local diagnostic
+ *     string); calls are thread-safe. `out` must not alias an input.
+ *   - Asynchrony: a call enqueues its kernels on `stream` (a hipStream_t; NULL
+ *     is the default stream) and returns without synchronizing.
+ *   - Errors: arguments are validated on the host before any HIP call; a
+ *     rejected call launches nothing and returns GDA_ERROR_INVALID_ARGUMENT or
+ *     GDA_ERROR_UNSUPPORTED. A HIP failure (including "no device") returns
+ *     GDA_ERROR_HIP. Nothing is thrown or aborted across the ABI.
+ *   - Offsets are 64-bit: a tensor may hold more than 2^31 elements.
+ *   - Results are bitwise reproducible run to run for identical inputs.
+ */
+#ifndef GDA_H
+#define GDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDA_SUCCESS = 0,
+  GDA_ERROR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, window < 0, head counts that
+                                     do not divide, unknown dtype                         */
+  GDA_ERROR_UNSUPPORTED = 2,      /* valid but not compiled: (dqk, dv) or head layout      */
+  GDA_ERROR_HIP = 3               /* a HIP runtime or launch failure                       */
+} gda_status;
+
+typedef enum { GDA_BF16 = 0, GDA_F32 = 1 } gda_dtype;
+
+/* Prefill (every query position of each sequence).
+ *   q_sig   [B, L, S,   dqk]      signal queries
+ *   q_noise [B, L, N,   dqk]      noise queries
+ *   k       [B, L, Hkv, dqk]      expanded keys (post-RoPE)
+ *   v       [B, L, Hkv, dv ]      expanded values
+ *   lambda  [B, L, S]             per-token, per-signal-head noise coefficient
+ *   gate    [B, L, S,   dv ]      output gate values
+ *   out     [B, L, S,   dv ]      written: gate * (H_S - lambda * Repeat_g(H_N))
+ * Requirements: all sizes >= 1; S % N == 0; S % Hkv == 0; N % Hkv == 0 or
+ * Hkv % N == 0; window >= 0 (0 = full causal, W >= 1 = keys t-W+1 .. t).
+ * GDA_BF16 needs (dqk, dv) in {(64,64), (128,128), (192,128)} and a head layout
+ * with N <= Hkv and (S/Hkv, Hkv/N) in {(1,1), (2,1), (4,1), (1,2), (2,2)}
+ * (returns GDA_ERROR_UNSUPPORTED otherwise). GDA_F32 takes any sizes and layout.
+ * Accumulation is fp32 in both dtypes; bf16 outputs are rounded to nearest even. */
+gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                   const void* lambda, const void* gate, void* out,
+                   int B, int L, int S, int N, int Hkv, int dqk, int dv,
+                   int window, gda_dtype dtype, void* stream);
+
+/* Decode: one new query token per sequence, attending over a KV cache that
+ * already holds that token's K/V at position cache_lens[b]-1.
+ *   q_sig   [B, S,   dqk]
+ *   q_noise [B, N,   dqk]
+ *   k_cache [B, Lmax, Hkv, dqk]
+ *   v_cache [B, Lmax, Hkv, dv ]
+ *   cache_lens  device int32 [B], or NULL for "every sequence holds Lmax tokens".
+ *               A length above Lmax is clamped to Lmax; a length below 1 yields
+ *               an all-zero output row (there is no key to attend to).
+ *   lambda  [B, S]
+ *   gate    [B, S, dv]
+ *   out     [B, S, dv]
+ * Same requirements as gda_fwd, plus Lmax >= 1. GDA_BF16 needs the same
+ * (dqk, dv) set and at most 16 query heads per unit (S/Hkv signal heads plus
+ * max(1, N/Hkv) noise heads). */
+gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cache,
+                      const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                      const void* gate, void* out,
+                      int B, int Lmax, int S, int N, int Hkv, int dqk, int dv,
+                      int window, gda_dtype dtype, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* gda_status_string(gda_status s);
+
+/* Static text of the last validation or HIP error seen on the calling thread
+ * ("" if none). Meant for diagnostics; not needed to use the library. */
+const char* gda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,116 @@
+"""The C ABI of libgda without a GPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call (so no pointer is ever
+dereferenced here; the pointers below are never valid device memory)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_gda_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # non-null, never dereferenced: every call below fails validation first
+BF16, F32 = _lib.GDA_BF16, _lib.GDA_F32
+INVALID, UNSUPPORTED, HIPERR = (_lib.GDA_ERROR_INVALID_ARGUMENT, _lib.GDA_ERROR_UNSUPPORTED,
+                                _lib.GDA_ERROR_HIP)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "gda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gda_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = _lib.load()
+    assert lib.gda_status_string(0) == b"GDA_SUCCESS"
+    assert lib.gda_status_string(1) == b"GDA_ERROR_INVALID_ARGUMENT"
+    assert lib.gda_status_string(2) == b"GDA_ERROR_UNSUPPORTED"
+    assert lib.gda_status_string(3) == b"GDA_ERROR_HIP"
+    assert lib.gda_status_string(77) == b"GDA_UNKNOWN_STATUS"
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, out=FAKE, B=1, L=64, S=8,
+             N=2, Hkv=2, dqk=64, dv=64, window=0, dtype=BF16, stream=None)
+    a.update(kw)
+    return _lib.fwd_raw(a["q"], a["qn"], a["k"], a["v"], a["lam"], a["gate"], a["out"], a["B"],
+                        a["L"], a["S"], a["N"], a["Hkv"], a["dqk"], a["dv"], a["window"],
+                        a["dtype"], a["stream"])
+
+
+def dec(**kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lens=None, lam=FAKE, gate=FAKE, out=FAKE, B=1,
+             Lmax=64, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0, dtype=BF16, stream=None)
+    a.update(kw)
+    return _lib.decode_raw(a["q"], a["qn"], a["k"], a["v"], a["lens"], a["lam"], a["gate"],
+                           a["out"], a["B"], a["Lmax"], a["S"], a["N"], a["Hkv"], a["dqk"],
+                           a["dv"], a["window"], a["dtype"], a["stream"])
+
+
+INVALID_CASES = [
+    dict(q=None), dict(qn=None), dict(k=None), dict(v=None), dict(lam=None), dict(gate=None),
+    dict(out=None), dict(B=0), dict(S=0), dict(N=0), dict(Hkv=0), dict(dqk=0), dict(dv=0),
+    dict(B=-1), dict(window=-1), dict(S=8, N=3), dict(S=6, N=2, Hkv=4),
+    dict(S=24, N=6, Hkv=4), dict(dtype=7),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID_CASES, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_fwd_invalid_arguments(kw):
+    assert fwd(**kw) == INVALID
+    assert _lib.load().gda_last_error() != b""
+
+
+@pytest.mark.parametrize("kw", INVALID_CASES + [dict(Lmax=0)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_decode_invalid_arguments(kw):
+    if "L" in kw:
+        kw = dict(kw, Lmax=kw.pop("L"))
+    assert dec(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(dqk=96, dv=96), dict(dqk=192, dv=192), dict(dqk=128, dv=64),
+                                dict(S=16, N=2, Hkv=2),        # 8 signal heads per KV head
+                                dict(S=16, N=4, Hkv=2),        # N > Hkv
+                                dict(S=16, N=2, Hkv=8)])       # Hkv/N = 4
+def test_fwd_bf16_unsupported(kw):
+    assert fwd(**kw) == UNSUPPORTED
+
+
+def test_decode_bf16_unsupported():
+    assert dec(dqk=96, dv=96) == UNSUPPORTED
+    assert dec(S=64, N=2, Hkv=2) == UNSUPPORTED  # 32 signal + 1 noise heads per unit
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
+def test_valid_call_without_device_returns_hip_error():
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: a valid call would launch on the fake pointers")
+    assert fwd() == HIPERR
+    assert fwd(dtype=F32, dqk=96, dv=80, S=12, N=4, Hkv=2) == HIPERR  # f32 takes any layout
+    assert dec() == HIPERR
+    assert b"device" in _lib.load().gda_last_error()
+
+
+def test_python_front_end_checks_before_calling():
+    import torch
+    from attention_gda_fwd_amd import api
+    x = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # CPU tensors are refused before the C call
+        api.gda_fwd(x, x[:, :, :2], x[:, :, :2], x[:, :, :2], x[..., 0], x)
+    with pytest.raises(TypeError):
+        api.gda_fwd(x.half(), x, x, x, x[..., 0], x)

@@ -1,0 +1,144 @@
+"""GPU parity: libgda (through its C ABI) against the fp64 oracle on the same seeded inputs.
+
+* Full outputs at sizes the oracle finishes in seconds, with every workload's head
+  layout, several tiles and a ragged tail.
+* The full-size workloads as the bench runs them, on sampled output rows the
+  oracle computes one by one.
+Tolerances: bf16 max |err| <= 2e-2 and mean |err| <= 2e-3; fp32 max |err| <= 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_gda_fwd_amd import configs as C
+from attention_gda_fwd_amd import inputs as gin
+from attention_gda_fwd_amd.api import gda_decode
+
+from . import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # the fp32 workload itself, every output
+    "cfg0_f32_full": dict(case_id=0, B=1, L=256, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0,
+                          dtype="f32"),
+    "motif2_layout_L300": dict(case_id=101, B=1, L=300, S=32, N=8, Hkv=16, dqk=128, dv=128,
+                               window=0, dtype="bf16"),
+    "motif3_layout_B2_L200": dict(case_id=102, B=2, L=200, S=64, N=16, Hkv=16, dqk=192,
+                                  dv=128, window=0, dtype="bf16", rope_dims=64),
+    "motif3_swa128_L700": dict(case_id=103, B=1, L=700, S=64, N=16, Hkv=16, dqk=192, dv=128,
+                               window=128, dtype="bf16", rope_dims=64),
+    "tiny_layout_bf16_B2_L130": dict(case_id=104, B=2, L=130, S=8, N=2, Hkv=2, dqk=64, dv=64,
+                                     window=0, dtype="bf16"),
+    "motif2_layout_f32_L100": dict(case_id=105, B=1, L=100, S=32, N=8, Hkv=16, dqk=128, dv=128,
+                                   window=0, dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_full_output(name):
+    kw = SMALL[name]
+    U.log(f"parity {name} {kw}")
+    case = U.FwdCase(**kw)
+    got = U.to_f64(case.run_gpu())
+    torch.cuda.synchronize()
+    ref = case.run_oracle()
+    U.assert_close(got, ref, kw["dtype"], name)
+
+
+@pytest.mark.parametrize("cfg", [C.CFG1, C.CFG2, C.CFG3], ids=lambda c: c.name)
+def test_full_size_sampled_rows(cfg):
+    U.log(f"parity {cfg.name}: generating inputs")
+    case = U.FwdCase(cfg.case_id, B=cfg.B, L=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk,
+                     dv=cfg.dv, window=cfg.window, dtype=cfg.dtype, rope_dims=cfg.rope_dims)
+    U.log(f"parity {cfg.name}: running gda_fwd")
+    out = case.run_gpu()
+    torch.cuda.synchronize()
+    rows = U.sample_rows(cfg.B, cfg.L, seed=cfg.case_id)
+    got = U.to_f64(out.reshape(cfg.B * cfg.L, cfg.S, cfg.dv)[torch.from_numpy(rows).cuda()])
+    U.log(f"parity {cfg.name}: oracle on {rows.size} rows")
+    ref = case.run_oracle(rows=rows)
+    U.assert_close(got, ref, cfg.dtype, f"{cfg.name} sampled rows")
+
+
+def _decode_case(case_id, *, B, Lmax, S, N, Hkv, dqk, dv, dtype, rope_dims=0):
+    host = gin.decode_inputs(case_id, B=B, Lmax=Lmax, S=S, N=N, Hkv=Hkv, dqk=dqk, dv=dv,
+                             dtype=dtype, rope_dims=rope_dims)
+    return host, {k: U.to_dev(v, dtype) for k, v in host.items()}
+
+
+DEC_SMALL = {
+    "motif3_layout": dict(case_id=201, B=6, Lmax=300, S=64, N=16, Hkv=16, dqk=192, dv=128,
+                          dtype="bf16", rope_dims=64),
+    "motif2_layout": dict(case_id=202, B=6, Lmax=300, S=32, N=8, Hkv=16, dqk=128, dv=128,
+                          dtype="bf16"),
+    "tiny_layout_f32": dict(case_id=203, B=6, Lmax=300, S=8, N=2, Hkv=2, dqk=64, dv=64,
+                            dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("window", [0, 128, 1])
+@pytest.mark.parametrize("name", sorted(DEC_SMALL))
+def test_decode_small_ragged(name, window):
+    kw = DEC_SMALL[name]
+    U.log(f"decode parity {name} window={window}")
+    host, dev = _decode_case(**kw)
+    lens = np.array([300, 1, 77, 128, 129, 0], dtype=np.int32)
+    lens_d = torch.from_numpy(lens).cuda()
+    out = gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"], dev["lam"],
+                     dev["gate"], cache_lens=lens_d, window=window)
+    got = U.to_f64(out)
+    ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"], host["v_cache"],
+                            host["lam"], host["gate"], lens, window=window)
+    U.assert_close(got, ref, kw["dtype"], f"decode {name} W={window}")
+    assert np.all(got[5] == 0.0), "a sequence with no visible key must give zeros"
+    # NULL lens = every sequence holds Lmax tokens; lens above Lmax clamp to Lmax
+    out_full = U.to_f64(gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"],
+                                   dev["lam"], dev["gate"], window=window))
+    big = torch.full((kw["B"],), 10**6, dtype=torch.int32, device="cuda")
+    out_big = U.to_f64(gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"],
+                                  dev["lam"], dev["gate"], cache_lens=big, window=window))
+    assert np.array_equal(out_full, out_big)
+    np.testing.assert_array_equal(out_full[0], got[0])
+
+
+def test_decode_full_size_sampled_sequences():
+    """The full-cache decode (B=64, Lmax=32768, Motif 3 heads) at W=0 and W=128;
+    the oracle checks 4 sequences of each."""
+    cfg = C.CFG4
+    U.log("decode full size: generating the 21.5 GB cache sequence by sequence")
+    shp = dict(Lmax=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk, dv=cfg.dv,
+               dtype=cfg.dtype, rope_dims=cfg.rope_dims)
+    dev = dict(q_sig=torch.empty(cfg.B, cfg.S, cfg.dqk, dtype=torch.bfloat16, device="cuda"),
+               q_noise=torch.empty(cfg.B, cfg.N, cfg.dqk, dtype=torch.bfloat16, device="cuda"),
+               k_cache=torch.empty(cfg.B, cfg.L, cfg.Hkv, cfg.dqk, dtype=torch.bfloat16,
+                                   device="cuda"),
+               v_cache=torch.empty(cfg.B, cfg.L, cfg.Hkv, cfg.dv, dtype=torch.bfloat16,
+                                   device="cuda"),
+               lam=torch.empty(cfg.B, cfg.S, dtype=torch.bfloat16, device="cuda"),
+               gate=torch.empty(cfg.B, cfg.S, cfg.dv, dtype=torch.bfloat16, device="cuda"))
+    keep = {0, 1, 37, 63}
+    kept = {}
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        for b0 in range(0, cfg.B, 8):  # 8 sequences (2.7 GB of host memory) at a time
+            rows = list(ex.map(lambda b: gin.decode_row(cfg.case_id, b, **shp),
+                               range(b0, min(b0 + 8, cfg.B))))
+            for b, row in zip(range(b0, b0 + len(rows)), rows):
+                for k, v in row.items():
+                    dev[k][b].copy_(torch.from_numpy(v).view(torch.bfloat16))
+                if b in keep:
+                    kept[b] = row
+            U.log(f"  generated {b0 + len(rows)}/{cfg.B} sequences")
+    seqs = sorted(keep)
+    for window in (0, 128):
+        out = gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"],
+                         dev["lam"], dev["gate"], window=window)
+        got = U.to_f64(out[seqs])
+        stack = {k: np.stack([kept[b][k] for b in seqs]) for k in kept[seqs[0]]}
+        U.log(f"decode full size W={window}: oracle on sequences {seqs}")
+        ref = oracle.ref_decode(stack["q_sig"], stack["q_noise"], stack["k_cache"],
+                                stack["v_cache"], stack["lam"], stack["gate"], None,
+                                window=window)
+        U.assert_close(got, ref, "bf16", f"{cfg.name} W={window} sampled sequences")
