@@ -9,15 +9,24 @@
 // Work decomposition (MI355X-first; the pages give no kernel design):
 //  * a workgroup owns (batch row b, unit u, tile of 64 queries); a unit is the
 //    set of KV heads, signal heads and noise heads that the fused epilogue
-//    needs together, so the noise output never leaves registers;
-//  * 4 waves, each owning 16 queries for ALL heads of the current phase: every
-//    K/V tile staged in LDS is read once per wave and used by every head;
+//    needs together, so the noise output never goes to HBM;
+//  * 8 waves: wave w owns the 16 queries of group w%4; waves 0-3 ("A") compute
+//    the noise head and the first signal heads, waves 4-7 ("B") the other
+//    signal heads. Each SIMD then runs one A and one B wave over the same
+//    queries (2 waves per SIMD, each under 256 registers), so one wave's
+//    softmax overlaps the other's MFMAs, and the noise output goes from A to B
+//    through LDS once per tile of queries;
+//  * K/V tiles stream HBM -> LDS with global_load_lds (no VGPRs), double
+//    buffered: the next tile is in flight while the current one is consumed.
+//    K is stored fragment-major (each 1 KB block is exactly one MFMA A operand
+//    of 16 keys x 32 dims, read back with one conflict-free ds_read_b128); V is
+//    row-major with its 16-byte chunks XOR-swizzled by row so that the
+//    transposed reads (ds_read_b64_tr_b16) that build the V^T operand hit
+//    distinct banks;
 //  * scores are computed transposed, S^T = K . Q^T (16x16x32 bf16 MFMA, fp32
-//    accumulation), so a lane owns one query column: the online softmax row
-//    max/sum is in-lane plus two permlane swaps;
-//  * P^T in the accumulator layout is already the B operand of O^T = V^T . P^T;
-//    V stays row-major in LDS and its transposed A operand comes from
-//    ds_read_b64_tr_b16;
+//    accumulation), so a lane owns one query column: the online-softmax row
+//    max/sum is in-lane plus two permlane swaps, and P^T in the accumulator
+//    layout is already the B operand of O^T = V^T . P^T;
 //  * lambda and the gate are applied to the fp32 accumulators in registers and
 //    the result is rounded to bf16 once.
 #include "gda_device.hpp"
@@ -26,195 +35,199 @@
 namespace gda {
 namespace {
 
-constexpr int BM = 64;  // queries per workgroup: 4 waves x 16
-constexpr int BN = 64;  // keys per LDS tile
-constexpr int NT = 256;
+constexpr int BM = 64;  // queries per workgroup: 4 query groups x 16
+constexpr float kRescaleTau = 8.f;  // lazy rescale threshold, log2 units
+constexpr float kNoMax = -1e30f;    // finite "no key seen yet" reference
 
-template <int DQK, int DV>
-struct FwdTile {
-  static constexpr int KS = DQK / 32;  // MFMA k-steps of Q.K
-  static constexpr int DB = DV / 16;   // 16-wide blocks of the output channels
-  // Row pads: K rows 16 B longer so the 16 rows of one ds_read_b128 fall on
-  // distinct banks; V rows 32 B longer for the 16 rows of one transposed read.
-  static constexpr int KROW = DQK + 8;
-  static constexpr int VROW = DV + 16;
-  static constexpr int KCH = DQK / 8;  // 16-byte chunks per K row
-  static constexpr int VCH = DV / 8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// ASIG signal heads + the noise head run in the A waves, BSIG signal heads in the
+// B waves; with TWO_KV the B heads read the unit's second KV head.
+template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_>
+struct Cfg {
+  static constexpr int DQK = DQK_, DV = DV_, ASIG = ASIG_, BSIG = BSIG_;
+  static constexpr bool TWO_KV = TWO_KV_;
+  static constexpr int NA = ASIG + 1;               // heads of an A wave
+  static constexpr int NB = BSIG;                   // heads of a B wave
+  static constexpr int NW = BSIG > 0 ? 8 : 4;       // waves per workgroup
+  static constexpr int NT = NW * 64;
+  static constexpr int BN = (TWO_KV && DQK > 128) ? 32 : 64;  // keys per LDS tile
+  static constexpr int KS = DQK / 32;               // MFMA k-steps of Q.K
+  static constexpr int DB = DV / 16;                // 16-channel blocks of the output
+  static constexpr int KBLK = (BN / 16) * KS;       // 1 KB fragment blocks of a K tile
+  static constexpr int VBLK = (BN * DV * 2) / 1024; // 1 KB blocks of a V tile
+  static constexpr int NKV = TWO_KV ? 2 : 1;
+  static constexpr int TBLK = NKV * (KBLK + VBLK);  // 1 KB blocks per tile (all KV heads)
+  static constexpr int K_ELEMS = BN * DQK;
+  static constexpr int V_ELEMS = BN * DV;
+  static constexpr int VCH = DV / 8;                // 16-byte chunks per V row
+  static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
 };
 
-struct FwdCtx {
+struct Ctx {
   const uint16_t* kg;
   const uint16_t* vg;
-  int L, Hkv, window;
-  int b;
-  int q_lo, q_hi;  // the workgroup's query rows [q_lo, q_hi]
+  int L, Hkv, window, b;
+  int kvA, kvB;
+  int q_lo, q_hi;  // the workgroup's query rows
   int w_lo, w_hi;  // this wave's query rows (empty when w_lo > w_hi)
-  int t;           // this lane's query row (may be >= L: then unused)
-  int col, g4, tid;
+  int t;           // this lane's query row (>= L for padding lanes)
+  int lane, col, g4, wave;
   float c;  // log2(e)/sqrt(dqk)
 };
 
-// Stage keys [k0, k0+BN) of KV head kvh into LDS (rows past L are zero).
-template <int DQK, int DV>
-__device__ __forceinline__ void load_kv_tile(const FwdCtx& x, int kvh, int k0, uint16_t* sK,
-                                             uint16_t* sV) {
-  using T = FwdTile<DQK, DV>;
-#pragma unroll
-  for (int i = 0; i < (BN * T::KCH) / NT; ++i) {
-    const int c = x.tid + i * NT;
-    const int key = c / T::KCH, ch = c % T::KCH;
-    const int ka = k0 + key;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (ka < x.L) val = ldg16(x.kg + (((int64_t)x.b * x.L + ka) * x.Hkv + kvh) * DQK + ch * 8);
-    *(u32x4*)(sK + key * T::KROW + ch * 8) = val;
-  }
-#pragma unroll
-  for (int i = 0; i < (BN * T::VCH) / NT; ++i) {
-    const int c = x.tid + i * NT;
-    const int key = c / T::VCH, ch = c % T::VCH;
-    const int ka = k0 + key;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (ka < x.L) val = ldg16(x.vg + (((int64_t)x.b * x.L + ka) * x.Hkv + kvh) * DV + ch * 8);
-    *(u32x4*)(sV + key * T::VROW + ch * 8) = val;
+// Issue one 1 KB direct-to-LDS block of a tile (keys k0 .. k0+BN-1). Rows past
+// L read row L-1 (finite data; those keys are masked).
+template <class C>
+__device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint16_t* sK0,
+                                           uint16_t* sV0, uint16_t* sK1, uint16_t* sV1) {
+  constexpr int per = C::KBLK + C::VBLK;
+  const int kvi = (C::TWO_KV && blk >= per) ? 1 : 0;
+  const int bi = blk - kvi * per;
+  const int kvh = kvi ? x.kvB : x.kvA;
+  uint16_t* sK = kvi ? sK1 : sK0;
+  uint16_t* sV = kvi ? sV1 : sV0;
+  if (bi < C::KBLK) {
+    const int kb = bi / C::KS, ks = bi - (bi / C::KS) * C::KS;
+    const int key = min(k0 + 16 * kb + (x.lane & 15), x.L - 1);
+    const uint16_t* src =
+        x.kg + (((int64_t)x.b * x.L + key) * x.Hkv + kvh) * C::DQK + 32 * ks + 8 * (x.lane >> 4);
+    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(sK + bi * 512), 16, 0, 0);
+  } else {
+    const int vi = bi - C::KBLK;
+    const int r = C::VRPB * vi + x.lane / C::VCH;
+    const int p = x.lane % C::VCH;
+    const int cch = p ^ (r % C::VCH);
+    const int key = min(k0 + r, x.L - 1);
+    const uint16_t* src = x.vg + (((int64_t)x.b * x.L + key) * x.Hkv + kvh) * C::DV + 8 * cch;
+    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(sV + vi * 512), 16, 0, 0);
   }
 }
 
-// Lazy rescaling threshold (log2 units): a column's reference max is only
-// raised when a score exceeds it by more than this, so P <= 2^8 and the
-// accumulators are rarely rescaled. O/l does not depend on the reference.
-constexpr float kRescaleTau = 8.f;
-constexpr float kNoMax = -1e30f;  // finite "no key seen yet" reference
-
-// One phase: NH query heads (row pointers qp, already at this lane's query row)
-// attend over KV head kvh. On return o[h] holds the unnormalised O^T tile and
-// lsum[h] the full softmax denominator of this lane's query.
-template <int DQK, int DV, int NH>
-__device__ __forceinline__ void attend(const FwdCtx& x, const uint16_t* const (&qp)[NH], int kvh,
-                                       uint16_t* sK, uint16_t* sV,
-                                       floatx4 (&o)[NH][DV / 16], float (&lsum)[NH]) {
-  using T = FwdTile<DQK, DV>;
-  bf16x8 qf[NH][T::KS];
+// Every wave issues its share of the tile's 1 KB blocks.
+template <class C>
+__device__ __forceinline__ void issue_tile(const Ctx& x, int k0, uint16_t* sK0, uint16_t* sV0,
+                                           uint16_t* sK1, uint16_t* sV1) {
 #pragma unroll
-  for (int h = 0; h < NH; ++h)
-#pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks)
-      qf[h][ks] = __builtin_bit_cast(bf16x8, ldg16(qp[h] + ks * 32 + 8 * x.g4));
-
-  float mref[NH];  // per column reference max, in log2 units (score * c)
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    mref[h] = kNoMax;
-    lsum[h] = 0.f;
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db) o[h][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < (C::TBLK + C::NW - 1) / C::NW; ++i) {
+    const int blk = x.wave + i * C::NW;
+    if (blk < C::TBLK) issue_block<C>(x, blk, k0, sK0, sV0, sK1, sV1);
   }
+}
 
+__device__ __forceinline__ void wait_loads_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+  __syncthreads();                // ... and every other wave's
+}
+
+// Per-wave online-softmax state for NH heads.
+template <class C, int NH>
+struct State {
+  bf16x8 q[NH][C::KS];
+  floatx4 o[NH][C::DB];
+  float mref[NH];  // per column reference max (log2 units)
+  float lsum[NH];  // per lane partial softmax denominator
+};
+
+// Consume one LDS tile (keys k0 .. k0+BN-1) for the NH heads of this wave.
+template <class C, int NH>
+__device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
+                                             const uint16_t* sV, int k0) {
   const int W = x.window;
-  const int k_lo = W ? max(0, x.q_lo - W + 1) : 0;
-  const int kt0 = k_lo / BN, kt1 = x.q_hi / BN;
-  const bool wave_active = x.w_lo <= x.w_hi;
   const int wk_lo = W ? max(0, x.w_lo - W + 1) : 0;
+#pragma unroll
+  for (int cc = 0; cc < C::BN / 32; ++cc) {
+    const int c0 = k0 + 32 * cc;
+    if (x.w_lo > x.w_hi || c0 > x.w_hi || c0 + 31 < wk_lo) continue;  // wave-uniform
+    const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
 
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int k0 = kt * BN;
-    __syncthreads();
-    load_kv_tile<DQK, DV>(x, kvh, k0, sK, sV);
-    __syncthreads();
-#pragma unroll 1
-    for (int cc = 0; cc < BN / 32; ++cc) {
-      const int c0 = k0 + 32 * cc;  // first key of this 32-key chunk
-      if (!wave_active || c0 > x.w_hi || c0 + 31 < wk_lo) continue;
-      const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
-
-      // S^T = K . Q^T for 2 key blocks of 16.
-      floatx4 s[NH][2];
+    floatx4 s[NH][2];
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        s[h][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-        s[h][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int h = 0; h < NH; ++h) {
+      s[h][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      s[h][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks) {
+    for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a =
-              *(const bf16x8*)(sK + (32 * cc + 16 * kb + x.col) * T::KROW + ks * 32 + 8 * x.g4);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a =
+            *(const bf16x8*)(sK + (((2 * cc + kb) * C::KS + ks) << 9) + 8 * x.lane);
 #pragma unroll
-          for (int h = 0; h < NH; ++h) s[h][kb] = mfma_16x16x32(a, qf[h][ks], s[h][kb]);
-        }
-      }
-
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = c0 + 16 * kb + 4 * x.g4 + r;
-            const bool vis = key <= x.t && (!W || x.t - key < W);
-            if (!vis)
-#pragma unroll
-              for (int h = 0; h < NH; ++h) s[h][kb][r] = -INFINITY;
-          }
-      }
-
-      // Online softmax per head; P^T packed to bf16 as the PV B operand.
-      bf16x8 pb[NH];
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        float mx = fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
-                         fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
-        const bool grow = mx * x.c > mref[h] + kRescaleTau;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float cm = col_max4(mx) * x.c;  // -inf if the column saw no key here
-          const float mnew = fmaxf(mref[h], cm);
-          const float alpha = fast_exp2(mref[h] - mnew);
-          mref[h] = mnew;
-          lsum[h] *= alpha;
-#pragma unroll
-          for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[h][db][r] *= alpha;
-        }
-        const float nm = -mref[h];
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(s[h][kb][r], x.c, nm));
-            ps += p;
-            pb[h][4 * kb + r] = (__bf16)p;
-          }
-        lsum[h] += ps;
-      }
-
-      // O^T += V^T . P^T over this chunk's 32 keys.
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const uint16_t* va =
-            sV + (32 * cc + 4 * x.g4 + (x.col >> 2)) * T::VROW + 16 * db + 4 * (x.col & 3);
-        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
-        const shortx4 hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(va + 16 * T::VROW));
-        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
-        const shortx8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) o[h][db] = mfma_16x16x32(a, pb[h], o[h][db]);
+        for (int h = 0; h < NH; ++h) s[h][kb] = mfma_16x16x32(a, st.q[h][ks], s[h][kb]);
       }
     }
-  }
 
+    if (need_mask) {
 #pragma unroll
-  for (int h = 0; h < NH; ++h) lsum[h] = col_sum4(lsum[h]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = c0 + 16 * kb + 4 * x.g4 + r;
+          const bool vis = key <= x.t && (!W || x.t - key < W);
+          if (!vis)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) s[h][kb][r] = -INFINITY;
+        }
+    }
+
+    bf16x8 pb[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float mx =
+          fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
+                fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
+      if (__builtin_amdgcn_ballot_w64(mx * x.c > st.mref[h] + kRescaleTau)) {
+        const float mnew = fmaxf(st.mref[h], col_max4(mx) * x.c);
+        const float alpha = fast_exp2(st.mref[h] - mnew);
+        st.mref[h] = mnew;
+        st.lsum[h] *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) st.o[h][db][r] *= alpha;
+      }
+      const float nm = -st.mref[h];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(s[h][kb][r], x.c, nm));
+          ps += p;
+          pb[h][4 * kb + r] = (__bf16)p;
+        }
+      st.lsum[h] += ps;
+    }
+
+    // O^T += V^T . P^T over the chunk's 32 keys; V^T from transposed LDS reads.
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      shortx4 half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = 32 * cc + 16 * hf + 4 * x.g4 + (x.col >> 2);
+        const int chunk = 2 * db + ((x.col & 3) >> 1);
+        const uint16_t* va = sV + r * C::DV + ((chunk ^ (r % C::VCH)) << 3) + 4 * (x.col & 1);
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
+      }
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
+      const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
+                          half[1][0], half[1][1], half[1][2], half[1][3]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) st.o[h][db] = mfma_16x16x32(a, pb[h], st.o[h][db]);
+    }
+  }
 }
 
-// out[t, i, :] = gate * (hs - lam * hn) for one signal head, this lane's 4*DB channels.
+// out[t, i, :] = gate * (hs/l_s - lam * hn) for one signal head, this lane's channels.
 template <int DV>
 __device__ __forceinline__ void store_head(const uint16_t* lam, const uint16_t* gate,
                                            uint16_t* out, int64_t row, int S, int i, int g4,
                                            const floatx4 (&hs)[DV / 16], float inv_s,
-                                           const float (&hn)[DV / 16][4]) {
+                                           const floatx4 (&hn)[DV / 16]) {
   const float lm = bf16_to_f32(lam[row * S + i]);
   const int64_t base = (row * S + i) * DV + 4 * g4;
 #pragma unroll
@@ -231,115 +244,176 @@ __device__ __forceinline__ void store_head(const uint16_t* lam, const uint16_t* 
   }
 }
 
-template <int DQK, int DV, int NS, int NN, int R>
-__global__ void __launch_bounds__(NT, 1)
+// The main loop of one wave group. Both groups run the same barrier sequence.
+template <class C, int NH>
+__device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
+                                          const uint16_t* const (&qrow)[NH], uint16_t* sKa0,
+                                          uint16_t* sVa0, uint16_t* sKb0, uint16_t* sVb0,
+                                          uint16_t* sKa1, uint16_t* sVa1, uint16_t* sKb1,
+                                          uint16_t* sVb1, bool group_b) {
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      st.q[h][ks] = __builtin_bit_cast(bf16x8, ldg16(qrow[h] + ks * 32 + 8 * x.g4));
+    st.mref[h] = kNoMax;
+    st.lsum[h] = 0.f;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) st.o[h][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int W = x.window;
+  const int k_lo = W ? max(0, x.q_lo - W + 1) : 0;
+  const int kt0 = k_lo / C::BN, kt1 = x.q_hi / C::BN;
+  const bool use_b = C::TWO_KV && group_b;
+  for (int kt = kt0; kt <= kt1; kt += 2) {
+    wait_loads_and_sync();
+    if (kt + 1 <= kt1) issue_tile<C>(x, (kt + 1) * C::BN, sKa1, sVa1, sKb1, sVb1);
+    if (use_b)
+      consume_tile<C, NH>(x, st, sKb0, sVb0, kt * C::BN);
+    else
+      consume_tile<C, NH>(x, st, sKa0, sVa0, kt * C::BN);
+    if (kt + 1 > kt1) break;
+    wait_loads_and_sync();
+    if (kt + 2 <= kt1) issue_tile<C>(x, (kt + 2) * C::BN, sKa0, sVa0, sKb0, sVb0);
+    if (use_b)
+      consume_tile<C, NH>(x, st, sKb1, sVb1, (kt + 1) * C::BN);
+    else
+      consume_tile<C, NH>(x, st, sKa1, sVa1, (kt + 1) * C::BN);
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h) st.lsum[h] = col_sum4(st.lsum[h]);
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::NT, 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
                 uint16_t* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
-                int units, int nqt, int heavy_first, float c) {
-  using T = FwdTile<DQK, DV>;
-  constexpr int DB = T::DB;
-  static_assert(R == 1 || NN == 1, "several phases only with one noise head per unit");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * T::KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * T::VROW];
+                int units, int R, int nqt, int heavy_first, float c) {
+  // Two K/V stages per KV head; distinct objects, so the compiler sees that the
+  // tile in flight never aliases the tile being read.
+  __shared__ __attribute__((aligned(16))) uint16_t sKa0[C::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sVa0[C::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sKa1[C::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sVa1[C::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sKb0[C::TWO_KV ? C::K_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sVb0[C::TWO_KV ? C::V_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sKb1[C::TWO_KV ? C::K_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sVb1[C::TWO_KV ? C::V_ELEMS : 8];
+  // Normalised noise output handed from the A waves to the B waves.
+  __shared__ __attribute__((aligned(16))) float sHN[C::BSIG > 0 ? 4 * C::DB * 4 * 64 : 4];
 
-  FwdCtx x;
+  Ctx x;
   x.kg = kg;
   x.vg = vg;
   x.L = L;
   x.Hkv = Hkv;
   x.window = window;
-  x.tid = threadIdx.x;
-  const int wave = x.tid >> 6, lane = x.tid & 63;
-  x.col = lane & 15;
-  x.g4 = lane >> 4;
+  const int tid = threadIdx.x;
+  x.wave = tid >> 6;
+  x.lane = tid & 63;
+  x.col = x.lane & 15;
+  x.g4 = x.lane >> 4;
   x.c = c;
+  const bool group_b = x.wave >= 4;
+  const int qg = x.wave & 3;
   const int per = B * units;
   const int slot = blockIdx.x / per;
   const int qt = heavy_first ? nqt - 1 - slot : slot;
   const int bu = blockIdx.x - slot * per;
   const int b = bu / units, u = bu - (bu / units) * units;
   x.b = b;
+  x.kvA = u * R;
+  x.kvB = C::TWO_KV ? u * R + 1 : u * R;
   x.q_lo = qt * BM;
   x.q_hi = min(x.q_lo + BM, L) - 1;
-  x.w_lo = x.q_lo + wave * 16;
+  x.w_lo = x.q_lo + qg * 16;
   x.w_hi = min(x.w_lo + 15, L - 1);
   x.t = x.w_lo + x.col;
   const bool t_ok = x.t < L;
   const int64_t row = (int64_t)b * L + min(x.t, L - 1);
-  const int sig0 = u * (R * NS);  // first signal head of the unit
+  const int sig0 = u * (C::ASIG + C::BSIG);  // first signal head of the unit
 
-  float hn[DB][4];
+  // The first tile is in flight before the Q loads.
   {
-    constexpr int NH = NS + NN;
-    const uint16_t* qp[NH];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qp[s] = q_sig + (row * S + sig0 + s) * DQK;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) qp[NS + n] = q_noise + (row * N + u * NN + n) * DQK;
-    floatx4 o[NH][DB];
-    float l[NH];
-    attend<DQK, DV, NH>(x, qp, u * R, sK, sV, o, l);
-    constexpr int g = NS / NN;  // signal heads per noise head within the phase
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int n = s / g;
-      const float inv_n = 1.f / l[NS + n];
-      float hns[DB][4];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hns[db][r] = o[NS + n][db][r] * inv_n;
-      if (t_ok) store_head<DV>(lam, gate, out, row, S, sig0 + s, x.g4, o[s], 1.f / l[s], hns);
-    }
-    if (R > 1) {
-      const float inv_n = 1.f / l[NS];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hn[db][r] = o[NS][db][r] * inv_n;
-    }
+    const int k_lo = window ? max(0, x.q_lo - window + 1) : 0;
+    issue_tile<C>(x, (k_lo / C::BN) * C::BN, sKa0, sVa0, sKb0, sVb0);
   }
-#pragma unroll 1
-  for (int ph = 1; ph < R; ++ph) {
-    const uint16_t* qp[NS];
+
+  if (!group_b) {
+    constexpr int NH = C::NA;
+    State<C, NH> st;
+    const uint16_t* qrow[NH];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qp[s] = q_sig + (row * S + sig0 + ph * NS + s) * DQK;
-    floatx4 o[NS][DB];
-    float l[NS];
-    attend<DQK, DV, NS>(x, qp, u * R + ph, sK, sV, o, l);
+    for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
+    qrow[C::ASIG] = q_noise + (row * N + u) * C::DQK;
+    run_tiles<C, NH>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, false);
+    const float inv_n = 1.f / st.lsum[C::ASIG];
+    floatx4 hn[C::DB];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      if (t_ok) store_head<DV>(lam, gate, out, row, S, sig0 + ph * NS + s, x.g4, o[s], 1.f / l[s], hn);
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hn[db][r] = st.o[C::ASIG][db][r] * inv_n;
+    if (C::BSIG > 0) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        *(floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4) = hn[db];
+    }
+    if (t_ok) {
+#pragma unroll
+      for (int s = 0; s < C::ASIG; ++s)
+        store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s], 1.f / st.lsum[s], hn);
+    }
+    if (C::BSIG > 0) __syncthreads();
+  } else if (C::BSIG > 0) {
+    constexpr int NH = C::NB > 0 ? C::NB : 1;
+    State<C, NH> st;
+    const uint16_t* qrow[NH];
+#pragma unroll
+    for (int s = 0; s < NH; ++s) qrow[s] = q_sig + (row * S + sig0 + C::ASIG + s) * C::DQK;
+    run_tiles<C, NH>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, true);
+    __syncthreads();  // the A waves' noise output is in sHN
+    floatx4 hn[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+      hn[db] = *(const floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4);
+    if (t_ok) {
+#pragma unroll
+      for (int s = 0; s < NH; ++s)
+        store_head<C::DV>(lam, gate, out, row, S, sig0 + C::ASIG + s, x.g4, st.o[s],
+                          1.f / st.lsum[s], hn);
+    }
   }
 }
 
-template <int DQK, int DV, int NS, int NN, int R>
+template <class C>
 hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.L + BM - 1) / BM;
   const int64_t grid = (int64_t)nqt * a.B * a.plan.units;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int heavy_first = a.window == 0 ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<DQK, DV, NS, NN, R>), dim3((unsigned)grid), dim3(NT), 0,
-                     stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
+  hipLaunchKernelGGL((fwd_bf16_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                     (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
                      (const uint16_t*)a.gate, (uint16_t*)a.out, a.B, a.L, a.S, a.N, a.Hkv,
-                     a.window, a.plan.units, nqt, heavy_first, a.scale_log2);
+                     a.window, a.plan.units, a.plan.R, nqt, heavy_first, a.scale_log2);
   return hipGetLastError();
 }
 
+// Head split of a unit into the A and B waves for each compiled layout
+// (NS signal heads per KV head, R KV heads per unit, one noise head per unit).
 template <int DQK, int DV>
 hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
   const UnitPlan& p = a.plan;
   if (p.NN != 1) return (hipError_t)-1;
   if (p.R == 1) {
-    if (p.NS == 1) return launch_inst<DQK, DV, 1, 1, 1>(a, stream);
-    if (p.NS == 2) return launch_inst<DQK, DV, 2, 1, 1>(a, stream);
-    if (p.NS == 4) return launch_inst<DQK, DV, 4, 1, 1>(a, stream);
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false>>(a, stream);
+    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false>>(a, stream);
   } else if (p.R == 2) {
-    if (p.NS == 1) return launch_inst<DQK, DV, 1, 1, 2>(a, stream);
-    if (p.NS == 2) return launch_inst<DQK, DV, 2, 1, 2>(a, stream);
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true>>(a, stream);
   }
   return (hipError_t)-1;
 }
