@@ -20,8 +20,9 @@
 //    buffered: the next tile is in flight while the current one is consumed.
 //    K is stored fragment-major (each 1 KB block is exactly one MFMA A operand
 //    of 16 keys x 32 dims, read back with one conflict-free ds_read_b128); V is
-//    row-major with its 16-byte chunks XOR-swizzled by row so that the
-//    transposed reads (ds_read_b64_tr_b16) that build the V^T operand hit
+//    row-major with its 32-byte chunk pairs XOR-swizzled by row (pair ^= r % 8)
+//    so that the 4 rows each 16-lane group of a transposed read
+//    (ds_read_b64_tr_b16) touches, and the 8 rows of each half wave, fall on
 //    distinct banks;
 //  * scores are computed transposed, S^T = K . Q^T (16x16x32 bf16 MFMA, fp32
 //    accumulation), so a lane owns one query column: the online-softmax row
@@ -62,6 +63,7 @@ struct Cfg {
   static constexpr int K_ELEMS = BN * DQK;
   static constexpr int V_ELEMS = BN * DV;
   static constexpr int VCH = DV / 8;                // 16-byte chunks per V row
+  static constexpr int VPAIR = VCH / 2;             // 32-byte chunk pairs per V row
   static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
 };
 
@@ -98,7 +100,7 @@ __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint1
     const int vi = bi - C::KBLK;
     const int r = C::VRPB * vi + x.lane / C::VCH;
     const int p = x.lane % C::VCH;
-    const int cch = p ^ (r % C::VCH);
+    const int cch = p ^ ((r % C::VPAIR) << 1);
     const int key = min(k0 + r, x.L - 1);
     const uint16_t* src = x.vg + (((int64_t)x.b * x.L + key) * x.Hkv + kvh) * C::DV + 8 * cch;
     __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(sV + vi * 512), 16, 0, 0);
@@ -209,7 +211,8 @@ __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, con
       for (int hf = 0; hf < 2; ++hf) {
         const int r = 32 * cc + 16 * hf + 4 * x.g4 + (x.col >> 2);
         const int chunk = 2 * db + ((x.col & 3) >> 1);
-        const uint16_t* va = sV + r * C::DV + ((chunk ^ (r % C::VCH)) << 3) + 4 * (x.col & 1);
+        const uint16_t* va =
+            sV + r * C::DV + ((chunk ^ ((r % C::VPAIR) << 1)) << 3) + 4 * (x.col & 1);
         half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
       }
       typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
@@ -311,7 +314,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   x.Hkv = Hkv;
   x.window = window;
   const int tid = threadIdx.x;
-  x.wave = tid >> 6;
+  x.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   x.lane = tid & 63;
   x.col = x.lane & 15;
   x.g4 = x.lane >> 4;
