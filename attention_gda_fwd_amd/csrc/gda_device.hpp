@@ -68,11 +68,32 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Read-only 16-byte global load.
-__device__ __forceinline__ u32x4 ld_g16(const void* p) {
-  return __builtin_nontemporal_load((const u32x4*)p);
-}
-
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS copy of 16 bytes per lane from sbase + voff (sbase
+// wave-uniform, voff a per-lane 32-bit byte offset): lane i's bytes land at
+// lds_base + 16*i (lds_base wave-uniform). Written as inline asm so that the
+// compiler does not track it as an LDS write: its conservative waits would
+// otherwise hold every later transposed LDS read (which carries no alias
+// information) until this copy completes. The instruction has no VGPR result;
+// callers wait for it explicitly (s_waitcnt vmcnt(0) + barrier) before reading
+// the destination, and any vmcnt wait the compiler emits for its own loads stays
+// conservative because vector-memory loads complete in order.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, lds_void* lds_base) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  // readfirstlane returns a signed int: go through uint32_t so that the low
+  // half is zero-extended, never sign-extended into the high half.
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m0v)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ u32x2 ldg8(const void* p) { return *(const u32x2*)p; }
 

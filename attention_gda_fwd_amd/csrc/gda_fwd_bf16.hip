@@ -16,7 +16,7 @@
 //    queries (2 waves per SIMD, each under 256 registers), so one wave's
 //    softmax overlaps the other's MFMAs, and the noise output goes from A to B
 //    through LDS once per tile of queries;
-//  * K/V tiles stream HBM -> LDS with global_load_lds (no VGPRs), double
+//  * K/V tiles stream HBM -> LDS with global_load_lds_dwordx4 (no VGPRs), double
 //    buffered: the next tile is in flight while the current one is consumed.
 //    K is stored fragment-major (each 1 KB block is exactly one MFMA A operand
 //    of 16 keys x 32 dims, read back with one conflict-free ds_read_b128); V is
@@ -40,18 +40,20 @@ constexpr int BM = 64;  // queries per workgroup: 4 query groups x 16
 constexpr float kRescaleTau = 8.f;  // lazy rescale threshold, log2 units
 constexpr float kNoMax = -1e30f;    // finite "no key seen yet" reference
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 // ASIG signal heads + the noise head run in the A waves, BSIG signal heads in the
-// B waves; with TWO_KV the B heads read the unit's second KV head.
-template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_>
+// B waves; with TWO_KV the B heads read the unit's second KV head. With SPLIT,
+// one more signal head is shared: the A waves take its even 32-key chunks and
+// the B waves its odd ones (each wave then does the same MFMA and softmax work
+// per tile); the two partial softmax states are merged at the end.
+template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_, bool SPLIT_ = false>
 struct Cfg {
   static constexpr int DQK = DQK_, DV = DV_, ASIG = ASIG_, BSIG = BSIG_;
-  static constexpr bool TWO_KV = TWO_KV_;
-  static constexpr int NA = ASIG + 1;               // heads of an A wave
-  static constexpr int NB = BSIG;                   // heads of a B wave
-  static constexpr int NW = BSIG > 0 ? 8 : 4;       // waves per workgroup
+  static constexpr bool TWO_KV = TWO_KV_, SPLIT = SPLIT_;
+  static constexpr int NA = ASIG + 1 + SPLIT;       // heads of an A wave
+  static constexpr int NB = BSIG + SPLIT;           // heads of a B wave
+  static constexpr int USIG = ASIG + SPLIT + BSIG;  // signal heads of a unit
+  static constexpr int NW = NB > 0 ? 8 : 4;         // waves per workgroup
   static constexpr int NT = NW * 64;
   static constexpr int BN = (TWO_KV && DQK > 128) ? 32 : 64;  // keys per LDS tile
   static constexpr int KS = DQK / 32;               // MFMA k-steps of Q.K
@@ -65,6 +67,7 @@ struct Cfg {
   static constexpr int VCH = DV / 8;                // 16-byte chunks per V row
   static constexpr int VPAIR = VCH / 2;             // 32-byte chunk pairs per V row
   static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
+  static_assert(!SPLIT || (BN == 64 && !TWO_KV), "the shared head alternates the 2 chunks of a tile");
 };
 
 struct Ctx {
@@ -90,20 +93,26 @@ __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint1
   const int kvh = kvi ? x.kvB : x.kvA;
   uint16_t* sK = kvi ? sK1 : sK0;
   uint16_t* sV = kvi ? sV1 : sV0;
+  // The per-lane part of every address is a 32-bit byte offset from a
+  // wave-uniform base row (clamped so the base never passes row L-1).
   if (bi < C::KBLK) {
     const int kb = bi / C::KS, ks = bi - (bi / C::KS) * C::KS;
-    const int key = min(k0 + 16 * kb + (x.lane & 15), x.L - 1);
-    const uint16_t* src =
-        x.kg + (((int64_t)x.b * x.L + key) * x.Hkv + kvh) * C::DQK + 32 * ks + 8 * (x.lane >> 4);
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(sK + bi * 512), 16, 0, 0);
+    const uint32_t stride = (uint32_t)x.Hkv * C::DQK * 2;
+    const int row0 = min(k0 + 16 * kb, x.L - 1);
+    const int rel = min(x.lane & 15, x.L - 1 - row0);
+    const char* base = (const char*)x.kg +
+                       ((((int64_t)x.b * x.L + row0) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
+    dma16(base, (uint32_t)rel * stride + 16u * (uint32_t)(x.lane >> 4), (lds_void*)(sK + bi * 512));
   } else {
     const int vi = bi - C::KBLK;
-    const int r = C::VRPB * vi + x.lane / C::VCH;
-    const int p = x.lane % C::VCH;
-    const int cch = p ^ ((r % C::VPAIR) << 1);
-    const int key = min(k0 + r, x.L - 1);
-    const uint16_t* src = x.vg + (((int64_t)x.b * x.L + key) * x.Hkv + kvh) * C::DV + 8 * cch;
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(sV + vi * 512), 16, 0, 0);
+    const int lr = x.lane / C::VCH;            // row within the block
+    const int r = C::VRPB * vi + lr;           // row within the tile
+    const int cch = (x.lane % C::VCH) ^ ((r % C::VPAIR) << 1);
+    const uint32_t stride = (uint32_t)x.Hkv * C::DV * 2;
+    const int row0 = min(k0 + C::VRPB * vi, x.L - 1);
+    const int rel = min(lr, x.L - 1 - row0);
+    const char* base = (const char*)x.vg + (((int64_t)x.b * x.L + row0) * x.Hkv + kvh) * C::DV * 2;
+    dma16(base, (uint32_t)rel * stride + 16u * (uint32_t)cch, (lds_void*)(sV + vi * 512));
   }
 }
 
@@ -132,96 +141,122 @@ struct State {
   float lsum[NH];  // per lane partial softmax denominator
 };
 
-// Consume one LDS tile (keys k0 .. k0+BN-1) for the NH heads of this wave.
-template <class C, int NH>
-__device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
-                                             const uint16_t* sV, int k0) {
+// One 32-key chunk (keys c0 .. c0+31, chunk cc of the LDS tile) for the first
+// NACT heads of this wave's NH.
+template <class C, int NH, int NACT>
+__device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
+                                              const uint16_t* sV, int c0, int cc) {
   const int W = x.window;
   const int wk_lo = W ? max(0, x.w_lo - W + 1) : 0;
-#pragma unroll
-  for (int cc = 0; cc < C::BN / 32; ++cc) {
-    const int c0 = k0 + 32 * cc;
-    if (x.w_lo > x.w_hi || c0 > x.w_hi || c0 + 31 < wk_lo) continue;  // wave-uniform
-    const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
+  if (x.w_lo > x.w_hi || c0 > x.w_hi || c0 + 31 < wk_lo) return;  // wave-uniform
+  const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
 
-    floatx4 s[NH][2];
+  floatx4 s[NACT][2];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      s[h][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-      s[h][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < NACT; ++h) {
+    s[h][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    s[h][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 a =
+          *(const bf16x8*)(sK + (((2 * cc + kb) * C::KS + ks) << 9) + 8 * x.lane);
+#pragma unroll
+      for (int h = 0; h < NACT; ++h) s[h][kb] = mfma_16x16x32(a, st.q[h][ks], s[h][kb]);
     }
+  }
+  // Schedule: the first two K fragment reads, then each fragment's MFMAs
+  // followed by the read of the fragment two steps ahead, so LDS latency hides
+  // behind MFMAs instead of stalling them.
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
+  for (int i = 0; i < 2 * C::KS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NACT, 0);
+    if (i + 2 < 2 * C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+
+  if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a =
-            *(const bf16x8*)(sK + (((2 * cc + kb) * C::KS + ks) << 9) + 8 * x.lane);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int h = 0; h < NH; ++h) s[h][kb] = mfma_16x16x32(a, st.q[h][ks], s[h][kb]);
+      for (int r = 0; r < 4; ++r) {
+        const int key = c0 + 16 * kb + 4 * x.g4 + r;
+        const bool vis = key <= x.t && (!W || x.t - key < W);
+        if (!vis)
+#pragma unroll
+          for (int h = 0; h < NACT; ++h) s[h][kb][r] = -INFINITY;
       }
-    }
+  }
 
-    if (need_mask) {
+  bf16x8 pb[NACT];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+  for (int h = 0; h < NACT; ++h) {
+    const float mx =
+        fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
+              fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
+    if (__builtin_amdgcn_ballot_w64(mx * x.c > st.mref[h] + kRescaleTau)) {
+      const float mnew = fmaxf(st.mref[h], col_max4(mx) * x.c);
+      const float alpha = fast_exp2(st.mref[h] - mnew);
+      st.mref[h] = mnew;
+      st.lsum[h] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = c0 + 16 * kb + 4 * x.g4 + r;
-          const bool vis = key <= x.t && (!W || x.t - key < W);
-          if (!vis)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int h = 0; h < NH; ++h) s[h][kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) st.o[h][db][r] *= alpha;
     }
-
-    bf16x8 pb[NH];
+    const float nm = -st.mref[h];
+    float ps = 0.f;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const float mx =
-          fmaxf(fmaxf(fmaxf(s[h][0][0], s[h][0][1]), fmaxf(s[h][0][2], s[h][0][3])),
-                fmaxf(fmaxf(s[h][1][0], s[h][1][1]), fmaxf(s[h][1][2], s[h][1][3])));
-      if (__builtin_amdgcn_ballot_w64(mx * x.c > st.mref[h] + kRescaleTau)) {
-        const float mnew = fmaxf(st.mref[h], col_max4(mx) * x.c);
-        const float alpha = fast_exp2(st.mref[h] - mnew);
-        st.mref[h] = mnew;
-        st.lsum[h] *= alpha;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) st.o[h][db][r] *= alpha;
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(s[h][kb][r], x.c, nm));
+        ps += p;
+        pb[h][4 * kb + r] = (__bf16)p;
       }
-      const float nm = -st.mref[h];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(s[h][kb][r], x.c, nm));
-          ps += p;
-          pb[h][4 * kb + r] = (__bf16)p;
-        }
-      st.lsum[h] += ps;
-    }
+    st.lsum[h] += ps;
+  }
 
-    // O^T += V^T . P^T over the chunk's 32 keys; V^T from transposed LDS reads.
+  // O^T += V^T . P^T over the chunk's 32 keys; V^T from transposed LDS reads.
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      shortx4 half[2];
+  for (int db = 0; db < C::DB; ++db) {
+    shortx4 half[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int r = 32 * cc + 16 * hf + 4 * x.g4 + (x.col >> 2);
-        const int chunk = 2 * db + ((x.col & 3) >> 1);
-        const uint16_t* va =
-            sV + r * C::DV + ((chunk ^ ((r % C::VPAIR) << 1)) << 3) + 4 * (x.col & 1);
-        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
-      }
-      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
-      const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
-                          half[1][0], half[1][1], half[1][2], half[1][3]};
-      const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-#pragma unroll
-      for (int h = 0; h < NH; ++h) st.o[h][db] = mfma_16x16x32(a, pb[h], st.o[h][db]);
+    for (int hf = 0; hf < 2; ++hf) {
+      const int r = 32 * cc + 16 * hf + 4 * x.g4 + (x.col >> 2);
+      const int chunk = 2 * db + ((x.col & 3) >> 1);
+      const uint16_t* va =
+          sV + r * C::DV + ((chunk ^ ((r % C::VPAIR) << 1)) << 3) + 4 * (x.col & 1);
+      half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
     }
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
+    const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
+                        half[1][0], half[1][1], half[1][2], half[1][3]};
+    const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+    for (int h = 0; h < NACT; ++h) st.o[h][db] = mfma_16x16x32(a, pb[h], st.o[h][db]);
+  }
+  // Schedule: V^T pairs for two channel blocks ahead of the MFMAs that use them.
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NACT, 1);
+    if (db + 2 < C::DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+}
+
+// Consume one LDS tile (keys k0 .. k0+BN-1). With a shared head (C::SPLIT) the
+// last head of the state is processed only on chunks whose parity is PARITY.
+template <class C, int NH, int PARITY>
+__device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
+                                             const uint16_t* sV, int k0) {
+  constexpr int N0 = (C::SPLIT && PARITY != 0) ? NH - 1 : NH;
+  consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
+  if constexpr (C::BN / 32 > 1) {
+    constexpr int N1 = (C::SPLIT && PARITY != 1) ? NH - 1 : NH;
+    consume_chunk<C, NH, N1>(x, st, sK, sV, k0 + 32, 1);
   }
 }
 
@@ -248,7 +283,7 @@ __device__ __forceinline__ void store_head(const uint16_t* lam, const uint16_t* 
 }
 
 // The main loop of one wave group. Both groups run the same barrier sequence.
-template <class C, int NH>
+template <class C, int NH, int PARITY>
 __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
                                           const uint16_t* const (&qrow)[NH], uint16_t* sKa0,
                                           uint16_t* sVa0, uint16_t* sKb0, uint16_t* sVb0,
@@ -272,16 +307,16 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
     wait_loads_and_sync();
     if (kt + 1 <= kt1) issue_tile<C>(x, (kt + 1) * C::BN, sKa1, sVa1, sKb1, sVb1);
     if (use_b)
-      consume_tile<C, NH>(x, st, sKb0, sVb0, kt * C::BN);
+      consume_tile<C, NH, PARITY>(x, st, sKb0, sVb0, kt * C::BN);
     else
-      consume_tile<C, NH>(x, st, sKa0, sVa0, kt * C::BN);
+      consume_tile<C, NH, PARITY>(x, st, sKa0, sVa0, kt * C::BN);
     if (kt + 1 > kt1) break;
     wait_loads_and_sync();
     if (kt + 2 <= kt1) issue_tile<C>(x, (kt + 2) * C::BN, sKa0, sVa0, sKb0, sVb0);
     if (use_b)
-      consume_tile<C, NH>(x, st, sKb1, sVb1, (kt + 1) * C::BN);
+      consume_tile<C, NH, PARITY>(x, st, sKb1, sVb1, (kt + 1) * C::BN);
     else
-      consume_tile<C, NH>(x, st, sKa1, sVa1, (kt + 1) * C::BN);
+      consume_tile<C, NH, PARITY>(x, st, sKa1, sVa1, (kt + 1) * C::BN);
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) st.lsum[h] = col_sum4(st.lsum[h]);
@@ -304,8 +339,11 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   __shared__ __attribute__((aligned(16))) uint16_t sVb0[C::TWO_KV ? C::V_ELEMS : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sKb1[C::TWO_KV ? C::K_ELEMS : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sVb1[C::TWO_KV ? C::V_ELEMS : 8];
-  // Normalised noise output handed from the A waves to the B waves.
-  __shared__ __attribute__((aligned(16))) float sHN[C::BSIG > 0 ? 4 * C::DB * 4 * 64 : 4];
+  // Normalised noise output handed from the A waves to the B waves, and the A
+  // waves' half of the shared head (O^T, reference max, sum per lane).
+  constexpr int SP_FLOATS = C::DB * 256 + 128;
+  __shared__ __attribute__((aligned(16))) float sHN[C::NB > 0 ? 4 * C::DB * 4 * 64 : 4];
+  __shared__ __attribute__((aligned(16))) float sSP[C::SPLIT ? 4 * SP_FLOATS : 4];
 
   Ctx x;
   x.kg = kg;
@@ -336,7 +374,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   x.t = x.w_lo + x.col;
   const bool t_ok = x.t < L;
   const int64_t row = (int64_t)b * L + min(x.t, L - 1);
-  const int sig0 = u * (C::ASIG + C::BSIG);  // first signal head of the unit
+  const int sig0 = u * C::USIG;  // first signal head of the unit
 
   // The first tile is in flight before the Q loads.
   {
@@ -345,47 +383,78 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   }
 
   if (!group_b) {
-    constexpr int NH = C::NA;
+    constexpr int NH = C::NA;  // [A signal heads][noise][shared head if SPLIT]
+    constexpr int NZ = C::ASIG;  // index of the noise head in the state
     State<C, NH> st;
     const uint16_t* qrow[NH];
 #pragma unroll
     for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
-    qrow[C::ASIG] = q_noise + (row * N + u) * C::DQK;
-    run_tiles<C, NH>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, false);
-    const float inv_n = 1.f / st.lsum[C::ASIG];
+    qrow[NZ] = q_noise + (row * N + u) * C::DQK;
+    if constexpr (C::SPLIT) qrow[NH - 1] = q_sig + (row * S + sig0 + C::ASIG) * C::DQK;
+    run_tiles<C, NH, 0>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, false);
+    const float inv_n = 1.f / st.lsum[NZ];
     floatx4 hn[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) hn[db][r] = st.o[C::ASIG][db][r] * inv_n;
-    if (C::BSIG > 0) {
+      for (int r = 0; r < 4; ++r) hn[db][r] = st.o[NZ][db][r] * inv_n;
+    if (C::NB > 0) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
         *(floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4) = hn[db];
+    }
+    if constexpr (C::SPLIT) {  // this group's half of the shared head, for the B waves
+      float* sp = sSP + qg * SP_FLOATS;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        *(floatx4*)(sp + (db * 64 + x.lane) * 4) = st.o[NH - 1][db];
+      sp[C::DB * 256 + x.lane] = st.mref[NH - 1];
+      sp[C::DB * 256 + 64 + x.lane] = st.lsum[NH - 1];
     }
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
         store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s], 1.f / st.lsum[s], hn);
     }
-    if (C::BSIG > 0) __syncthreads();
-  } else if (C::BSIG > 0) {
-    constexpr int NH = C::NB > 0 ? C::NB : 1;
+    if (C::NB > 0) __syncthreads();
+  } else if (C::NB > 0) {
+    constexpr int NH = C::NB > 0 ? C::NB : 1;  // [B signal heads][shared head if SPLIT]
+    constexpr int b_first = C::ASIG + (C::SPLIT ? 1 : 0);  // first B head, unit-relative
     State<C, NH> st;
     const uint16_t* qrow[NH];
 #pragma unroll
-    for (int s = 0; s < NH; ++s) qrow[s] = q_sig + (row * S + sig0 + C::ASIG + s) * C::DQK;
-    run_tiles<C, NH>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, true);
-    __syncthreads();  // the A waves' noise output is in sHN
+    for (int s = 0; s < C::BSIG; ++s) qrow[s] = q_sig + (row * S + sig0 + b_first + s) * C::DQK;
+    if constexpr (C::SPLIT) qrow[NH - 1] = q_sig + (row * S + sig0 + C::ASIG) * C::DQK;
+    run_tiles<C, NH, 1>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, true);
+    __syncthreads();  // the A waves' noise output (and shared-head half) is in LDS
     floatx4 hn[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
       hn[db] = *(const floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4);
     if (t_ok) {
 #pragma unroll
-      for (int s = 0; s < NH; ++s)
-        store_head<C::DV>(lam, gate, out, row, S, sig0 + C::ASIG + s, x.g4, st.o[s],
+      for (int s = 0; s < C::BSIG; ++s)
+        store_head<C::DV>(lam, gate, out, row, S, sig0 + b_first + s, x.g4, st.o[s],
                           1.f / st.lsum[s], hn);
+    }
+    if constexpr (C::SPLIT) {
+      // Merge the two halves of the shared head: m* = max(mA, mB),
+      // O = 2^(mA-m*) O_A + 2^(mB-m*) O_B, l likewise (mref is in log2 units).
+      const float* sp = sSP + qg * SP_FLOATS;
+      const float ma = sp[C::DB * 256 + x.lane], la = sp[C::DB * 256 + 64 + x.lane];
+      const float mb = st.mref[NH - 1], lb = st.lsum[NH - 1];
+      const float ms = fmaxf(ma, mb);
+      const float ea = fast_exp2(ma - ms), eb = fast_exp2(mb - ms);
+      floatx4 om[C::DB];
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const floatx4 oa = *(const floatx4*)(sp + (db * 64 + x.lane) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) om[db][r] = ea * oa[r] + eb * st.o[NH - 1][db][r];
+      }
+      if (t_ok)
+        store_head<C::DV>(lam, gate, out, row, S, sig0 + C::ASIG, x.g4, om,
+                          1.f / (ea * la + eb * lb), hn);
     }
   }
 }
@@ -413,7 +482,7 @@ hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
   if (p.R == 1) {
     if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false>>(a, stream);
     if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false>>(a, stream);
-    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false>>(a, stream);
+    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, false>>(a, stream);
   } else if (p.R == 2) {
     if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true>>(a, stream);
     if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true>>(a, stream);
