@@ -36,7 +36,6 @@
 namespace gda {
 namespace {
 
-constexpr int BM = 64;  // queries per workgroup: 4 query groups x 16
 constexpr float kRescaleTau = 8.f;  // lazy rescale threshold, log2 units
 constexpr float kNoMax = -1e30f;    // finite "no key seen yet" reference
 
@@ -46,16 +45,23 @@ constexpr float kNoMax = -1e30f;    // finite "no key seen yet" reference
 // one more signal head is shared: the A waves take its even 32-key chunks and
 // the B waves its odd ones (each wave then does the same MFMA and softmax work
 // per tile); the two partial softmax states are merged at the end.
-template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_, bool SPLIT_ = false>
+//
+// NQG query groups of 16 make a workgroup's query tile (BM = 16*NQG); BN keys
+// make an LDS tile. (NQG, BN) = (4, 64) fills a CU with one workgroup; (2, 32)
+// uses under 80 KB of LDS and 4 waves, so two workgroups share a CU and one's
+// memory phases overlap the other's compute.
+template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_, bool SPLIT_, int NQG_, int BN_>
 struct Cfg {
   static constexpr int DQK = DQK_, DV = DV_, ASIG = ASIG_, BSIG = BSIG_;
   static constexpr bool TWO_KV = TWO_KV_, SPLIT = SPLIT_;
+  static constexpr int NQG = NQG_;                  // query groups of 16 per workgroup
+  static constexpr int BM = 16 * NQG;               // queries per workgroup
   static constexpr int NA = ASIG + 1 + SPLIT;       // heads of an A wave
   static constexpr int NB = BSIG + SPLIT;           // heads of a B wave
   static constexpr int USIG = ASIG + SPLIT + BSIG;  // signal heads of a unit
-  static constexpr int NW = NB > 0 ? 8 : 4;         // waves per workgroup
+  static constexpr int NW = NQG * (NB > 0 ? 2 : 1); // waves per workgroup
   static constexpr int NT = NW * 64;
-  static constexpr int BN = (TWO_KV && DQK > 128) ? 32 : 64;  // keys per LDS tile
+  static constexpr int BN = BN_;                    // keys per LDS tile
   static constexpr int KS = DQK / 32;               // MFMA k-steps of Q.K
   static constexpr int DB = DV / 16;                // 16-channel blocks of the output
   static constexpr int KBLK = (BN / 16) * KS;       // 1 KB fragment blocks of a K tile
@@ -67,7 +73,8 @@ struct Cfg {
   static constexpr int VCH = DV / 8;                // 16-byte chunks per V row
   static constexpr int VPAIR = VCH / 2;             // 32-byte chunk pairs per V row
   static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
-  static_assert(!SPLIT || (BN == 64 && !TWO_KV), "the shared head alternates the 2 chunks of a tile");
+  static_assert(BN == 32 || BN == 64, "an LDS tile is one or two 32-key chunks");
+  static_assert(!SPLIT || !TWO_KV, "the shared head lives on the unit's only KV head");
 };
 
 struct Ctx {
@@ -247,16 +254,21 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
   }
 }
 
-// Consume one LDS tile (keys k0 .. k0+BN-1). With a shared head (C::SPLIT) the
-// last head of the state is processed only on chunks whose parity is PARITY.
-template <class C, int NH, int PARITY>
+// Consume one LDS tile (keys k0 .. k0+BN-1) held in LDS stage STAGE. With a
+// shared head (C::SPLIT) the last head of the state is processed by this wave
+// group (PARITY) on every other 32-key chunk: on chunks of parity PARITY when
+// a tile holds two chunks, on tiles of stage PARITY when it holds one.
+template <class C, int NH, int PARITY, int STAGE>
 __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
                                              const uint16_t* sV, int k0) {
-  constexpr int N0 = (C::SPLIT && PARITY != 0) ? NH - 1 : NH;
-  consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
-  if constexpr (C::BN / 32 > 1) {
+  if constexpr (C::BN == 64) {
+    constexpr int N0 = (C::SPLIT && PARITY != 0) ? NH - 1 : NH;
     constexpr int N1 = (C::SPLIT && PARITY != 1) ? NH - 1 : NH;
+    consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
     consume_chunk<C, NH, N1>(x, st, sK, sV, k0 + 32, 1);
+  } else {
+    constexpr int N0 = (C::SPLIT && PARITY != STAGE) ? NH - 1 : NH;
+    consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
   }
 }
 
@@ -307,23 +319,25 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
     wait_loads_and_sync();
     if (kt + 1 <= kt1) issue_tile<C>(x, (kt + 1) * C::BN, sKa1, sVa1, sKb1, sVb1);
     if (use_b)
-      consume_tile<C, NH, PARITY>(x, st, sKb0, sVb0, kt * C::BN);
+      consume_tile<C, NH, PARITY, 0>(x, st, sKb0, sVb0, kt * C::BN);
     else
-      consume_tile<C, NH, PARITY>(x, st, sKa0, sVa0, kt * C::BN);
+      consume_tile<C, NH, PARITY, 0>(x, st, sKa0, sVa0, kt * C::BN);
     if (kt + 1 > kt1) break;
     wait_loads_and_sync();
     if (kt + 2 <= kt1) issue_tile<C>(x, (kt + 2) * C::BN, sKa0, sVa0, sKb0, sVb0);
     if (use_b)
-      consume_tile<C, NH, PARITY>(x, st, sKb1, sVb1, (kt + 1) * C::BN);
+      consume_tile<C, NH, PARITY, 1>(x, st, sKb1, sVb1, (kt + 1) * C::BN);
     else
-      consume_tile<C, NH, PARITY>(x, st, sKa1, sVa1, (kt + 1) * C::BN);
+      consume_tile<C, NH, PARITY, 1>(x, st, sKa1, sVa1, (kt + 1) * C::BN);
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) st.lsum[h] = col_sum4(st.lsum[h]);
 }
 
+// A 4-wave workgroup is meant to share its CU with a second one (2 waves per
+// SIMD, so at most 256 registers per wave).
 template <class C>
-__global__ void __launch_bounds__(C::NT, 1)
+__global__ void __launch_bounds__(C::NT, C::NW == 4 ? 2 : 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
@@ -342,8 +356,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   // Normalised noise output handed from the A waves to the B waves, and the A
   // waves' half of the shared head (O^T, reference max, sum per lane).
   constexpr int SP_FLOATS = C::DB * 256 + 128;
-  __shared__ __attribute__((aligned(16))) float sHN[C::NB > 0 ? 4 * C::DB * 4 * 64 : 4];
-  __shared__ __attribute__((aligned(16))) float sSP[C::SPLIT ? 4 * SP_FLOATS : 4];
+  __shared__ __attribute__((aligned(16))) float sHN[C::NB > 0 ? C::NQG * C::DB * 4 * 64 : 4];
+  __shared__ __attribute__((aligned(16))) float sSP[C::SPLIT ? C::NQG * SP_FLOATS : 4];
 
   Ctx x;
   x.kg = kg;
@@ -357,8 +371,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   x.col = x.lane & 15;
   x.g4 = x.lane >> 4;
   x.c = c;
-  const bool group_b = x.wave >= 4;
-  const int qg = x.wave & 3;
+  const bool group_b = x.wave >= C::NQG;
+  const int qg = x.wave % C::NQG;
   const int per = B * units;
   const int slot = blockIdx.x / per;
   const int qt = heavy_first ? nqt - 1 - slot : slot;
@@ -367,8 +381,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   x.b = b;
   x.kvA = u * R;
   x.kvB = C::TWO_KV ? u * R + 1 : u * R;
-  x.q_lo = qt * BM;
-  x.q_hi = min(x.q_lo + BM, L) - 1;
+  x.q_lo = qt * C::BM;
+  x.q_hi = min(x.q_lo + C::BM, L) - 1;
   x.w_lo = x.q_lo + qg * 16;
   x.w_hi = min(x.w_lo + 15, L - 1);
   x.t = x.w_lo + x.col;
@@ -461,7 +475,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 
 template <class C>
 hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = (a.L + BM - 1) / BM;
+  const int nqt = (a.L + C::BM - 1) / C::BM;
   const int64_t grid = (int64_t)nqt * a.B * a.plan.units;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int heavy_first = a.window == 0 ? 1 : 0;
@@ -473,21 +487,32 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Head split of a unit into the A and B waves for each compiled layout
-// (NS signal heads per KV head, R KV heads per unit, one noise head per unit).
-template <int DQK, int DV>
+// Head groups of each compiled layout (NS signal heads per KV head, R KV heads
+// per unit, one noise head per unit), for a (query groups, key tile) shape.
+template <int DQK, int DV, int NQG, int BN>
 hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
   const UnitPlan& p = a.plan;
   if (p.NN != 1) return (hipError_t)-1;
   if (p.R == 1) {
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false>>(a, stream);
-    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, false>>(a, stream);
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false, false, NQG, BN>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false, false, NQG, BN>>(a, stream);
+    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, false, NQG, BN>>(a, stream);
   } else if (p.R == 2) {
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true>>(a, stream);
+    constexpr int BN2 = (DQK > 128 && BN > 32) ? 32 : BN;  // two KV heads' tiles in LDS
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, false, NQG, BN2>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, false, NQG, BN2>>(a, stream);
   }
   return (hipError_t)-1;
+}
+
+// Causal full attention: 64-query tiles over 64-key tiles, one workgroup per
+// CU. Sliding window: each query tile only touches ~W keys, so the workgroup is
+// short and its memory phases dominate; 32-query tiles over 32-key tiles let
+// two workgroups share a CU.
+template <int DQK, int DV>
+hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
+  if (a.window > 0) return dispatch_layout<DQK, DV, 2, 32>(a, stream);
+  return dispatch_layout<DQK, DV, 4, 64>(a, stream);
 }
 
 }  // namespace
@@ -501,9 +526,9 @@ bool fwd_bf16_supported(int dqk, int dv, const UnitPlan& p) {
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  if (a.dqk == 64 && a.dv == 64) return dispatch_layout<64, 64>(a, stream);
-  if (a.dqk == 128 && a.dv == 128) return dispatch_layout<128, 128>(a, stream);
-  if (a.dqk == 192 && a.dv == 128) return dispatch_layout<192, 128>(a, stream);
+  if (a.dqk == 64 && a.dv == 64) return dispatch_shape<64, 64>(a, stream);
+  if (a.dqk == 128 && a.dv == 128) return dispatch_shape<128, 128>(a, stream);
+  if (a.dqk == 192 && a.dv == 128) return dispatch_shape<192, 128>(a, stream);
   return (hipError_t)-1;
 }
 
