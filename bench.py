@@ -28,6 +28,19 @@ import numpy as np
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E, published
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "attention_gda_fwd_amd", "csrc")
+
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (one pass
+# each, `python3 bench.py --profile`), each scaled by the factor the same counter reads on
+# a 1 GiB elementwise copy in the same pass. A figure holds only for the kernel source it
+# was taken on (sha256 of the file below); once that file changes it is reported as null.
+MEASURED_TRAFFIC = {
+    "prefill": {"source": "gda_fwd_bf16.hip", "bytes": 2487681996,
+                "sha256": "1e2786a5069de1326c2428fde7d19963a324c39e2d8b0865648e137aba75dce6"},
+    "decode": {"source": "gda_decode_bf16.hip", "bytes": 21656083383,
+               "sha256": "fd449beb60527daa366f990cbd58206f1bc40ae0e97faaa6f5448deb7162e171"},
+}
 
 
 def log(msg):
@@ -42,7 +55,21 @@ def parse():
     p.add_argument("--breakdown-reps", type=int, default=20)
     p.add_argument("--cpu-rows", type=int, default=512,
                    help="prefill rows of the CPU-baseline sample")
+    p.add_argument("--profile", action="store_true",
+                   help="short run for hardware counters: a 1 GiB copy kernel for scale, "
+                        "then the timed steps only (no breakdown, no CPU baseline)")
     return p.parse_args()
+
+
+def measured_traffic(kind: str):
+    """Counter-measured HBM bytes per launch, or None if the kernel source has changed."""
+    import hashlib
+    m = MEASURED_TRAFFIC[kind]
+    if m["bytes"] is None:
+        return None
+    with open(os.path.join(CSRC, m["source"]), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return m["bytes"] if sha == m["sha256"] else None
 
 
 def host_threads() -> int:
@@ -86,6 +113,8 @@ def fill_decode(cfg, torch, gin):
             for b, row in zip(range(b0, b0 + len(rows)), rows):
                 for k, v in row.items():
                     dev[k][b].copy_(torch.from_numpy(v).view(torch.bfloat16))
+            if (b0 // 8) % 2 == 1:
+                log(f"  {b0 + len(rows)} of {cfg.B} sequences")
     return dev
 
 
@@ -138,6 +167,15 @@ def main():
         gda_decode(ddev["q_sig"], ddev["q_noise"], ddev["k_cache"], ddev["v_cache"],
                    ddev["lam"], ddev["gate"], window=window, out=dout)
 
+    if args.profile:
+        # Scale for the byte counters: an elementwise copy that reads and writes 1 GiB.
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log("copy kernel: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
+
     # ---- timed steps: warmup, barrier + sync, K steps, sync -------------------------
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -168,6 +206,10 @@ def main():
     d_bytes = dec_cfg.algorithmic_bytes()
     d_gbps = d_bytes / (d_avg * 1e-3) / 1e9
     log(f"prefill {f_avg:.3f} ms = {f_tflops:.1f} TFLOP/s; decode {d_avg:.3f} ms = {d_gbps:.0f} GB/s")
+    if args.profile:
+        print(json.dumps({"mode": "profile", "prefill_ms": round(f_avg, 4),
+                          "decode_ms": round(d_avg, 4)}), flush=True)
+        return
 
     # ---- sampled parity of the timed outputs ----------------------------------------
     rows = np.linspace(0, fwd_cfg.L - 1, args.cpu_rows).astype(np.int64)
@@ -241,11 +283,13 @@ def main():
         "decode_hbm_frac": round(d_gbps / PEAK_HBM_GBPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(f_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(f_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "fwd_bf16_kernel<192,128,4,1,1>",
+                     "traffic": measured_traffic("prefill"),
+                     "kernel": "fwd_bf16_kernel<Cfg<192,128,2,2,false,false,4,64>>",
                      "flops_per_launch": f_flops, "avg_launch_ms": round(f_avg, 4)},
         "decode_roofline": {"bound": "hbm", "achieved": round(d_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
-                            "traffic": None, "kernel": "decode_bf16_kernel<192,128>",
+                            "traffic": measured_traffic("decode"),
+                            "kernel": "decode_bf16_kernel<192,128>",
                             "bytes_per_launch": d_bytes, "avg_launch_ms": round(d_avg, 4)},
         "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
                          "cores": threads, "kind": "oracle",
