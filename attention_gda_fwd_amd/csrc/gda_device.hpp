@@ -95,6 +95,19 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, lds_void
                : "memory", "m0");
 }
 
+// The same copy with the LDS destination given as a wave-uniform LDS byte address.
+__device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(m0v)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ u32x2 ldg8(const void* p) { return *(const u32x2*)p; }
 
 }  // namespace gda

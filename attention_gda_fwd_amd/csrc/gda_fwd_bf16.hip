@@ -70,11 +70,15 @@ struct Cfg {
   static constexpr int TBLK = NKV * (KBLK + VBLK);  // 1 KB blocks per tile (all KV heads)
   static constexpr int K_ELEMS = BN * DQK;
   static constexpr int V_ELEMS = BN * DV;
+  static constexpr int KV_ELEMS = K_ELEMS + V_ELEMS;  // one KV head's tile: K then V
+  static constexpr int STAGE_ELEMS = NKV * KV_ELEMS;
   static constexpr int VCH = DV / 8;                // 16-byte chunks per V row
   static constexpr int VPAIR = VCH / 2;             // 32-byte chunk pairs per V row
   static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
   static_assert(BN == 32 || BN == 64, "an LDS tile is one or two 32-key chunks");
   static_assert(!SPLIT || !TWO_KV, "the shared head lives on the unit's only KV head");
+  static_assert(TBLK % NW == 0, "every wave issues the same number of tile blocks");
+  static_assert(KBLK % NW == 0 && VBLK % NW == 0, "runs of NW blocks never mix K and V");
 };
 
 struct Ctx {
@@ -128,10 +132,50 @@ template <class C>
 __device__ __forceinline__ void issue_tile(const Ctx& x, int k0, uint16_t* sK0, uint16_t* sV0,
                                            uint16_t* sK1, uint16_t* sV1) {
 #pragma unroll
-  for (int i = 0; i < (C::TBLK + C::NW - 1) / C::NW; ++i) {
-    const int blk = x.wave + i * C::NW;
-    if (blk < C::TBLK) issue_block<C>(x, blk, k0, sK0, sV0, sK1, sV1);
+  for (int i = 0; i < C::TBLK / C::NW; ++i) issue_block<C>(x, x.wave + i * C::NW, k0, sK0, sV0, sK1, sV1);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// Block i of this wave's share of a tile (key k0, ending inside the sequence)
+// into ring stage DST. Blocks are dealt round-robin (block wave + i*NW); with
+// the tile sizes used here every multiple of NW starts a run of blocks of one
+// kind (K or V of one KV head), so the kind is known at compile time and only
+// the index within the kind depends on the wave.
+template <class C, int DST>
+__device__ __forceinline__ void issue_block_fast(const Ctx& x, uint32_t ring_lds, int k0, int i) {
+  constexpr int per = C::KBLK + C::VBLK;
+  const int first = i * C::NW;  // compile-time after unrolling
+  const int kvi = (C::TWO_KV && first >= per) ? 1 : 0;
+  const int fb = first - kvi * per;
+  const int kvh = kvi ? x.kvB : x.kvA;
+  const uint32_t st_off = 2u * (uint32_t)((DST * C::NKV + kvi) * C::KV_ELEMS);
+  if (fb < C::KBLK) {
+    const int bi = fb + x.wave;
+    const int kb = bi / C::KS, ks = bi - (bi / C::KS) * C::KS;
+    const char* g = (const char*)x.kg +
+                    ((((int64_t)x.b * x.L + k0 + 16 * kb) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
+    dma16_lds(g, (uint32_t)(x.lane & 15) * (uint32_t)(x.Hkv * C::DQK * 2) + 16u * (uint32_t)(x.lane >> 4),
+              ring_lds + st_off + 1024u * (uint32_t)bi);
+  } else {
+    const int vi = fb - C::KBLK + x.wave;
+    const int lr = x.lane / C::VCH;
+    const int r = C::VRPB * vi + lr;
+    const int cch = (x.lane % C::VCH) ^ ((r % C::VPAIR) << 1);
+    const char* g = (const char*)x.vg + (((int64_t)x.b * x.L + k0 + C::VRPB * vi) * x.Hkv + kvh) * C::DV * 2;
+    dma16_lds(g, (uint32_t)lr * (uint32_t)(x.Hkv * C::DV * 2) + 16u * (uint32_t)cch,
+              ring_lds + st_off + 2u * C::K_ELEMS + 1024u * (uint32_t)vi);
   }
+}
+
+template <class C, int DST>
+__device__ __forceinline__ void issue_tile_fast(const Ctx& x, uint32_t ring_lds, int k0, int i0,
+                                                int i1) {
+#pragma unroll
+  for (int i = 0; i < C::TBLK / C::NW; ++i)
+    if (i >= i0 && i < i1) issue_block_fast<C, DST>(x, ring_lds, k0, i);
 }
 
 __device__ __forceinline__ void wait_loads_and_sync() {
@@ -148,17 +192,17 @@ struct State {
   float lsum[NH];  // per lane partial softmax denominator
 };
 
-// One 32-key chunk (keys c0 .. c0+31, chunk cc of the LDS tile) for the first
-// NACT heads of this wave's NH.
-template <class C, int NH, int NACT>
-__device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
-                                              const uint16_t* sV, int c0, int cc) {
+// Is any key of chunk c0 .. c0+31 visible to a query of this wave? (wave-uniform)
+__device__ __forceinline__ bool chunk_live(const Ctx& x, int c0) {
   const int W = x.window;
   const int wk_lo = W ? max(0, x.w_lo - W + 1) : 0;
-  if (x.w_lo > x.w_hi || c0 > x.w_hi || c0 + 31 < wk_lo) return;  // wave-uniform
-  const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
+  return x.w_lo <= x.w_hi && c0 <= x.w_hi && c0 + 31 >= wk_lo;
+}
 
-  floatx4 s[NACT][2];
+// S^T = K . Q^T for chunk cc of the LDS tile (keys 32 cc .. +31), first NACT heads.
+template <class C, int NH, int NACT>
+__device__ __forceinline__ void chunk_qk(const Ctx& x, const State<C, NH>& st, const uint16_t* sK,
+                                         int cc, floatx4 (&s)[NH][2]) {
 #pragma unroll
   for (int h = 0; h < NACT; ++h) {
     s[h][0] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -177,13 +221,22 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
   // Schedule: the first two K fragment reads, then each fragment's MFMAs
   // followed by the read of the fragment two steps ahead, so LDS latency hides
   // behind MFMAs instead of stalling them.
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  constexpr int AH = 2;  // K fragments in flight (more do not fit in registers)
+  __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
   for (int i = 0; i < 2 * C::KS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, NACT, 0);
-    if (i + 2 < 2 * C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i + AH < 2 * C::KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+}
 
+// Mask chunk c0 .. c0+31, update the lazy online-softmax state and return
+// P = 2^(S c - mref) as bf16 (first NACT heads).
+template <class C, int NH, int NACT>
+__device__ __forceinline__ void chunk_softmax(const Ctx& x, State<C, NH>& st, floatx4 (&s)[NH][2],
+                                              int c0, bf16x8 (&pb)[NH]) {
+  const int W = x.window;
+  const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
   if (need_mask) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -196,8 +249,6 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
           for (int h = 0; h < NACT; ++h) s[h][kb][r] = -INFINITY;
       }
   }
-
-  bf16x8 pb[NACT];
 #pragma unroll
   for (int h = 0; h < NACT; ++h) {
     const float mx =
@@ -225,8 +276,12 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
       }
     st.lsum[h] += ps;
   }
+}
 
-  // O^T += V^T . P^T over the chunk's 32 keys; V^T from transposed LDS reads.
+// O^T += V^T . P^T over chunk cc of the LDS tile; V^T from transposed LDS reads.
+template <class C, int NH, int NACT>
+__device__ __forceinline__ void chunk_pv(const Ctx& x, State<C, NH>& st, const uint16_t* sV,
+                                         int cc, const bf16x8 (&pb)[NH]) {
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
     shortx4 half[2];
@@ -246,25 +301,47 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
     for (int h = 0; h < NACT; ++h) st.o[h][db] = mfma_16x16x32(a, pb[h], st.o[h][db]);
   }
   // Schedule: V^T pairs for two channel blocks ahead of the MFMAs that use them.
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+  constexpr int AV = 2;  // V^T channel blocks in flight
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV, 1);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
     __builtin_amdgcn_sched_group_barrier(0x008, NACT, 1);
-    if (db + 2 < C::DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    if (db + AV < C::DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
+}
+
+// One 32-key chunk (keys c0 .. c0+31, chunk cc of the LDS tile), first NACT heads.
+template <class C, int NH, int NACT>
+__device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
+                                              const uint16_t* sV, int c0, int cc) {
+  if (!chunk_live(x, c0)) return;
+  floatx4 s[NH][2];
+  bf16x8 pb[NH];
+  chunk_qk<C, NH, NACT>(x, st, sK, cc, s);
+  chunk_softmax<C, NH, NACT>(x, st, s, c0, pb);
+  chunk_pv<C, NH, NACT>(x, st, sV, cc, pb);
 }
 
 // Consume one LDS tile (keys k0 .. k0+BN-1) held in LDS stage STAGE. With a
 // shared head (C::SPLIT) the last head of the state is processed by this wave
 // group (PARITY) on every other 32-key chunk: on chunks of parity PARITY when
 // a tile holds two chunks, on tiles of stage PARITY when it holds one.
+// The wave's copies of the next tile (key dma_k0 >= 0, into the other stage)
+// go out half before this tile's first chunk and half between its chunks, so
+// that they do not all land at once.
 template <class C, int NH, int PARITY, int STAGE>
 __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
-                                             const uint16_t* sV, int k0) {
+                                             const uint16_t* sV, int k0, uint32_t ring_lds,
+                                             int dma_k0) {
+  constexpr int DST = 1 - STAGE;
+  constexpr int NI = C::TBLK / C::NW;
+  constexpr int H1 = C::BN == 64 ? (NI + 1) / 2 : NI;
+  if (dma_k0 >= 0) issue_tile_fast<C, DST>(x, ring_lds, dma_k0, 0, H1);
   if constexpr (C::BN == 64) {
     constexpr int N0 = (C::SPLIT && PARITY != 0) ? NH - 1 : NH;
     constexpr int N1 = (C::SPLIT && PARITY != 1) ? NH - 1 : NH;
     consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
+    if (dma_k0 >= 0) issue_tile_fast<C, DST>(x, ring_lds, dma_k0, H1, NI);
     consume_chunk<C, NH, N1>(x, st, sK, sV, k0 + 32, 1);
   } else {
     constexpr int N0 = (C::SPLIT && PARITY != STAGE) ? NH - 1 : NH;
@@ -297,10 +374,8 @@ __device__ __forceinline__ void store_head(const uint16_t* lam, const uint16_t* 
 // The main loop of one wave group. Both groups run the same barrier sequence.
 template <class C, int NH, int PARITY>
 __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
-                                          const uint16_t* const (&qrow)[NH], uint16_t* sKa0,
-                                          uint16_t* sVa0, uint16_t* sKb0, uint16_t* sVb0,
-                                          uint16_t* sKa1, uint16_t* sVa1, uint16_t* sKb1,
-                                          uint16_t* sVb1, bool group_b) {
+                                          const uint16_t* const (&qrow)[NH], uint32_t ring_lds,
+                                          uint16_t* (&sk)[2][2], uint16_t* (&sv)[2][2]) {
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
 #pragma unroll
@@ -314,21 +389,26 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
   const int W = x.window;
   const int k_lo = W ? max(0, x.q_lo - W + 1) : 0;
   const int kt0 = k_lo / C::BN, kt1 = x.q_hi / C::BN;
-  const bool use_b = C::TWO_KV && group_b;
+  constexpr int kv = (C::TWO_KV && PARITY == 1) ? 1 : 0;  // the B waves read the second KV head
+  // The next tile's copies: spread over this tile when it ends inside the
+  // sequence, else issued at once with row clamping.
+  auto next_job = [&](int knext, int dst) -> int {
+    if (knext > kt1 * C::BN) return -1;
+    if (knext + C::BN <= x.L) return knext;
+    if (dst == 0)
+      issue_tile<C>(x, knext, sk[0][0], sv[0][0], sk[0][1], sv[0][1]);
+    else
+      issue_tile<C>(x, knext, sk[1][0], sv[1][0], sk[1][1], sv[1][1]);
+    return -1;
+  };
   for (int kt = kt0; kt <= kt1; kt += 2) {
     wait_loads_and_sync();
-    if (kt + 1 <= kt1) issue_tile<C>(x, (kt + 1) * C::BN, sKa1, sVa1, sKb1, sVb1);
-    if (use_b)
-      consume_tile<C, NH, PARITY, 0>(x, st, sKb0, sVb0, kt * C::BN);
-    else
-      consume_tile<C, NH, PARITY, 0>(x, st, sKa0, sVa0, kt * C::BN);
+    consume_tile<C, NH, PARITY, 0>(x, st, sk[0][kv], sv[0][kv], kt * C::BN, ring_lds,
+                                   next_job((kt + 1) * C::BN, 1));
     if (kt + 1 > kt1) break;
     wait_loads_and_sync();
-    if (kt + 2 <= kt1) issue_tile<C>(x, (kt + 2) * C::BN, sKa0, sVa0, sKb0, sVb0);
-    if (use_b)
-      consume_tile<C, NH, PARITY, 1>(x, st, sKb1, sVb1, (kt + 1) * C::BN);
-    else
-      consume_tile<C, NH, PARITY, 1>(x, st, sKa1, sVa1, (kt + 1) * C::BN);
+    consume_tile<C, NH, PARITY, 1>(x, st, sk[1][kv], sv[1][kv], (kt + 1) * C::BN, ring_lds,
+                                   next_job((kt + 2) * C::BN, 0));
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) st.lsum[h] = col_sum4(st.lsum[h]);
@@ -343,16 +423,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
                 uint16_t* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
                 int units, int R, int nqt, int heavy_first, float c) {
-  // Two K/V stages per KV head; distinct objects, so the compiler sees that the
-  // tile in flight never aliases the tile being read.
-  __shared__ __attribute__((aligned(16))) uint16_t sKa0[C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVa0[C::V_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sKa1[C::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVa1[C::V_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sKb0[C::TWO_KV ? C::K_ELEMS : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sVb0[C::TWO_KV ? C::V_ELEMS : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sKb1[C::TWO_KV ? C::K_ELEMS : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sVb1[C::TWO_KV ? C::V_ELEMS : 8];
+  // K/V ring: two stages, each the tiles of the unit's KV heads.
+  __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
   // Normalised noise output handed from the A waves to the B waves, and the A
   // waves' half of the shared head (O^T, reference max, sum per lane).
   constexpr int SP_FLOATS = C::DB * 256 + 128;
@@ -390,10 +462,24 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   const int64_t row = (int64_t)b * L + min(x.t, L - 1);
   const int sig0 = u * C::USIG;  // first signal head of the unit
 
+  uint16_t* sk[2][2];
+  uint16_t* sv[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      sk[st][kv] = ring + (st * C::NKV + (C::TWO_KV ? kv : 0)) * C::KV_ELEMS;
+      sv[st][kv] = sk[st][kv] + C::K_ELEMS;
+    }
+  const uint32_t ring_lds = lds_addr(ring);
   // The first tile is in flight before the Q loads.
   {
     const int k_lo = window ? max(0, x.q_lo - window + 1) : 0;
-    issue_tile<C>(x, (k_lo / C::BN) * C::BN, sKa0, sVa0, sKb0, sVb0);
+    const int kf = (k_lo / C::BN) * C::BN;
+    if (kf + C::BN <= L)
+      issue_tile_fast<C, 0>(x, ring_lds, kf, 0, C::TBLK / C::NW);
+    else
+      issue_tile<C>(x, kf, sk[0][0], sv[0][0], sk[0][1], sv[0][1]);
   }
 
   if (!group_b) {
@@ -405,7 +491,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
     qrow[NZ] = q_noise + (row * N + u) * C::DQK;
     if constexpr (C::SPLIT) qrow[NH - 1] = q_sig + (row * S + sig0 + C::ASIG) * C::DQK;
-    run_tiles<C, NH, 0>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, false);
+    run_tiles<C, NH, 0>(x, st, qrow, ring_lds, sk, sv);
     const float inv_n = 1.f / st.lsum[NZ];
     floatx4 hn[C::DB];
 #pragma unroll
@@ -439,7 +525,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
     for (int s = 0; s < C::BSIG; ++s) qrow[s] = q_sig + (row * S + sig0 + b_first + s) * C::DQK;
     if constexpr (C::SPLIT) qrow[NH - 1] = q_sig + (row * S + sig0 + C::ASIG) * C::DQK;
-    run_tiles<C, NH, 1>(x, st, qrow, sKa0, sVa0, sKb0, sVb0, sKa1, sVa1, sKb1, sVb1, true);
+    run_tiles<C, NH, 1>(x, st, qrow, ring_lds, sk, sv);
     __syncthreads();  // the A waves' noise output (and shared-head half) is in LDS
     floatx4 hn[C::DB];
 #pragma unroll
@@ -498,9 +584,12 @@ hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
     if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false, false, NQG, BN>>(a, stream);
     if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, false, NQG, BN>>(a, stream);
   } else if (p.R == 2) {
-    constexpr int BN2 = (DQK > 128 && BN > 32) ? 32 : BN;  // two KV heads' tiles in LDS
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, false, NQG, BN2>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, false, NQG, BN2>>(a, stream);
+    // Two KV heads' tiles per stage: with dqk = 192 only 32-key tiles fit, and
+    // those split evenly over 4 waves, not 8.
+    constexpr int NQG2 = DQK > 128 ? 2 : NQG;
+    constexpr int BN2 = DQK > 128 ? 32 : BN;
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, false, NQG2, BN2>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, false, NQG2, BN2>>(a, stream);
   }
   return (hipError_t)-1;
 }

@@ -47,6 +47,31 @@ def test_small_full_output(name):
     U.assert_close(got, ref, kw["dtype"], name)
 
 
+# Every compiled bf16 prefill layout (signal heads per KV head NS, KV heads per
+# unit R) at every head size, causal and with a window: several key tiles and
+# a ragged tail, so every tile shape, the partial last tile and every wave
+# split run against the oracle.
+LAYOUTS = {"ns1_r1": (4, 4, 4), "ns2_r1": (8, 4, 4), "ns4_r1": (16, 4, 4),
+           "ns1_r2": (8, 4, 8), "ns2_r2": (16, 4, 8)}  # (S, N, Hkv)
+DIMS = {"d64": (64, 64), "d128": (128, 128), "d192": (192, 128)}
+
+
+@pytest.mark.parametrize("window", [0, 80], ids=["causal", "w80"])
+@pytest.mark.parametrize("dims", sorted(DIMS))
+@pytest.mark.parametrize("layout", sorted(LAYOUTS))
+def test_layout_sweep(layout, dims, window):
+    S, N, Hkv = LAYOUTS[layout]
+    dqk, dv = DIMS[dims]
+    cid = 300 + 10 * sorted(LAYOUTS).index(layout) + sorted(DIMS).index(dims)
+    kw = dict(B=1, L=231, S=S, N=N, Hkv=Hkv, dqk=dqk, dv=dv, window=window, dtype="bf16")
+    U.log(f"parity layout {layout} {dims} window={window} {kw}")
+    case = U.FwdCase(cid, **kw)
+    got = U.to_f64(case.run_gpu())
+    torch.cuda.synchronize()
+    ref = case.run_oracle()
+    U.assert_close(got, ref, "bf16", f"{layout} {dims} window={window}")
+
+
 @pytest.mark.parametrize("cfg", [C.CFG1, C.CFG2, C.CFG3], ids=lambda c: c.name)
 def test_full_size_sampled_rows(cfg):
     U.log(f"parity {cfg.name}: generating inputs")
