@@ -41,24 +41,21 @@ constexpr float kNoMax = -1e30f;    // finite "no key seen yet" reference
 
 
 // ASIG signal heads + the noise head run in the A waves, BSIG signal heads in the
-// B waves; with TWO_KV the B heads read the unit's second KV head. With SPLIT,
-// one more signal head is shared: the A waves take its even 32-key chunks and
-// the B waves its odd ones (each wave then does the same MFMA and softmax work
-// per tile); the two partial softmax states are merged at the end.
+// B waves; with TWO_KV the B heads read the unit's second KV head.
 //
 // NQG query groups of 16 make a workgroup's query tile (BM = 16*NQG); BN keys
 // make an LDS tile. (NQG, BN) = (4, 64) fills a CU with one workgroup; (2, 32)
 // uses under 80 KB of LDS and 4 waves, so two workgroups share a CU and one's
 // memory phases overlap the other's compute.
-template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_, bool SPLIT_, int NQG_, int BN_>
+template <int DQK_, int DV_, int ASIG_, int BSIG_, bool TWO_KV_, int NQG_, int BN_>
 struct Cfg {
   static constexpr int DQK = DQK_, DV = DV_, ASIG = ASIG_, BSIG = BSIG_;
-  static constexpr bool TWO_KV = TWO_KV_, SPLIT = SPLIT_;
+  static constexpr bool TWO_KV = TWO_KV_;
   static constexpr int NQG = NQG_;                  // query groups of 16 per workgroup
   static constexpr int BM = 16 * NQG;               // queries per workgroup
-  static constexpr int NA = ASIG + 1 + SPLIT;       // heads of an A wave
-  static constexpr int NB = BSIG + SPLIT;           // heads of a B wave
-  static constexpr int USIG = ASIG + SPLIT + BSIG;  // signal heads of a unit
+  static constexpr int NA = ASIG + 1;              // heads of an A wave
+  static constexpr int NB = BSIG;                  // heads of a B wave
+  static constexpr int USIG = ASIG + BSIG;         // signal heads of a unit
   static constexpr int NW = NQG * (NB > 0 ? 2 : 1); // waves per workgroup
   static constexpr int NT = NW * 64;
   static constexpr int BN = BN_;                    // keys per LDS tile
@@ -76,7 +73,6 @@ struct Cfg {
   static constexpr int VPAIR = VCH / 2;             // 32-byte chunk pairs per V row
   static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
   static_assert(BN == 32 || BN == 64, "an LDS tile is one or two 32-key chunks");
-  static_assert(!SPLIT || !TWO_KV, "the shared head lives on the unit's only KV head");
   static_assert(TBLK % NW == 0, "every wave issues the same number of tile blocks");
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "runs of NW blocks never mix K and V");
 };
@@ -322,14 +318,11 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
   chunk_pv<C, NH, NACT>(x, st, sV, cc, pb);
 }
 
-// Consume one LDS tile (keys k0 .. k0+BN-1) held in LDS stage STAGE. With a
-// shared head (C::SPLIT) the last head of the state is processed by this wave
-// group (PARITY) on every other 32-key chunk: on chunks of parity PARITY when
-// a tile holds two chunks, on tiles of stage PARITY when it holds one.
-// The wave's copies of the next tile (key dma_k0 >= 0, into the other stage)
-// go out half before this tile's first chunk and half between its chunks, so
-// that they do not all land at once.
-template <class C, int NH, int PARITY, int STAGE>
+// Consume the tile (keys k0 .. k0+BN-1) held in LDS stage STAGE. The wave's
+// copies of the next tile (key dma_k0 >= 0, into the other stage) go out half
+// before the tile's first chunk and half between its chunks, so that they do
+// not all land at once.
+template <class C, int NH, int STAGE>
 __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, const uint16_t* sK,
                                              const uint16_t* sV, int k0, uint32_t ring_lds,
                                              int dma_k0) {
@@ -337,15 +330,10 @@ __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, con
   constexpr int NI = C::TBLK / C::NW;
   constexpr int H1 = C::BN == 64 ? (NI + 1) / 2 : NI;
   if (dma_k0 >= 0) issue_tile_fast<C, DST>(x, ring_lds, dma_k0, 0, H1);
+  consume_chunk<C, NH, NH>(x, st, sK, sV, k0, 0);
   if constexpr (C::BN == 64) {
-    constexpr int N0 = (C::SPLIT && PARITY != 0) ? NH - 1 : NH;
-    constexpr int N1 = (C::SPLIT && PARITY != 1) ? NH - 1 : NH;
-    consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
     if (dma_k0 >= 0) issue_tile_fast<C, DST>(x, ring_lds, dma_k0, H1, NI);
-    consume_chunk<C, NH, N1>(x, st, sK, sV, k0 + 32, 1);
-  } else {
-    constexpr int N0 = (C::SPLIT && PARITY != STAGE) ? NH - 1 : NH;
-    consume_chunk<C, NH, N0>(x, st, sK, sV, k0, 0);
+    consume_chunk<C, NH, NH>(x, st, sK, sV, k0 + 32, 1);
   }
 }
 
@@ -389,7 +377,7 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
   const int W = x.window;
   const int k_lo = W ? max(0, x.q_lo - W + 1) : 0;
   const int kt0 = k_lo / C::BN, kt1 = x.q_hi / C::BN;
-  constexpr int kv = (C::TWO_KV && PARITY == 1) ? 1 : 0;  // the B waves read the second KV head
+  constexpr int kv = (C::TWO_KV && PARITY == 1) ? 1 : 0;  // the B waves (PARITY 1) read the second KV head
   // The next tile's copies: spread over this tile when it ends inside the
   // sequence, else issued at once with row clamping.
   auto next_job = [&](int knext, int dst) -> int {
@@ -403,11 +391,11 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
   };
   for (int kt = kt0; kt <= kt1; kt += 2) {
     wait_loads_and_sync();
-    consume_tile<C, NH, PARITY, 0>(x, st, sk[0][kv], sv[0][kv], kt * C::BN, ring_lds,
+    consume_tile<C, NH, 0>(x, st, sk[0][kv], sv[0][kv], kt * C::BN, ring_lds,
                                    next_job((kt + 1) * C::BN, 1));
     if (kt + 1 > kt1) break;
     wait_loads_and_sync();
-    consume_tile<C, NH, PARITY, 1>(x, st, sk[1][kv], sv[1][kv], (kt + 1) * C::BN, ring_lds,
+    consume_tile<C, NH, 1>(x, st, sk[1][kv], sv[1][kv], (kt + 1) * C::BN, ring_lds,
                                    next_job((kt + 2) * C::BN, 0));
   }
 #pragma unroll
@@ -425,11 +413,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                 int units, int R, int nqt, int heavy_first, float c) {
   // K/V ring: two stages, each the tiles of the unit's KV heads.
   __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
-  // Normalised noise output handed from the A waves to the B waves, and the A
-  // waves' half of the shared head (O^T, reference max, sum per lane).
-  constexpr int SP_FLOATS = C::DB * 256 + 128;
+  // Normalised noise output handed from the A waves to the B waves.
   __shared__ __attribute__((aligned(16))) float sHN[C::NB > 0 ? C::NQG * C::DB * 4 * 64 : 4];
-  __shared__ __attribute__((aligned(16))) float sSP[C::SPLIT ? C::NQG * SP_FLOATS : 4];
 
   Ctx x;
   x.kg = kg;
@@ -483,14 +468,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   }
 
   if (!group_b) {
-    constexpr int NH = C::NA;  // [A signal heads][noise][shared head if SPLIT]
+    constexpr int NH = C::NA;  // [A signal heads][noise]
     constexpr int NZ = C::ASIG;  // index of the noise head in the state
     State<C, NH> st;
     const uint16_t* qrow[NH];
 #pragma unroll
     for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
     qrow[NZ] = q_noise + (row * N + u) * C::DQK;
-    if constexpr (C::SPLIT) qrow[NH - 1] = q_sig + (row * S + sig0 + C::ASIG) * C::DQK;
     run_tiles<C, NH, 0>(x, st, qrow, ring_lds, sk, sv);
     const float inv_n = 1.f / st.lsum[NZ];
     floatx4 hn[C::DB];
@@ -503,14 +487,6 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
       for (int db = 0; db < C::DB; ++db)
         *(floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4) = hn[db];
     }
-    if constexpr (C::SPLIT) {  // this group's half of the shared head, for the B waves
-      float* sp = sSP + qg * SP_FLOATS;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        *(floatx4*)(sp + (db * 64 + x.lane) * 4) = st.o[NH - 1][db];
-      sp[C::DB * 256 + x.lane] = st.mref[NH - 1];
-      sp[C::DB * 256 + 64 + x.lane] = st.lsum[NH - 1];
-    }
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
@@ -518,15 +494,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     }
     if (C::NB > 0) __syncthreads();
   } else if (C::NB > 0) {
-    constexpr int NH = C::NB > 0 ? C::NB : 1;  // [B signal heads][shared head if SPLIT]
-    constexpr int b_first = C::ASIG + (C::SPLIT ? 1 : 0);  // first B head, unit-relative
+    constexpr int NH = C::NB > 0 ? C::NB : 1;  // [B signal heads]
+    constexpr int b_first = C::ASIG;           // first B head, unit-relative
     State<C, NH> st;
     const uint16_t* qrow[NH];
 #pragma unroll
     for (int s = 0; s < C::BSIG; ++s) qrow[s] = q_sig + (row * S + sig0 + b_first + s) * C::DQK;
-    if constexpr (C::SPLIT) qrow[NH - 1] = q_sig + (row * S + sig0 + C::ASIG) * C::DQK;
     run_tiles<C, NH, 1>(x, st, qrow, ring_lds, sk, sv);
-    __syncthreads();  // the A waves' noise output (and shared-head half) is in LDS
+    __syncthreads();  // the A waves' noise output is in LDS
     floatx4 hn[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -536,25 +511,6 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
       for (int s = 0; s < C::BSIG; ++s)
         store_head<C::DV>(lam, gate, out, row, S, sig0 + b_first + s, x.g4, st.o[s],
                           1.f / st.lsum[s], hn);
-    }
-    if constexpr (C::SPLIT) {
-      // Merge the two halves of the shared head: m* = max(mA, mB),
-      // O = 2^(mA-m*) O_A + 2^(mB-m*) O_B, l likewise (mref is in log2 units).
-      const float* sp = sSP + qg * SP_FLOATS;
-      const float ma = sp[C::DB * 256 + x.lane], la = sp[C::DB * 256 + 64 + x.lane];
-      const float mb = st.mref[NH - 1], lb = st.lsum[NH - 1];
-      const float ms = fmaxf(ma, mb);
-      const float ea = fast_exp2(ma - ms), eb = fast_exp2(mb - ms);
-      floatx4 om[C::DB];
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const floatx4 oa = *(const floatx4*)(sp + (db * 64 + x.lane) * 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) om[db][r] = ea * oa[r] + eb * st.o[NH - 1][db][r];
-      }
-      if (t_ok)
-        store_head<C::DV>(lam, gate, out, row, S, sig0 + C::ASIG, x.g4, om,
-                          1.f / (ea * la + eb * lb), hn);
     }
   }
 }
@@ -580,16 +536,16 @@ hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
   const UnitPlan& p = a.plan;
   if (p.NN != 1) return (hipError_t)-1;
   if (p.R == 1) {
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false, false, NQG, BN>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false, false, NQG, BN>>(a, stream);
-    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, false, NQG, BN>>(a, stream);
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false, NQG, BN>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false, NQG, BN>>(a, stream);
+    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, NQG, BN>>(a, stream);
   } else if (p.R == 2) {
     // Two KV heads' tiles per stage: with dqk = 192 only 32-key tiles fit, and
     // those split evenly over 4 waves, not 8.
     constexpr int NQG2 = DQK > 128 ? 2 : NQG;
     constexpr int BN2 = DQK > 128 ? 32 : BN;
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, false, NQG2, BN2>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, false, NQG2, BN2>>(a, stream);
+    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, NQG2, BN2>>(a, stream);
+    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, NQG2, BN2>>(a, stream);
   }
   return (hipError_t)-1;
 }
