@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 
 #include "../../include/gda.h"
@@ -65,6 +66,15 @@ gda_status check_bf16_dims(int dqk, int dv) {
   return GDA_SUCCESS;
 }
 
+bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
+
+gda_status check_alignment(const void* a, const void* b, const void* c, const void* d,
+                           const void* e, const void* f, const void* g) {
+  for (const void* p : {a, b, c, d, e, f, g})
+    if (!aligned(p, 16)) return fail(GDA_ERROR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+  return GDA_SUCCESS;
+}
+
 gda_status from_hip(hipError_t e) {
   if (e == hipSuccess) {
     g_last_error[0] = '\0';
@@ -92,7 +102,9 @@ gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const 
                    int Hkv, int dqk, int dv, int window, gda_dtype dtype, void* stream) {
   if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out)
     return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
-  gda_status st = validate_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
+  gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, out);
+  if (st != GDA_SUCCESS) return st;
+  st = validate_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
   if (st != GDA_SUCCESS) return st;
   gda::FwdArgs a;
   a.q_sig = q_sig;
@@ -129,7 +141,10 @@ gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cach
                       int dqk, int dv, int window, gda_dtype dtype, void* stream) {
   if (!q_sig || !q_noise || !k_cache || !v_cache || !lambda || !gate || !out)
     return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
-  gda_status st = validate_common(B, Lmax, S, N, Hkv, dqk, dv, window, dtype);
+  gda_status st = check_alignment(q_sig, q_noise, k_cache, v_cache, lambda, gate, out);
+  if (st != GDA_SUCCESS) return st;
+  if (!aligned(cache_lens, 4)) return fail(GDA_ERROR_INVALID_ARGUMENT, "cache_lens must be 4-byte aligned");
+  st = validate_common(B, Lmax, S, N, Hkv, dqk, dv, window, dtype);
   if (st != GDA_SUCCESS) return st;
   gda::DecodeArgs a;
   a.q_sig = q_sig;

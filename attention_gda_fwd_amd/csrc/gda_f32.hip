@@ -2,14 +2,26 @@
 //
 // Same operation as the bf16 kernels (Motif 3 technical-report walk-through,
 // step 2 "GDLA forward", equation D_t, then the sigmoid gate), for fp32
-// tensors. It exists for fp32 callers and for checking the method at full fp32
-// precision; it is a plain VALU kernel (fp32 FMA, fp32 softmax, no bf16
-// rounding anywhere), not the tuned path. Any head layout the API accepts
-// works here.
+// tensors, with no bf16 rounding anywhere: scores, softmax weights P and
+// accumulators are all fp32.
 //
-// One thread computes 16 output channels of one (query row, signal head): it
-// streams the visible keys twice, once with the signal query and once with the
-// noise query of its group, each with an online softmax, and combines them.
+// Prefill at head sizes (64,64), (128,128), (192,128): fwd_f32_mfma_kernel, on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32). A workgroup takes 16 query
+// rows of one batch row and one noise head j with its g = S/N signal heads;
+// wave 0 computes noise head j, every other wave one signal head, each a whole
+// head in registers:
+//   S^T = K Q^T (A = a 16-key tile, B = the wave's 16 query rows), so lane l
+//   holds the scores of keys 4(l/16)..+3 of query row l%16; an online softmax
+//   per row (the row's four lane groups combine with lane swaps); then
+//   O^T += V^T P^T, whose B operand is P^T exactly as S^T left it in the
+//   lanes, provided the k index of step s is key 4(l/16)+s (the A operand,
+//   V^T, is loaded in that key order).
+// The noise head's normalised output goes through LDS in the accumulator
+// layout, so each signal wave reads back exactly its own lanes' rows and
+// channels, then applies lambda and the gate and stores.
+//
+// Any other head size: fwd_f32_kernel, a plain VALU kernel (one thread per 16
+// output channels of one (row, signal head)). Decode uses the VALU form too.
 #include "gda_device.hpp"
 #include "gda_kernels.hpp"
 
@@ -139,11 +151,190 @@ decode_f32_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_n
               gate + ((int64_t)b * S + i) * dv, o);
 }
 
+// ---- fp32 MFMA prefill ---------------------------------------------------------
+
+constexpr int MF_MAX_WAVES = 8;  // wave 0: noise head; waves 1..7: signal heads
+
+__device__ __forceinline__ floatx4 mfma_16x16x4(float a, float b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One head over 16 query rows: o[c] = normalised softmax(q k^T * scale) v, in
+// the accumulator layout (lane l: row row0 + l%16, channels 16c + 4(l/16) .. +3).
+// q points at row 0 of this head (row stride qstride floats), kb / vb at key 0
+// of its KV head (key strides kstride / vstride). Rows >= L are computed on
+// clamped (valid) addresses and never stored by the caller.
+template <int DQK, int DV>
+__device__ void head_f32(const float* __restrict__ q, int64_t qstride,
+                         const float* __restrict__ kb, const float* __restrict__ vb,
+                         int64_t kstride, int64_t vstride, int row0, int L, int window,
+                         float scale_log2, floatx4 (&o)[DV / 16]) {
+  constexpr int QB = DQK / 16, VC = DV / 16;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int row = row0 + lr;
+  // Dimension block sb of lane group lq is dims 16sb + 4lq .. +3; MFMA step
+  // 4sb + e takes component e, for Q and K alike (the dot product's terms are
+  // permuted the same way on both sides).
+  float4 qv[QB];
+  {
+    const float* qr = q + (int64_t)min(row, L - 1) * qstride + 4 * lq;
+#pragma unroll
+    for (int sb = 0; sb < QB; ++sb) qv[sb] = *(const float4*)(qr + 16 * sb);
+  }
+#pragma unroll
+  for (int c = 0; c < VC; ++c) o[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+  const int last = min(row0 + 15, L - 1);
+  const int first = window ? max(0, row0 - window + 1) : 0;
+  for (int key0 = first & ~15; key0 <= last; key0 += 16) {
+    float4 kv[QB];
+    {
+      const float* kr = kb + (int64_t)min(key0 + lr, L - 1) * kstride + 4 * lq;
+#pragma unroll
+      for (int sb = 0; sb < QB; ++sb) kv[sb] = *(const float4*)(kr + 16 * sb);
+    }
+    float vv[4][VC];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const float* vr = vb + (int64_t)min(key0 + 4 * lq + st, L - 1) * vstride + lr;
+#pragma unroll
+      for (int c = 0; c < VC; ++c) vv[st][c] = vr[16 * c];
+    }
+    floatx4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sb = 0; sb < QB; ++sb) {
+      sc = mfma_16x16x4(kv[sb].x, qv[sb].x, sc);
+      sc = mfma_16x16x4(kv[sb].y, qv[sb].y, sc);
+      sc = mfma_16x16x4(kv[sb].z, qv[sb].z, sc);
+      sc = mfma_16x16x4(kv[sb].w, qv[sb].w, sc);
+    }
+    float z[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 4 * lq + r;
+      const bool vis = key <= row && (window == 0 || row - key < window);
+      z[r] = vis ? sc[r] * scale_log2 : -INFINITY;
+      mt = fmaxf(mt, z[r]);
+    }
+    mt = col_max4(mt);
+    const float mn = fmaxf(m, mt);
+    float p[4];
+    float alpha = 1.f;
+    if (mn == -INFINITY) {  // no key of this row visible yet
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = 0.f;
+    } else {
+      alpha = fast_exp2(m - mn);  // 0 when m is still -inf
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(z[r] - mn);
+    }
+    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m = mn;
+#pragma unroll
+    for (int c = 0; c < VC; ++c) {
+      floatx4 acc = o[c] * alpha;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) acc = mfma_16x16x4(vv[st][c], p[st], acc);
+      o[c] = acc;
+    }
+  }
+  const float inv = 1.f / col_sum4(lsum);
+#pragma unroll
+  for (int c = 0; c < VC; ++c) o[c] = o[c] * inv;
+}
+
+template <int DQK, int DV>
+__global__ void __launch_bounds__(64 * MF_MAX_WAVES)
+fwd_f32_mfma_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_noise,
+                    const float* __restrict__ kg, const float* __restrict__ vg,
+                    const float* __restrict__ lam, const float* __restrict__ gate,
+                    float* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
+                    float scale_log2) {
+  constexpr int VC = DV / 16;
+  __shared__ floatx4 sHN[VC][64];
+  const int ntiles = (L + 15) / 16;
+  // Longest (latest) query tiles first.
+  const int bid = blockIdx.x;
+  const int j = bid % N;
+  const int b = (bid / N) % B;
+  const int tile = ntiles - 1 - bid / (N * B);
+  const int row0 = tile * 16;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
+  const int g = S / N;
+  const int64_t kstride = (int64_t)Hkv * DQK, vstride = (int64_t)Hkv * DV;
+  const float* kb0 = kg + (int64_t)b * L * kstride;
+  const float* vb0 = vg + (int64_t)b * L * vstride;
+  floatx4 o[VC];
+  int i = -1;
+  if (wave == 0) {
+    const int hk = (int)(((int64_t)j * Hkv) / N);
+    head_f32<DQK, DV>(q_noise + ((int64_t)b * L * N + j) * DQK, (int64_t)N * DQK,
+                      kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0, L,
+                      window, scale_log2, o);
+#pragma unroll
+    for (int c = 0; c < VC; ++c) sHN[c][lane] = o[c];
+  } else {
+    i = j * g + wave - 1;
+    if (i < (j + 1) * g) {
+      const int hk = (int)(((int64_t)i * Hkv) / S);
+      head_f32<DQK, DV>(q_sig + ((int64_t)b * L * S + i) * DQK, (int64_t)S * DQK,
+                        kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0,
+                        L, window, scale_log2, o);
+    }
+  }
+  __syncthreads();
+  if (wave == 0) return;
+  const int row = row0 + lr;
+  for (; i < (j + 1) * g; i += nw - 1) {
+    if (i != j * g + wave - 1) {  // heads beyond the first pass
+      const int hk = (int)(((int64_t)i * Hkv) / S);
+      head_f32<DQK, DV>(q_sig + ((int64_t)b * L * S + i) * DQK, (int64_t)S * DQK,
+                        kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0,
+                        L, window, scale_log2, o);
+    }
+    if (row < L) {
+      const int64_t ri = ((int64_t)b * L + row) * S + i;
+      const float li = lam[ri];
+      const float* gr = gate + ri * DV + 4 * lq;
+      float* orow = out + ri * DV + 4 * lq;
+#pragma unroll
+      for (int c = 0; c < VC; ++c) {
+        const floatx4 hn = sHN[c][lane];
+        const float4 gt = *(const float4*)(gr + 16 * c);
+        float4 y;
+        y.x = gt.x * (o[c][0] - li * hn[0]);
+        y.y = gt.y * (o[c][1] - li * hn[1]);
+        y.z = gt.z * (o[c][2] - li * hn[2]);
+        y.w = gt.w * (o[c][3] - li * hn[3]);
+        *(float4*)(orow + 16 * c) = y;
+      }
+    }
+  }
+}
+
+template <int DQK, int DV>
+hipError_t launch_f32_mfma(const FwdArgs& a, hipStream_t stream) {
+  const int g = a.S / a.N;
+  const int nw = 1 + min(g, MF_MAX_WAVES - 1);
+  const int64_t nblk = (int64_t)((a.L + 15) / 16) * a.B * a.N;
+  if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_f32_mfma_kernel<DQK, DV>), dim3((unsigned)nblk), dim3(64 * nw), 0,
+                     stream, (const float*)a.q_sig, (const float*)a.q_noise, (const float*)a.k,
+                     (const float*)a.v, (const float*)a.lam, (const float*)a.gate,
+                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.window, a.scale_log2);
+  return hipGetLastError();
+}
+
 int64_t blocks_for(int64_t threads) { return (threads + NT - 1) / NT; }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  if (a.dqk == 64 && a.dv == 64) return launch_f32_mfma<64, 64>(a, stream);
+  if (a.dqk == 128 && a.dv == 128) return launch_f32_mfma<128, 128>(a, stream);
+  if (a.dqk == 192 && a.dv == 128) return launch_f32_mfma<192, 128>(a, stream);
   const int64_t nblk = blocks_for((int64_t)a.B * a.L * a.S * ((a.dv + DCH - 1) / DCH));
   if (nblk > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)nblk), dim3(NT), 0, stream,

@@ -12,8 +12,16 @@ The headline ``value`` is the prefill's attention TFLOP/s, FLOPs counted as
 decode's HBM GB/s is reported beside it. Inputs are resident in HBM before the
 timed region; times come from HIP events on the stream the kernels run on.
 A breakdown times every other workload (Motif-2 layer, sliding window W=128,
-W=128 decode) outside the step. The CPU baseline is the fp64 oracle timed on a
-bounded sample of the prefill rows. Prints ONE JSON line.
+W=128 decode, the fp32 tiny case) outside the step: 10 warmup launches, 50 timed
+(median and min), and for the small ones a second run with a 1 GiB write between
+launches so that no input is left in L2 or the memory-side cache. The GPU clock
+is read with amd-smi while the prefill runs. The CPU baseline is the fp64 oracle
+timed on a bounded sample of the prefill rows. Prints ONE JSON line.
+
+    python bench.py --only <workload> [--steps K] [--warmup W]
+
+times one workload alone (and a 1 GiB copy kernel first, the scale for the
+byte counters): the form the hardware-counter runs use.
 """
 from __future__ import annotations
 
@@ -50,14 +58,16 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--breakdown-reps", type=int, default=20)
-    p.add_argument("--cpu-rows", type=int, default=512,
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--breakdown-reps", type=int, default=50)
+    p.add_argument("--cpu-rows", type=int, default=2048,
                    help="prefill rows of the CPU-baseline sample")
     p.add_argument("--profile", action="store_true",
                    help="short run for hardware counters: a 1 GiB copy kernel for scale, "
                         "then the timed steps only (no breakdown, no CPU baseline)")
+    p.add_argument("--only", default=None,
+                   help="time this one workload alone (a name from configs.CONFIGS)")
     return p.parse_args()
 
 
@@ -118,19 +128,123 @@ def fill_decode(cfg, torch, gin):
     return dev
 
 
-def event_times(torch, fn, reps, warmup):
-    """Per-launch milliseconds, HIP events on the current stream around each launch."""
+def event_times(torch, fn, reps, warmup, flush=None):
+    """Per-launch milliseconds, HIP events on the current stream around each launch.
+    With ``flush`` (a large device buffer) every launch is preceded, outside its
+    events, by a write of the whole buffer, which evicts the inputs from the caches."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(i)
         a.record()
         fn()
         b.record()
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
+
+
+def smi_clocks():
+    """Current graphics clocks (MHz) that amd-smi reports, or None if it cannot be read."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:  # a missing tool or an unexpected format only loses this figure
+        log(f"amd-smi clock read failed: {e}")
+        return None
+    found = []
+
+    def num(x):
+        if isinstance(x, dict):
+            x = x.get("value")
+        m = re.match(r"\s*([0-9.]+)", str(x)) if x is not None else None
+        return float(m.group(1)) if m else None
+
+    def walk(node):
+        if isinstance(node, dict):
+            for k, v in node.items():
+                if re.fullmatch(r"gfx_\d+", str(k).lower()) and isinstance(v, dict):
+                    mhz = num(v.get("clk"))
+                    if mhz is not None:
+                        found.append(mhz)
+                else:
+                    walk(v)
+        elif isinstance(node, list):
+            for v in node:
+                walk(v)
+    walk(data)
+    if not found:
+        log(f"amd-smi clock output not understood: {r.stdout[:1500]!r}")
+    return found or None
+
+
+def observed_clock(torch, fn, launches):
+    """Graphics clock read with amd-smi (in a thread) while ``launches`` launches of
+    ``fn`` run; None unless the GPU was still busy when the read ended."""
+    import threading
+    got = {}
+    reader = threading.Thread(target=lambda: got.update(mhz=smi_clocks()))
+    end = torch.cuda.Event()
+    fn()
+    torch.cuda.synchronize()
+    reader.start()
+    for _ in range(launches):
+        fn()
+    end.record()
+    reader.join()
+    busy = not end.query()
+    torch.cuda.synchronize()
+    clocks = got.get("mhz")
+    log(f"clock read: {clocks} MHz, GPU still busy after the read: {busy}")
+    if not clocks or not busy:
+        return None
+    return {"mhz_min": min(clocks), "mhz_max": max(clocks), "n_readings": len(clocks),
+            "source": "amd-smi metric --clock, read while the prefill ran"}
+
+
+def run_only(args, torch, C, gin, gda_fwd, gda_decode):
+    """One workload alone: a 1 GiB copy kernel (the byte counters' scale), then warmup
+    and timed launches. Prints a short JSON line."""
+    cfg = C.CONFIGS[args.only]
+    if cfg.kind == "fwd":
+        dev, _ = fill_fwd(cfg, torch, gin)
+        out = torch.empty_like(dev["gate"])
+
+        def fn():
+            gda_fwd(dev["q_sig"], dev["q_noise"], dev["k"], dev["v"], dev["lam"], dev["gate"],
+                    window=cfg.window, out=out)
+    else:
+        dev = fill_decode(cfg, torch, gin)
+        out = torch.empty_like(dev["gate"])
+
+        def fn():
+            gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"],
+                       dev["lam"], dev["gate"], window=cfg.window, out=out)
+    copy_kernel(torch)
+    ms = event_times(torch, fn, args.steps, args.warmup)
+    med = float(np.median(ms))
+    log(f"{cfg.name}: median {med:.4f} ms, min {min(ms):.4f} ms")
+    print(json.dumps({"mode": "only", "workload": cfg.name, "steps": args.steps,
+                      "warmup": args.warmup, "median_ms": round(med, 4),
+                      "min_ms": round(min(ms), 4), "avg_ms": round(sum(ms) / len(ms), 4),
+                      "tflops": round(cfg.flops() / (med * 1e-3) / 1e12, 2),
+                      "gbps": round(cfg.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}),
+          flush=True)
+
+
+def copy_kernel(torch):
+    """An elementwise copy that reads and writes 1 GiB: the scale for the byte counters."""
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("copy kernel: 1073741824 bytes read, 1073741824 bytes written")
 
 
 def main():
@@ -150,6 +264,9 @@ def main():
     from attention_gda_fwd_amd.api import gda_decode, gda_fwd
 
     torch.cuda.set_device(0)
+    if args.only:
+        run_only(args, torch, C, gin, gda_fwd, gda_decode)
+        return
     fwd_cfg, dec_cfg = C.CFG2, C.CFG4
     log(f"generating {fwd_cfg.name}")
     fdev, fhost0 = fill_fwd(fwd_cfg, torch, gin)
@@ -168,13 +285,7 @@ def main():
                    ddev["lam"], ddev["gate"], window=window, out=dout)
 
     if args.profile:
-        # Scale for the byte counters: an elementwise copy that reads and writes 1 GiB.
-        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        log("copy kernel: 1073741824 bytes read, 1073741824 bytes written")
-        del src, dst
+        copy_kernel(torch)
 
     # ---- timed steps: warmup, barrier + sync, K steps, sync -------------------------
     log(f"warmup {args.warmup} steps")
@@ -200,6 +311,8 @@ def main():
     fwd_ms = [a.elapsed_time(b) for a, b in fwd_ev]
     dec_ms = [a.elapsed_time(b) for a, b in dec_ev]
     f_avg = sum(fwd_ms) / len(fwd_ms)
+    log(f"prefill per launch: median {np.median(fwd_ms):.4f} min {min(fwd_ms):.4f} ms; "
+        f"decode median {np.median(dec_ms):.4f} min {min(dec_ms):.4f} ms")
     d_avg = sum(dec_ms) / len(dec_ms)
     f_flops = fwd_cfg.flops()
     f_tflops = f_flops / (f_avg * 1e-3) / 1e12
@@ -232,6 +345,9 @@ def main():
     # ---- breakdown: every other workload, timed on its own ----------------------------
     breakdown = {}
 
+    def flushed(ms):
+        return dict(median_ms=round(float(np.median(ms)), 4), min_ms=round(min(ms), 4))
+
     def record(cfg, ms, extra=None):
         med = float(np.median(ms))
         fl, by = cfg.flops(), cfg.algorithmic_bytes()
@@ -247,18 +363,27 @@ def main():
 
     record(fwd_cfg, fwd_ms)
     record(dec_cfg, dec_ms)
+    log("GPU clock while the prefill runs")
+    clock = observed_clock(torch, run_fwd, 1500)
     reps = args.breakdown_reps
-    record(C.CFG4W, event_times(torch, lambda: run_dec(128), reps, 5))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    log(f"breakdown {C.CFG4W.name}")
+    record(C.CFG4W, event_times(torch, lambda: run_dec(128), reps, 10), {
+        "flushed": flushed(event_times(torch, lambda: run_dec(128), reps, 10, flush))})
     del ddev
     torch.cuda.empty_cache()
     for cfg in (C.CFG1, C.CFG3, C.CFG0):
         log(f"breakdown {cfg.name}")
         dev, _ = fill_fwd(cfg, torch, gin)
         o = torch.empty_like(dev["gate"])
-        ms = event_times(torch, lambda: gda_fwd(dev["q_sig"], dev["q_noise"], dev["k"], dev["v"],
-                                                dev["lam"], dev["gate"], window=cfg.window,
-                                                out=o), reps, 5)
-        record(cfg, ms)
+
+        def fn():
+            gda_fwd(dev["q_sig"], dev["q_noise"], dev["k"], dev["v"], dev["lam"], dev["gate"],
+                    window=cfg.window, out=o)
+        extra = None
+        if cfg is not C.CFG3:  # the small workloads: also from cold caches
+            extra = {"flushed": flushed(event_times(torch, fn, reps, 10, flush))}
+        record(cfg, event_times(torch, fn, reps, 10), extra)
         del dev, o
         torch.cuda.empty_cache()
 
@@ -284,7 +409,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(f_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(f_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("prefill"),
-                     "kernel": "fwd_bf16_kernel<Cfg<192,128,2,2,false,false,4,64>>",
+                     "kernel": "fwd_bf16_kernel<Cfg<192,128,2,2,false,4,64>>",
                      "flops_per_launch": f_flops, "avg_launch_ms": round(f_avg, 4)},
         "decode_roofline": {"bound": "hbm", "achieved": round(d_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
@@ -298,6 +423,7 @@ def main():
                                    f"{cpu_flops / 1e9:.1f} GFLOP in {cpu_s:.1f} s"},
         "parity_sampled": {"rows": int(rows.size), "max_abs": float(err.max()),
                            "mean_abs": float(err.mean())},
+        "gpu_clock": clock,
         "breakdown": breakdown,
     }
     print(json.dumps(result), flush=True)

@@ -42,8 +42,8 @@ extern "C" {
 
 typedef enum {
   GDA_SUCCESS = 0,
-  GDA_ERROR_INVALID_ARGUMENT = 1, /* null pointer, size < 1, window < 0, head counts that
-                                     do not divide, unknown dtype                         */
+  GDA_ERROR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, size < 1, window < 0,
+                                     head counts that do not divide, unknown dtype         */
   GDA_ERROR_UNSUPPORTED = 2,      /* valid but not compiled: (dqk, dv) or head layout      */
   GDA_ERROR_HIP = 3               /* a HIP runtime or launch failure                       */
 } gda_status;
@@ -75,7 +75,7 @@ gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const 
  *   q_noise [B, N,   dqk]
  *   k_cache [B, Lmax, Hkv, dqk]
  *   v_cache [B, Lmax, Hkv, dv ]
- *   cache_lens  device int32 [B], or NULL for "every sequence holds Lmax tokens".
+ *   cache_lens  device int32 [B] (4-byte aligned), or NULL for "every sequence holds Lmax tokens".
  *               A length above Lmax is clamped to Lmax; a length below 1 yields
  *               an all-zero output row (there is no key to attend to).
  *   lambda  [B, S]

@@ -57,6 +57,8 @@ def _load():
         lib.gda_ref_fwd.argtypes = [vp] * 7 + [i64] * 8 + [ctypes.c_int, vp, i64, ctypes.c_int]
         lib.gda_ref_decode.restype = ctypes.c_int
         lib.gda_ref_decode.argtypes = [vp] * 8 + [i64] * 8 + [ctypes.c_int, ctypes.c_int]
+        lib.gda_ref_threads.restype = ctypes.c_int
+        lib.gda_ref_threads.argtypes = []
         _lib = lib
     return _lib
 
@@ -78,6 +80,11 @@ def _c(a: np.ndarray, code: int) -> np.ndarray:
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(_load().gda_ref_threads())
 
 
 def ref_fwd(q_sig, q_noise, k, v, lam, gate, *, window: int, rows=None,

@@ -25,6 +25,7 @@
 #include "gda_ref.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -227,3 +228,5 @@ int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
   }
   return failed ? -8 : 0;
 }
+
+int gda_ref_threads(void) { return omp_get_max_threads(); }

@@ -68,6 +68,9 @@ int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
                    int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
                    int64_t dqk, int64_t dv, int64_t window, int dtype, int mutant);
 
+/* Threads an OpenMP parallel region of this library starts with (for timing reports). */
+int gda_ref_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,13 +71,3 @@ class FwdCase:
         return oracle.ref_fwd(h["q_sig"], h["q_noise"], h["k"], h["v"], h["lam"], h["gate"],
                               window=self.window if window is None else window, rows=rows)
 
-
-def sample_rows(B: int, L: int, seed: int, extra: int = 8) -> np.ndarray:
-    """Flat row indices b*L + t: tile edges, both ends, window edges, and a few random rows."""
-    g = np.random.default_rng(seed)
-    ts = {0, 1, 15, 16, 63, 64, 65, 127, 128, 129, L // 2, L - 65, L - 64, L - 2, L - 1}
-    rows = []
-    for b in range(B):
-        tt = sorted(t for t in ts if 0 <= t < L) + list(g.integers(0, L, size=extra))
-        rows += [b * L + int(t) for t in tt]
-    return np.array(sorted(set(rows)), dtype=np.int64)

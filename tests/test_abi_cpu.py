@@ -62,6 +62,7 @@ INVALID_CASES = [
     dict(out=None), dict(B=0), dict(S=0), dict(N=0), dict(Hkv=0), dict(dqk=0), dict(dv=0),
     dict(B=-1), dict(window=-1), dict(S=8, N=3), dict(S=6, N=2, Hkv=4),
     dict(S=24, N=6, Hkv=4), dict(dtype=7),
+    dict(q=FAKE + 8), dict(k=FAKE + 4), dict(gate=FAKE + 2), dict(out=FAKE + 8),  # not 16B aligned
 ]
 
 
@@ -77,6 +78,11 @@ def test_decode_invalid_arguments(kw):
     if "L" in kw:
         kw = dict(kw, Lmax=kw.pop("L"))
     assert dec(**kw) == INVALID
+
+
+def test_decode_misaligned_lengths():
+    assert dec(lens=FAKE + 2) == INVALID
+    assert b"aligned" in _lib.load().gda_last_error()
 
 
 @pytest.mark.parametrize("kw", [dict(dqk=96, dv=96), dict(dqk=192, dv=192), dict(dqk=128, dv=64),

@@ -2,10 +2,12 @@
 
 * Full outputs at sizes the oracle finishes in seconds, with every workload's head
   layout, several tiles and a ragged tail.
-* The full-size workloads as the bench runs them, on sampled output rows the
-  oracle computes one by one.
+* The full-size workloads as the bench runs them (both windows for decode),
+  every output element.
 Tolerances: bf16 max |err| <= 2e-2 and mean |err| <= 2e-3; fp32 max |err| <= 1e-5.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -33,6 +35,18 @@ SMALL = {
                                      window=0, dtype="bf16"),
     "motif2_layout_f32_L100": dict(case_id=105, B=1, L=100, S=32, N=8, Hkv=16, dqk=128, dv=128,
                                    window=0, dtype="f32"),
+    # fp32 matrix-core kernel: head size 192 with a window and a ragged tail; g = 8
+    # signal heads per noise head (one wave takes a second head); more noise heads
+    # than KV heads
+    "f32_d192_w37_B2_L200": dict(case_id=106, B=2, L=200, S=8, N=2, Hkv=2, dqk=192, dv=128,
+                                 window=37, dtype="f32"),
+    "f32_g8_L77": dict(case_id=107, B=1, L=77, S=16, N=2, Hkv=2, dqk=64, dv=64, window=0,
+                       dtype="f32"),
+    "f32_n4_hkv2_w16_L90": dict(case_id=108, B=1, L=90, S=8, N=4, Hkv=2, dqk=128, dv=128,
+                                window=16, dtype="f32"),
+    # fp32 at a head size with no matrix-core instance (the VALU kernel)
+    "f32_odd_dims_L50": dict(case_id=109, B=2, L=50, S=4, N=2, Hkv=2, dqk=40, dv=24, window=0,
+                             dtype="f32"),
 }
 
 
@@ -72,19 +86,23 @@ def test_layout_sweep(layout, dims, window):
     U.assert_close(got, ref, "bf16", f"{layout} {dims} window={window}")
 
 
-@pytest.mark.parametrize("cfg", [C.CFG1, C.CFG2, C.CFG3], ids=lambda c: c.name)
-def test_full_size_sampled_rows(cfg):
+@pytest.mark.parametrize("cfg", [C.CFG1, C.CFG3, C.CFG2], ids=lambda c: c.name)
+def test_full_size_full_output(cfg):
+    """The full-size prefill workloads as the bench runs them, every output element
+    against the oracle (fp64, all host cores; the Motif-3 full layer takes ~2 minutes)."""
     U.log(f"parity {cfg.name}: generating inputs")
     case = U.FwdCase(cfg.case_id, B=cfg.B, L=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk,
                      dv=cfg.dv, window=cfg.window, dtype=cfg.dtype, rope_dims=cfg.rope_dims)
     U.log(f"parity {cfg.name}: running gda_fwd")
-    out = case.run_gpu()
+    got = U.to_f64(case.run_gpu())
     torch.cuda.synchronize()
-    rows = U.sample_rows(cfg.B, cfg.L, seed=cfg.case_id)
-    got = U.to_f64(out.reshape(cfg.B * cfg.L, cfg.S, cfg.dv)[torch.from_numpy(rows).cuda()])
-    U.log(f"parity {cfg.name}: oracle on {rows.size} rows")
-    ref = case.run_oracle(rows=rows)
-    U.assert_close(got, ref, cfg.dtype, f"{cfg.name} sampled rows")
+    U.log(f"parity {cfg.name}: oracle on all {cfg.B * cfg.L} rows")
+    t0 = time.perf_counter()
+    ref = case.run_oracle()
+    dt = time.perf_counter() - t0
+    U.log(f"parity {cfg.name}: oracle {dt:.1f} s = {cfg.flops() / dt / 1e9:.1f} GFLOP/s, "
+          f"{cfg.tokens() / dt:.0f} tokens/s ({oracle.threads()} threads)")
+    U.assert_close(got, ref, cfg.dtype, f"{cfg.name} full output")
 
 
 def _decode_case(case_id, *, B, Lmax, S, N, Hkv, dqk, dv, dtype, rope_dims=0):
@@ -128,42 +146,34 @@ def test_decode_small_ragged(name, window):
     np.testing.assert_array_equal(out_full[0], got[0])
 
 
-def test_decode_full_size_sampled_sequences():
-    """The full-cache decode (B=64, Lmax=32768, Motif 3 heads) at W=0 and W=128;
-    the oracle checks 4 sequences of each."""
+def test_decode_full_size_full_output():
+    """The full-cache decode (B=64, Lmax=32768, Motif 3 heads) at W=0 and W=128, every
+    sequence against the oracle. The 21.5 GB cache is generated on the host 8 sequences
+    at a time (a thread each), kept there for the oracle and copied to the device."""
+    from concurrent.futures import ThreadPoolExecutor
     cfg = C.CFG4
-    U.log("decode full size: generating the 21.5 GB cache sequence by sequence")
     shp = dict(Lmax=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk, dv=cfg.dv,
                dtype=cfg.dtype, rope_dims=cfg.rope_dims)
-    dev = dict(q_sig=torch.empty(cfg.B, cfg.S, cfg.dqk, dtype=torch.bfloat16, device="cuda"),
-               q_noise=torch.empty(cfg.B, cfg.N, cfg.dqk, dtype=torch.bfloat16, device="cuda"),
-               k_cache=torch.empty(cfg.B, cfg.L, cfg.Hkv, cfg.dqk, dtype=torch.bfloat16,
-                                   device="cuda"),
-               v_cache=torch.empty(cfg.B, cfg.L, cfg.Hkv, cfg.dv, dtype=torch.bfloat16,
-                                   device="cuda"),
-               lam=torch.empty(cfg.B, cfg.S, dtype=torch.bfloat16, device="cuda"),
-               gate=torch.empty(cfg.B, cfg.S, cfg.dv, dtype=torch.bfloat16, device="cuda"))
-    keep = {0, 1, 37, 63}
-    kept = {}
-    from concurrent.futures import ThreadPoolExecutor
+    host = None
+    U.log("decode full size: generating the 21.5 GB cache")
     with ThreadPoolExecutor(8) as ex:
-        for b0 in range(0, cfg.B, 8):  # 8 sequences (2.7 GB of host memory) at a time
-            rows = list(ex.map(lambda b: gin.decode_row(cfg.case_id, b, **shp),
-                               range(b0, min(b0 + 8, cfg.B))))
-            for b, row in zip(range(b0, b0 + len(rows)), rows):
+        for b0 in range(0, cfg.B, 8):
+            rows = ex.map(lambda b: gin.decode_row(cfg.case_id, b, **shp), range(b0, b0 + 8))
+            for b, row in zip(range(b0, b0 + 8), rows):
+                if host is None:
+                    host = {k: np.empty((cfg.B,) + v.shape, v.dtype) for k, v in row.items()}
                 for k, v in row.items():
-                    dev[k][b].copy_(torch.from_numpy(v).view(torch.bfloat16))
-                if b in keep:
-                    kept[b] = row
-            U.log(f"  generated {b0 + len(rows)}/{cfg.B} sequences")
-    seqs = sorted(keep)
+                    host[k][b] = v
+            U.log(f"  generated {b0 + 8}/{cfg.B} sequences")
+    dev = {k: U.to_dev(v, cfg.dtype) for k, v in host.items()}
     for window in (0, 128):
         out = gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"],
                          dev["lam"], dev["gate"], window=window)
-        got = U.to_f64(out[seqs])
-        stack = {k: np.stack([kept[b][k] for b in seqs]) for k in kept[seqs[0]]}
-        U.log(f"decode full size W={window}: oracle on sequences {seqs}")
-        ref = oracle.ref_decode(stack["q_sig"], stack["q_noise"], stack["k_cache"],
-                                stack["v_cache"], stack["lam"], stack["gate"], None,
-                                window=window)
-        U.assert_close(got, ref, "bf16", f"{cfg.name} W={window} sampled sequences")
+        got = U.to_f64(out)
+        U.log(f"decode full size W={window}: oracle on all {cfg.B} sequences")
+        t0 = time.perf_counter()
+        ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"],
+                                host["v_cache"], host["lam"], host["gate"], None, window=window)
+        U.log(f"decode full size W={window}: oracle {time.perf_counter() - t0:.1f} s "
+              f"({oracle.threads()} threads)")
+        U.assert_close(got, ref, "bf16", f"{cfg.name} W={window} full output")
