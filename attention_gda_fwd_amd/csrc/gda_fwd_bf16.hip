@@ -540,10 +540,11 @@ hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
     if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false, NQG, BN>>(a, stream);
     if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, NQG, BN>>(a, stream);
   } else if (p.R == 2) {
-    // Two KV heads' tiles per stage: with dqk = 192 only 32-key tiles fit, and
-    // those split evenly over 4 waves, not 8.
+    // Two KV heads' tiles per stage. With dqk = 192 only 32-key tiles fit, and
+    // those split evenly over 4 waves, not 8. With dqk = 128, 32-key tiles too:
+    // the 64-key form needs all 256 registers and runs 8% slower.
     constexpr int NQG2 = DQK > 128 ? 2 : NQG;
-    constexpr int BN2 = DQK > 128 ? 32 : BN;
+    constexpr int BN2 = DQK >= 128 ? 32 : BN;
     if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, NQG2, BN2>>(a, stream);
     if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, NQG2, BN2>>(a, stream);
   }

@@ -68,6 +68,8 @@ def parse():
                         "then the timed steps only (no breakdown, no CPU baseline)")
     p.add_argument("--only", default=None,
                    help="time this one workload alone (a name from configs.CONFIGS)")
+    p.add_argument("--clock", action="store_true",
+                   help="with --only: also read the graphics clock while it runs (~4 s)")
     return p.parse_args()
 
 
@@ -205,7 +207,7 @@ def observed_clock(torch, fn, launches):
     if not clocks or not busy:
         return None
     return {"mhz_min": min(clocks), "mhz_max": max(clocks), "n_readings": len(clocks),
-            "source": "amd-smi metric --clock, read while the prefill ran"}
+            "source": "amd-smi metric --clock, read while the kernel ran back to back"}
 
 
 def run_only(args, torch, C, gin, gda_fwd, gda_decode):
@@ -230,11 +232,13 @@ def run_only(args, torch, C, gin, gda_fwd, gda_decode):
     ms = event_times(torch, fn, args.steps, args.warmup)
     med = float(np.median(ms))
     log(f"{cfg.name}: median {med:.4f} ms, min {min(ms):.4f} ms")
+    clock = observed_clock(torch, fn, min(20000, max(50, int(4000 / med)))) if args.clock else None
     print(json.dumps({"mode": "only", "workload": cfg.name, "steps": args.steps,
                       "warmup": args.warmup, "median_ms": round(med, 4),
                       "min_ms": round(min(ms), 4), "avg_ms": round(sum(ms) / len(ms), 4),
                       "tflops": round(cfg.flops() / (med * 1e-3) / 1e12, 2),
-                      "gbps": round(cfg.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}),
+                      "gbps": round(cfg.algorithmic_bytes() / (med * 1e-3) / 1e9, 1),
+                      "gpu_clock": clock}),
           flush=True)
 
 
