@@ -108,6 +108,30 @@ __device__ __forceinline__ void dma16_lds(const void* sbase, uint32_t voff, uint
                : "memory", "m0");
 }
 
+// The same copy with the nontemporal hint: for data read once (a KV cache
+// stream). Each instruction should cover whole 128-byte lines; a line read in
+// two halves by two nontemporal instructions can be fetched twice.
+__device__ __forceinline__ void dma16_lds_nt(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t m0v = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(base), "s"(m0v)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding
+// (they complete in order, so the oldest ones have landed). Also a compiler
+// memory barrier: no LDS read of the landed data is moved above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 __device__ __forceinline__ u32x2 ldg8(const void* p) { return *(const u32x2*)p; }
 
 }  // namespace gda

@@ -418,7 +418,7 @@ def main():
         "decode_roofline": {"bound": "hbm", "achieved": round(d_gbps, 1), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
                             "traffic": measured_traffic("decode"),
-                            "kernel": "decode_bf16_kernel<192,128>",
+                            "kernel": "decode_stream_kernel<192,128>",
                             "bytes_per_launch": d_bytes, "avg_launch_ms": round(d_avg, 4)},
         "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
                          "cores": threads, "kind": "oracle",

@@ -146,6 +146,35 @@ def test_decode_small_ragged(name, window):
     np.testing.assert_array_equal(out_full[0], got[0])
 
 
+# Spans of 2048 keys and more take the streaming decode kernel (K/V chunks copied
+# to LDS); shorter ones the kernel above. Ragged lengths: a partial last chunk,
+# a single key, an empty cache, chunk-count edges.
+DEC_STREAM = {
+    "motif3_layout": dict(case_id=211, B=6, Lmax=2100, S=64, N=16, Hkv=16, dqk=192, dv=128,
+                          dtype="bf16", rope_dims=64),
+    "motif2_layout": dict(case_id=212, B=6, Lmax=2100, S=32, N=8, Hkv=16, dqk=128, dv=128,
+                          dtype="bf16"),
+    "tiny_layout": dict(case_id=213, B=6, Lmax=2100, S=8, N=2, Hkv=2, dqk=64, dv=64,
+                        dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("window", [0, 2050])
+@pytest.mark.parametrize("name", sorted(DEC_STREAM))
+def test_decode_stream_ragged(name, window):
+    kw = DEC_STREAM[name]
+    U.log(f"decode (streaming) parity {name} window={window}")
+    host, dev = _decode_case(**kw)
+    lens = np.array([2100, 1, 2048, 2049, 1377, 0], dtype=np.int32)
+    out = gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"], dev["lam"],
+                     dev["gate"], cache_lens=torch.from_numpy(lens).cuda(), window=window)
+    got = U.to_f64(out)
+    ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"], host["v_cache"],
+                            host["lam"], host["gate"], lens, window=window)
+    U.assert_close(got, ref, "bf16", f"decode stream {name} W={window}")
+    assert np.all(got[5] == 0.0), "a sequence with no visible key must give zeros"
+
+
 def test_decode_full_size_full_output():
     """The full-cache decode (B=64, Lmax=32768, Motif 3 heads) at W=0 and W=128, every
     sequence against the oracle. The 21.5 GB cache is generated on the host 8 sequences
