@@ -1,4 +1,4 @@
-"""The five workloads of the GDA forward path (shapes only; no arithmetic).
+"""The workloads of the GDA forward path (shapes only; no arithmetic).
 
 Head layouts follow the pages: Motif-2-12.7B has 32 signal + 8 noise query heads
 over 16 KV heads (overview page, sections 2.1-2.2); Motif 3 has 64 signal + 16
@@ -74,16 +74,23 @@ class Case:
         return self.B * self.L if self.kind == "fwd" else self.B
 
 
-CFG0 = Case("cfg0_f32_tiny", "fwd", "f32", B=1, L=256, S=8, N=2, Hkv=2, dqk=64, dv=64,
+TINY_F32 = Case("tiny_f32_L256", "fwd", "f32", B=1, L=256, S=8, N=2, Hkv=2, dqk=64, dv=64,
             window=0, case_id=0)
-CFG1 = Case("cfg1_motif2_L4096", "fwd", "bf16", B=1, L=4096, S=32, N=8, Hkv=16, dqk=128,
+MOTIF2 = Case("motif2_L4096", "fwd", "bf16", B=1, L=4096, S=32, N=8, Hkv=16, dqk=128,
             dv=128, window=0, case_id=1)
-CFG2 = Case("cfg2_motif3_full_B2_L8192", "fwd", "bf16", B=2, L=8192, S=64, N=16, Hkv=16,
+MOTIF3_FULL = Case("motif3_full_B2_L8192", "fwd", "bf16", B=2, L=8192, S=64, N=16, Hkv=16,
             dqk=192, dv=128, window=0, rope_dims=64, case_id=2)
-CFG3 = Case("cfg3_motif3_swa128_L32768", "fwd", "bf16", B=1, L=32768, S=64, N=16, Hkv=16,
+MOTIF3_SWA = Case("motif3_swa128_L32768", "fwd", "bf16", B=1, L=32768, S=64, N=16, Hkv=16,
             dqk=192, dv=128, window=128, rope_dims=64, case_id=3)
-CFG4 = Case("cfg4_motif3_decode_B64_Lk32768", "decode", "bf16", B=64, L=32768, S=64, N=16,
+MOTIF3_DECODE = Case("motif3_decode_B64_Lk32768", "decode", "bf16", B=64, L=32768, S=64, N=16,
             Hkv=16, dqk=192, dv=128, window=0, rope_dims=64, case_id=4)
-CFG4W = CFG4.with_(name="cfg4w_motif3_decode_B64_Lk32768_swa128", window=128)
+MOTIF3_DECODE_SWA = MOTIF3_DECODE.with_(name="motif3_decode_swa128_B64_Lk32768", window=128)
 
-CONFIGS = {c.name: c for c in (CFG0, CFG1, CFG2, CFG3, CFG4, CFG4W)}
+# One GPU's share of the Motif 3 full layer when 8 GPUs split its 16 units (whole
+# noise groups) with no exchange: 2 units, i.e. 8 signal + 2 noise heads over 2 KV
+# heads, at the same batch and length.
+MOTIF3_FULL_SHARD8 = MOTIF3_FULL.with_(name="motif3_full_B2_L8192_shard8", S=8, N=2, Hkv=2,
+                                       case_id=5)
+
+CONFIGS = {c.name: c for c in (TINY_F32, MOTIF2, MOTIF3_FULL, MOTIF3_SWA, MOTIF3_DECODE,
+                               MOTIF3_DECODE_SWA, MOTIF3_FULL_SHARD8)}

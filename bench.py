@@ -12,10 +12,10 @@ The headline ``value`` is the prefill's attention TFLOP/s, FLOPs counted as
 decode's HBM GB/s is reported beside it. Inputs are resident in HBM before the
 timed region; times come from HIP events on the stream the kernels run on.
 A breakdown times every other workload (Motif-2 layer, sliding window W=128,
-W=128 decode, the fp32 tiny case) outside the step: 10 warmup launches, 50 timed
+W=128 decode, one GPU's share of the full layer split over 8 GPUs, the fp32
+tiny case) outside the step: 10 warmup launches, 50 timed
 (median and min), and for the small ones a second run with a 1 GiB write between
-launches so that no input is left in L2 or the memory-side cache. The GPU clock
-is read with amd-smi while the prefill runs. The CPU baseline is the fp64 oracle
+launches so that no input is left in L2 or the memory-side cache. The CPU baseline is the fp64 oracle
 timed on a bounded sample of the prefill rows. Prints ONE JSON line.
 
     python bench.py --only <workload> [--steps K] [--warmup W]
@@ -68,8 +68,6 @@ def parse():
                         "then the timed steps only (no breakdown, no CPU baseline)")
     p.add_argument("--only", default=None,
                    help="time this one workload alone (a name from configs.CONFIGS)")
-    p.add_argument("--clock", action="store_true",
-                   help="with --only: also read the graphics clock while it runs (~4 s)")
     return p.parse_args()
 
 
@@ -82,6 +80,17 @@ def measured_traffic(kind: str):
     with open(os.path.join(CSRC, m["source"]), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     return m["bytes"] if sha == m["sha256"] else None
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def host_threads() -> int:
@@ -149,67 +158,6 @@ def event_times(torch, fn, reps, warmup, flush=None):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def smi_clocks():
-    """Current graphics clocks (MHz) that amd-smi reports, or None if it cannot be read."""
-    import re
-    import subprocess
-    try:
-        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
-                           text=True, timeout=30)
-        data = json.loads(r.stdout)
-    except Exception as e:  # a missing tool or an unexpected format only loses this figure
-        log(f"amd-smi clock read failed: {e}")
-        return None
-    found = []
-
-    def num(x):
-        if isinstance(x, dict):
-            x = x.get("value")
-        m = re.match(r"\s*([0-9.]+)", str(x)) if x is not None else None
-        return float(m.group(1)) if m else None
-
-    def walk(node):
-        if isinstance(node, dict):
-            for k, v in node.items():
-                if re.fullmatch(r"gfx_\d+", str(k).lower()) and isinstance(v, dict):
-                    mhz = num(v.get("clk"))
-                    if mhz is not None:
-                        found.append(mhz)
-                else:
-                    walk(v)
-        elif isinstance(node, list):
-            for v in node:
-                walk(v)
-    walk(data)
-    if not found:
-        log(f"amd-smi clock output not understood: {r.stdout[:1500]!r}")
-    return found or None
-
-
-def observed_clock(torch, fn, launches):
-    """Graphics clock read with amd-smi (in a thread) while ``launches`` launches of
-    ``fn`` run; None unless the GPU was still busy when the read ended."""
-    import threading
-    got = {}
-    reader = threading.Thread(target=lambda: got.update(mhz=smi_clocks()))
-    end = torch.cuda.Event()
-    fn()
-    torch.cuda.synchronize()
-    reader.start()
-    for _ in range(launches):
-        fn()
-    end.record()
-    reader.join()
-    busy = not end.query()
-    torch.cuda.synchronize()
-    clocks = got.get("mhz")
-    log(f"clock read: {clocks} MHz, GPU still busy after the read: {busy}")
-    if not clocks or not busy:
-        return None
-    return {"mhz_min": min(clocks), "mhz_max": max(clocks), "n_readings": len(clocks),
-            "source": "amd-smi metric --clock, read while the kernel ran back to back"}
-
-
 def run_only(args, torch, C, gin, gda_fwd, gda_decode):
     """One workload alone: a 1 GiB copy kernel (the byte counters' scale), then warmup
     and timed launches. Prints a short JSON line."""
@@ -232,13 +180,11 @@ def run_only(args, torch, C, gin, gda_fwd, gda_decode):
     ms = event_times(torch, fn, args.steps, args.warmup)
     med = float(np.median(ms))
     log(f"{cfg.name}: median {med:.4f} ms, min {min(ms):.4f} ms")
-    clock = observed_clock(torch, fn, min(20000, max(50, int(4000 / med)))) if args.clock else None
     print(json.dumps({"mode": "only", "workload": cfg.name, "steps": args.steps,
                       "warmup": args.warmup, "median_ms": round(med, 4),
                       "min_ms": round(min(ms), 4), "avg_ms": round(sum(ms) / len(ms), 4),
                       "tflops": round(cfg.flops() / (med * 1e-3) / 1e12, 2),
-                      "gbps": round(cfg.algorithmic_bytes() / (med * 1e-3) / 1e9, 1),
-                      "gpu_clock": clock}),
+                      "gbps": round(cfg.algorithmic_bytes() / (med * 1e-3) / 1e9, 1)}),
           flush=True)
 
 
@@ -271,7 +217,7 @@ def main():
     if args.only:
         run_only(args, torch, C, gin, gda_fwd, gda_decode)
         return
-    fwd_cfg, dec_cfg = C.CFG2, C.CFG4
+    fwd_cfg, dec_cfg = C.MOTIF3_FULL, C.MOTIF3_DECODE
     log(f"generating {fwd_cfg.name}")
     fdev, fhost0 = fill_fwd(fwd_cfg, torch, gin)
     log(f"generating {dec_cfg.name} (21.5 GB cache)")
@@ -367,16 +313,14 @@ def main():
 
     record(fwd_cfg, fwd_ms)
     record(dec_cfg, dec_ms)
-    log("GPU clock while the prefill runs")
-    clock = observed_clock(torch, run_fwd, 1500)
     reps = args.breakdown_reps
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-    log(f"breakdown {C.CFG4W.name}")
-    record(C.CFG4W, event_times(torch, lambda: run_dec(128), reps, 10), {
+    log(f"breakdown {C.MOTIF3_DECODE_SWA.name}")
+    record(C.MOTIF3_DECODE_SWA, event_times(torch, lambda: run_dec(128), reps, 10), {
         "flushed": flushed(event_times(torch, lambda: run_dec(128), reps, 10, flush))})
     del ddev
     torch.cuda.empty_cache()
-    for cfg in (C.CFG1, C.CFG3, C.CFG0):
+    for cfg in (C.MOTIF2, C.MOTIF3_SWA, C.MOTIF3_FULL_SHARD8, C.TINY_F32):
         log(f"breakdown {cfg.name}")
         dev, _ = fill_fwd(cfg, torch, gin)
         o = torch.empty_like(dev["gate"])
@@ -385,7 +329,7 @@ def main():
             gda_fwd(dev["q_sig"], dev["q_noise"], dev["k"], dev["v"], dev["lam"], dev["gate"],
                     window=cfg.window, out=o)
         extra = None
-        if cfg is not C.CFG3:  # the small workloads: also from cold caches
+        if cfg in (C.MOTIF2, C.TINY_F32):  # the small workloads: also from cold caches
             extra = {"flushed": flushed(event_times(torch, fn, reps, 10, flush))}
         record(cfg, event_times(torch, fn, reps, 10), extra)
         del dev, o
@@ -421,13 +365,12 @@ def main():
                             "kernel": "decode_stream_kernel<192,128>",
                             "bytes_per_launch": d_bytes, "avg_launch_ms": round(d_avg, 4)},
         "cpu_baseline": {"value": round(cpu_flops / cpu_s / 1e12, 6), "unit": "TFLOP/s",
-                         "cores": threads, "kind": "oracle",
+                         "cores": threads, "kind": "oracle", "cpu": host_cpu_model(),
                          "sample": f"{rows.size} query rows of batch row 0 of the prefill "
                                    f"workload (all 64 signal + 16 noise heads), "
                                    f"{cpu_flops / 1e9:.1f} GFLOP in {cpu_s:.1f} s"},
         "parity_sampled": {"rows": int(rows.size), "max_abs": float(err.max()),
                            "mean_abs": float(err.mean())},
-        "gpu_clock": clock,
         "breakdown": breakdown,
     }
     print(json.dumps(result), flush=True)

@@ -25,6 +25,20 @@ def log(msg: str) -> None:
     print(f"[gda-test {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
+def host_cpu() -> str:
+    """CPU model and the threads the oracle runs on, for timing logs."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {oracle.threads()} oracle threads"
+
+
 def to_dev(a: np.ndarray, dtype: str, device="cuda:0") -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype == "bf16":

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 SMALL = {
     # the fp32 workload itself, every output
-    "cfg0_f32_full": dict(case_id=0, B=1, L=256, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0,
+    "tiny_f32_L256_full": dict(case_id=0, B=1, L=256, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0,
                           dtype="f32"),
     "motif2_layout_L300": dict(case_id=101, B=1, L=300, S=32, N=8, Hkv=16, dqk=128, dv=128,
                                window=0, dtype="bf16"),
@@ -86,7 +86,8 @@ def test_layout_sweep(layout, dims, window):
     U.assert_close(got, ref, "bf16", f"{layout} {dims} window={window}")
 
 
-@pytest.mark.parametrize("cfg", [C.CFG1, C.CFG3, C.CFG2], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C.MOTIF2, C.MOTIF3_SWA, C.MOTIF3_FULL_SHARD8, C.MOTIF3_FULL],
+                         ids=lambda c: c.name)
 def test_full_size_full_output(cfg):
     """The full-size prefill workloads as the bench runs them, every output element
     against the oracle (fp64, all host cores; the Motif-3 full layer takes ~2 minutes)."""
@@ -101,7 +102,7 @@ def test_full_size_full_output(cfg):
     ref = case.run_oracle()
     dt = time.perf_counter() - t0
     U.log(f"parity {cfg.name}: oracle {dt:.1f} s = {cfg.flops() / dt / 1e9:.1f} GFLOP/s, "
-          f"{cfg.tokens() / dt:.0f} tokens/s ({oracle.threads()} threads)")
+          f"{cfg.tokens() / dt:.0f} tokens/s ({U.host_cpu()})")
     U.assert_close(got, ref, cfg.dtype, f"{cfg.name} full output")
 
 
@@ -180,7 +181,7 @@ def test_decode_full_size_full_output():
     sequence against the oracle. The 21.5 GB cache is generated on the host 8 sequences
     at a time (a thread each), kept there for the oracle and copied to the device."""
     from concurrent.futures import ThreadPoolExecutor
-    cfg = C.CFG4
+    cfg = C.MOTIF3_DECODE
     shp = dict(Lmax=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk, dv=cfg.dv,
                dtype=cfg.dtype, rope_dims=cfg.rope_dims)
     host = None
@@ -203,6 +204,7 @@ def test_decode_full_size_full_output():
         t0 = time.perf_counter()
         ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"],
                                 host["v_cache"], host["lam"], host["gate"], None, window=window)
-        U.log(f"decode full size W={window}: oracle {time.perf_counter() - t0:.1f} s "
-              f"({oracle.threads()} threads)")
+        dt = time.perf_counter() - t0
+        U.log(f"decode full size W={window}: oracle {dt:.2f} s = "
+              f"{cfg.with_(window=window).flops() / dt / 1e9:.1f} GFLOP/s ({U.host_cpu()})")
         U.assert_close(got, ref, "bf16", f"{cfg.name} W={window} full output")
