@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgda_ref.so")
 SRC = os.path.join(_HERE, "gda_ref.c")
 
 BF16, F32 = 0, 1
+LAMBDA_LOGITS, GATE_LOGITS = 1, 2
 (EXACT, MUT_DROP_LAMBDA, MUT_PLUS_LAMBDA, MUT_TILED_REPEAT, MUT_KV_INTERLEAVE, MUT_WINDOW_OBO,
  MUT_SCALE_DV, MUT_NO_GATE, MUT_NO_CAUSAL, MUT_K_TRANSPOSED, MUT_LAMBDA_BY_GROUP,
  MUT_NO_NORMALIZE, MUT_DECODE_POS, MUT_SKIP_FIRST_KEY) = range(14)
@@ -57,6 +58,13 @@ def _load():
         lib.gda_ref_fwd.argtypes = [vp] * 7 + [i64] * 8 + [ctypes.c_int, vp, i64, ctypes.c_int]
         lib.gda_ref_decode.restype = ctypes.c_int
         lib.gda_ref_decode.argtypes = [vp] * 8 + [i64] * 8 + [ctypes.c_int, ctypes.c_int]
+        f64 = ctypes.c_double
+        lib.gda_ref_fwd_ex.restype = ctypes.c_int
+        lib.gda_ref_fwd_ex.argtypes = ([vp] * 7 + [i64] * 8 + [ctypes.c_int, vp, i64, f64,
+                                                                ctypes.c_int, ctypes.c_int])
+        lib.gda_ref_decode_ex.restype = ctypes.c_int
+        lib.gda_ref_decode_ex.argtypes = ([vp] * 8 + [i64] * 8 + [ctypes.c_int, f64, ctypes.c_int,
+                                                                  ctypes.c_int])
         lib.gda_ref_threads.restype = ctypes.c_int
         lib.gda_ref_threads.argtypes = []
         _lib = lib
@@ -87,11 +95,18 @@ def threads() -> int:
     return int(_load().gda_ref_threads())
 
 
+def _flags(lambda_logits: bool, gate_logits: bool) -> int:
+    return (LAMBDA_LOGITS if lambda_logits else 0) | (GATE_LOGITS if gate_logits else 0)
+
+
 def ref_fwd(q_sig, q_noise, k, v, lam, gate, *, window: int, rows=None,
-            mutant: int = EXACT) -> np.ndarray:
+            mutant: int = EXACT, scale: float | None = None, lambda_logits: bool = False,
+            gate_logits: bool = False) -> np.ndarray:
     """Prefill oracle. Shapes: q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk],
     v [B,L,Hkv,dv], lam [B,L,S], gate [B,L,S,dv]. ``rows`` selects flat (b*L + t) rows;
-    the result is [B,L,S,dv] when ``rows`` is None, else [len(rows),S,dv] (float64)."""
+    the result is [B,L,S,dv] when ``rows`` is None, else [len(rows),S,dv] (float64).
+    ``scale`` replaces 1/sqrt(dqk); ``lambda_logits`` / ``gate_logits`` say those inputs
+    are logits (the sigmoid is applied here)."""
     code = _dtype_code(q_sig)
     q_sig, q_noise, k, v, lam, gate = (_c(x, code) for x in (q_sig, q_noise, k, v, lam, gate))
     B, L, S, dqk = q_sig.shape
@@ -107,16 +122,18 @@ def ref_fwd(q_sig, q_noise, k, v, lam, gate, *, window: int, rows=None,
         n_rows = rows_arr.size
         out = np.empty((n_rows, S, dv), dtype=np.float64)
         rp = _ptr(rows_arr)
-    rc = _load().gda_ref_fwd(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam), _ptr(gate),
-                             _ptr(out), B, L, S, N, Hkv, dqk, dv, int(window), code, rp, n_rows,
-                             int(mutant))
+    rc = _load().gda_ref_fwd_ex(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam),
+                                _ptr(gate), _ptr(out), B, L, S, N, Hkv, dqk, dv, int(window),
+                                code, rp, n_rows, float(scale or 0.0),
+                                _flags(lambda_logits, gate_logits), int(mutant))
     if rc != 0:
         raise ValueError(f"gda_ref_fwd rejected its arguments (code {rc})")
     return out
 
 
 def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window: int,
-               mutant: int = EXACT) -> np.ndarray:
+               mutant: int = EXACT, scale: float | None = None, lambda_logits: bool = False,
+               gate_logits: bool = False) -> np.ndarray:
     """Decode oracle. Shapes: q_sig [B,S,dqk], q_noise [B,N,dqk], k_cache [B,Lmax,Hkv,dqk],
     v_cache [B,Lmax,Hkv,dv], lam [B,S], gate [B,S,dv], lens int32 [B] or None (= Lmax).
     Returns [B,S,dv] float64."""
@@ -134,9 +151,10 @@ def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window
         assert lens.size == B
         lp = _ptr(lens)
     out = np.empty((B, S, dv), dtype=np.float64)
-    rc = _load().gda_ref_decode(_ptr(q_sig), _ptr(q_noise), _ptr(k_cache), _ptr(v_cache), lp,
-                                _ptr(lam), _ptr(gate), _ptr(out), B, Lmax, S, N, Hkv, dqk, dv,
-                                int(window), code, int(mutant))
+    rc = _load().gda_ref_decode_ex(_ptr(q_sig), _ptr(q_noise), _ptr(k_cache), _ptr(v_cache),
+                                   lp, _ptr(lam), _ptr(gate), _ptr(out), B, Lmax, S, N, Hkv,
+                                   dqk, dv, int(window), code, float(scale or 0.0),
+                                   _flags(lambda_logits, gate_logits), int(mutant))
     if rc != 0:
         raise ValueError(f"gda_ref_decode rejected its arguments (code {rc})")
     return out

@@ -16,7 +16,11 @@
  *     floor(j*Hkv/N), and noise head j serves signal heads g*j .. g*j+g-1
  *     (block order of "repeated g times by group");
  *   - lambda is one value per (token, signal head), broadcast over dv; lambda
- *     and gate arrive as values in (0,1) (the sigmoid is upstream);
+ *     and gate arrive as values in (0,1) (the sigmoid is upstream), or, when the
+ *     caller says so, as logits that the sigmoid 1/(1+exp(-x)) turns into those
+ *     values here (the walk-through's sigmoid gate G_t and sigmoid-bounded
+ *     per-token lambda, novelty point one);
+ *   - an explicit softmax scale replaces 1/sqrt(dqk) when the caller gives one;
  *   - key s is visible from query t iff s <= t and, for a window W >= 1,
  *     t - s <= W - 1 (W keys including the query's own); W = 0 is full causal;
  *   - decode attends from position len-1 of a cache that already holds it.
@@ -35,7 +39,11 @@ typedef struct {
   int64_t Lk, Hkv, dqk, dv;
   int dtype;
   int mutant;
+  double scale;  /* softmax scale given by the caller, or 0 for 1/sqrt(dqk) */
+  int flags;     /* GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS */
 } kv_view;
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /* Stored value -> double. bf16 is the upper half of a float32, so the
  * widening is exact. */
@@ -111,7 +119,9 @@ static void gda_row(const void* q_sig, int64_t qs_off, const void* q_noise, int6
   const int64_t Hkv = kv->Hkv, dqk = kv->dqk, dv = kv->dv;
   const int mut = kv->mutant;
   const int64_t g = S / N;
-  const double scale = 1.0 / sqrt((double)(mut == GDA_REF_MUT_SCALE_DV ? dv : dqk));
+  const double scale = kv->scale > 0.0
+                           ? kv->scale
+                           : 1.0 / sqrt((double)(mut == GDA_REF_MUT_SCALE_DV ? dv : dqk));
   int64_t lo, hi;
   visible_range(t, window, kv->Lk, mut, &lo, &hi);
 
@@ -124,8 +134,8 @@ static void gda_row(const void* q_sig, int64_t qs_off, const void* q_noise, int6
     const int64_t kvs = (mut == GDA_REF_MUT_KV_INTERLEAVE) ? i % Hkv : (i * Hkv) / S;
     attend(q_sig, qs_off + i * dqk, kv, b, kvs, lo, hi, scale, z, Hs);
     const int64_t j = (mut == GDA_REF_MUT_TILED_REPEAT) ? i % N : i / g;
-    const double lam = rd(lambda, lam_off + (mut == GDA_REF_MUT_LAMBDA_BY_GROUP ? j : i),
-                          kv->dtype);
+    double lam = rd(lambda, lam_off + (mut == GDA_REF_MUT_LAMBDA_BY_GROUP ? j : i), kv->dtype);
+    if (kv->flags & GDA_REF_LAMBDA_LOGITS) lam = sigmoid(lam);
     for (int64_t e = 0; e < dv; ++e) {
       double D;
       if (mut == GDA_REF_MUT_DROP_LAMBDA)
@@ -134,7 +144,8 @@ static void gda_row(const void* q_sig, int64_t qs_off, const void* q_noise, int6
         D = Hs[e] + lam * Hn[j * dv + e];
       else
         D = Hs[e] - lam * Hn[j * dv + e];
-      const double G = rd(gate, gate_off + i * dv + e, kv->dtype);
+      double G = rd(gate, gate_off + i * dv + e, kv->dtype);
+      if (kv->flags & GDA_REF_GATE_LOGITS) G = sigmoid(G);
       out[i * dv + e] = (mut == GDA_REF_MUT_NO_GATE) ? D : G * D;
     }
   }
@@ -154,10 +165,21 @@ int gda_ref_fwd(const void* q_sig, const void* q_noise, const void* k, const voi
                 const void* lambda, const void* gate, double* out, int64_t B, int64_t L,
                 int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
                 int dtype, const int64_t* rows, int64_t n_rows, int mutant) {
+  return gda_ref_fwd_ex(q_sig, q_noise, k, v, lambda, gate, out, B, L, S, N, Hkv, dqk, dv,
+                        window, dtype, rows, n_rows, 0.0, 0, mutant);
+}
+
+int gda_ref_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                   const void* lambda, const void* gate, double* out, int64_t B, int64_t L,
+                   int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
+                   int dtype, const int64_t* rows, int64_t n_rows, double softmax_scale,
+                   int flags, int mutant) {
   int rc = check_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
   if (rc) return rc;
   if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out) return -6;
-  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, mutant};
+  if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
+    return -9;
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
   const int64_t total = rows ? n_rows : B * L;
   for (int64_t r = 0; r < total; ++r) {
     const int64_t flat = rows ? rows[r] : r;
@@ -193,10 +215,21 @@ int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
                    const void* gate, double* out, int64_t B, int64_t Lmax, int64_t S,
                    int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window, int dtype,
                    int mutant) {
+  return gda_ref_decode_ex(q_sig, q_noise, k_cache, v_cache, cache_lens, lambda, gate, out, B,
+                           Lmax, S, N, Hkv, dqk, dv, window, dtype, 0.0, 0, mutant);
+}
+
+int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cache,
+                      const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                      const void* gate, double* out, int64_t B, int64_t Lmax, int64_t S,
+                      int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
+                      int dtype, double softmax_scale, int flags, int mutant) {
   int rc = check_common(B, Lmax, S, N, Hkv, dqk, dv, window, dtype);
   if (rc) return rc;
   if (!q_sig || !q_noise || !k_cache || !v_cache || !lambda || !gate || !out) return -6;
-  const kv_view kv = {k_cache, v_cache, Lmax, Hkv, dqk, dv, dtype, mutant};
+  if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
+    return -9;
+  const kv_view kv = {k_cache, v_cache, Lmax, Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
   int failed = 0;
 #pragma omp parallel
   {

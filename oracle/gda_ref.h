@@ -68,6 +68,25 @@ int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
                    int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
                    int64_t dqk, int64_t dv, int64_t window, int dtype, int mutant);
 
+/* Options of the _ex forms (0 and 0 give the plain forms above):
+ *   softmax_scale > 0 replaces 1/sqrt(dqk); 0 keeps it; negative or NaN is rejected;
+ *   flags: lambda and/or gate hold logits, turned into values by 1/(1+exp(-x)). */
+enum { GDA_REF_LAMBDA_LOGITS = 1, GDA_REF_GATE_LOGITS = 2 };
+
+int gda_ref_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                   const void* lambda, const void* gate, double* out,
+                   int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
+                   int64_t dqk, int64_t dv, int64_t window, int dtype,
+                   const int64_t* rows, int64_t n_rows, double softmax_scale, int flags,
+                   int mutant);
+
+int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cache,
+                      const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                      const void* gate, double* out,
+                      int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
+                      int64_t dqk, int64_t dv, int64_t window, int dtype,
+                      double softmax_scale, int flags, int mutant);
+
 /* Threads an OpenMP parallel region of this library starts with (for timing reports). */
 int gda_ref_threads(void);
 

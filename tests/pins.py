@@ -69,13 +69,13 @@ def band_mask(L, window):
     return m
 
 
-def sdpa(q, k, v, window):
+def sdpa(q, k, v, window, scale=None):
     """torch CPU float64 SDPA. q [B,L,d], k [B,L,d], v [B,L,e] -> [B,L,e]."""
     qt = torch.from_numpy(q)[:, None]
     kt = torch.from_numpy(k)[:, None]
     vt = torch.from_numpy(v)[:, None]
     out = torch.nn.functional.scaled_dot_product_attention(
-        qt, kt, vt, attn_mask=band_mask(q.shape[1], window))
+        qt, kt, vt, attn_mask=band_mask(q.shape[1], window), scale=scale)
     return out[:, 0].numpy()
 
 
@@ -302,6 +302,54 @@ def pin_brute_force(fwd):
                 ref = np.array(ref)
                 err = np.abs(o - ref).max() / max(1e-300, np.abs(ref).max())
                 _fail(msgs, f"brute force {name} L={L} W={W} {dtype}", err, 1e-12)
+    return msgs
+
+
+def pin_options(fwd_opt, decode_opt):
+    """The call options against library routines: an explicit softmax scale is SDPA's own
+    ``scale``; lambda/gate given as logits are torch.sigmoid of them (fp64); a zero logit
+    is exactly 0.5; decode with options is the last prefill row with the same options."""
+    msgs = []
+    for lay_name, W, scale in (("A", 0, 0.37), ("B", 3, 1.9), ("C", 0, 0.05)):
+        lay = LAYOUTS[lay_name]
+        x = make(lay_name, dqk=6, dv=4, L=7, case_id=1150)
+        qs, qn, k, v = (f64(x[n]) for n in ("q_sig", "q_noise", "k", "v"))
+        HS = np.stack([sdpa(qs[:, :, i], k[:, :, lay["kv_sig"](i)], v[:, :, lay["kv_sig"](i)], W,
+                            scale) for i in range(lay["S"])], axis=2)
+        HN = np.stack([sdpa(qn[:, :, j], k[:, :, lay["kv_noise"](j)], v[:, :, lay["kv_noise"](j)],
+                            W, scale) for j in range(lay["N"])], axis=2)
+        rep_ = HN[:, :, [lay["group"](i) for i in range(lay["S"])]]
+        # lam and gate storage reused as logits: N(0,1)-ish values via a shift
+        lam_logit = gin.to_storage((f64(x["lam"]) * 6.0 - 3.0).astype(np.float32), "f32")
+        gate_logit = gin.to_storage((f64(x["gate"]) * 8.0 - 4.0).astype(np.float32), "f32")
+        lamv = torch.sigmoid(torch.from_numpy(f64(lam_logit))).numpy()
+        gatev = torch.sigmoid(torch.from_numpy(f64(gate_logit))).numpy()
+        args = (x["q_sig"], x["q_noise"], x["k"], x["v"])
+        o = fwd_opt(*args, x["lam"], x["gate"], window=W, scale=scale)
+        exp_ = f64(x["gate"]) * (HS - f64(x["lam"])[..., None] * rep_)
+        _fail(msgs, f"explicit scale layout {lay_name} W={W}", np.abs(o - exp_).max(), 1e-12)
+        o = fwd_opt(*args, lam_logit, gate_logit, window=W, scale=scale, lambda_logits=True,
+                    gate_logits=True)
+        exp_ = gatev * (HS - lamv[..., None] * rep_)
+        _fail(msgs, f"logits layout {lay_name} W={W}", np.abs(o - exp_).max(), 1e-12)
+        o = fwd_opt(*args, x["lam"], gate_logit, window=W, scale=scale, gate_logits=True)
+        exp_ = gatev * (HS - f64(x["lam"])[..., None] * rep_)
+        _fail(msgs, f"gate logits only layout {lay_name} W={W}", np.abs(o - exp_).max(), 1e-12)
+        # zero logits are exactly one half
+        z = zeros_like_storage(x["lam"]), zeros_like_storage(x["gate"])
+        half = (gin.to_storage(np.full(x["lam"].shape, 0.5, np.float32), "f32"),
+                gin.to_storage(np.full(x["gate"].shape, 0.5, np.float32), "f32"))
+        oz = fwd_opt(*args, *z, window=W, lambda_logits=True, gate_logits=True)
+        oh = fwd_opt(*args, *half, window=W)
+        if not np.array_equal(oz, oh):
+            msgs.append(f"zero logits != 0.5 values layout {lay_name}")
+        # decode = last prefill row, with the same options
+        dec = decode_opt(x["q_sig"][:, -1], x["q_noise"][:, -1], x["k"], x["v"],
+                         lam_logit[:, -1], gate_logit[:, -1], window=W, scale=scale,
+                         lambda_logits=True, gate_logits=True)
+        full = fwd_opt(*args, lam_logit, gate_logit, window=W, scale=scale, lambda_logits=True,
+                       gate_logits=True)
+        _fail(msgs, f"decode options layout {lay_name}", np.abs(dec - full[:, -1]).max(), 1e-13)
     return msgs
 
 

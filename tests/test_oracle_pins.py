@@ -38,6 +38,36 @@ def test_planted_mistake_is_caught(name):
     assert pins.all_pins(fwd, dec), f"no pin catches the planted mistake {name!r}"
 
 
+def test_options_pin():
+    """Explicit softmax scale and logit inputs, against torch's SDPA and sigmoid."""
+    assert pins.pin_options(oracle.ref_fwd, oracle.ref_decode) == []
+
+
+def test_options_pin_catches_a_missing_sigmoid():
+    def fwd_no_sigmoid(*a, window, scale=None, lambda_logits=False, gate_logits=False):
+        return oracle.ref_fwd(*a, window=window, scale=scale, lambda_logits=lambda_logits)
+
+    def dec_no_sigmoid(*a, window, scale=None, lambda_logits=False, gate_logits=False):
+        return oracle.ref_decode(*a, window=window, scale=scale, lambda_logits=lambda_logits)
+
+    assert pins.pin_options(fwd_no_sigmoid, dec_no_sigmoid)
+
+    def fwd_default_scale(*a, window, scale=None, lambda_logits=False, gate_logits=False):
+        return oracle.ref_fwd(*a, window=window, lambda_logits=lambda_logits,
+                              gate_logits=gate_logits)
+
+    assert pins.pin_options(fwd_default_scale, oracle.ref_decode)
+
+
+def test_options_rejected():
+    x = pins.make("A", L=4)
+    args = (x["q_sig"], x["q_noise"], x["k"], x["v"], x["lam"], x["gate"])
+    with pytest.raises(ValueError):
+        oracle.ref_fwd(*args, window=0, scale=-1.0)
+    with pytest.raises(ValueError):
+        oracle.ref_fwd(*args, window=0, scale=float("nan"))
+
+
 def test_hand_worked_example():
     with open(os.path.join(HERE, "golden", "hand_worked_example.json")) as f:
         ex = json.load(f)
