@@ -13,8 +13,16 @@ LIB_PATH = os.path.join(PKG, "libgda.so")
 
 GDA_SUCCESS, GDA_ERROR_INVALID_ARGUMENT, GDA_ERROR_UNSUPPORTED, GDA_ERROR_HIP = range(4)
 GDA_BF16, GDA_F32 = 0, 1
+GDA_LAMBDA_LOGITS, GDA_GATE_LOGITS = 1, 2
 
-EXPORTED = ("gda_fwd", "gda_decode", "gda_status_string", "gda_last_error")
+EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_status_string",
+            "gda_last_error")
+
+
+class Options(ctypes.Structure):
+    """gda_options: softmax_scale (0 = 1/sqrt(dqk)) and flags."""
+    _fields_ = [("softmax_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
 
 _lib = None
 
@@ -41,6 +49,10 @@ def load() -> ctypes.CDLL:
     lib.gda_fwd.argtypes = [vp] * 7 + [i32] * 8 + [i32, vp]
     lib.gda_decode.restype = i32
     lib.gda_decode.argtypes = [vp] * 8 + [i32] * 8 + [i32, vp]
+    lib.gda_fwd_ex.restype = i32
+    lib.gda_fwd_ex.argtypes = [vp] * 7 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
+    lib.gda_decode_ex.restype = i32
+    lib.gda_decode_ex.argtypes = [vp] * 8 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
     lib.gda_status_string.restype = ctypes.c_char_p
     lib.gda_status_string.argtypes = [i32]
     lib.gda_last_error.restype = ctypes.c_char_p
@@ -69,3 +81,27 @@ def decode_raw(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax, 
     """Direct call of gda_decode with integer pointers; returns the status code."""
     return load().gda_decode(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax,
                              S, N, Hkv, dqk, dv, window, dtype, stream)
+
+
+def options(scale=None, lambda_logits=False, gate_logits=False):
+    """An Options value, or None when every option is the default."""
+    if scale is None and not lambda_logits and not gate_logits:
+        return None
+    flags = (GDA_LAMBDA_LOGITS if lambda_logits else 0) | (GDA_GATE_LOGITS if gate_logits else 0)
+    return Options(float(scale or 0.0), flags)
+
+
+def fwd_ex_raw(q_sig, q_noise, k, v, lam, gate, out, B, L, S, N, Hkv, dqk, dv, window, dtype,
+               opts, stream) -> int:
+    """Direct call of gda_fwd_ex (opts an Options or None)."""
+    return load().gda_fwd_ex(q_sig, q_noise, k, v, lam, gate, out, B, L, S, N, Hkv, dqk, dv,
+                             window, dtype, ctypes.byref(opts) if opts is not None else None,
+                             stream)
+
+
+def decode_ex_raw(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax, S, N, Hkv,
+                  dqk, dv, window, dtype, opts, stream) -> int:
+    """Direct call of gda_decode_ex (opts an Options or None)."""
+    return load().gda_decode_ex(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax,
+                                S, N, Hkv, dqk, dv, window, dtype,
+                                ctypes.byref(opts) if opts is not None else None, stream)

@@ -38,9 +38,12 @@ def _stream(device) -> int:
 
 def gda_fwd(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             lam: torch.Tensor, gate: torch.Tensor, window: int = 0,
-            out: torch.Tensor | None = None) -> torch.Tensor:
+            out: torch.Tensor | None = None, scale: float | None = None,
+            lambda_logits: bool = False, gate_logits: bool = False) -> torch.Tensor:
     """Prefill. q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk], v [B,L,Hkv,dv],
-    lam [B,L,S], gate [B,L,S,dv] -> out [B,L,S,dv] = gate*(H_S - lam*Repeat_g(H_N))."""
+    lam [B,L,S], gate [B,L,S,dv] -> out [B,L,S,dv] = gate*(H_S - lam*Repeat_g(H_N)).
+    ``scale`` replaces 1/sqrt(dqk); ``lambda_logits`` / ``gate_logits`` mark those inputs
+    as logits (the kernels apply the sigmoid)."""
     if q_sig.dim() != 4 or q_noise.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("gda_fwd: q_sig, q_noise, k, v must be 4-D")
     B, L, S, dqk = q_sig.shape
@@ -58,19 +61,21 @@ def gda_fwd(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor, v: torc
     if out is None:
         out = torch.empty((B, L, S, dv), dtype=dt, device=dev)
     _check("out", out, (B, L, S, dv), dt, dev)
-    _lib.check(_lib.fwd_raw(q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            lam.data_ptr(), gate.data_ptr(), out.data_ptr(), B, L, S, N, Hkv,
-                            dqk, dv, int(window), code, _stream(dev)))
+    _lib.check(_lib.fwd_ex_raw(q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(),
+                               v.data_ptr(), lam.data_ptr(), gate.data_ptr(), out.data_ptr(), B,
+                               L, S, N, Hkv, dqk, dv, int(window), code,
+                               _lib.options(scale, lambda_logits, gate_logits), _stream(dev)))
     return out
 
 
 def gda_decode(q_sig: torch.Tensor, q_noise: torch.Tensor, k_cache: torch.Tensor,
                v_cache: torch.Tensor, lam: torch.Tensor, gate: torch.Tensor,
                cache_lens: torch.Tensor | None = None, window: int = 0,
-               out: torch.Tensor | None = None) -> torch.Tensor:
+               out: torch.Tensor | None = None, scale: float | None = None,
+               lambda_logits: bool = False, gate_logits: bool = False) -> torch.Tensor:
     """Decode. q_sig [B,S,dqk], q_noise [B,N,dqk], k_cache [B,Lmax,Hkv,dqk],
     v_cache [B,Lmax,Hkv,dv], lam [B,S], gate [B,S,dv], cache_lens int32 [B] on the
-    device (or None = Lmax) -> out [B,S,dv]."""
+    device (or None = Lmax) -> out [B,S,dv]. Options as for gda_fwd."""
     if q_sig.dim() != 3 or q_noise.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("gda_decode: q_sig/q_noise must be 3-D and the caches 4-D")
     B, S, dqk = q_sig.shape
@@ -92,8 +97,9 @@ def gda_decode(q_sig: torch.Tensor, q_noise: torch.Tensor, k_cache: torch.Tensor
     if out is None:
         out = torch.empty((B, S, dv), dtype=dt, device=dev)
     _check("out", out, (B, S, dv), dt, dev)
-    _lib.check(_lib.decode_raw(q_sig.data_ptr(), q_noise.data_ptr(), k_cache.data_ptr(),
-                               v_cache.data_ptr(), lens_ptr, lam.data_ptr(), gate.data_ptr(),
-                               out.data_ptr(), B, Lmax, S, N, Hkv, dqk, dv, int(window), code,
-                               _stream(dev)))
+    _lib.check(_lib.decode_ex_raw(q_sig.data_ptr(), q_noise.data_ptr(), k_cache.data_ptr(),
+                                  v_cache.data_ptr(), lens_ptr, lam.data_ptr(), gate.data_ptr(),
+                                  out.data_ptr(), B, Lmax, S, N, Hkv, dqk, dv, int(window),
+                                  code, _lib.options(scale, lambda_logits, gate_logits),
+                                  _stream(dev)))
     return out

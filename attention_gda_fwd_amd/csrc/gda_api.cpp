@@ -75,6 +75,25 @@ gda_status check_alignment(const void* a, const void* b, const void* c, const vo
   return GDA_SUCCESS;
 }
 
+// Options of the _ex calls -> softmax scale and kernel flags; NULL is the plain call.
+gda_status apply_options(const gda_options* opts, int dqk, float* scale, float* scale_log2,
+                         int* flags) {
+  double sc = 1.0 / std::sqrt((double)dqk);
+  uint32_t fl = 0;
+  if (opts) {
+    if (!(opts->softmax_scale >= 0.0f) || !std::isfinite(opts->softmax_scale))
+      return fail(GDA_ERROR_INVALID_ARGUMENT, "softmax_scale must be 0 or a finite positive value");
+    if (opts->flags & ~(uint32_t)(GDA_LAMBDA_LOGITS | GDA_GATE_LOGITS))
+      return fail(GDA_ERROR_INVALID_ARGUMENT, "unknown option flags");
+    if (opts->softmax_scale > 0.0f) sc = (double)opts->softmax_scale;
+    fl = opts->flags;
+  }
+  *scale = (float)sc;
+  *scale_log2 = (float)(1.4426950408889634 * sc);
+  *flags = (int)fl;
+  return GDA_SUCCESS;
+}
+
 gda_status from_hip(hipError_t e) {
   if (e == hipSuccess) {
     g_last_error[0] = '\0';
@@ -100,6 +119,14 @@ extern "C" {
 gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
                    const void* lambda, const void* gate, void* out, int B, int L, int S, int N,
                    int Hkv, int dqk, int dv, int window, gda_dtype dtype, void* stream) {
+  return gda_fwd_ex(q_sig, q_noise, k, v, lambda, gate, out, B, L, S, N, Hkv, dqk, dv, window,
+                    dtype, nullptr, stream);
+}
+
+gda_status gda_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                      const void* lambda, const void* gate, void* out, int B, int L, int S,
+                      int N, int Hkv, int dqk, int dv, int window, gda_dtype dtype,
+                      const gda_options* opts, void* stream) {
   if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out)
     return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
   gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, out);
@@ -123,8 +150,8 @@ gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const 
   a.dv = dv;
   a.window = window;
   a.plan = make_plan(S, N, Hkv);
-  a.scale = (float)(1.0 / std::sqrt((double)dqk));
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dqk));
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
   if (dtype == GDA_BF16) {
     if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
     if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
@@ -139,6 +166,15 @@ gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cach
                       const void* v_cache, const int32_t* cache_lens, const void* lambda,
                       const void* gate, void* out, int B, int Lmax, int S, int N, int Hkv,
                       int dqk, int dv, int window, gda_dtype dtype, void* stream) {
+  return gda_decode_ex(q_sig, q_noise, k_cache, v_cache, cache_lens, lambda, gate, out, B, Lmax,
+                       S, N, Hkv, dqk, dv, window, dtype, nullptr, stream);
+}
+
+gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_cache,
+                         const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                         const void* gate, void* out, int B, int Lmax, int S, int N, int Hkv,
+                         int dqk, int dv, int window, gda_dtype dtype, const gda_options* opts,
+                         void* stream) {
   if (!q_sig || !q_noise || !k_cache || !v_cache || !lambda || !gate || !out)
     return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
   gda_status st = check_alignment(q_sig, q_noise, k_cache, v_cache, lambda, gate, out);
@@ -164,8 +200,8 @@ gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cach
   a.dv = dv;
   a.window = window;
   a.plan = make_plan(S, N, Hkv);
-  a.scale = (float)(1.0 / std::sqrt((double)dqk));
-  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dqk));
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
   if (dtype == GDA_BF16) {
     if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
     if (!gda::decode_bf16_supported(dqk, dv, a.plan))

@@ -78,7 +78,8 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
                    const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                    const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
                    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int Lmax,
-                   int S, int N, int Hkv, int window, int units, int NS, int NN, int R, float c) {
+                   int S, int N, int Hkv, int window, int units, int NS, int NN, int R, float c,
+                   int flags) {
   using T = DecTile<DQK, DV>;
   constexpr int DB = T::DB;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::SHARED_BYTES];
@@ -237,8 +238,10 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
         hn = sHN[d];
       }
       const int64_t o_idx = ((int64_t)b * S + i) * DV + d;
-      const float lm = bf16_to_f32(lam[(int64_t)b * S + i]);
-      const float gv = bf16_to_f32(gate[o_idx]);
+      float lm = bf16_to_f32(lam[(int64_t)b * S + i]);
+      float gv = bf16_to_f32(gate[o_idx]);
+      if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
+      if (flags & kGateLogits) gv = sigmoid_f32(gv);
       out[o_idx] = f32_to_bf16(gv * (hs - lm * hn));
     }
     __syncthreads();  // sH / stage reuse by the next phase
@@ -307,7 +310,7 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
                      const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
                      const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int Lmax,
                      int S, int N, int Hkv, int window, int units, int NS, int NN, int R,
-                     float c) {
+                     float c, int flags) {
   using T = StreamTile<DQK, DV>;
   constexpr int DB = T::DB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::SHARED_BYTES];
@@ -486,8 +489,10 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
         hn = hn_keep;  // this thread's d is the same in every phase (NT % DV == 0)
       }
       const int64_t o_idx = ((int64_t)b * S + i) * DV + d;
-      const float lm = bf16_to_f32(lam[(int64_t)b * S + i]);
-      const float gv = bf16_to_f32(gate[o_idx]);
+      float lm = bf16_to_f32(lam[(int64_t)b * S + i]);
+      float gv = bf16_to_f32(gate[o_idx]);
+      if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
+      if (flags & kGateLogits) gv = sigmoid_f32(gv);
       out[o_idx] = f32_to_bf16(gv * (hs - lm * hn));
     }
     __syncthreads();  // the next phase's copies overwrite the merge area
@@ -506,7 +511,8 @@ hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.lens, (const uint16_t*)a.lam,
                      (const uint16_t*)a.gate, (uint16_t*)a.out, a.Lmax, a.S, a.N, a.Hkv,
-                     a.window, a.plan.units, a.plan.NS, a.plan.NN, a.plan.R, a.scale_log2);
+                     a.window, a.plan.units, a.plan.NS, a.plan.NN, a.plan.R, a.scale_log2,
+                     a.flags);
   return hipGetLastError();
 }
 
@@ -518,7 +524,8 @@ hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.lens, (const uint16_t*)a.lam,
                      (const uint16_t*)a.gate, (uint16_t*)a.out, a.Lmax, a.S, a.N, a.Hkv,
-                     a.window, a.plan.units, a.plan.NS, a.plan.NN, a.plan.R, a.scale_log2);
+                     a.window, a.plan.units, a.plan.NS, a.plan.NN, a.plan.R, a.scale_log2,
+                     a.flags);
   return hipGetLastError();
 }
 

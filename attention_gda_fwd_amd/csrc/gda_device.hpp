@@ -67,6 +67,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Flags of the call options (the values of GDA_LAMBDA_LOGITS / GDA_GATE_LOGITS).
+constexpr int kLambdaLogits = 1, kGateLogits = 2;
+
+// 1 / (1 + e^-x) in fp32, for lambda and gate given as logits (a few ulp; 0 and 1
+// at the extremes, never NaN for finite x).
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + __expf(-x)); }
+
 // Read-only 16-byte global load.
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 

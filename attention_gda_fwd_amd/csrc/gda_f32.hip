@@ -72,14 +72,18 @@ struct F32Row {
 
 __device__ void combine_f32(const F32Row& r, int64_t kstride, int64_t vstride, int lo, int hi,
                             int dqk, int d0, int nd, float scale, float lam,
-                            const float* __restrict__ gate, float* __restrict__ out) {
+                            const float* __restrict__ gate, float* __restrict__ out, int flags) {
+  if (flags & kLambdaLogits) lam = sigmoid_f32(lam);
   float hs[DCH], hn[DCH], ls, ln;
   attend_row_f32(r.qs, r.kbase, r.vbase, kstride, vstride, lo, hi, dqk, d0, nd, scale, hs, ls);
   attend_row_f32(r.qn, r.knb, r.vnb, kstride, vstride, lo, hi, dqk, d0, nd, scale, hn, ln);
   const float is = 1.f / ls, in = 1.f / ln;
 #pragma unroll
   for (int e = 0; e < DCH; ++e)
-    if (e < nd) out[d0 + e] = gate[d0 + e] * (hs[e] * is - lam * (hn[e] * in));
+    if (e < nd) {
+      const float gv = (flags & kGateLogits) ? sigmoid_f32(gate[d0 + e]) : gate[d0 + e];
+      out[d0 + e] = gv * (hs[e] * is - lam * (hn[e] * in));
+    }
 }
 
 __global__ void __launch_bounds__(NT)
@@ -87,7 +91,7 @@ fwd_f32_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_nois
                const float* __restrict__ kg, const float* __restrict__ vg,
                const float* __restrict__ lam, const float* __restrict__ gate,
                float* __restrict__ out, int B, int L, int S, int N, int Hkv, int dqk, int dv,
-               int window, float scale) {
+               int window, float scale, int flags) {
   const int nchunk = (dv + DCH - 1) / DCH;
   const int64_t total = (int64_t)B * L * S * nchunk;
   const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
@@ -110,7 +114,7 @@ fwd_f32_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_nois
   r.vnb = vg + (int64_t)b * L * vstride + (int64_t)hn * dv;
   const int d0 = ch * DCH;
   combine_f32(r, kstride, vstride, lo, t, dqk, d0, min(DCH, dv - d0), scale, lam[row * S + i],
-              gate + (row * S + i) * dv, out + (row * S + i) * dv);
+              gate + (row * S + i) * dv, out + (row * S + i) * dv, flags);
 }
 
 __global__ void __launch_bounds__(NT)
@@ -118,7 +122,7 @@ decode_f32_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_n
                   const float* __restrict__ kg, const float* __restrict__ vg,
                   const int32_t* __restrict__ lens, const float* __restrict__ lam,
                   const float* __restrict__ gate, float* __restrict__ out, int B, int Lmax,
-                  int S, int N, int Hkv, int dqk, int dv, int window, float scale) {
+                  int S, int N, int Hkv, int dqk, int dv, int window, float scale, int flags) {
   const int nchunk = (dv + DCH - 1) / DCH;
   const int64_t total = (int64_t)B * S * nchunk;
   const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
@@ -148,7 +152,7 @@ decode_f32_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_n
   r.knb = kg + (int64_t)b * Lmax * kstride + (int64_t)hn * dqk;
   r.vnb = vg + (int64_t)b * Lmax * vstride + (int64_t)hn * dv;
   combine_f32(r, kstride, vstride, lo, pos, dqk, d0, nd, scale, lam[(int64_t)b * S + i],
-              gate + ((int64_t)b * S + i) * dv, o);
+              gate + ((int64_t)b * S + i) * dv, o, flags);
 }
 
 // ---- fp32 MFMA prefill ---------------------------------------------------------
@@ -250,7 +254,7 @@ fwd_f32_mfma_kernel(const float* __restrict__ q_sig, const float* __restrict__ q
                     const float* __restrict__ kg, const float* __restrict__ vg,
                     const float* __restrict__ lam, const float* __restrict__ gate,
                     float* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
-                    float scale_log2) {
+                    float scale_log2, int flags) {
   constexpr int VC = DV / 16;
   __shared__ floatx4 sHN[VC][64];
   const int ntiles = (L + 15) / 16;
@@ -296,13 +300,20 @@ fwd_f32_mfma_kernel(const float* __restrict__ q_sig, const float* __restrict__ q
     }
     if (row < L) {
       const int64_t ri = ((int64_t)b * L + row) * S + i;
-      const float li = lam[ri];
+      const float li = (flags & kLambdaLogits) ? sigmoid_f32(lam[ri]) : lam[ri];
+      const bool glog = (flags & kGateLogits) != 0;
       const float* gr = gate + ri * DV + 4 * lq;
       float* orow = out + ri * DV + 4 * lq;
 #pragma unroll
       for (int c = 0; c < VC; ++c) {
         const floatx4 hn = sHN[c][lane];
-        const float4 gt = *(const float4*)(gr + 16 * c);
+        float4 gt = *(const float4*)(gr + 16 * c);
+        if (glog) {
+          gt.x = sigmoid_f32(gt.x);
+          gt.y = sigmoid_f32(gt.y);
+          gt.z = sigmoid_f32(gt.z);
+          gt.w = sigmoid_f32(gt.w);
+        }
         float4 y;
         y.x = gt.x * (o[c][0] - li * hn[0]);
         y.y = gt.y * (o[c][1] - li * hn[1]);
@@ -323,7 +334,7 @@ hipError_t launch_f32_mfma(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_f32_mfma_kernel<DQK, DV>), dim3((unsigned)nblk), dim3(64 * nw), 0,
                      stream, (const float*)a.q_sig, (const float*)a.q_noise, (const float*)a.k,
                      (const float*)a.v, (const float*)a.lam, (const float*)a.gate,
-                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.window, a.scale_log2);
+                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.window, a.scale_log2, a.flags);
   return hipGetLastError();
 }
 
@@ -340,7 +351,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)nblk), dim3(NT), 0, stream,
                      (const float*)a.q_sig, (const float*)a.q_noise, (const float*)a.k,
                      (const float*)a.v, (const float*)a.lam, (const float*)a.gate,
-                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.dqk, a.dv, a.window, a.scale);
+                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.dqk, a.dv, a.window, a.scale,
+                     a.flags);
   return hipGetLastError();
 }
 
@@ -351,7 +363,7 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
                      (const float*)a.q_sig, (const float*)a.q_noise, (const float*)a.k,
                      (const float*)a.v, a.lens, (const float*)a.lam, (const float*)a.gate,
                      (float*)a.out, a.B, a.Lmax, a.S, a.N, a.Hkv, a.dqk, a.dv, a.window,
-                     a.scale);
+                     a.scale, a.flags);
   return hipGetLastError();
 }
 

@@ -342,20 +342,39 @@ template <int DV>
 __device__ __forceinline__ void store_head(const uint16_t* lam, const uint16_t* gate,
                                            uint16_t* out, int64_t row, int S, int i, int g4,
                                            const floatx4 (&hs)[DV / 16], float inv_s,
-                                           const floatx4 (&hn)[DV / 16]) {
-  const float lm = bf16_to_f32(lam[row * S + i]);
+                                           const floatx4 (&hn)[DV / 16], int flags) {
+  constexpr int DB = DV / 16;
   const int64_t base = (row * S + i) * DV + 4 * g4;
+  // Every gate load is issued before anything waits on one (the epilogue is
+  // latency-bound in short workgroups); the logit branches come after.
+  u32x2 gw[DB];
 #pragma unroll
-  for (int db = 0; db < DV / 16; ++db) {
-    const u32x2 gw = ldg8(gate + base + 16 * db);
-    const float d0 = hs[db][0] * inv_s - lm * hn[db][0];
-    const float d1 = hs[db][1] * inv_s - lm * hn[db][1];
-    const float d2 = hs[db][2] * inv_s - lm * hn[db][2];
-    const float d3 = hs[db][3] * inv_s - lm * hn[db][3];
-    u32x2 ow;
-    ow[0] = pack_bf16x2(bf16_lo(gw[0]) * d0, bf16_hi(gw[0]) * d1);
-    ow[1] = pack_bf16x2(bf16_lo(gw[1]) * d2, bf16_hi(gw[1]) * d3);
-    *(u32x2*)(out + base + 16 * db) = ow;
+  for (int db = 0; db < DB; ++db) gw[db] = ldg8(gate + base + 16 * db);
+  float lm = bf16_to_f32(lam[row * S + i]);
+  if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
+  float d[DB][4];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d[db][r] = hs[db][r] * inv_s - lm * hn[db][r];
+  if (flags & kGateLogits) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      u32x2 ow;
+      ow[0] = pack_bf16x2(sigmoid_f32(bf16_lo(gw[db][0])) * d[db][0],
+                          sigmoid_f32(bf16_hi(gw[db][0])) * d[db][1]);
+      ow[1] = pack_bf16x2(sigmoid_f32(bf16_lo(gw[db][1])) * d[db][2],
+                          sigmoid_f32(bf16_hi(gw[db][1])) * d[db][3]);
+      *(u32x2*)(out + base + 16 * db) = ow;
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      u32x2 ow;
+      ow[0] = pack_bf16x2(bf16_lo(gw[db][0]) * d[db][0], bf16_hi(gw[db][0]) * d[db][1]);
+      ow[1] = pack_bf16x2(bf16_lo(gw[db][1]) * d[db][2], bf16_hi(gw[db][1]) * d[db][3]);
+      *(u32x2*)(out + base + 16 * db) = ow;
+    }
   }
 }
 
@@ -410,7 +429,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
                 uint16_t* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
-                int units, int R, int nqt, int heavy_first, float c) {
+                int units, int R, int nqt, int heavy_first, float c, int flags) {
   // K/V ring: two stages, each the tiles of the unit's KV heads.
   __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
   // Normalised noise output handed from the A waves to the B waves.
@@ -490,7 +509,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
-        store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s], 1.f / st.lsum[s], hn);
+        store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s], 1.f / st.lsum[s], hn,
+                          flags);
     }
     if (C::NB > 0) __syncthreads();
   } else if (C::NB > 0) {
@@ -510,7 +530,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
       for (int s = 0; s < C::BSIG; ++s)
         store_head<C::DV>(lam, gate, out, row, S, sig0 + b_first + s, x.g4, st.o[s],
-                          1.f / st.lsum[s], hn);
+                          1.f / st.lsum[s], hn, flags);
     }
   }
 }
@@ -525,7 +545,7 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
                      (const uint16_t*)a.gate, (uint16_t*)a.out, a.B, a.L, a.S, a.N, a.Hkv,
-                     a.window, a.plan.units, a.plan.R, nqt, heavy_first, a.scale_log2);
+                     a.window, a.plan.units, a.plan.R, nqt, heavy_first, a.scale_log2, a.flags);
   return hipGetLastError();
 }
 

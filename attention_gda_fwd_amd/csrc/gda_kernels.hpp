@@ -26,8 +26,9 @@ struct FwdArgs {
   void* out;
   int B, L, S, N, Hkv, dqk, dv, window;
   UnitPlan plan;
-  float scale_log2;  // log2(e) / sqrt(dqk)
-  float scale;       // 1 / sqrt(dqk)
+  float scale_log2;  // log2(e) * softmax scale
+  float scale;       // softmax scale (1 / sqrt(dqk) unless the caller gives one)
+  int flags;         // GDA_LAMBDA_LOGITS | GDA_GATE_LOGITS
 };
 
 struct DecodeArgs {
@@ -43,6 +44,7 @@ struct DecodeArgs {
   UnitPlan plan;
   float scale_log2;
   float scale;
+  int flags;
 };
 
 // Each returns hipSuccess or the launch error; -1 cast to hipError_t means no

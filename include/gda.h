@@ -90,6 +90,36 @@ gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cach
                       int B, int Lmax, int S, int N, int Hkv, int dqk, int dv,
                       int window, gda_dtype dtype, void* stream);
 
+/* Call options of the _ex entry points (fused neighbours of the attention core).
+ *   softmax_scale: 0 = 1/sqrt(dqk) (the plain calls); > 0 = scores are q.k times
+ *     this value (for example a long-context mscale folded in); negative, NaN or
+ *     infinite values are rejected.
+ *   flags: GDA_LAMBDA_LOGITS - lambda holds logits; the kernels apply the
+ *     sigmoid 1/(1+exp(-x)) that makes lambda a per-token value in (0,1) (the
+ *     Motif 3 walk-through, novelty point one); GDA_GATE_LOGITS - the gate holds
+ *     logits, likewise (step 2's sigmoid gate G_t). Other bits are rejected.
+ * The sigmoid is computed in fp32 from the stored value. */
+typedef struct {
+  float softmax_scale;
+  uint32_t flags;
+} gda_options;
+
+enum { GDA_LAMBDA_LOGITS = 1u, GDA_GATE_LOGITS = 2u };
+
+/* gda_fwd / gda_decode with options; opts == NULL is the plain call. Everything
+ * else (arguments, layouts, ownership, errors) as for the plain calls; invalid
+ * options return GDA_ERROR_INVALID_ARGUMENT. */
+gda_status gda_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                      const void* lambda, const void* gate, void* out,
+                      int B, int L, int S, int N, int Hkv, int dqk, int dv,
+                      int window, gda_dtype dtype, const gda_options* opts, void* stream);
+
+gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_cache,
+                         const void* v_cache, const int32_t* cache_lens, const void* lambda,
+                         const void* gate, void* out,
+                         int B, int Lmax, int S, int N, int Hkv, int dqk, int dv,
+                         int window, gda_dtype dtype, const gda_options* opts, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* gda_status_string(gda_status s);
 

@@ -80,6 +80,38 @@ def test_decode_invalid_arguments(kw):
     assert dec(**kw) == INVALID
 
 
+def fwd_ex(opts, **kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, out=FAKE, B=1, L=64, S=8,
+             N=2, Hkv=2, dqk=64, dv=64, window=0, dtype=BF16, stream=None)
+    a.update(kw)
+    return _lib.fwd_ex_raw(a["q"], a["qn"], a["k"], a["v"], a["lam"], a["gate"], a["out"], a["B"],
+                           a["L"], a["S"], a["N"], a["Hkv"], a["dqk"], a["dv"], a["window"],
+                           a["dtype"], opts, a["stream"])
+
+
+def dec_ex(opts, **kw):
+    return _lib.decode_ex_raw(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 64, 8, 2, 2, 64,
+                              64, 0, kw.get("dtype", BF16), opts, None)
+
+
+@pytest.mark.parametrize("opts", [_lib.Options(-1.0, 0), _lib.Options(float("nan"), 0),
+                                  _lib.Options(float("inf"), 0), _lib.Options(0.0, 4),
+                                  _lib.Options(0.1, 0x80000000)],
+                         ids=["negative_scale", "nan_scale", "inf_scale", "flag4", "flag31"])
+def test_invalid_options(opts):
+    assert fwd_ex(opts) == INVALID
+    assert dec_ex(opts) == INVALID
+    assert fwd_ex(opts, dtype=F32) == INVALID
+
+
+def test_valid_options_reach_the_device_check():
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: a valid call would launch on the fake pointers")
+    for opts in (None, _lib.Options(0.0, 0), _lib.Options(0.125, 3)):
+        assert fwd_ex(opts) == HIPERR
+        assert dec_ex(opts) == HIPERR
+
+
 def test_decode_misaligned_lengths():
     assert dec(lens=FAKE + 2) == INVALID
     assert b"aligned" in _lib.load().gda_last_error()

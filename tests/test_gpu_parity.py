@@ -15,7 +15,7 @@ import torch
 import oracle
 from attention_gda_fwd_amd import configs as C
 from attention_gda_fwd_amd import inputs as gin
-from attention_gda_fwd_amd.api import gda_decode
+from attention_gda_fwd_amd.api import gda_decode, gda_fwd
 
 from . import gpu_util as U
 
@@ -174,6 +174,74 @@ def test_decode_stream_ragged(name, window):
                             host["lam"], host["gate"], lens, window=window)
     U.assert_close(got, ref, "bf16", f"decode stream {name} W={window}")
     assert np.all(got[5] == 0.0), "a sequence with no visible key must give zeros"
+
+
+# Call options: an explicit softmax scale, and lambda/gate given as logits (the kernels
+# apply the sigmoid). The logits are fresh N(0,1) draws in place of the sigmoid values.
+OPT_FWD = {
+    "bf16_motif3_w80_L200": (dict(case_id=121, B=1, L=200, S=64, N=16, Hkv=16, dqk=192,
+                                  dv=128, window=80, dtype="bf16", rope_dims=64),
+                             dict(scale=0.11, lambda_logits=True, gate_logits=True)),
+    "bf16_motif2_L150": (dict(case_id=122, B=1, L=150, S=32, N=8, Hkv=16, dqk=128, dv=128,
+                              window=0, dtype="bf16"), dict(scale=0.2, lambda_logits=True)),
+    "bf16_tiny_L99": (dict(case_id=123, B=2, L=99, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0,
+                           dtype="bf16"), dict(gate_logits=True)),
+    "f32_tiny_L100": (dict(case_id=124, B=1, L=100, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0,
+                           dtype="f32"), dict(scale=0.3, lambda_logits=True, gate_logits=True)),
+    "f32_odd_dims_L40": (dict(case_id=125, B=1, L=40, S=4, N=2, Hkv=2, dqk=40, dv=24, window=7,
+                              dtype="f32"), dict(scale=0.25, gate_logits=True)),
+}
+
+
+def _logits(case_id, shape, dtype):
+    return np.stack([gin.normal(case_id, 40 + len(shape), b, shape[1:], dtype)
+                     for b in range(shape[0])])
+
+
+@pytest.mark.parametrize("name", sorted(OPT_FWD))
+def test_fwd_options(name):
+    kw, opts = OPT_FWD[name]
+    U.log(f"options parity {name} {opts}")
+    case = U.FwdCase(**kw)
+    if opts.get("lambda_logits"):
+        case.host["lam"] = _logits(kw["case_id"], case.host["lam"].shape, kw["dtype"])
+    if opts.get("gate_logits"):
+        case.host["gate"] = _logits(kw["case_id"], case.host["gate"].shape, kw["dtype"])
+    d = {k: U.to_dev(v, kw["dtype"]) for k, v in case.host.items()}
+    got = U.to_f64(gda_fwd(d["q_sig"], d["q_noise"], d["k"], d["v"], d["lam"], d["gate"],
+                           window=kw["window"], **opts))
+    h = case.host
+    ref = oracle.ref_fwd(h["q_sig"], h["q_noise"], h["k"], h["v"], h["lam"], h["gate"],
+                         window=kw["window"], **opts)
+    U.assert_close(got, ref, kw["dtype"], f"options {name}")
+
+
+OPT_DEC = {
+    "short_motif3": (DEC_SMALL["motif3_layout"], 0,
+                     dict(scale=0.09, lambda_logits=True, gate_logits=True)),
+    "short_f32": (DEC_SMALL["tiny_layout_f32"], 5, dict(scale=0.3, gate_logits=True)),
+    "stream_tiny": (DEC_STREAM["tiny_layout"], 0,
+                    dict(scale=0.2, lambda_logits=True, gate_logits=True)),
+    "stream_motif2": (DEC_STREAM["motif2_layout"], 0, dict(lambda_logits=True)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(OPT_DEC))
+def test_decode_options(name):
+    kw, window, opts = OPT_DEC[name]
+    U.log(f"decode options parity {name} {opts}")
+    host, _ = _decode_case(**kw)
+    if opts.get("lambda_logits"):
+        host["lam"] = _logits(kw["case_id"], host["lam"].shape, kw["dtype"])
+    if opts.get("gate_logits"):
+        host["gate"] = _logits(kw["case_id"], host["gate"].shape, kw["dtype"])
+    dev = {k: U.to_dev(v, kw["dtype"]) for k, v in host.items()}
+    lens = np.array([kw["Lmax"], 1, 77, kw["Lmax"] - 1, 40, 0], dtype=np.int32)
+    out = gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"], dev["lam"],
+                     dev["gate"], cache_lens=torch.from_numpy(lens).cuda(), window=window, **opts)
+    ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"], host["v_cache"],
+                            host["lam"], host["gate"], lens, window=window, **opts)
+    U.assert_close(U.to_f64(out), ref, kw["dtype"], f"decode options {name}")
 
 
 def test_decode_full_size_full_output():
