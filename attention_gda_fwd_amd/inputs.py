@@ -20,6 +20,10 @@ Motif 3 head layouts, the values stand in for post-RoPE layer activations):
   ``rope_dims`` key columns are one draw per (b, token) shared by every KV head,
   mirroring the decoupled rotary key that the Motif 3 walk-through says is
   broadcast to all heads (step 2 and novelty point one).
+* latent-cache decode: the KV latent ``c_kv`` is ``standard_normal`` (unit RMS,
+  standing in for the RMSNorm output), the rotary key ``k_rope`` likewise; the
+  up-projection ``w_kv_b`` [Hkv, Dn + dv, Dc] is ``standard_normal / sqrt(Dc)``
+  (so that expanded keys and values have unit variance), drawn once per case.
 
 bf16 tensors are returned as ``uint16`` arrays holding the bf16 bit patterns.
 """
@@ -29,7 +33,7 @@ import numpy as np
 
 SEED_ROOT = 0x6DA
 
-T_QSIG, T_QNOISE, T_K, T_V, T_LAMBDA, T_GATE, T_KROPE = range(7)
+T_QSIG, T_QNOISE, T_K, T_V, T_LAMBDA, T_GATE, T_KROPE, T_CKV, T_WKVB = range(9)
 
 DTYPES = ("bf16", "f32")
 
@@ -139,3 +143,30 @@ def ragged_lens(case_id: int, B: int, Lmax: int) -> np.ndarray:
     if B >= 2:
         lens[1] = 1
     return lens.astype(np.int32)
+
+
+def latent_weights(case_id: int, *, Hkv, Dn, dv, Dc, dtype) -> np.ndarray:
+    """The up-projection W^KV_b [Hkv, Dn + dv, Dc] of a latent-cache case."""
+    z = rng(case_id, T_WKVB, 0).standard_normal(size=(Hkv, Dn + dv, Dc), dtype=np.float32)
+    return to_storage(z * np.float32(1.0 / np.sqrt(Dc)), dtype)
+
+
+def decode_latent_row(case_id, b, *, Lmax, S, N, Dn, Dr, Dc, dv, dtype):
+    """Latent-cache decode inputs of sequence b: q_sig [S,Dn+Dr], q_noise [N,Dn+Dr],
+    c_kv [Lmax,Dc], k_rope [Lmax,Dr], lam [S], gate [S,dv]."""
+    return dict(
+        q_sig=normal(case_id, T_QSIG, b, (S, Dn + Dr), dtype),
+        q_noise=normal(case_id, T_QNOISE, b, (N, Dn + Dr), dtype),
+        c_kv=normal(case_id, T_CKV, b, (Lmax, Dc), dtype),
+        k_rope=normal(case_id, T_KROPE, b, (Lmax, Dr), dtype),
+        lam=sigmoid_normal(case_id, T_LAMBDA, b, (S,), dtype),
+        gate=sigmoid_normal(case_id, T_GATE, b, (S, dv), dtype),
+    )
+
+
+def decode_latent_inputs(case_id, *, B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, dtype):
+    rows = [decode_latent_row(case_id, b, Lmax=Lmax, S=S, N=N, Dn=Dn, Dr=Dr, Dc=Dc, dv=dv,
+                              dtype=dtype) for b in range(B)]
+    out = {name: np.stack([r[name] for r in rows]) for name in rows[0]}
+    out["w_kv_b"] = latent_weights(case_id, Hkv=Hkv, Dn=Dn, dv=dv, Dc=Dc, dtype=dtype)
+    return out

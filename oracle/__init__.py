@@ -23,7 +23,8 @@ BF16, F32 = 0, 1
 LAMBDA_LOGITS, GATE_LOGITS = 1, 2
 (EXACT, MUT_DROP_LAMBDA, MUT_PLUS_LAMBDA, MUT_TILED_REPEAT, MUT_KV_INTERLEAVE, MUT_WINDOW_OBO,
  MUT_SCALE_DV, MUT_NO_GATE, MUT_NO_CAUSAL, MUT_K_TRANSPOSED, MUT_LAMBDA_BY_GROUP,
- MUT_NO_NORMALIZE, MUT_DECODE_POS, MUT_SKIP_FIRST_KEY) = range(14)
+ MUT_NO_NORMALIZE, MUT_DECODE_POS, MUT_SKIP_FIRST_KEY, MUT_LATENT_W_T, MUT_LATENT_NO_ROPE,
+ MUT_LATENT_V_ROWS) = range(17)
 MUTANTS = {
     "drop_lambda": MUT_DROP_LAMBDA, "plus_lambda": MUT_PLUS_LAMBDA,
     "tiled_repeat": MUT_TILED_REPEAT, "kv_interleave": MUT_KV_INTERLEAVE,
@@ -32,6 +33,9 @@ MUTANTS = {
     "lambda_by_group": MUT_LAMBDA_BY_GROUP, "no_normalize": MUT_NO_NORMALIZE,
     "decode_position": MUT_DECODE_POS, "skip_first_key": MUT_SKIP_FIRST_KEY,
 }
+# Planted mistakes of the latent-cache decode only.
+LATENT_MUTANTS = {"w_transposed": MUT_LATENT_W_T, "no_rope": MUT_LATENT_NO_ROPE,
+                  "value_from_key_rows": MUT_LATENT_V_ROWS}
 
 
 def build(force: bool = False) -> str:
@@ -65,6 +69,9 @@ def _load():
         lib.gda_ref_decode_ex.restype = ctypes.c_int
         lib.gda_ref_decode_ex.argtypes = ([vp] * 8 + [i64] * 8 + [ctypes.c_int, f64, ctypes.c_int,
                                                                   ctypes.c_int])
+        lib.gda_ref_decode_latent.restype = ctypes.c_int
+        lib.gda_ref_decode_latent.argtypes = ([vp] * 9 + [i64] * 10 + [ctypes.c_int, f64,
+                                                                     ctypes.c_int, ctypes.c_int])
         lib.gda_ref_threads.restype = ctypes.c_int
         lib.gda_ref_threads.argtypes = []
         _lib = lib
@@ -157,4 +164,39 @@ def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window
                                    _flags(lambda_logits, gate_logits), int(mutant))
     if rc != 0:
         raise ValueError(f"gda_ref_decode rejected its arguments (code {rc})")
+    return out
+
+
+def ref_decode_latent(q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, lens=None, *,
+                      window: int, scale: float | None = None, lambda_logits: bool = False,
+                      gate_logits: bool = False, mutant: int = EXACT) -> np.ndarray:
+    """Latent-cache decode oracle. Shapes: q_sig [B,S,Dn+Dr], q_noise [B,N,Dn+Dr],
+    c_kv [B,Lmax,Dc], k_rope [B,Lmax,Dr], w_kv_b [Hkv,Dn+dv,Dc], lam [B,S], gate [B,S,dv],
+    lens int32 [B] or None. Dr is k_rope's last dim; dv = w_kv_b rows - Dn. Returns
+    [B,S,dv] float64."""
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate = (
+        _c(x, code) for x in (q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate))
+    B, S, dqk = q_sig.shape
+    N = q_noise.shape[1]
+    Lmax, Dc = c_kv.shape[1], c_kv.shape[2]
+    Dr = k_rope.shape[2]
+    Hkv, rows = w_kv_b.shape[0], w_kv_b.shape[1]
+    Dn = dqk - Dr
+    dv = rows - Dn
+    assert q_noise.shape == (B, N, dqk) and c_kv.shape == (B, Lmax, Dc)
+    assert k_rope.shape == (B, Lmax, Dr) and w_kv_b.shape == (Hkv, Dn + dv, Dc)
+    assert lam.shape == (B, S) and gate.shape == (B, S, dv)
+    lp = None
+    if lens is not None:
+        lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32).reshape(-1))
+        assert lens.size == B
+        lp = _ptr(lens)
+    out = np.empty((B, S, dv), dtype=np.float64)
+    rc = _load().gda_ref_decode_latent(
+        _ptr(q_sig), _ptr(q_noise), _ptr(c_kv), _ptr(k_rope), _ptr(w_kv_b), lp, _ptr(lam),
+        _ptr(gate), _ptr(out), B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, int(window), code,
+        float(scale or 0.0), _flags(lambda_logits, gate_logits), int(mutant))
+    if rc != 0:
+        raise ValueError(f"gda_ref_decode_latent rejected its arguments (code {rc})")
     return out

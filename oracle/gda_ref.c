@@ -262,4 +262,132 @@ int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cach
   return failed ? -8 : 0;
 }
 
+/* ---- Latent-cache decode --------------------------------------------------------
+ * The cache holds, per token, the KV latent c (Dc values, after its RMSNorm) and
+ * the decoupled rotary key (Dr values, shared by every head); W^KV_b expands the
+ * latent into the KV heads (walk-through step 2: c_KV in R^512 -> RMSNorm -> W^KV_b
+ * -> 16 KV heads; novelty point one: both query paths share the up-projected KV
+ * and the broadcast rotary key, so the cache is MLA-sized). Written out plainly:
+ *   key of head h at s   = [ W[h][0:Dn] c_s ; k_rope_s ]      (Dn + Dr values)
+ *   value of head h at s = W[h][Dn:Dn+dv] c_s                 (dv values)
+ * each computed in double, then the decode of gda_ref_decode_ex over those keys
+ * and values (same head maps, window, lambda, gate, options). */
+static void expand_head(const void* c_kv, const void* w, int64_t b, int64_t h, int64_t lo,
+                        int64_t hi, int64_t Lmax, int64_t Dn, int64_t Dc, int64_t dv, int dtype,
+                        int mutant, double* Kh, double* Vh) {
+  const int64_t rows = Dn + dv;
+  for (int64_t s = lo; s <= hi; ++s) {
+    const int64_t c0 = (b * Lmax + s) * Dc;
+    for (int64_t r = 0; r < rows; ++r) {
+      int64_t wr = r;
+      if (mutant == GDA_REF_MUT_LATENT_V_ROWS && r >= Dn) wr = r - Dn; /* value from key rows */
+      double acc = 0.0;
+      for (int64_t c = 0; c < Dc; ++c) {
+        const int64_t wi = (mutant == GDA_REF_MUT_LATENT_W_T) ? (h * Dc + c) * rows + wr
+                                                               : (h * rows + wr) * Dc + c;
+        acc += rd(w, wi, dtype) * rd(c_kv, c0 + c, dtype);
+      }
+      if (r < Dn)
+        Kh[(s - lo) * Dn + r] = acc;
+      else
+        Vh[(s - lo) * dv + (r - Dn)] = acc;
+    }
+  }
+}
+
+/* Attention of one query head over the expanded keys/values of its KV head. */
+static void attend_latent(const void* q, int64_t q_off, const void* k_rope, int64_t b,
+                          int64_t lo, int64_t hi, int64_t Lmax, int64_t Dn, int64_t Dr,
+                          int64_t dv, int dtype, int mutant, double scale, const double* Kh,
+                          const double* Vh, double* z, double* H) {
+  for (int64_t e = 0; e < dv; ++e) H[e] = 0.0;
+  double m = -INFINITY;
+  for (int64_t s = lo; s <= hi; ++s) {
+    double acc = 0.0;
+    for (int64_t d = 0; d < Dn; ++d) acc += rd(q, q_off + d, dtype) * Kh[(s - lo) * Dn + d];
+    if (mutant != GDA_REF_MUT_LATENT_NO_ROPE)
+      for (int64_t r = 0; r < Dr; ++r)
+        acc += rd(q, q_off + Dn + r, dtype) * rd(k_rope, (b * Lmax + s) * Dr + r, dtype);
+    z[s - lo] = scale * acc;
+    if (z[s - lo] > m) m = z[s - lo];
+  }
+  double l = 0.0;
+  for (int64_t s = lo; s <= hi; ++s) {
+    z[s - lo] = exp(z[s - lo] - m);
+    l += z[s - lo];
+  }
+  for (int64_t s = lo; s <= hi; ++s)
+    for (int64_t e = 0; e < dv; ++e) H[e] += z[s - lo] * Vh[(s - lo) * dv + e];
+  for (int64_t e = 0; e < dv; ++e) H[e] /= l;
+}
+
+int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_kv,
+                          const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
+                          const void* lambda, const void* gate, double* out, int64_t B,
+                          int64_t Lmax, int64_t S, int64_t N, int64_t Hkv, int64_t Dn,
+                          int64_t Dr, int64_t Dc, int64_t dv, int64_t window, int dtype,
+                          double softmax_scale, int flags, int mutant) {
+  int rc = check_common(B, Lmax, S, N, Hkv, Dn + Dr, dv, window, dtype);
+  if (rc) return rc;
+  if (Dn < 1 || Dr < 0 || Dc < 1) return -1;
+  if (!q_sig || !q_noise || !c_kv || (Dr > 0 && !k_rope) || !w_kv_b || !lambda || !gate || !out)
+    return -6;
+  if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
+    return -9;
+  const int64_t dqk = Dn + Dr, g = S / N;
+  const double scale = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)dqk);
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* Kh = (double*)malloc(sizeof(double) * (size_t)(Lmax * Dn));
+    double* Vh = (double*)malloc(sizeof(double) * (size_t)(Lmax * dv));
+    double* z = (double*)malloc(sizeof(double) * (size_t)Lmax);
+    double* Hs = (double*)malloc(sizeof(double) * (size_t)(S * dv));
+    double* Hn = (double*)malloc(sizeof(double) * (size_t)(N * dv));
+    if (!Kh || !Vh || !z || !Hs || !Hn) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t b = 0; b < B; ++b) {
+        int64_t len = cache_lens ? (int64_t)cache_lens[b] : Lmax;
+        if (len > Lmax) len = Lmax;
+        double* o = out + b * S * dv;
+        if (len < 1) {
+          for (int64_t x = 0; x < S * dv; ++x) o[x] = 0.0;
+          continue;
+        }
+        const int64_t pos = len - 1;
+        const int64_t lo = window ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
+        for (int64_t h = 0; h < Hkv; ++h) {
+          expand_head(c_kv, w_kv_b, b, h, lo, pos, Lmax, Dn, Dc, dv, dtype, mutant, Kh, Vh);
+          for (int64_t j = 0; j < N; ++j)
+            if ((j * Hkv) / N == h)
+              attend_latent(q_noise, (b * N + j) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
+                            dtype, mutant, scale, Kh, Vh, z, Hn + j * dv);
+          for (int64_t i = 0; i < S; ++i)
+            if ((i * Hkv) / S == h)
+              attend_latent(q_sig, (b * S + i) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
+                            dtype, mutant, scale, Kh, Vh, z, Hs + i * dv);
+        }
+        for (int64_t i = 0; i < S; ++i) {
+          double lam = rd(lambda, b * S + i, dtype);
+          if (flags & GDA_REF_LAMBDA_LOGITS) lam = sigmoid(lam);
+          for (int64_t e = 0; e < dv; ++e) {
+            double G = rd(gate, (b * S + i) * dv + e, dtype);
+            if (flags & GDA_REF_GATE_LOGITS) G = sigmoid(G);
+            o[i * dv + e] = G * (Hs[i * dv + e] - lam * Hn[(i / g) * dv + e]);
+          }
+        }
+      }
+    }
+    free(Kh);
+    free(Vh);
+    free(z);
+    free(Hs);
+    free(Hn);
+  }
+  return failed ? -8 : 0;
+}
+
 int gda_ref_threads(void) { return omp_get_max_threads(); }

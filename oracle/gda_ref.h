@@ -41,7 +41,10 @@ enum {
   GDA_REF_MUT_NO_NORMALIZE = 11, /* softmax weights not divided by their sum */
   GDA_REF_MUT_DECODE_POS = 12,   /* decode query at position len, not len-1  */
   GDA_REF_MUT_SKIP_FIRST_KEY = 13, /* key 0 never visible                    */
-  GDA_REF_MUT_COUNT = 14
+  GDA_REF_MUT_LATENT_W_T = 14,   /* latent: W^KV_b read as [Hkv, Dc, Dn+dv]   */
+  GDA_REF_MUT_LATENT_NO_ROPE = 15, /* latent: rotary key term dropped         */
+  GDA_REF_MUT_LATENT_V_ROWS = 16, /* latent: value from the key rows of W     */
+  GDA_REF_MUT_COUNT = 17
 };
 
 /* Prefill. Layouts (row-major, innermost contiguous):
@@ -86,6 +89,19 @@ int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cach
                       int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
                       int64_t dqk, int64_t dv, int64_t window, int dtype,
                       double softmax_scale, int flags, int mutant);
+
+/* Latent-cache decode: the cache holds per token the KV latent c (Dc values) and
+ * the decoupled rotary key (Dr values, shared by all heads); w_kv_b [Hkv, Dn+dv, Dc]
+ * expands c into head h's key [W[h][0:Dn] c ; k_rope] and value W[h][Dn:Dn+dv] c.
+ *   q_sig [B,S,Dn+Dr], q_noise [B,N,Dn+Dr], c_kv [B,Lmax,Dc], k_rope [B,Lmax,Dr],
+ *   lambda [B,S], gate [B,S,dv], cache_lens as in gda_ref_decode; out [B,S,dv].
+ * The expansion is computed in double, then the decode definition applies. */
+int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_kv,
+                          const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
+                          const void* lambda, const void* gate, double* out,
+                          int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
+                          int64_t Dn, int64_t Dr, int64_t Dc, int64_t dv, int64_t window,
+                          int dtype, double softmax_scale, int flags, int mutant);
 
 /* Threads an OpenMP parallel region of this library starts with (for timing reports). */
 int gda_ref_threads(void);

@@ -353,6 +353,70 @@ def pin_options(fwd_opt, decode_opt):
     return msgs
 
 
+def _latent_expanded(x, w_sel=None):
+    """Expanded K/V tensors of a latent case for the (already pinned) expanded-cache
+    oracle. With ``w_sel`` = (cols, signs) [Hkv, Dn+dv] the up-projection is a signed
+    column selection, so the expansion is an exact copy of latent entries (any dtype);
+    otherwise it is a numpy float64 matmul stored as float32."""
+    ckv = f64(x["c_kv"])
+    B, Lmax, Dc = ckv.shape
+    Dr = x["k_rope"].shape[2]
+    Dn = x["q_sig"].shape[2] - Dr
+    if w_sel is not None:
+        cols, signs = w_sel
+        kvx = ckv[:, :, cols] * signs  # [B, Lmax, Hkv, Dn+dv], exact
+        st = "bf16" if x["c_kv"].dtype == np.uint16 else "f32"
+    else:
+        kvx = np.einsum("hrc,bsc->bshr", f64(x["w_kv_b"]), ckv)
+        st = "f32"
+    Hkv = kvx.shape[2]
+    k = np.concatenate([kvx[..., :Dn], np.broadcast_to(f64(x["k_rope"])[:, :, None, :],
+                                                        (B, Lmax, Hkv, Dr))], axis=-1)
+    v = kvx[..., Dn:]
+    conv = lambda a: gin.to_storage(np.ascontiguousarray(a).astype(np.float32), st)  # noqa: E731
+    return conv(k), conv(v), st
+
+
+def _pin_latent_layout(decode_latent, decode, shp):
+    msgs = []
+    lens = np.array([11, 1, 7, 0, 5], dtype=np.int32)
+    for dtype in ("f32", "bf16"):
+        x = gin.decode_latent_inputs(1300, B=5, Lmax=11, dtype=dtype, **shp)
+        rng = np.random.default_rng(1301)
+        cols = np.stack([rng.permutation(shp["Dc"])[:shp["Dn"] + shp["dv"]]
+                         for _ in range(shp["Hkv"])])
+        signs = rng.choice([-1.0, 1.0], size=cols.shape)
+        w = np.zeros((shp["Hkv"], shp["Dn"] + shp["dv"], shp["Dc"]), np.float32)
+        for h in range(shp["Hkv"]):
+            w[h, np.arange(cols.shape[1]), cols[h]] = signs[h]
+        xs = dict(x, w_kv_b=gin.to_storage(w, dtype))
+        k, v, st = _latent_expanded(xs, (cols, signs))
+        for W in (0, 3):
+            got = decode_latent(xs["q_sig"], xs["q_noise"], xs["c_kv"], xs["k_rope"], xs["w_kv_b"],
+                                xs["lam"], xs["gate"], lens, window=W)
+            ref = decode(xs["q_sig"], xs["q_noise"], k, v, xs["lam"], xs["gate"], lens, window=W)
+            _fail(msgs, f"latent selection {shp} {dtype} W={W}", np.abs(got - ref).max(), 1e-12)
+    x = gin.decode_latent_inputs(1302, B=5, Lmax=11, dtype="f32", **shp)
+    k, v, _ = _latent_expanded(x)
+    for W in (0, 4):
+        got = decode_latent(x["q_sig"], x["q_noise"], x["c_kv"], x["k_rope"], x["w_kv_b"],
+                            x["lam"], x["gate"], lens, window=W)
+        ref = decode(x["q_sig"], x["q_noise"], k, v, x["lam"], x["gate"], lens, window=W)
+        _fail(msgs, f"latent random {shp} W={W}", np.abs(got - ref).max(), 2e-6)
+    return msgs
+
+
+def pin_latent(decode_latent, decode):
+    """Latent-cache decode against the expanded-cache decode oracle on explicitly
+    expanded K/V: exactly (signed selection up-projections, bf16 and fp32) and to
+    float32 rounding (random up-projections), ragged lengths and windows."""
+    msgs = []
+    for shp in (dict(S=8, N=2, Hkv=2, Dn=6, Dr=4, Dc=16, dv=5),
+                dict(S=8, N=2, Hkv=4, Dn=5, Dr=3, Dc=12, dv=4)):  # noise on every other KV head
+        msgs += _pin_latent_layout(decode_latent, decode, shp)
+    return msgs
+
+
 def all_pins(fwd, decode):
     msgs = []
     for p in (pin_library_sdpa, pin_noise_one_hot, pin_identical_queries_zero,

@@ -68,6 +68,20 @@ def test_options_rejected():
         oracle.ref_fwd(*args, window=0, scale=float("nan"))
 
 
+def test_latent_pin():
+    assert pins.pin_latent(oracle.ref_decode_latent, oracle.ref_decode) == []
+
+
+@pytest.mark.parametrize("name", sorted(oracle.LATENT_MUTANTS))
+def test_latent_planted_mistake_is_caught(name):
+    m = oracle.LATENT_MUTANTS[name]
+
+    def planted(*a, window, **kw):
+        return oracle.ref_decode_latent(*a, window=window, mutant=m, **kw)
+
+    assert pins.pin_latent(planted, oracle.ref_decode), f"no pin catches {name!r}"
+
+
 def test_hand_worked_example():
     with open(os.path.join(HERE, "golden", "hand_worked_example.json")) as f:
         ex = json.load(f)
