@@ -15,8 +15,8 @@ GDA_SUCCESS, GDA_ERROR_INVALID_ARGUMENT, GDA_ERROR_UNSUPPORTED, GDA_ERROR_HIP = 
 GDA_BF16, GDA_F32 = 0, 1
 GDA_LAMBDA_LOGITS, GDA_GATE_LOGITS = 1, 2
 
-EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_status_string",
-            "gda_last_error")
+EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_decode_latent",
+            "gda_decode_latent_workspace_bytes", "gda_status_string", "gda_last_error")
 
 
 class Options(ctypes.Structure):
@@ -53,6 +53,11 @@ def load() -> ctypes.CDLL:
     lib.gda_fwd_ex.argtypes = [vp] * 7 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
     lib.gda_decode_ex.restype = i32
     lib.gda_decode_ex.argtypes = [vp] * 8 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
+    lib.gda_decode_latent_workspace_bytes.restype = ctypes.c_size_t
+    lib.gda_decode_latent_workspace_bytes.argtypes = [i32] * 5
+    lib.gda_decode_latent.restype = i32
+    lib.gda_decode_latent.argtypes = ([vp] * 9 + [i32] * 10 + [i32, ctypes.POINTER(Options), vp,
+                                                               ctypes.c_size_t, vp])
     lib.gda_status_string.restype = ctypes.c_char_p
     lib.gda_status_string.argtypes = [i32]
     lib.gda_last_error.restype = ctypes.c_char_p
@@ -105,3 +110,17 @@ def decode_ex_raw(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lma
     return load().gda_decode_ex(q_sig, q_noise, k_cache, v_cache, lens, lam, gate, out, B, Lmax,
                                 S, N, Hkv, dqk, dv, window, dtype,
                                 ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def latent_workspace_bytes(B, Lmax, S, N, window) -> int:
+    return int(load().gda_decode_latent_workspace_bytes(B, Lmax, S, N, window))
+
+
+def decode_latent_raw(q_sig, q_noise, c_kv, k_rope, w_kv_b, lens, lam, gate, out, B, Lmax, S, N,
+                      Hkv, Dn, Dr, Dc, dv, window, dtype, opts, workspace, workspace_bytes,
+                      stream) -> int:
+    """Direct call of gda_decode_latent (opts an Options or None)."""
+    return load().gda_decode_latent(q_sig, q_noise, c_kv, k_rope, w_kv_b, lens, lam, gate, out,
+                                    B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window, dtype,
+                                    ctypes.byref(opts) if opts is not None else None, workspace,
+                                    workspace_bytes, stream)

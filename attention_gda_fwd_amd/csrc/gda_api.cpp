@@ -212,6 +212,60 @@ gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_c
   return from_hip(dtype == GDA_BF16 ? gda::launch_decode_bf16(a, s) : gda::launch_decode_f32(a, s));
 }
 
+size_t gda_decode_latent_workspace_bytes(int B, int Lmax, int S, int N, int window) {
+  if (B < 1 || Lmax < 1 || S < 1 || N < 1 || window < 0) return 0;
+  return gda::latent_workspace_bytes(B, Lmax, S, N, window);
+}
+
+gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void* c_kv,
+                             const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
+                             const void* lambda, const void* gate, void* out, int B, int Lmax,
+                             int S, int N, int Hkv, int Dn, int Dr, int Dc, int dv, int window,
+                             gda_dtype dtype, const gda_options* opts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!q_sig || !q_noise || !c_kv || !k_rope || !w_kv_b || !lambda || !gate || !out)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
+  gda_status st = check_alignment(q_sig, q_noise, c_kv, k_rope, w_kv_b, lambda, gate);
+  if (st != GDA_SUCCESS) return st;
+  if (!aligned(out, 16)) return fail(GDA_ERROR_INVALID_ARGUMENT, "tensors must be 16-byte aligned");
+  if (!aligned(cache_lens, 4)) return fail(GDA_ERROR_INVALID_ARGUMENT, "cache_lens must be 4-byte aligned");
+  if (Dn < 1 || Dr < 0 || Dc < 1)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "every size must be >= 1 (Dr >= 0)");
+  st = validate_common(B, Lmax, S, N, Hkv, Dn + Dr, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  gda::LatentArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.w_kv_b = w_kv_b;
+  a.lens = cache_lens;
+  a.lam = lambda;
+  a.gate = gate;
+  a.out = out;
+  a.workspace = workspace;
+  a.B = B;
+  a.Lmax = Lmax;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.window = window;
+  float scale = 0.f;
+  if ((st = apply_options(opts, Dn + Dr, &scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
+  if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "latent decode: bf16 only");
+  if (!gda::latent_supported(Dn, Dr, Dc, dv, S, N, Hkv))
+    return fail(GDA_ERROR_UNSUPPORTED,
+                "latent decode: needs (Dn,Dr,Dc,dv) = (128,64,512,128), S+N <= 128, "
+                "g <= 15 and <= 16 query heads per KV head");
+  if (!workspace || !aligned(workspace, 16))
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "latent decode: workspace missing or misaligned");
+  if (workspace_bytes < gda::latent_workspace_bytes(B, Lmax, S, N, window))
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "latent decode: workspace too small");
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  return from_hip(gda::launch_decode_latent(a, (hipStream_t)stream));
+}
+
 const char* gda_status_string(gda_status s) {
   switch (s) {
     case GDA_SUCCESS:

@@ -357,6 +357,8 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
         if (qp) w = ldg16(qp + ks * 32 + 8 * g4);
         qf[ks] = __builtin_bit_cast(bf16x8, w);
       }
+#pragma unroll
+      for (int ks = 0; ks < T::KS; ++ks) settle(qf[ks]);  // before any copy is issued
     }
     const char* kcol = (const char*)(kg + ((int64_t)b * Lmax * Hkv + kvh) * DQK);  // key 0
     const char* vcol = (const char*)(vg + ((int64_t)b * Lmax * Hkv + kvh) * DV);

@@ -130,6 +130,13 @@ __device__ __forceinline__ void dma16_lds_nt(const void* sbase, uint32_t voff, u
                : "memory", "m0");
 }
 
+// Completes the loads that wrote v here. The compiler waits for a load just
+// before the first instruction that reads its result; when that first read sits
+// inside a loop, the wait (a vmcnt count that ignores the direct-to-LDS copies it
+// cannot see, and loads complete in order) runs every iteration and drains every
+// copy in flight. An empty asm that reads v moves the wait here, once.
+__device__ __forceinline__ void settle(const bf16x8& v) { asm volatile("" : : "v"(v)); }
+
 // Wait until at most N of this wave's vector-memory operations are outstanding
 // (they complete in order, so the oldest ones have landed). Also a compiler
 // memory barrier: no LDS read of the landed data is moved above it.

@@ -47,6 +47,22 @@ struct DecodeArgs {
   int flags;
 };
 
+struct LatentArgs {
+  const void* q_sig;   // [B, S, Dn+Dr]
+  const void* q_noise; // [B, N, Dn+Dr]
+  const void* c_kv;    // [B, Lmax, Dc]
+  const void* k_rope;  // [B, Lmax, Dr]
+  const void* w_kv_b;  // [Hkv, Dn+dv, Dc]
+  const int32_t* lens;
+  const void* lam;
+  const void* gate;
+  void* out;
+  void* workspace;
+  int B, Lmax, S, N, Hkv, window;
+  float scale_log2;
+  int flags;
+};
+
 // Each returns hipSuccess or the launch error; -1 cast to hipError_t means no
 // compiled instance matches (the host API checks support first).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
@@ -55,6 +71,9 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 bool fwd_bf16_supported(int dqk, int dv, const UnitPlan& plan);
+hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream);
+bool latent_supported(int Dn, int Dr, int Dc, int dv, int S, int N, int Hkv);
+size_t latent_workspace_bytes(int B, int Lmax, int S, int N, int window);
 bool decode_bf16_supported(int dqk, int dv, const UnitPlan& plan);
 
 }  // namespace gda

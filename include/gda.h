@@ -34,6 +34,7 @@
 #ifndef GDA_H
 #define GDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -119,6 +120,37 @@ gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_c
                          const void* gate, void* out,
                          int B, int Lmax, int S, int N, int Hkv, int dqk, int dv,
                          int window, gda_dtype dtype, const gda_options* opts, void* stream);
+
+/* Decode over the latent KV cache (GDLA's inference form; Motif 3 walk-through,
+ * step 2 "GDLA forward" and novelty point one: the cache holds the KV latent and
+ * the decoupled rotary key, MLA-sized, and W^KV_b expands the latent into the KV
+ * heads that signal and noise queries share).
+ *   q_sig   [B, S, Dn+Dr]   signal queries: Dn non-rotary dims, then Dr rotary dims
+ *   q_noise [B, N, Dn+Dr]
+ *   c_kv    [B, Lmax, Dc]   KV latent per cached token (after its RMSNorm)
+ *   k_rope  [B, Lmax, Dr]   decoupled rotary key per cached token (all heads)
+ *   w_kv_b  [Hkv, Dn+dv, Dc] up-projection of KV head h: rows 0..Dn-1 give the
+ *                           key's non-rotary part, rows Dn..Dn+dv-1 the value
+ *   cache_lens, lambda [B,S], gate [B,S,dv], out [B,S,dv], window: as gda_decode.
+ * Head h's key at token s is [w_kv_b[h][0:Dn] c_s ; k_rope_s], its value
+ * w_kv_b[h][Dn:Dn+dv] c_s; then exactly the gda_decode operation (scale
+ * 1/sqrt(Dn+Dr) unless opts gives one). Nothing is expanded in memory: the
+ * kernels attend in the latent space and up-project the result.
+ * workspace: device memory of at least gda_decode_latent_workspace_bytes(...)
+ * bytes, 16-byte aligned, owned by the caller and not read across calls; calls
+ * that share a workspace must be ordered (same stream).
+ * Supported: GDA_BF16, (Dn, Dr, Dc, dv) = (128, 64, 512, 128), S + N <= 128, at
+ * most 15 signal heads per noise head and 16 query heads per KV head
+ * (GDA_ERROR_UNSUPPORTED otherwise); a workspace that is too small or missing
+ * returns GDA_ERROR_INVALID_ARGUMENT. */
+size_t gda_decode_latent_workspace_bytes(int B, int Lmax, int S, int N, int window);
+
+gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void* c_kv,
+                             const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
+                             const void* lambda, const void* gate, void* out,
+                             int B, int Lmax, int S, int N, int Hkv, int Dn, int Dr, int Dc,
+                             int dv, int window, gda_dtype dtype, const gda_options* opts,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, never-NULL description of a status code. */
 const char* gda_status_string(gda_status s);

@@ -336,57 +336,66 @@ int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_
     return -9;
   const int64_t dqk = Dn + Dr, g = S / N;
   const double scale = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)dqk);
+  /* Per-head outputs of every sequence, then the combine. */
+  double* Hs = (double*)calloc((size_t)(B * S * dv), sizeof(double));
+  double* Hn = (double*)calloc((size_t)(B * N * dv), sizeof(double));
+  if (!Hs || !Hn) {
+    free(Hs);
+    free(Hn);
+    return -8;
+  }
   int failed = 0;
 #pragma omp parallel
   {
     double* Kh = (double*)malloc(sizeof(double) * (size_t)(Lmax * Dn));
     double* Vh = (double*)malloc(sizeof(double) * (size_t)(Lmax * dv));
     double* z = (double*)malloc(sizeof(double) * (size_t)Lmax);
-    double* Hs = (double*)malloc(sizeof(double) * (size_t)(S * dv));
-    double* Hn = (double*)malloc(sizeof(double) * (size_t)(N * dv));
-    if (!Kh || !Vh || !z || !Hs || !Hn) {
+    if (!Kh || !Vh || !z) {
 #pragma omp atomic write
       failed = 1;
     } else {
 #pragma omp for schedule(dynamic, 1)
-      for (int64_t b = 0; b < B; ++b) {
+      for (int64_t bh = 0; bh < B * Hkv; ++bh) {
+        const int64_t b = bh / Hkv, h = bh % Hkv;
         int64_t len = cache_lens ? (int64_t)cache_lens[b] : Lmax;
         if (len > Lmax) len = Lmax;
-        double* o = out + b * S * dv;
-        if (len < 1) {
-          for (int64_t x = 0; x < S * dv; ++x) o[x] = 0.0;
-          continue;
-        }
+        if (len < 1) continue;
         const int64_t pos = len - 1;
         const int64_t lo = window ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
-        for (int64_t h = 0; h < Hkv; ++h) {
-          expand_head(c_kv, w_kv_b, b, h, lo, pos, Lmax, Dn, Dc, dv, dtype, mutant, Kh, Vh);
-          for (int64_t j = 0; j < N; ++j)
-            if ((j * Hkv) / N == h)
-              attend_latent(q_noise, (b * N + j) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
-                            dtype, mutant, scale, Kh, Vh, z, Hn + j * dv);
-          for (int64_t i = 0; i < S; ++i)
-            if ((i * Hkv) / S == h)
-              attend_latent(q_sig, (b * S + i) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
-                            dtype, mutant, scale, Kh, Vh, z, Hs + i * dv);
-        }
-        for (int64_t i = 0; i < S; ++i) {
-          double lam = rd(lambda, b * S + i, dtype);
-          if (flags & GDA_REF_LAMBDA_LOGITS) lam = sigmoid(lam);
-          for (int64_t e = 0; e < dv; ++e) {
-            double G = rd(gate, (b * S + i) * dv + e, dtype);
-            if (flags & GDA_REF_GATE_LOGITS) G = sigmoid(G);
-            o[i * dv + e] = G * (Hs[i * dv + e] - lam * Hn[(i / g) * dv + e]);
-          }
-        }
+        expand_head(c_kv, w_kv_b, b, h, lo, pos, Lmax, Dn, Dc, dv, dtype, mutant, Kh, Vh);
+        for (int64_t j = 0; j < N; ++j)
+          if ((j * Hkv) / N == h)
+            attend_latent(q_noise, (b * N + j) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
+                          dtype, mutant, scale, Kh, Vh, z, Hn + (b * N + j) * dv);
+        for (int64_t i = 0; i < S; ++i)
+          if ((i * Hkv) / S == h)
+            attend_latent(q_sig, (b * S + i) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
+                          dtype, mutant, scale, Kh, Vh, z, Hs + (b * S + i) * dv);
       }
     }
     free(Kh);
     free(Vh);
     free(z);
-    free(Hs);
-    free(Hn);
   }
+  for (int64_t b = 0; b < B && !failed; ++b) {
+    int64_t len = cache_lens ? (int64_t)cache_lens[b] : Lmax;
+    double* o = out + b * S * dv;
+    for (int64_t i = 0; i < S; ++i) {
+      double lam = rd(lambda, b * S + i, dtype);
+      if (flags & GDA_REF_LAMBDA_LOGITS) lam = sigmoid(lam);
+      for (int64_t e = 0; e < dv; ++e) {
+        if (len < 1) {
+          o[i * dv + e] = 0.0;
+          continue;
+        }
+        double G = rd(gate, (b * S + i) * dv + e, dtype);
+        if (flags & GDA_REF_GATE_LOGITS) G = sigmoid(G);
+        o[i * dv + e] = G * (Hs[(b * S + i) * dv + e] - lam * Hn[(b * N + i / g) * dv + e]);
+      }
+    }
+  }
+  free(Hs);
+  free(Hn);
   return failed ? -8 : 0;
 }
 

@@ -112,6 +112,41 @@ def test_valid_options_reach_the_device_check():
         assert dec_ex(opts) == HIPERR
 
 
+def lat(ws=FAKE, ws_bytes=1 << 30, **kw):
+    a = dict(q=FAKE, qn=FAKE, c=FAKE, r=FAKE, w=FAKE, lens=None, lam=FAKE, gate=FAKE, out=FAKE,
+             B=2, Lmax=64, S=64, N=16, Hkv=16, Dn=128, Dr=64, Dc=512, dv=128, window=0,
+             dtype=BF16)
+    a.update(kw)
+    return _lib.decode_latent_raw(a["q"], a["qn"], a["c"], a["r"], a["w"], a["lens"], a["lam"],
+                                  a["gate"], a["out"], a["B"], a["Lmax"], a["S"], a["N"],
+                                  a["Hkv"], a["Dn"], a["Dr"], a["Dc"], a["dv"], a["window"],
+                                  a["dtype"], None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(c=None), dict(r=None), dict(w=None),
+                                dict(out=None), dict(c=FAKE + 8), dict(w=FAKE + 2), dict(B=0),
+                                dict(Dn=0), dict(Dr=-1), dict(S=8, N=3), dict(window=-1),
+                                dict(ws=None), dict(ws=FAKE + 8), dict(ws_bytes=100)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_latent_invalid_arguments(kw):
+    assert lat(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=F32), dict(Dc=256), dict(Dn=64), dict(dv=64),
+                                dict(S=128, N=16, Hkv=16),   # 144 query heads
+                                dict(S=64, N=4, Hkv=4)],     # 16 signal heads per noise head
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_latent_unsupported(kw):
+    assert lat(**kw) == UNSUPPORTED
+
+
+def test_latent_workspace_size():
+    n = _lib.latent_workspace_bytes(64, 32768, 64, 16, 0)
+    assert 0 < n < 512 << 20
+    assert _lib.latent_workspace_bytes(64, 32768, 64, 16, 128) <= n
+    assert _lib.latent_workspace_bytes(0, 1, 1, 1, 0) == 0
+
+
 def test_decode_misaligned_lengths():
     assert dec(lens=FAKE + 2) == INVALID
     assert b"aligned" in _lib.load().gda_last_error()

@@ -15,7 +15,7 @@ import torch
 import oracle
 from attention_gda_fwd_amd import configs as C
 from attention_gda_fwd_amd import inputs as gin
-from attention_gda_fwd_amd.api import gda_decode, gda_fwd
+from attention_gda_fwd_amd.api import gda_decode, gda_decode_latent, gda_fwd
 
 from . import gpu_util as U
 
@@ -242,6 +242,97 @@ def test_decode_options(name):
     ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"], host["v_cache"],
                             host["lam"], host["gate"], lens, window=window, **opts)
     U.assert_close(U.to_f64(out), ref, kw["dtype"], f"decode options {name}")
+
+
+# Latent-cache decode (the cache is c_kv [Lmax, 512] + k_rope [Lmax, 64] per sequence,
+# expanded by W^KV_b): every query-head count the kernel splits into waves (80, 40 and 10
+# heads: 5, 3 and 1 waves), ragged lengths (a partial last chunk, one key, an empty cache),
+# windows and the call options.
+LAT_SMALL = {
+    "motif3_heads": dict(case_id=231, B=5, Lmax=700, S=64, N=16, Hkv=16),
+    "motif2_heads": dict(case_id=232, B=5, Lmax=700, S=32, N=8, Hkv=16),
+    "tiny_heads": dict(case_id=233, B=5, Lmax=700, S=8, N=2, Hkv=2),
+}
+LAT_DIMS = dict(Dn=128, Dr=64, Dc=512, dv=128)
+
+
+def _latent_case(case_id, B, Lmax, S, N, Hkv):
+    host = gin.decode_latent_inputs(case_id, B=B, Lmax=Lmax, S=S, N=N, Hkv=Hkv, dtype="bf16",
+                                    **LAT_DIMS)
+    return host, {k: U.to_dev(v, "bf16") for k, v in host.items()}
+
+
+def _run_latent(dev, lens, window, **opts):
+    return gda_decode_latent(dev["q_sig"], dev["q_noise"], dev["c_kv"], dev["k_rope"],
+                             dev["w_kv_b"], dev["lam"], dev["gate"], cache_lens=lens,
+                             window=window, **opts)
+
+
+def _ref_latent(host, lens, window, **opts):
+    return oracle.ref_decode_latent(host["q_sig"], host["q_noise"], host["c_kv"],
+                                    host["k_rope"], host["w_kv_b"], host["lam"], host["gate"],
+                                    lens, window=window, **opts)
+
+
+@pytest.mark.parametrize("window", [0, 100])
+@pytest.mark.parametrize("name", sorted(LAT_SMALL))
+def test_latent_small_ragged(name, window):
+    kw = LAT_SMALL[name]
+    U.log(f"latent decode parity {name} window={window}")
+    host, dev = _latent_case(**kw)
+    lens = np.array([700, 1, 33, 0, 517], dtype=np.int32)
+    got = U.to_f64(_run_latent(dev, torch.from_numpy(lens).cuda(), window))
+    ref = _ref_latent(host, lens, window)
+    U.assert_close(got, ref, "bf16", f"latent {name} W={window}")
+    assert np.all(got[3] == 0.0), "an empty cache must give zeros"
+
+
+def test_latent_options_and_null_lengths():
+    kw = LAT_SMALL["motif3_heads"]
+    host, dev = _latent_case(**kw)
+    for k, tid in (("lam", 60), ("gate", 61)):
+        host[k] = np.stack([gin.normal(kw["case_id"], tid, b, host[k].shape[1:], "bf16")
+                            for b in range(kw["B"])])
+        dev[k] = U.to_dev(host[k], "bf16")
+    opts = dict(scale=0.07, lambda_logits=True, gate_logits=True)
+    got = U.to_f64(_run_latent(dev, None, 0, **opts))
+    ref = _ref_latent(host, None, 0, **opts)
+    U.assert_close(got, ref, "bf16", "latent options, full caches")
+
+
+def test_latent_full_size_sampled_sequences():
+    """The full latent cache (B=64 sequences of 32768 tokens, Motif 3 heads: 2.4 GB instead
+    of the expanded 21.5 GB) at W=0 and W=128; the oracle expands 4 sequences in fp64."""
+    cfg = C.MOTIF3_DECODE
+    B, Lmax = cfg.B, cfg.L
+    shp = dict(Lmax=Lmax, S=cfg.S, N=cfg.N, dtype="bf16", **{k: LAT_DIMS[k] for k in
+                                                              ("Dn", "Dr", "Dc", "dv")})
+    case_id = 241
+    U.log("latent full size: generating the 2.4 GB latent cache")
+    dev = None
+    keep = {0, 1, 37, 63}
+    kept = {}
+    for b in range(B):
+        row = gin.decode_latent_row(case_id, b, **shp)
+        if dev is None:
+            dev = {k: torch.empty((B,) + v.shape, dtype=torch.bfloat16, device="cuda")
+                   for k, v in row.items()}
+        for k, v in row.items():
+            dev[k][b].copy_(torch.from_numpy(v).view(torch.bfloat16))
+        if b in keep:
+            kept[b] = row
+    w = gin.latent_weights(case_id, Hkv=cfg.Hkv, Dn=128, dv=128, Dc=512, dtype="bf16")
+    dev["w_kv_b"] = U.to_dev(w, "bf16")
+    seqs = sorted(keep)
+    for window in (0, 128):
+        got = U.to_f64(_run_latent(dev, None, window)[seqs])
+        host = {k: np.stack([kept[b][k] for b in seqs]) for k in kept[seqs[0]]}
+        host["w_kv_b"] = w
+        t0 = time.perf_counter()
+        ref = _ref_latent(host, None, window)
+        U.log(f"latent full size W={window}: oracle on sequences {seqs} "
+              f"{time.perf_counter() - t0:.1f} s ({U.host_cpu()})")
+        U.assert_close(got, ref, "bf16", f"latent full size W={window}")
 
 
 def test_decode_full_size_full_output():
