@@ -15,7 +15,7 @@ from dataclasses import dataclass, replace
 @dataclass(frozen=True)
 class Case:
     name: str
-    kind: str          # "fwd" (prefill) or "decode"
+    kind: str          # "fwd" (prefill), "decode" (expanded cache) or "latent" (latent cache)
     dtype: str         # "bf16" or "f32"
     B: int
     L: int             # prefill sequence length, or decode cache length Lmax
@@ -27,6 +27,7 @@ class Case:
     window: int        # 0 = full causal
     rope_dims: int = 0
     case_id: int = 0   # seed key
+    latent: int = 0    # KV latent width Dc of a latent-cache decode (rope_dims = Dr)
 
     @property
     def g(self) -> int:
@@ -67,6 +68,11 @@ class Case:
             n = B * L * (S * dqk + N * dqk + H * dqk + H * dv + S + 2 * S * dv)
             return n * e
         keys = self.visible_pairs(lens)
+        if self.kind == "latent":  # per token: the latent and the rotary key; plus W^KV_b
+            Dn = dqk - self.rope_dims
+            n = (B * (S * dqk + N * dqk + S + 2 * S * dv) + keys * (self.latent + self.rope_dims)
+                 + H * (Dn + dv) * self.latent)
+            return n * e + (4 * B if lens is not None else 0)
         n = B * (S * dqk + N * dqk + S + 2 * S * dv) + keys * H * (dqk + dv)
         return n * e + (4 * B if lens is not None else 0)
 
@@ -92,5 +98,13 @@ MOTIF3_DECODE_SWA = MOTIF3_DECODE.with_(name="motif3_decode_swa128_B64_Lk32768",
 MOTIF3_FULL_SHARD8 = MOTIF3_FULL.with_(name="motif3_full_B2_L8192_shard8", S=8, N=2, Hkv=2,
                                        case_id=5)
 
+# The Motif 3 decode over the latent cache (512-wide KV latent + 64-wide rotary key per
+# token, expanded by W^KV_b into the 16 KV heads), full and W=128.
+MOTIF3_LATENT = MOTIF3_DECODE.with_(name="motif3_latent_decode_B64_Lk32768", kind="latent",
+                                    latent=512, case_id=7)
+MOTIF3_LATENT_SWA = MOTIF3_LATENT.with_(name="motif3_latent_decode_swa128_B64_Lk32768",
+                                        window=128)
+
 CONFIGS = {c.name: c for c in (TINY_F32, MOTIF2, MOTIF3_FULL, MOTIF3_SWA, MOTIF3_DECODE,
-                               MOTIF3_DECODE_SWA, MOTIF3_FULL_SHARD8)}
+                               MOTIF3_DECODE_SWA, MOTIF3_FULL_SHARD8, MOTIF3_LATENT,
+                               MOTIF3_LATENT_SWA)}

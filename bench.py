@@ -12,8 +12,8 @@ The headline ``value`` is the prefill's attention TFLOP/s, FLOPs counted as
 decode's HBM GB/s is reported beside it. Inputs are resident in HBM before the
 timed region; times come from HIP events on the stream the kernels run on.
 A breakdown times every other workload (Motif-2 layer, sliding window W=128,
-W=128 decode, one GPU's share of the full layer split over 8 GPUs, the fp32
-tiny case) outside the step: 10 warmup launches, 50 timed
+W=128 decode, the decode over the latent cache (full and W=128), one GPU's share
+of the full layer split over 8 GPUs, the fp32 tiny case) outside the step: 10 warmup launches, 50 timed
 (median and min), and for the small ones a second run with a 1 GiB write between
 launches so that no input is left in L2 or the memory-side cache. The CPU baseline is the fp64 oracle
 timed on a bounded sample of the prefill rows. Prints ONE JSON line.
@@ -44,10 +44,10 @@ CSRC = os.path.join(ROOT, "attention_gda_fwd_amd", "csrc")
 # a 1 GiB elementwise copy in the same pass. A figure holds only for the kernel source it
 # was taken on (sha256 of the file below); once that file changes it is reported as null.
 MEASURED_TRAFFIC = {
-    "prefill": {"source": "gda_fwd_bf16.hip", "bytes": 2487027461,
-                "sha256": "571d4cc85a49061edeeda9f76f11cdf36caf8b21e8bc3d12544930226dc0cc04"},
-    "decode": {"source": "gda_decode_bf16.hip", "bytes": 21477956699,
-               "sha256": "03176b30439314a250bb3727a912e70502f7ee36dd810bef08aa375eef4668c3"},
+    "prefill": {"source": "gda_fwd_bf16.hip", "bytes": 2486954861,
+                "sha256": "42f65f345ea70332267eb51596b2d7f35038505e5b19034660c1472687c9cebc"},
+    "decode": {"source": "gda_decode_bf16.hip", "bytes": 21477984816,
+               "sha256": "c84bb16b28d53f926fb69ce8eeed59c281cb705a8de754fdd9e165d3b0765b14"},
 }
 
 
@@ -139,6 +139,38 @@ def fill_decode(cfg, torch, gin):
     return dev
 
 
+def fill_latent(cfg, torch, gin):
+    """Device tensors of a latent-cache decode, generated per sequence on the host."""
+    Dr, Dc = cfg.rope_dims, cfg.latent
+    Dn = cfg.dqk - Dr
+    shp = dict(Lmax=cfg.L, S=cfg.S, N=cfg.N, Dn=Dn, Dr=Dr, Dc=Dc, dv=cfg.dv, dtype=cfg.dtype)
+    dev = None
+    with ThreadPoolExecutor(host_threads()) as ex:
+        for b0 in range(0, cfg.B, 8):
+            rows = list(ex.map(lambda b: gin.decode_latent_row(cfg.case_id, b, **shp),
+                               range(b0, min(b0 + 8, cfg.B))))
+            for b, row in zip(range(b0, b0 + len(rows)), rows):
+                if dev is None:
+                    dev = {k: torch.empty((cfg.B,) + v.shape, dtype=torch.bfloat16, device="cuda")
+                           for k, v in row.items()}
+                for k, v in row.items():
+                    dev[k][b].copy_(torch.from_numpy(v).view(torch.bfloat16))
+    w = gin.latent_weights(cfg.case_id, Hkv=cfg.Hkv, Dn=Dn, dv=cfg.dv, Dc=Dc, dtype=cfg.dtype)
+    dev["w_kv_b"] = torch.from_numpy(w).view(torch.bfloat16).cuda()
+    return dev
+
+
+def latent_fn(torch, dev, cfg, out, api):
+    ws = torch.empty(api.latent_workspace_bytes(cfg.B, cfg.L, cfg.S, cfg.N, cfg.window),
+                     dtype=torch.uint8, device="cuda")
+
+    def fn():
+        api.gda_decode_latent(dev["q_sig"], dev["q_noise"], dev["c_kv"], dev["k_rope"],
+                              dev["w_kv_b"], dev["lam"], dev["gate"], window=cfg.window, out=out,
+                              workspace=ws)
+    return fn
+
+
 def event_times(torch, fn, reps, warmup, flush=None):
     """Per-launch milliseconds, HIP events on the current stream around each launch.
     With ``flush`` (a large device buffer) every launch is preceded, outside its
@@ -162,7 +194,11 @@ def run_only(args, torch, C, gin, gda_fwd, gda_decode):
     """One workload alone: a 1 GiB copy kernel (the byte counters' scale), then warmup
     and timed launches. Prints a short JSON line."""
     cfg = C.CONFIGS[args.only]
-    if cfg.kind == "fwd":
+    if cfg.kind == "latent":
+        from attention_gda_fwd_amd import api
+        dev = fill_latent(cfg, torch, gin)
+        fn = latent_fn(torch, dev, cfg, torch.empty_like(dev["gate"]), api)
+    elif cfg.kind == "fwd":
         dev, _ = fill_fwd(cfg, torch, gin)
         out = torch.empty_like(dev["gate"])
 
@@ -319,6 +355,17 @@ def main():
     record(C.MOTIF3_DECODE_SWA, event_times(torch, lambda: run_dec(128), reps, 10), {
         "flushed": flushed(event_times(torch, lambda: run_dec(128), reps, 10, flush))})
     del ddev
+    torch.cuda.empty_cache()
+    from attention_gda_fwd_amd import api
+    log(f"breakdown {C.MOTIF3_LATENT.name} (2.4 GB latent cache)")
+    ldev = fill_latent(C.MOTIF3_LATENT, torch, gin)
+    lout = torch.empty_like(ldev["gate"])
+    record(C.MOTIF3_LATENT, event_times(torch, latent_fn(torch, ldev, C.MOTIF3_LATENT, lout, api),
+                                        20, 10))
+    fn = latent_fn(torch, ldev, C.MOTIF3_LATENT_SWA, lout, api)
+    record(C.MOTIF3_LATENT_SWA, event_times(torch, fn, reps, 10),
+           {"flushed": flushed(event_times(torch, fn, reps, 10, flush))})
+    del ldev, lout
     torch.cuda.empty_cache()
     for cfg in (C.MOTIF2, C.MOTIF3_SWA, C.MOTIF3_FULL_SHARD8, C.TINY_F32):
         log(f"breakdown {cfg.name}")
