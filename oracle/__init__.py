@@ -69,6 +69,9 @@ def _load():
         lib.gda_ref_decode_ex.restype = ctypes.c_int
         lib.gda_ref_decode_ex.argtypes = ([vp] * 8 + [i64] * 8 + [ctypes.c_int, f64, ctypes.c_int,
                                                                   ctypes.c_int])
+        lib.gda_ref_fwd_varlen.restype = ctypes.c_int
+        lib.gda_ref_fwd_varlen.argtypes = ([vp] * 9 + [i64] * 7 + [ctypes.c_int, f64,
+                                                                  ctypes.c_int])
         lib.gda_ref_decode_latent.restype = ctypes.c_int
         lib.gda_ref_decode_latent.argtypes = ([vp] * 9 + [i64] * 10 + [ctypes.c_int, f64,
                                                                      ctypes.c_int, ctypes.c_int])
@@ -199,4 +202,28 @@ def ref_decode_latent(q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, lens=None
         float(scale or 0.0), _flags(lambda_logits, gate_logits), int(mutant))
     if rc != 0:
         raise ValueError(f"gda_ref_decode_latent rejected its arguments (code {rc})")
+    return out
+
+
+def ref_fwd_varlen(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k, *, window: int,
+                   scale: float | None = None, lambda_logits: bool = False,
+                   gate_logits: bool = False) -> np.ndarray:
+    """Packed-sequence prefill oracle. q_sig [Tq,S,dqk], q_noise [Tq,N,dqk], k [Tk,Hkv,dqk],
+    v [Tk,Hkv,dv], lam [Tq,S], gate [Tq,S,dv]; cu_q, cu_k int32 [nseq+1] (host). Local
+    query t of sequence i sits at key position (Lk_i - Lq_i) + t. Returns [Tq,S,dv]."""
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, k, v, lam, gate = (_c(x, code) for x in (q_sig, q_noise, k, v, lam, gate))
+    Tq, S, dqk = q_sig.shape
+    N, Hkv, dv = q_noise.shape[1], k.shape[1], v.shape[2]
+    cu_q = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
+    cu_k = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
+    nseq = cu_q.size - 1
+    assert cu_k.size == nseq + 1 and cu_q[-1] == Tq and cu_k[-1] == k.shape[0]
+    out = np.empty((Tq, S, dv), dtype=np.float64)
+    rc = _load().gda_ref_fwd_varlen(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam),
+                                    _ptr(gate), _ptr(out), _ptr(cu_q), _ptr(cu_k), nseq, S, N,
+                                    Hkv, dqk, dv, int(window), code, float(scale or 0.0),
+                                    _flags(lambda_logits, gate_logits))
+    if rc != 0:
+        raise ValueError(f"gda_ref_fwd_varlen rejected its arguments (code {rc})")
     return out

@@ -262,6 +262,66 @@ int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cach
   return failed ? -8 : 0;
 }
 
+/* ---- Packed sequences with a query offset -----------------------------------------
+ * Sequence i owns query rows cu_q[i] .. cu_q[i+1]-1 and key rows cu_k[i] ..
+ * cu_k[i+1]-1 of the packed tensors (Lq_i and Lk_i rows). Its queries are the last
+ * Lq_i positions of its keys: local query t sits at key position (Lk_i - Lq_i) + t,
+ * and sees the keys s <= that position (and within the window). Packed documents
+ * are the case Lq_i = Lk_i; a sliding-window layer's halo exchange (walk-through
+ * step 5: one halo exchange of the window's keys) is the case Lk_i = Lq_i + W - 1.
+ * A query at a negative position sees no key and gives zeros. */
+static const void* offset_ptr(const void* base, int64_t elems, int dtype) {
+  return (const char*)base + elems * (dtype == GDA_REF_F32 ? 4 : 2);
+}
+
+int gda_ref_fwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                       const void* lambda, const void* gate, double* out,
+                       const int32_t* cu_q, const int32_t* cu_k, int64_t nseq, int64_t S,
+                       int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
+                       int dtype, double softmax_scale, int flags) {
+  int rc = check_common(1, 1, S, N, Hkv, dqk, dv, window, dtype);
+  if (rc) return rc;
+  if (nseq < 1 || !cu_q || !cu_k) return -1;
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out) return -6;
+  if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
+    return -9;
+  if (cu_q[0] != 0 || cu_k[0] != 0) return -10;
+  int64_t maxk = 1;
+  for (int64_t i = 0; i < nseq; ++i) {
+    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i]) return -10;
+    if (cu_k[i + 1] - cu_k[i] > maxk) maxk = cu_k[i + 1] - cu_k[i];
+  }
+  const int64_t Tq = cu_q[nseq];
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)maxk);
+    double* Hn = (double*)malloc(sizeof(double) * (size_t)(N * dv));
+    double* Hs = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!z || !Hn || !Hs) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < Tq; ++r) {
+        int64_t i = 0;
+        while (cu_q[i + 1] <= r) ++i;  /* the sequence of query row r */
+        const int64_t Lq = cu_q[i + 1] - cu_q[i], Lk = cu_k[i + 1] - cu_k[i];
+        const int64_t pos = (Lk - Lq) + (r - cu_q[i]);
+        const kv_view kv = {offset_ptr(k, (int64_t)cu_k[i] * Hkv * dqk, dtype),
+                            offset_ptr(v, (int64_t)cu_k[i] * Hkv * dv, dtype),
+                            Lk, Hkv, dqk, dv, dtype, GDA_REF_EXACT, softmax_scale, flags};
+        gda_row(q_sig, r * S * dqk, q_noise, r * N * dqk, lambda, r * S, gate, r * S * dv, &kv,
+                0, pos, S, N, window, z, Hn, Hs, out + r * S * dv);
+      }
+    }
+    free(z);
+    free(Hn);
+    free(Hs);
+  }
+  return failed ? -8 : 0;
+}
+
 /* ---- Latent-cache decode --------------------------------------------------------
  * The cache holds, per token, the KV latent c (Dc values, after its RMSNorm) and
  * the decoupled rotary key (Dr values, shared by every head); W^KV_b expands the

@@ -90,6 +90,18 @@ int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cach
                       int64_t dqk, int64_t dv, int64_t window, int dtype,
                       double softmax_scale, int flags, int mutant);
 
+/* Packed sequences with a query offset. Sequence i has query rows cu_q[i] ..
+ * cu_q[i+1]-1 and key rows cu_k[i] .. cu_k[i+1]-1 of the packed tensors
+ * q_sig [Tq,S,dqk], q_noise [Tq,N,dqk], k [Tk,Hkv,dqk], v [Tk,Hkv,dv], lambda [Tq,S],
+ * gate [Tq,S,dv]; out is [Tq,S,dv]. Local query t of a sequence with Lq queries and
+ * Lk keys sits at key position Lk - Lq + t; a query at a negative position gives
+ * zeros. cu_q and cu_k are host arrays of nseq+1 nondecreasing values from 0. */
+int gda_ref_fwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                       const void* lambda, const void* gate, double* out,
+                       const int32_t* cu_q, const int32_t* cu_k, int64_t nseq,
+                       int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv,
+                       int64_t window, int dtype, double softmax_scale, int flags);
+
 /* Latent-cache decode: the cache holds per token the KV latent c (Dc values) and
  * the decoupled rotary key (Dr values, shared by all heads); w_kv_b [Hkv, Dn+dv, Dc]
  * expands c into head h's key [W[h][0:Dn] c ; k_rope] and value W[h][Dn:Dn+dv] c.

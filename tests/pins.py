@@ -417,6 +417,51 @@ def pin_latent(decode_latent, decode):
     return msgs
 
 
+ARGS = ("q_sig", "q_noise", "k", "v", "lam", "gate")
+
+
+def pin_varlen(fwd_varlen):
+    """Packed sequences with a query offset against the batched oracle, which is pinned
+    above: one whole sequence; packed documents of different lengths each equal to its own
+    prefill; a halo chunk (queries = the last rows, keys = all rows) equal to the last
+    rows of the full prefill; fewer keys than queries: zeros at negative positions, the
+    rest equal to a prefill whose queries are shifted by the difference."""
+    msgs = []
+    for dtype in ("f32", "bf16"):
+        for W in (0, 4):
+            x = make("A", B=3, L=23, dqk=6, dv=4, dtype=dtype, case_id=1400)
+            one = {n: x[n][0] for n in ARGS}
+            full = oracle.ref_fwd(*(x[n][:1] for n in ARGS), window=W)[0]
+            o = fwd_varlen(*(one[n] for n in ARGS), [0, 23], [0, 23], window=W)
+            if not np.array_equal(o, full):
+                msgs.append(f"varlen one sequence {dtype} W={W}")
+            # packed documents: lengths 11, 5, 8 taken from three batch rows
+            lens = (11, 5, 8)
+            pk = {n: np.concatenate([x[n][b, :lens[b]] for b in range(3)]) for n in ARGS}
+            cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+            o = fwd_varlen(*(pk[n] for n in ARGS), cu, cu, window=W)
+            for b in range(3):
+                ref = oracle.ref_fwd(*(x[n][b:b + 1, :lens[b]] for n in ARGS), window=W)[0]
+                if not np.array_equal(o[cu[b]:cu[b + 1]], ref):
+                    msgs.append(f"varlen packed document {b} {dtype} W={W}")
+            # halo: the last 9 queries over all 23 keys
+            qa = {n: one[n][14:] if n in ("q_sig", "q_noise", "lam", "gate") else one[n] for n in ARGS}
+            o = fwd_varlen(*(qa[n] for n in ARGS), [0, 9], [0, 23], window=W)
+            if not np.array_equal(o, full[14:]):
+                msgs.append(f"varlen halo {dtype} W={W}")
+            # fewer keys than queries: 23 queries over the first 20 keys
+            kk = {n: one[n][:20] if n in ("k", "v") else one[n] for n in ARGS}
+            o = fwd_varlen(*(kk[n] for n in ARGS), [0, 23], [0, 20], window=W)
+            if np.any(o[:3] != 0.0):
+                msgs.append(f"varlen negative positions not zero {dtype} W={W}")
+            sh = {n: (one[n][3:] if n in ("q_sig", "q_noise", "lam", "gate") else one[n][:20])
+                  for n in ARGS}
+            ref = oracle.ref_fwd(*(sh[n][None] for n in ARGS), window=W)[0]
+            if not np.array_equal(o[3:], ref):
+                msgs.append(f"varlen shifted queries {dtype} W={W}")
+    return msgs
+
+
 def all_pins(fwd, decode):
     msgs = []
     for p in (pin_library_sdpa, pin_noise_one_hot, pin_identical_queries_zero,

@@ -68,6 +68,29 @@ def test_options_rejected():
         oracle.ref_fwd(*args, window=0, scale=float("nan"))
 
 
+def test_varlen_pin():
+    assert pins.pin_varlen(oracle.ref_fwd_varlen) == []
+
+
+def test_varlen_pin_catches_a_wrong_offset():
+    """A plausible mistake: each sequence's queries aligned to its first keys (query t at
+    key position t) instead of its last. For a single sequence that is the correct
+    computation over only its first Lq keys."""
+    def top_left(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k, *, window):
+        cu_q, cu_k = np.asarray(cu_q), np.asarray(cu_k)
+        if cu_q.size != 2:
+            return oracle.ref_fwd_varlen(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k,
+                                         window=window)
+        lq = int(cu_q[1])
+        if lq > int(cu_k[1]):
+            return oracle.ref_fwd_varlen(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k,
+                                         window=window)
+        return oracle.ref_fwd_varlen(q_sig, q_noise, k[:lq], v[:lq], lam, gate, cu_q,
+                                     [0, lq], window=window)
+
+    assert pins.pin_varlen(top_left)
+
+
 def test_latent_pin():
     assert pins.pin_latent(oracle.ref_decode_latent, oracle.ref_decode) == []
 
