@@ -15,7 +15,8 @@ GDA_SUCCESS, GDA_ERROR_INVALID_ARGUMENT, GDA_ERROR_UNSUPPORTED, GDA_ERROR_HIP = 
 GDA_BF16, GDA_F32 = 0, 1
 GDA_LAMBDA_LOGITS, GDA_GATE_LOGITS = 1, 2
 
-EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_decode_latent",
+EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_fwd_varlen",
+            "gda_decode_latent",
             "gda_decode_latent_workspace_bytes", "gda_status_string", "gda_last_error")
 
 
@@ -53,6 +54,8 @@ def load() -> ctypes.CDLL:
     lib.gda_fwd_ex.argtypes = [vp] * 7 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
     lib.gda_decode_ex.restype = i32
     lib.gda_decode_ex.argtypes = [vp] * 8 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
+    lib.gda_fwd_varlen.restype = i32
+    lib.gda_fwd_varlen.argtypes = [vp] * 9 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp]
     lib.gda_decode_latent_workspace_bytes.restype = ctypes.c_size_t
     lib.gda_decode_latent_workspace_bytes.argtypes = [i32] * 5
     lib.gda_decode_latent.restype = i32
@@ -124,3 +127,11 @@ def decode_latent_raw(q_sig, q_noise, c_kv, k_rope, w_kv_b, lens, lam, gate, out
                                     B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window, dtype,
                                     ctypes.byref(opts) if opts is not None else None, workspace,
                                     workspace_bytes, stream)
+
+
+def fwd_varlen_raw(q_sig, q_noise, k, v, lam, gate, out, cu_q, cu_k, nseq, max_seqlen_q, S, N,
+                   Hkv, dqk, dv, window, dtype, opts, stream) -> int:
+    """Direct call of gda_fwd_varlen (opts an Options or None)."""
+    return load().gda_fwd_varlen(q_sig, q_noise, k, v, lam, gate, out, cu_q, cu_k, nseq,
+                                 max_seqlen_q, S, N, Hkv, dqk, dv, window, dtype,
+                                 ctypes.byref(opts) if opts is not None else None, stream)

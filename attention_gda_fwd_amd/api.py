@@ -105,6 +105,43 @@ def gda_decode(q_sig: torch.Tensor, q_noise: torch.Tensor, k_cache: torch.Tensor
     return out
 
 
+def gda_fwd_varlen(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor,
+                   v: torch.Tensor, lam: torch.Tensor, gate: torch.Tensor,
+                   cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                   window: int = 0, out: torch.Tensor | None = None, scale: float | None = None,
+                   lambda_logits: bool = False, gate_logits: bool = False) -> torch.Tensor:
+    """Packed-sequence prefill. q_sig [Tq,S,dqk], q_noise [Tq,N,dqk], k [Tk,Hkv,dqk],
+    v [Tk,Hkv,dv], lam [Tq,S], gate [Tq,S,dv]; cu_seqlens_q / cu_seqlens_k int32 [nseq+1] on
+    the device. Local query t of sequence i sits at key position Lk_i - Lq_i + t.
+    -> out [Tq,S,dv]."""
+    if q_sig.dim() != 3 or q_noise.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("gda_fwd_varlen: q_sig, q_noise, k, v must be 3-D (packed rows)")
+    Tq, S, dqk = q_sig.shape
+    N, Tk, Hkv, dv = q_noise.shape[1], k.shape[0], k.shape[1], v.shape[2]
+    dev, dt = q_sig.device, q_sig.dtype
+    code = _dtype_code(q_sig)
+    if dev.type != "cuda":
+        raise ValueError("gda_fwd_varlen: tensors must be on a HIP (cuda) device")
+    nseq = cu_seqlens_q.numel() - 1
+    _check("q_sig", q_sig, (Tq, S, dqk), dt, dev)
+    _check("q_noise", q_noise, (Tq, N, dqk), dt, dev)
+    _check("k", k, (Tk, Hkv, dqk), dt, dev)
+    _check("v", v, (Tk, Hkv, dv), dt, dev)
+    _check("lam", lam, (Tq, S), dt, dev)
+    _check("gate", gate, (Tq, S, dv), dt, dev)
+    _check("cu_seqlens_q", cu_seqlens_q, (nseq + 1,), torch.int32, dev)
+    _check("cu_seqlens_k", cu_seqlens_k, (nseq + 1,), torch.int32, dev)
+    if out is None:
+        out = torch.empty((Tq, S, dv), dtype=dt, device=dev)
+    _check("out", out, (Tq, S, dv), dt, dev)
+    _lib.check(_lib.fwd_varlen_raw(
+        q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), out.data_ptr(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), nseq,
+        int(max_seqlen_q), S, N, Hkv, dqk, dv, int(window), code,
+        _lib.options(scale, lambda_logits, gate_logits), _stream(dev)))
+    return out
+
+
 def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Tensor,
                       k_rope: torch.Tensor, w_kv_b: torch.Tensor, lam: torch.Tensor,
                       gate: torch.Tensor, cache_lens: torch.Tensor | None = None,

@@ -141,6 +141,8 @@ gda_status gda_fwd_ex(const void* q_sig, const void* q_noise, const void* k, con
   a.lam = lambda;
   a.gate = gate;
   a.out = out;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
   a.B = B;
   a.L = L;
   a.S = S;
@@ -210,6 +212,51 @@ gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_c
   if ((st = require_device()) != GDA_SUCCESS) return st;
   const hipStream_t s = (hipStream_t)stream;
   return from_hip(dtype == GDA_BF16 ? gda::launch_decode_bf16(a, s) : gda::launch_decode_f32(a, s));
+}
+
+gda_status gda_fwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                          const void* lambda, const void* gate, void* out,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                          int max_seqlen_q, int S, int N, int Hkv, int dqk, int dv, int window,
+                          gda_dtype dtype, const gda_options* opts, void* stream) {
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out || !cu_seqlens_q ||
+      !cu_seqlens_k)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null pointer");
+  gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, out);
+  if (st != GDA_SUCCESS) return st;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "cu_seqlens must be 4-byte aligned");
+  st = validate_common(nseq, max_seqlen_q, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  gda::FwdArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.gate = gate;
+  a.out = out;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.B = nseq;
+  a.L = max_seqlen_q;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  a.plan = make_plan(S, N, Hkv);
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
+  if (dtype == GDA_BF16) {
+    if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+    if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
+      return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+  }
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  const hipStream_t s = (hipStream_t)stream;
+  return from_hip(dtype == GDA_BF16 ? gda::launch_fwd_bf16(a, s) : gda::launch_fwd_f32(a, s));
 }
 
 size_t gda_decode_latent_workspace_bytes(int B, int Lmax, int S, int N, int window) {

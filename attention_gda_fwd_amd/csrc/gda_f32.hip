@@ -77,7 +77,8 @@ __device__ void combine_f32(const F32Row& r, int64_t kstride, int64_t vstride, i
   float hs[DCH], hn[DCH], ls, ln;
   attend_row_f32(r.qs, r.kbase, r.vbase, kstride, vstride, lo, hi, dqk, d0, nd, scale, hs, ls);
   attend_row_f32(r.qn, r.knb, r.vnb, kstride, vstride, lo, hi, dqk, d0, nd, scale, hn, ln);
-  const float is = 1.f / ls, in = 1.f / ln;
+  // A query at a negative position (packed sequences) has no visible key: zeros.
+  const float is = ls > 0.f ? 1.f / ls : 0.f, in = ln > 0.f ? 1.f / ln : 0.f;
 #pragma unroll
   for (int e = 0; e < DCH; ++e)
     if (e < nd) {
@@ -90,30 +91,43 @@ __global__ void __launch_bounds__(NT)
 fwd_f32_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_noise,
                const float* __restrict__ kg, const float* __restrict__ vg,
                const float* __restrict__ lam, const float* __restrict__ gate,
-               float* __restrict__ out, int B, int L, int S, int N, int Hkv, int dqk, int dv,
-               int window, float scale, int flags) {
+               float* __restrict__ out, const int32_t* __restrict__ cu_q,
+               const int32_t* __restrict__ cu_k, int B, int L, int S, int N, int Hkv, int dqk,
+               int dv, int window, float scale, int flags) {
   const int nchunk = (dv + DCH - 1) / DCH;
   const int64_t total = (int64_t)B * L * S * nchunk;
   const int64_t gid = (int64_t)blockIdx.x * NT + threadIdx.x;
   if (gid >= total) return;
   const int ch = (int)(gid % nchunk);
   const int i = (int)((gid / nchunk) % S);
-  const int64_t row = gid / ((int64_t)nchunk * S);  // b*L + t
-  const int b = (int)(row / L), t = (int)(row % L);
+  const int64_t bt = gid / ((int64_t)nchunk * S);  // b*L + t
+  const int b = (int)(bt / L), t = (int)(bt % L);
+  // Sequence b (a batch row, or packed sequence b with its query offset).
+  int64_t qbase = (int64_t)b * L, kbase = (int64_t)b * L;
+  int Lq = L, Lk = L;
+  if (cu_q) {
+    qbase = cu_q[b];
+    Lq = cu_q[b + 1] - cu_q[b];
+    kbase = cu_k[b];
+    Lk = cu_k[b + 1] - cu_k[b];
+    if (t >= Lq) return;
+  }
+  const int64_t row = qbase + t;
+  const int pos = Lk - Lq + t;  // key position of the query
   const int g = S / N;
   const int j = i / g;
   const int hs = (int)(((int64_t)i * Hkv) / S), hn = (int)(((int64_t)j * Hkv) / N);
-  const int lo = window ? max(0, t - window + 1) : 0;
+  const int lo = window ? max(0, pos - window + 1) : 0;
   const int64_t kstride = (int64_t)Hkv * dqk, vstride = (int64_t)Hkv * dv;
   F32Row r;
   r.qs = q_sig + (row * S + i) * dqk;
   r.qn = q_noise + (row * N + j) * dqk;
-  r.kbase = kg + (int64_t)b * L * kstride + (int64_t)hs * dqk;
-  r.vbase = vg + (int64_t)b * L * vstride + (int64_t)hs * dv;
-  r.knb = kg + (int64_t)b * L * kstride + (int64_t)hn * dqk;
-  r.vnb = vg + (int64_t)b * L * vstride + (int64_t)hn * dv;
+  r.kbase = kg + kbase * kstride + (int64_t)hs * dqk;
+  r.vbase = vg + kbase * vstride + (int64_t)hs * dv;
+  r.knb = kg + kbase * kstride + (int64_t)hn * dqk;
+  r.vnb = vg + kbase * vstride + (int64_t)hn * dv;
   const int d0 = ch * DCH;
-  combine_f32(r, kstride, vstride, lo, t, dqk, d0, min(DCH, dv - d0), scale, lam[row * S + i],
+  combine_f32(r, kstride, vstride, lo, pos, dqk, d0, min(DCH, dv - d0), scale, lam[row * S + i],
               gate + (row * S + i) * dv, out + (row * S + i) * dv, flags);
 }
 
@@ -165,31 +179,35 @@ __device__ __forceinline__ floatx4 mfma_16x16x4(float a, float b, const floatx4&
 
 // One head over 16 query rows: o[c] = normalised softmax(q k^T * scale) v, in
 // the accumulator layout (lane l: row row0 + l%16, channels 16c + 4(l/16) .. +3).
-// q points at row 0 of this head (row stride qstride floats), kb / vb at key 0
-// of its KV head (key strides kstride / vstride). Rows >= L are computed on
-// clamped (valid) addresses and never stored by the caller.
+// q points at query 0 of this head (row stride qstride floats), kb / vb at key 0
+// of its KV head (key strides kstride / vstride); the sequence has Lq queries and
+// Lk keys, query t at key position Lk - Lq + t. Rows >= Lq are computed on clamped
+// (valid) addresses and never stored by the caller; a query at a negative position
+// sees no key and gets zeros.
 template <int DQK, int DV>
 __device__ void head_f32(const float* __restrict__ q, int64_t qstride,
                          const float* __restrict__ kb, const float* __restrict__ vb,
-                         int64_t kstride, int64_t vstride, int row0, int L, int window,
-                         float scale_log2, floatx4 (&o)[DV / 16]) {
+                         int64_t kstride, int64_t vstride, int row0, int Lq, int Lk,
+                         int window, float scale_log2, floatx4 (&o)[DV / 16]) {
   constexpr int QB = DQK / 16, VC = DV / 16;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-  const int row = row0 + lr;
+  const int qoff = Lk - Lq;
+  const int row = qoff + row0 + lr;  // the lane's query position
+  const int L = Lk;
   // Dimension block sb of lane group lq is dims 16sb + 4lq .. +3; MFMA step
   // 4sb + e takes component e, for Q and K alike (the dot product's terms are
   // permuted the same way on both sides).
   float4 qv[QB];
   {
-    const float* qr = q + (int64_t)min(row, L - 1) * qstride + 4 * lq;
+    const float* qr = q + (int64_t)min(row0 + lr, Lq - 1) * qstride + 4 * lq;
 #pragma unroll
     for (int sb = 0; sb < QB; ++sb) qv[sb] = *(const float4*)(qr + 16 * sb);
   }
 #pragma unroll
   for (int c = 0; c < VC; ++c) o[c] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, lsum = 0.f;
-  const int last = min(row0 + 15, L - 1);
-  const int first = window ? max(0, row0 - window + 1) : 0;
+  const int last = qoff + min(row0 + 15, Lq - 1);
+  const int first = window ? max(0, qoff + row0 - window + 1) : 0;
   for (int key0 = first & ~15; key0 <= last; key0 += 16) {
     float4 kv[QB];
     {
@@ -243,7 +261,8 @@ __device__ void head_f32(const float* __restrict__ q, int64_t qstride,
       o[c] = acc;
     }
   }
-  const float inv = 1.f / col_sum4(lsum);
+  const float tot = col_sum4(lsum);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
   for (int c = 0; c < VC; ++c) o[c] = o[c] * inv;
 }
@@ -253,8 +272,9 @@ __global__ void __launch_bounds__(64 * MF_MAX_WAVES)
 fwd_f32_mfma_kernel(const float* __restrict__ q_sig, const float* __restrict__ q_noise,
                     const float* __restrict__ kg, const float* __restrict__ vg,
                     const float* __restrict__ lam, const float* __restrict__ gate,
-                    float* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
-                    float scale_log2, int flags) {
+                    float* __restrict__ out, const int32_t* __restrict__ cu_q,
+                    const int32_t* __restrict__ cu_k, int B, int L, int S, int N, int Hkv,
+                    int window, float scale_log2, int flags) {
   constexpr int VC = DV / 16;
   __shared__ floatx4 sHN[VC][64];
   const int ntiles = (L + 15) / 16;
@@ -264,28 +284,38 @@ fwd_f32_mfma_kernel(const float* __restrict__ q_sig, const float* __restrict__ q
   const int b = (bid / N) % B;
   const int tile = ntiles - 1 - bid / (N * B);
   const int row0 = tile * 16;
+  // Sequence b (a batch row, or packed sequence b with its query offset).
+  int64_t qbase = (int64_t)b * L, kbase = (int64_t)b * L;
+  int Lq = L, Lk = L;
+  if (cu_q) {
+    qbase = cu_q[b];
+    Lq = cu_q[b + 1] - cu_q[b];
+    kbase = cu_k[b];
+    Lk = cu_k[b + 1] - cu_k[b];
+    if (row0 >= Lq) return;  // the whole workgroup
+  }
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
   const int g = S / N;
   const int64_t kstride = (int64_t)Hkv * DQK, vstride = (int64_t)Hkv * DV;
-  const float* kb0 = kg + (int64_t)b * L * kstride;
-  const float* vb0 = vg + (int64_t)b * L * vstride;
+  const float* kb0 = kg + kbase * kstride;
+  const float* vb0 = vg + kbase * vstride;
   floatx4 o[VC];
   int i = -1;
   if (wave == 0) {
     const int hk = (int)(((int64_t)j * Hkv) / N);
-    head_f32<DQK, DV>(q_noise + ((int64_t)b * L * N + j) * DQK, (int64_t)N * DQK,
-                      kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0, L,
-                      window, scale_log2, o);
+    head_f32<DQK, DV>(q_noise + (qbase * N + j) * DQK, (int64_t)N * DQK,
+                      kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0, Lq,
+                      Lk, window, scale_log2, o);
 #pragma unroll
     for (int c = 0; c < VC; ++c) sHN[c][lane] = o[c];
   } else {
     i = j * g + wave - 1;
     if (i < (j + 1) * g) {
       const int hk = (int)(((int64_t)i * Hkv) / S);
-      head_f32<DQK, DV>(q_sig + ((int64_t)b * L * S + i) * DQK, (int64_t)S * DQK,
+      head_f32<DQK, DV>(q_sig + (qbase * S + i) * DQK, (int64_t)S * DQK,
                         kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0,
-                        L, window, scale_log2, o);
+                        Lq, Lk, window, scale_log2, o);
     }
   }
   __syncthreads();
@@ -294,12 +324,12 @@ fwd_f32_mfma_kernel(const float* __restrict__ q_sig, const float* __restrict__ q
   for (; i < (j + 1) * g; i += nw - 1) {
     if (i != j * g + wave - 1) {  // heads beyond the first pass
       const int hk = (int)(((int64_t)i * Hkv) / S);
-      head_f32<DQK, DV>(q_sig + ((int64_t)b * L * S + i) * DQK, (int64_t)S * DQK,
+      head_f32<DQK, DV>(q_sig + (qbase * S + i) * DQK, (int64_t)S * DQK,
                         kb0 + (int64_t)hk * DQK, vb0 + (int64_t)hk * DV, kstride, vstride, row0,
-                        L, window, scale_log2, o);
+                        Lq, Lk, window, scale_log2, o);
     }
-    if (row < L) {
-      const int64_t ri = ((int64_t)b * L + row) * S + i;
+    if (row < Lq) {
+      const int64_t ri = (qbase + row) * S + i;
       const float li = (flags & kLambdaLogits) ? sigmoid_f32(lam[ri]) : lam[ri];
       const bool glog = (flags & kGateLogits) != 0;
       const float* gr = gate + ri * DV + 4 * lq;
@@ -334,7 +364,8 @@ hipError_t launch_f32_mfma(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_f32_mfma_kernel<DQK, DV>), dim3((unsigned)nblk), dim3(64 * nw), 0,
                      stream, (const float*)a.q_sig, (const float*)a.q_noise, (const float*)a.k,
                      (const float*)a.v, (const float*)a.lam, (const float*)a.gate,
-                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.window, a.scale_log2, a.flags);
+                     (float*)a.out, a.cu_q, a.cu_k, a.B, a.L, a.S, a.N, a.Hkv, a.window,
+                     a.scale_log2, a.flags);
   return hipGetLastError();
 }
 
@@ -351,8 +382,8 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(fwd_f32_kernel, dim3((unsigned)nblk), dim3(NT), 0, stream,
                      (const float*)a.q_sig, (const float*)a.q_noise, (const float*)a.k,
                      (const float*)a.v, (const float*)a.lam, (const float*)a.gate,
-                     (float*)a.out, a.B, a.L, a.S, a.N, a.Hkv, a.dqk, a.dv, a.window, a.scale,
-                     a.flags);
+                     (float*)a.out, a.cu_q, a.cu_k, a.B, a.L, a.S, a.N, a.Hkv, a.dqk, a.dv,
+                     a.window, a.scale, a.flags);
   return hipGetLastError();
 }
 

@@ -78,19 +78,21 @@ struct Cfg {
 };
 
 struct Ctx {
-  const uint16_t* kg;
-  const uint16_t* vg;
-  int L, Hkv, window, b;
+  const uint16_t* kg;  // this sequence's key 0
+  const uint16_t* vg;  // this sequence's value 0
+  int L, Hkv, window;  // L: this sequence's keys
   int kvA, kvB;
-  int q_lo, q_hi;  // the workgroup's query rows
-  int w_lo, w_hi;  // this wave's query rows (empty when w_lo > w_hi)
-  int t;           // this lane's query row (>= L for padding lanes)
+  // Query positions in key coordinates (a sequence's Lq queries are its last Lq
+  // key positions: local query t sits at position L - Lq + t).
+  int q_lo, q_hi;  // the workgroup's queries
+  int w_lo, w_hi;  // this wave's queries (empty when w_lo > w_hi)
+  int t;           // this lane's query (past the last for padding lanes)
   int lane, col, g4, wave;
   float c;  // log2(e)/sqrt(dqk)
 };
 
 // Issue one 1 KB direct-to-LDS block of a tile (keys k0 .. k0+BN-1). Rows past
-// L read row L-1 (finite data; those keys are masked).
+// the sequence's last key read that key (finite data; those keys are masked).
 template <class C>
 __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint16_t* sK0,
                                            uint16_t* sV0, uint16_t* sK1, uint16_t* sV1) {
@@ -108,7 +110,7 @@ __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint1
     const int row0 = min(k0 + 16 * kb, x.L - 1);
     const int rel = min(x.lane & 15, x.L - 1 - row0);
     const char* base = (const char*)x.kg +
-                       ((((int64_t)x.b * x.L + row0) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
+                       (((int64_t)row0 * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
     dma16(base, (uint32_t)rel * stride + 16u * (uint32_t)(x.lane >> 4), (lds_void*)(sK + bi * 512));
   } else {
     const int vi = bi - C::KBLK;
@@ -118,7 +120,7 @@ __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint1
     const uint32_t stride = (uint32_t)x.Hkv * C::DV * 2;
     const int row0 = min(k0 + C::VRPB * vi, x.L - 1);
     const int rel = min(lr, x.L - 1 - row0);
-    const char* base = (const char*)x.vg + (((int64_t)x.b * x.L + row0) * x.Hkv + kvh) * C::DV * 2;
+    const char* base = (const char*)x.vg + ((int64_t)row0 * x.Hkv + kvh) * C::DV * 2;
     dma16(base, (uint32_t)rel * stride + 16u * (uint32_t)cch, (lds_void*)(sV + vi * 512));
   }
 }
@@ -152,7 +154,7 @@ __device__ __forceinline__ void issue_block_fast(const Ctx& x, uint32_t ring_lds
     const int bi = fb + x.wave;
     const int kb = bi / C::KS, ks = bi - (bi / C::KS) * C::KS;
     const char* g = (const char*)x.kg +
-                    ((((int64_t)x.b * x.L + k0 + 16 * kb) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
+                    (((int64_t)(k0 + 16 * kb) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
     dma16_lds(g, (uint32_t)(x.lane & 15) * (uint32_t)(x.Hkv * C::DQK * 2) + 16u * (uint32_t)(x.lane >> 4),
               ring_lds + st_off + 1024u * (uint32_t)bi);
   } else {
@@ -160,7 +162,7 @@ __device__ __forceinline__ void issue_block_fast(const Ctx& x, uint32_t ring_lds
     const int lr = x.lane / C::VCH;
     const int r = C::VRPB * vi + lr;
     const int cch = (x.lane % C::VCH) ^ ((r % C::VPAIR) << 1);
-    const char* g = (const char*)x.vg + (((int64_t)x.b * x.L + k0 + C::VRPB * vi) * x.Hkv + kvh) * C::DV * 2;
+    const char* g = (const char*)x.vg + ((int64_t)(k0 + C::VRPB * vi) * x.Hkv + kvh) * C::DV * 2;
     dma16_lds(g, (uint32_t)lr * (uint32_t)(x.Hkv * C::DV * 2) + 16u * (uint32_t)cch,
               ring_lds + st_off + 2u * C::K_ELEMS + 1024u * (uint32_t)vi);
   }
@@ -428,17 +430,15 @@ __global__ void __launch_bounds__(C::NT, C::NW == 4 ? 2 : 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
-                uint16_t* __restrict__ out, int B, int L, int S, int N, int Hkv, int window,
-                int units, int R, int nqt, int heavy_first, float c, int flags) {
+                uint16_t* __restrict__ out, const int32_t* __restrict__ cu_q,
+                const int32_t* __restrict__ cu_k, int B, int L, int S, int N, int Hkv,
+                int window, int units, int R, int nqt, int heavy_first, float c, int flags) {
   // K/V ring: two stages, each the tiles of the unit's KV heads.
   __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
   // Normalised noise output handed from the A waves to the B waves.
   __shared__ __attribute__((aligned(16))) float sHN[C::NB > 0 ? C::NQG * C::DB * 4 * 64 : 4];
 
   Ctx x;
-  x.kg = kg;
-  x.vg = vg;
-  x.L = L;
   x.Hkv = Hkv;
   x.window = window;
   const int tid = threadIdx.x;
@@ -454,17 +454,44 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   const int qt = heavy_first ? nqt - 1 - slot : slot;
   const int bu = blockIdx.x - slot * per;
   const int b = bu / units, u = bu - (bu / units) * units;
-  x.b = b;
+  // Sequence b: Lq queries from packed row qbase, Lk keys from packed row kbase
+  // (packed sequences), or rows b*L .. b*L+L-1 of both (a batch).
+  int64_t qbase, kbase;
+  int Lq, Lk;
+  if (cu_q) {
+    qbase = cu_q[b];
+    Lq = cu_q[b + 1] - cu_q[b];
+    kbase = cu_k[b];
+    Lk = cu_k[b + 1] - cu_k[b];
+  } else {
+    qbase = kbase = (int64_t)b * L;
+    Lq = Lk = L;
+  }
+  const int ql = qt * C::BM;  // this tile's first query of the sequence
+  if (ql >= Lq) return;        // past the sequence (the whole workgroup)
+  const int qoff = Lk - Lq;
+  const int sig0 = u * C::USIG;  // first signal head of the unit
+  x.L = Lk;
+  x.kg = kg + kbase * Hkv * C::DQK;
+  x.vg = vg + kbase * Hkv * C::DV;
   x.kvA = u * R;
   x.kvB = C::TWO_KV ? u * R + 1 : u * R;
-  x.q_lo = qt * C::BM;
-  x.q_hi = min(x.q_lo + C::BM, L) - 1;
+  x.q_lo = qoff + ql;
+  x.q_hi = qoff + min(ql + C::BM, Lq) - 1;
+  if (x.q_hi < 0) {  // every query before the first key (or no key): zeros
+    const int nq = min(ql + C::BM, Lq) - ql;
+    for (int idx = threadIdx.x; idx < nq * C::USIG * C::DV; idx += C::NT) {
+      const int r = idx / (C::USIG * C::DV), rem = idx - r * (C::USIG * C::DV);
+      out[((qbase + ql + r) * S + sig0) * C::DV + rem] = 0;
+    }
+    return;
+  }
   x.w_lo = x.q_lo + qg * 16;
-  x.w_hi = min(x.w_lo + 15, L - 1);
+  x.w_hi = min(x.w_lo + 15, x.q_hi);
   x.t = x.w_lo + x.col;
-  const bool t_ok = x.t < L;
-  const int64_t row = (int64_t)b * L + min(x.t, L - 1);
-  const int sig0 = u * C::USIG;  // first signal head of the unit
+  const int tl = x.t - qoff;  // the lane's query, local to the sequence
+  const bool t_ok = tl < Lq;
+  const int64_t row = qbase + min(tl, Lq - 1);
 
   uint16_t* sk[2][2];
   uint16_t* sv[2][2];
@@ -480,7 +507,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   {
     const int k_lo = window ? max(0, x.q_lo - window + 1) : 0;
     const int kf = (k_lo / C::BN) * C::BN;
-    if (kf + C::BN <= L)
+    if (kf + C::BN <= Lk)
       issue_tile_fast<C, 0>(x, ring_lds, kf, 0, C::TBLK / C::NW);
     else
       issue_tile<C>(x, kf, sk[0][0], sv[0][0], sk[0][1], sv[0][1]);
@@ -495,7 +522,9 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
     qrow[NZ] = q_noise + (row * N + u) * C::DQK;
     run_tiles<C, NH, 0>(x, st, qrow, ring_lds, sk, sv);
-    const float inv_n = 1.f / st.lsum[NZ];
+    // A query at a negative position has no visible key: its sums stay 0 and it
+    // gives zeros.
+    const float inv_n = st.lsum[NZ] > 0.f ? 1.f / st.lsum[NZ] : 0.f;
     floatx4 hn[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -509,8 +538,8 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
-        store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s], 1.f / st.lsum[s], hn,
-                          flags);
+        store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s],
+                          st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, flags);
     }
     if (C::NB > 0) __syncthreads();
   } else if (C::NB > 0) {
@@ -530,13 +559,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
       for (int s = 0; s < C::BSIG; ++s)
         store_head<C::DV>(lam, gate, out, row, S, sig0 + b_first + s, x.g4, st.o[s],
-                          1.f / st.lsum[s], hn, flags);
+                          st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, flags);
     }
   }
 }
 
 template <class C>
 hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
+  // Packed sequences: B sequences of at most L queries each.
   const int nqt = (a.L + C::BM - 1) / C::BM;
   const int64_t grid = (int64_t)nqt * a.B * a.plan.units;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -544,7 +574,8 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_bf16_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
-                     (const uint16_t*)a.gate, (uint16_t*)a.out, a.B, a.L, a.S, a.N, a.Hkv,
+                     (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L, a.S,
+                     a.N, a.Hkv,
                      a.window, a.plan.units, a.plan.R, nqt, heavy_first, a.scale_log2, a.flags);
   return hipGetLastError();
 }

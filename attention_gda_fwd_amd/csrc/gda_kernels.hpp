@@ -24,6 +24,11 @@ struct FwdArgs {
   const void* lam;
   const void* gate;
   void* out;
+  // Packed sequences (both NULL for a batch): B sequences, sequence i owning query
+  // rows cu_q[i] .. cu_q[i+1]-1 and key rows cu_k[i] .. cu_k[i+1]-1 (device arrays);
+  // L is then the longest query count.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
   int B, L, S, N, Hkv, dqk, dv, window;
   UnitPlan plan;
   float scale_log2;  // log2(e) * softmax scale

@@ -115,6 +115,26 @@ def fwd_inputs(case_id, *, B, L, S, N, Hkv, dqk, dv, dtype, rope_dims=0):
     return {name: np.stack([r[name] for r in rows]) for name in rows[0]}
 
 
+def varlen_inputs(case_id, *, lens_q, lens_k, S, N, Hkv, dqk, dv, dtype, rope_dims=0):
+    """Packed-sequence prefill inputs. Sequence i draws its query-side tensors with
+    lens_q[i] rows and its keys and values with lens_k[i] rows from the streams of batch
+    row i, then every sequence is concatenated along the rows: q_sig [Tq,S,dqk],
+    q_noise [Tq,N,dqk], k [Tk,Hkv,dqk], v [Tk,Hkv,dv], lam [Tq,S], gate [Tq,S,dv], and
+    cu_q, cu_k int32 [nseq+1] (row offsets, from 0)."""
+    parts = {n: [] for n in ("q_sig", "q_noise", "k", "v", "lam", "gate")}
+    for i, (lq, lk) in enumerate(zip(lens_q, lens_k)):
+        parts["q_sig"].append(normal(case_id, T_QSIG, i, (lq, S, dqk), dtype))
+        parts["q_noise"].append(normal(case_id, T_QNOISE, i, (lq, N, dqk), dtype))
+        parts["k"].append(keys(case_id, i, lk, Hkv, dqk, rope_dims, dtype))
+        parts["v"].append(normal(case_id, T_V, i, (lk, Hkv, dv), dtype))
+        parts["lam"].append(sigmoid_normal(case_id, T_LAMBDA, i, (lq, S), dtype))
+        parts["gate"].append(sigmoid_normal(case_id, T_GATE, i, (lq, S, dv), dtype))
+    out = {n: np.concatenate(v) for n, v in parts.items()}
+    out["cu_q"] = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    out["cu_k"] = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    return out
+
+
 def decode_row(case_id, b, *, Lmax, S, N, Hkv, dqk, dv, dtype, rope_dims=0):
     """All decode inputs of sequence b: q_sig [S,dqk], q_noise [N,dqk], k_cache [Lmax,Hkv,dqk],
     v_cache [Lmax,Hkv,dv], lam [S], gate [S,dv]."""

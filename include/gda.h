@@ -121,6 +121,30 @@ gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_c
                          int B, int Lmax, int S, int N, int Hkv, int dqk, int dv,
                          int window, gda_dtype dtype, const gda_options* opts, void* stream);
 
+/* Prefill over packed sequences with a query offset (packed documents, and the
+ * chunk-with-halo form of a sequence-sharded sliding-window layer: the Motif 3
+ * walk-through's step 5 exchanges one halo of the window's keys per rank).
+ *   q_sig   [Tq, S, dqk], q_noise [Tq, N, dqk], lambda [Tq, S], gate [Tq, S, dv],
+ *   out     [Tq, S, dv]    the queries of all sequences, packed
+ *   k       [Tk, Hkv, dqk], v [Tk, Hkv, dv]   the keys of all sequences, packed
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [nseq+1], nondecreasing from 0;
+ *     sequence i owns query rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 and key
+ *     rows cu_seqlens_k[i] .. cu_seqlens_k[i+1]-1 (Lq_i and Lk_i rows; Tq and Tk
+ *     are the last entries).
+ *   max_seqlen_q >= every Lq_i (sizes the grid).
+ * Local query t of sequence i sits at key position Lk_i - Lq_i + t (its queries are
+ * its last Lq_i positions) and sees keys s <= that position (and, with a window,
+ * within W of it). Lq_i = Lk_i is a packed document; Lk_i = Lq_i + W - 1 is a
+ * chunk whose previous W-1 keys came as a halo. A query at a negative position
+ * (Lk_i < Lq_i) sees no key and gets zeros. The cu_seqlens contents are not
+ * validated (device memory): values outside the tensors are undefined behaviour.
+ * Everything else as gda_fwd_ex (head maps, dtypes, options, support). */
+gda_status gda_fwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                          const void* lambda, const void* gate, void* out,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                          int max_seqlen_q, int S, int N, int Hkv, int dqk, int dv, int window,
+                          gda_dtype dtype, const gda_options* opts, void* stream);
+
 /* Decode over the latent KV cache (GDLA's inference form; Motif 3 walk-through,
  * step 2 "GDLA forward" and novelty point one: the cache holds the KV latent and
  * the decoupled rotary key, MLA-sized, and W^KV_b expands the latent into the KV

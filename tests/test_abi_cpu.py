@@ -147,6 +147,34 @@ def test_latent_workspace_size():
     assert _lib.latent_workspace_bytes(0, 1, 1, 1, 0) == 0
 
 
+def varlen(**kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, out=FAKE, cu_q=FAKE,
+             cu_k=FAKE, nseq=3, maxq=64, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0, dtype=BF16,
+             opts=None)
+    a.update(kw)
+    return _lib.fwd_varlen_raw(a["q"], a["qn"], a["k"], a["v"], a["lam"], a["gate"], a["out"],
+                               a["cu_q"], a["cu_k"], a["nseq"], a["maxq"], a["S"], a["N"],
+                               a["Hkv"], a["dqk"], a["dv"], a["window"], a["dtype"], a["opts"],
+                               None)
+
+
+@pytest.mark.parametrize("kw", [dict(cu_q=None), dict(cu_k=None), dict(q=None), dict(out=None),
+                                dict(cu_q=FAKE + 2), dict(k=FAKE + 8), dict(nseq=0),
+                                dict(maxq=0), dict(window=-1), dict(S=8, N=3),
+                                dict(opts=_lib.Options(-1.0, 0)), dict(dtype=7)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_varlen_invalid_arguments(kw):
+    assert varlen(**kw) == INVALID
+
+
+def test_varlen_unsupported_and_device_check():
+    assert varlen(dqk=96, dv=96) == UNSUPPORTED
+    assert varlen(S=16, N=2, Hkv=2) == UNSUPPORTED
+    if not _gpu_visible():
+        assert varlen() == HIPERR
+        assert varlen(dtype=F32, dqk=40, dv=24) == HIPERR
+
+
 def test_decode_misaligned_lengths():
     assert dec(lens=FAKE + 2) == INVALID
     assert b"aligned" in _lib.load().gda_last_error()
