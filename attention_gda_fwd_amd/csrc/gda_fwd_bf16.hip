@@ -72,6 +72,10 @@ struct Cfg {
   static constexpr int VCH = DV / 8;                // 16-byte chunks per V row
   static constexpr int VPAIR = VCH / 2;             // 32-byte chunk pairs per V row
   static constexpr int VRPB = 512 / DV;             // V rows per 1 KB block
+  // Short workgroups (two per CU) issue their epilogue loads right after the
+  // key loop and release the B waves before the A waves' stores; long ones
+  // (one per CU) run their measured-faster order: A stores, then B.
+  static constexpr bool kEarlyEpilogue = NQG == 2;
   static_assert(BN == 32 || BN == 64, "an LDS tile is one or two 32-key chunks");
   static_assert(TBLK % NW == 0, "every wave issues the same number of tile blocks");
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "runs of NW blocks never mix K and V");
@@ -339,44 +343,70 @@ __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, con
   }
 }
 
-// out[t, i, :] = gate * (hs/l_s - lam * hn) for one signal head, this lane's channels.
+// The epilogue of one signal head: out[t, i, :] = gate * (hs/l_s - lam * hn).
+// In the accumulator layout a lane holds 4 channels of each 16-channel block, so
+// a store would move 8 bytes per lane and 32 contiguous bytes per query row.
+// Block pairs (2p, 2p+1) are first regrouped across lanes l and l^16 (one
+// permlane16 swap per value; both lanes hold the same query): lane group g
+// then holds the 8 consecutive channels 32p + 16(g&1) + 8(g>>1) .. +7, so each
+// gate load and output store moves 16 bytes per lane and 64 contiguous bytes
+// per query row.
 template <int DV>
-__device__ __forceinline__ void store_head(const uint16_t* lam, const uint16_t* gate,
-                                           uint16_t* out, int64_t row, int S, int i, int g4,
+struct HeadIn {
+  u32x4 gate[DV / 32];  // this lane's 8-channel gate pieces
+  float lam;
+};
+
+__device__ __forceinline__ int64_t head_base(int64_t row, int S, int i, int g4, int DV) {
+  return (row * S + i) * DV + 16 * (g4 & 1) + 8 * (g4 >> 1);
+}
+
+// Issue the gate and lambda loads of one head (row is always a valid row).
+template <int DV>
+__device__ __forceinline__ void load_head_in(const uint16_t* lam, const uint16_t* gate,
+                                             int64_t row, int S, int i, int g4, HeadIn<DV>& in) {
+  const int64_t base = head_base(row, S, i, g4, DV);
+#pragma unroll
+  for (int p = 0; p < DV / 32; ++p) in.gate[p] = ldg16(gate + base + 32 * p);
+  in.lam = bf16_to_f32(lam[row * S + i]);
+}
+
+template <int DV>
+__device__ __forceinline__ void store_head(uint16_t* out, int64_t row, int S, int i, int g4,
                                            const floatx4 (&hs)[DV / 16], float inv_s,
-                                           const floatx4 (&hn)[DV / 16], int flags) {
-  constexpr int DB = DV / 16;
-  const int64_t base = (row * S + i) * DV + 4 * g4;
-  // Every gate load is issued before anything waits on one (the epilogue is
-  // latency-bound in short workgroups); the logit branches come after.
-  u32x2 gw[DB];
+                                           const floatx4 (&hn)[DV / 16], const HeadIn<DV>& in,
+                                           int flags) {
+  constexpr int NP = DV / 32;
+  static_assert(DV % 32 == 0, "channel blocks come in pairs");
+  const int64_t base = head_base(row, S, i, g4, DV);
+  const float lm = (flags & kLambdaLogits) ? sigmoid_f32(in.lam) : in.lam;
+  float e[NP][8];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) gw[db] = ldg8(gate + base + 16 * db);
-  float lm = bf16_to_f32(lam[row * S + i]);
-  if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
-  float d[DB][4];
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) d[db][r] = hs[db][r] * inv_s - lm * hn[db][r];
-  if (flags & kGateLogits) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      u32x2 ow;
-      ow[0] = pack_bf16x2(sigmoid_f32(bf16_lo(gw[db][0])) * d[db][0],
-                          sigmoid_f32(bf16_hi(gw[db][0])) * d[db][1]);
-      ow[1] = pack_bf16x2(sigmoid_f32(bf16_lo(gw[db][1])) * d[db][2],
-                          sigmoid_f32(bf16_hi(gw[db][1])) * d[db][3]);
-      *(u32x2*)(out + base + 16 * db) = ow;
+    for (int r = 0; r < 4; ++r) {
+      const float a = hs[2 * p][r] * inv_s - lm * hn[2 * p][r];
+      const float b = hs[2 * p + 1][r] * inv_s - lm * hn[2 * p + 1][r];
+      // vdst's odd rows trade places with vsrc's even rows.
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b),
+                                                       false, false);
+      e[p][r] = __uint_as_float(sw[0]);
+      e[p][4 + r] = __uint_as_float(sw[1]);
     }
-  } else {
+  const bool logits = (flags & kGateLogits) != 0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      u32x2 ow;
-      ow[0] = pack_bf16x2(bf16_lo(gw[db][0]) * d[db][0], bf16_hi(gw[db][0]) * d[db][1]);
-      ow[1] = pack_bf16x2(bf16_lo(gw[db][1]) * d[db][2], bf16_hi(gw[db][1]) * d[db][3]);
-      *(u32x2*)(out + base + 16 * db) = ow;
+  for (int p = 0; p < NP; ++p) {
+    u32x4 ow;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float glo = bf16_lo(in.gate[p][w]), ghi = bf16_hi(in.gate[p][w]);
+      if (logits) {
+        glo = sigmoid_f32(glo);
+        ghi = sigmoid_f32(ghi);
+      }
+      ow[w] = pack_bf16x2(glo * e[p][2 * w], ghi * e[p][2 * w + 1]);
     }
+    *(u32x4*)(out + base + 32 * p) = ow;
   }
 }
 
@@ -522,6 +552,12 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
     qrow[NZ] = q_noise + (row * N + u) * C::DQK;
     run_tiles<C, NH, 0>(x, st, qrow, ring_lds, sk, sv);
+    HeadIn<C::DV> in[C::ASIG];
+    if constexpr (C::kEarlyEpilogue) {
+#pragma unroll
+      for (int s = 0; s < C::ASIG; ++s)
+        load_head_in<C::DV>(lam, gate, row, S, sig0 + s, x.g4, in[s]);
+    }
     // A query at a negative position has no visible key: its sums stay 0 and it
     // gives zeros.
     const float inv_n = st.lsum[NZ] > 0.f ? 1.f / st.lsum[NZ] : 0.f;
@@ -534,14 +570,22 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
         *(floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4) = hn[db];
+      if constexpr (C::kEarlyEpilogue) __syncthreads();  // release the B waves first
+    }
+    if constexpr (!C::kEarlyEpilogue) {
+#pragma unroll
+      for (int s = 0; s < C::ASIG; ++s)
+        load_head_in<C::DV>(lam, gate, row, S, sig0 + s, x.g4, in[s]);
     }
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
-        store_head<C::DV>(lam, gate, out, row, S, sig0 + s, x.g4, st.o[s],
-                          st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, flags);
+        store_head<C::DV>(out, row, S, sig0 + s, x.g4, st.o[s],
+                          st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
     }
-    if (C::NB > 0) __syncthreads();
+    if constexpr (!C::kEarlyEpilogue) {
+      if (C::NB > 0) __syncthreads();
+    }
   } else if (C::NB > 0) {
     constexpr int NH = C::NB > 0 ? C::NB : 1;  // [B signal heads]
     constexpr int b_first = C::ASIG;           // first B head, unit-relative
@@ -550,16 +594,27 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
     for (int s = 0; s < C::BSIG; ++s) qrow[s] = q_sig + (row * S + sig0 + b_first + s) * C::DQK;
     run_tiles<C, NH, 1>(x, st, qrow, ring_lds, sk, sv);
+    HeadIn<C::DV> in[NH];
+    if constexpr (C::kEarlyEpilogue) {  // in flight while waiting for the A waves
+#pragma unroll
+      for (int s = 0; s < C::BSIG; ++s)
+        load_head_in<C::DV>(lam, gate, row, S, sig0 + b_first + s, x.g4, in[s]);
+    }
     __syncthreads();  // the A waves' noise output is in LDS
     floatx4 hn[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
       hn[db] = *(const floatx4*)(sHN + ((qg * C::DB + db) * 64 + x.lane) * 4);
+    if constexpr (!C::kEarlyEpilogue) {
+#pragma unroll
+      for (int s = 0; s < C::BSIG; ++s)
+        load_head_in<C::DV>(lam, gate, row, S, sig0 + b_first + s, x.g4, in[s]);
+    }
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::BSIG; ++s)
-        store_head<C::DV>(lam, gate, out, row, S, sig0 + b_first + s, x.g4, st.o[s],
-                          st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, flags);
+        store_head<C::DV>(out, row, S, sig0 + b_first + s, x.g4, st.o[s],
+                          st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
     }
   }
 }
