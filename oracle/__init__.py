@@ -24,7 +24,8 @@ LAMBDA_LOGITS, GATE_LOGITS = 1, 2
 (EXACT, MUT_DROP_LAMBDA, MUT_PLUS_LAMBDA, MUT_TILED_REPEAT, MUT_KV_INTERLEAVE, MUT_WINDOW_OBO,
  MUT_SCALE_DV, MUT_NO_GATE, MUT_NO_CAUSAL, MUT_K_TRANSPOSED, MUT_LAMBDA_BY_GROUP,
  MUT_NO_NORMALIZE, MUT_DECODE_POS, MUT_SKIP_FIRST_KEY, MUT_LATENT_W_T, MUT_LATENT_NO_ROPE,
- MUT_LATENT_V_ROWS) = range(17)
+ MUT_LATENT_V_ROWS, MUT_BWD_NO_DELTA, MUT_BWD_LAMBDA_SIGN, MUT_BWD_NOISE_KV, MUT_BWD_DK_SCALE,
+ MUT_BWD_GATE_DERIV) = range(22)
 MUTANTS = {
     "drop_lambda": MUT_DROP_LAMBDA, "plus_lambda": MUT_PLUS_LAMBDA,
     "tiled_repeat": MUT_TILED_REPEAT, "kv_interleave": MUT_KV_INTERLEAVE,
@@ -33,6 +34,10 @@ MUTANTS = {
     "lambda_by_group": MUT_LAMBDA_BY_GROUP, "no_normalize": MUT_NO_NORMALIZE,
     "decode_position": MUT_DECODE_POS, "skip_first_key": MUT_SKIP_FIRST_KEY,
 }
+# Planted mistakes of the backward only.
+BWD_MUTANTS = {"no_delta": MUT_BWD_NO_DELTA, "lambda_sign": MUT_BWD_LAMBDA_SIGN,
+               "noise_not_in_dkv": MUT_BWD_NOISE_KV, "dk_without_scale": MUT_BWD_DK_SCALE,
+               "gate_logit_derivative": MUT_BWD_GATE_DERIV}
 # Planted mistakes of the latent-cache decode only.
 LATENT_MUTANTS = {"w_transposed": MUT_LATENT_W_T, "no_rope": MUT_LATENT_NO_ROPE,
                   "value_from_key_rows": MUT_LATENT_V_ROWS}
@@ -75,6 +80,12 @@ def _load():
         lib.gda_ref_decode_latent.restype = ctypes.c_int
         lib.gda_ref_decode_latent.argtypes = ([vp] * 9 + [i64] * 10 + [ctypes.c_int, f64,
                                                                      ctypes.c_int, ctypes.c_int])
+        ci = ctypes.c_int
+        lib.gda_ref_fwd_train.restype = ci
+        lib.gda_ref_fwd_train.argtypes = [vp] * 10 + [i64] * 8 + [ci, f64, ci]
+        lib.gda_ref_bwd.restype = ci
+        lib.gda_ref_bwd.argtypes = ([vp] * 13 + [i64] * 8 + [ci, f64, ci, vp, i64, vp, i64,
+                                                            ci])
         lib.gda_ref_threads.restype = ctypes.c_int
         lib.gda_ref_threads.argtypes = []
         _lib = lib
@@ -226,4 +237,79 @@ def ref_fwd_varlen(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k, *, window: int,
                                     _flags(lambda_logits, gate_logits))
     if rc != 0:
         raise ValueError(f"gda_ref_fwd_varlen rejected its arguments (code {rc})")
+    return out
+
+
+def _shape4(q_sig, q_noise, k, v, lam, gate):
+    B, L, S, dqk = q_sig.shape
+    N, Hkv, dv = q_noise.shape[2], v.shape[2], v.shape[3]
+    assert q_noise.shape == (B, L, N, dqk) and k.shape == (B, L, Hkv, dqk)
+    assert v.shape == (B, L, Hkv, dv) and lam.shape == (B, L, S) and gate.shape == (B, L, S, dv)
+    return B, L, S, N, Hkv, dqk, dv
+
+
+def ref_fwd_train(q_sig, q_noise, k, v, lam, gate, *, window: int, scale: float | None = None,
+                  lambda_logits: bool = False, gate_logits: bool = False):
+    """Training form of the prefill oracle. Returns (out [B,L,S,dv], h_sig [B,L,S,dv],
+    h_noise [B,L,N,dv], lse [B,S+N,L]): the output, each path's normalised attention output
+    and each attention row's log-sum-exp of its scaled scores (natural log; signal heads
+    first, then noise heads), all float64."""
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, k, v, lam, gate = (_c(x, code) for x in (q_sig, q_noise, k, v, lam, gate))
+    B, L, S, N, Hkv, dqk, dv = _shape4(q_sig, q_noise, k, v, lam, gate)
+    out = np.empty((B, L, S, dv), dtype=np.float64)
+    h_sig = np.empty((B, L, S, dv), dtype=np.float64)
+    h_noise = np.empty((B, L, N, dv), dtype=np.float64)
+    lse = np.empty((B, S + N, L), dtype=np.float64)
+    rc = _load().gda_ref_fwd_train(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam),
+                                   _ptr(gate), _ptr(out), _ptr(h_sig), _ptr(h_noise), _ptr(lse),
+                                   B, L, S, N, Hkv, dqk, dv, int(window), code,
+                                   float(scale or 0.0), _flags(lambda_logits, gate_logits))
+    if rc != 0:
+        raise ValueError(f"gda_ref_fwd_train rejected its arguments (code {rc})")
+    return out, h_sig, h_noise, lse
+
+
+def ref_bwd(q_sig, q_noise, k, v, lam, gate, d_out, *, window: int, scale: float | None = None,
+            lambda_logits: bool = False, gate_logits: bool = False, q_rows=None, k_rows=None,
+            mutant: int = EXACT) -> dict:
+    """Backward oracle: gradients of sum(d_out * out). d_out [B,L,S,dv] at the inputs'
+    storage type. Returns float64 dq_sig, dq_noise, dk, dv, dlam, dgate with the inputs'
+    shapes, or, with ``q_rows`` / ``k_rows`` (flat b*L+t rows), only those rows:
+    dq_sig [nq,S,dqk], dq_noise [nq,N,dqk], dlam [nq,S], dgate [nq,S,dv], dk [nk,Hkv,dqk],
+    dv [nk,Hkv,dv]."""
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, k, v, lam, gate, d_out = (
+        _c(x, code) for x in (q_sig, q_noise, k, v, lam, gate, d_out))
+    B, L, S, N, Hkv, dqk, dv = _shape4(q_sig, q_noise, k, v, lam, gate)
+    assert d_out.shape == (B, L, S, dv)
+
+    def rows_of(r):
+        if r is None:
+            return None, B * L, None
+        a = np.ascontiguousarray(np.asarray(r, dtype=np.int64).reshape(-1))
+        return a, a.size, _ptr(a)
+
+    qa, nq, qp = rows_of(q_rows)
+    ka, nk, kp = rows_of(k_rows)
+    dq_sig = np.empty((nq, S, dqk)); dq_noise = np.empty((nq, N, dqk))
+    dlam = np.empty((nq, S)); dgate = np.empty((nq, S, dv))
+    dk = np.empty((nk, Hkv, dqk)); dvv = np.empty((nk, Hkv, dv))
+    rc = _load().gda_ref_bwd(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam), _ptr(gate),
+                             _ptr(d_out), _ptr(dq_sig), _ptr(dq_noise), _ptr(dk), _ptr(dvv),
+                             _ptr(dlam), _ptr(dgate), B, L, S, N, Hkv, dqk, dv, int(window), code,
+                             float(scale or 0.0), _flags(lambda_logits, gate_logits), qp,
+                             nq if qa is not None else 0, kp, nk if ka is not None else 0,
+                             int(mutant))
+    if rc != 0:
+        raise ValueError(f"gda_ref_bwd rejected its arguments (code {rc})")
+    out = dict(dq_sig=dq_sig, dq_noise=dq_noise, dk=dk, dv=dvv, dlam=dlam, dgate=dgate)
+    if q_rows is None:
+        out["dq_sig"] = dq_sig.reshape(B, L, S, dqk)
+        out["dq_noise"] = dq_noise.reshape(B, L, N, dqk)
+        out["dlam"] = dlam.reshape(B, L, S)
+        out["dgate"] = dgate.reshape(B, L, S, dv)
+    if k_rows is None:
+        out["dk"] = dk.reshape(B, L, Hkv, dqk)
+        out["dv"] = dvv.reshape(B, L, Hkv, dv)
     return out

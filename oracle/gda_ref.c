@@ -459,4 +459,311 @@ int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_
   return failed ? -8 : 0;
 }
 
+/* ---- Training form of the forward, and the backward ----------------------------
+ * The backward is the chain rule taken through the forward definition above, its
+ * steps in reverse order:
+ *   out = G (.) D with D = H_S - lambda Repeat_g(H_N):
+ *     dG = d_out (.) D                       (times G(1-G) when the gate is a logit)
+ *     dD = d_out (.) G
+ *     dlambda_i = -sum_e dD_i,e H_N,j(i),e    (times lambda(1-lambda) for a logit)
+ *     dH_S,i = dD_i,   dH_N,j = -sum over the group's signal heads of lambda_i dD_i
+ *   every attention row (query t of head h over KV head kv(h)), with the
+ *   normalised weights P_s = exp(z_s - lse) of its scaled scores z:
+ *     dP_s = dH . v_s,   delta = sum_s P_s dP_s,   dz_s = P_s (dP_s - delta)
+ *     dq_t = scale sum_s dz_s k_s,   dk_s += scale dz_s q_t,   dv_s += P_s dH
+ */
+
+static double score(const void* q, int64_t q_off, const kv_view* kv, int64_t b, int64_t h,
+                    int64_t s, double scale) {
+  double acc = 0.0;
+  for (int64_t d = 0; d < kv->dqk; ++d)
+    acc += rd(q, q_off + d, kv->dtype) * rd(kv->k, k_index(kv, b, s, h, d), kv->dtype);
+  return scale * acc;
+}
+
+/* Scaled scores of one query row over keys lo..hi into z; returns their
+ * log-sum-exp (natural log), -inf when no key is visible. */
+static double row_lse(const void* q, int64_t q_off, const kv_view* kv, int64_t b, int64_t h,
+                      int64_t lo, int64_t hi, double scale, double* z) {
+  if (hi < lo) return -INFINITY;
+  double m = -INFINITY;
+  for (int64_t s = lo; s <= hi; ++s) {
+    z[s - lo] = score(q, q_off, kv, b, h, s, scale);
+    if (z[s - lo] > m) m = z[s - lo];
+  }
+  double l = 0.0;
+  for (int64_t s = lo; s <= hi; ++s) l += exp(z[s - lo] - m);
+  return m + log(l);
+}
+
+static double softmax_scale_of(const kv_view* kv) {
+  return kv->scale > 0.0 ? kv->scale : 1.0 / sqrt((double)kv->dqk);
+}
+
+/* Head h of a row (0..S-1 signal, S..S+N-1 noise): its query offset and KV head. */
+static void head_of(int64_t h, int64_t flat, int64_t S, int64_t N, int64_t Hkv, int64_t dqk,
+                    const void* q_sig, const void* q_noise, const void** q, int64_t* q_off,
+                    int64_t* kvh) {
+  if (h < S) {
+    *q = q_sig;
+    *q_off = (flat * S + h) * dqk;
+    *kvh = (h * Hkv) / S;
+  } else {
+    *q = q_noise;
+    *q_off = (flat * N + (h - S)) * dqk;
+    *kvh = ((h - S) * Hkv) / N;
+  }
+}
+
+int gda_ref_fwd_train(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                      const void* lambda, const void* gate, double* out, double* h_sig,
+                      double* h_noise, double* lse, int64_t B, int64_t L, int64_t S,
+                      int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
+                      int dtype, double softmax_scale, int flags) {
+  int rc = gda_ref_fwd_ex(q_sig, q_noise, k, v, lambda, gate, out, B, L, S, N, Hkv, dqk, dv,
+                          window, dtype, NULL, 0, softmax_scale, flags, GDA_REF_EXACT);
+  if (rc) return rc;
+  if (!h_sig || !h_noise || !lse) return -6;
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, GDA_REF_EXACT, softmax_scale, flags};
+  const double scale = softmax_scale_of(&kv);
+  const int64_t HT = S + N;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!z) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t flat = 0; flat < B * L; ++flat) {
+        const int64_t b = flat / L, t = flat % L;
+        int64_t lo, hi;
+        visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, flat, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          const double ls = row_lse(q, q_off, &kv, b, kvh, lo, hi, scale, z);
+          lse[(b * HT + h) * L + t] = ls;
+          double* H = h < S ? h_sig + (flat * S + h) * dv : h_noise + (flat * N + h - S) * dv;
+          for (int64_t e = 0; e < dv; ++e) H[e] = 0.0;
+          for (int64_t s2 = lo; s2 <= hi; ++s2) {
+            const double P = exp(z[s2 - lo] - ls);
+            for (int64_t e = 0; e < dv; ++e)
+              H[e] += P * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
+          }
+        }
+      }
+    }
+    free(z);
+  }
+  return failed ? -8 : 0;
+}
+
+int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                const void* lambda, const void* gate, const void* d_out, double* dq_sig,
+                double* dq_noise, double* dk, double* dv_out, double* dlambda, double* dgate,
+                int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv, int64_t dqk,
+                int64_t dv, int64_t window, int dtype, double softmax_scale, int flags,
+                const int64_t* q_rows, int64_t n_q_rows, const int64_t* k_rows,
+                int64_t n_k_rows, int mutant) {
+  int rc = check_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
+  if (rc) return rc;
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !d_out || !dq_sig || !dq_noise ||
+      !dk || !dv_out || !dlambda || !dgate)
+    return -6;
+  if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
+    return -9;
+  const int64_t BL = B * L, HT = S + N, g = S / N;
+  const int64_t nq = q_rows ? n_q_rows : BL, nk = k_rows ? n_k_rows : BL;
+  for (int64_t r = 0; r < nq; ++r)
+    if (q_rows && (q_rows[r] < 0 || q_rows[r] >= BL)) return -7;
+  for (int64_t r = 0; r < nk; ++r)
+    if (k_rows && (k_rows[r] < 0 || k_rows[r] >= BL)) return -7;
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
+  const double scale = softmax_scale_of(&kv);
+
+  /* Query rows whose forward quantities are needed: the query-side outputs, and
+   * every query that sees one of the key-side rows. */
+  int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)BL);
+  if (!slot) return -8;
+  for (int64_t i = 0; i < BL; ++i) slot[i] = -1;
+  for (int64_t r = 0; r < nq; ++r) slot[q_rows ? q_rows[r] : r] = 0;
+  for (int64_t r = 0; r < nk; ++r) {
+    const int64_t flat = k_rows ? k_rows[r] : r, b = flat / L, s = flat % L;
+    const int64_t t_hi = window ? (s + window - 1 < L - 1 ? s + window - 1 : L - 1) : L - 1;
+    for (int64_t t = s; t <= t_hi; ++t) slot[b * L + t] = 0;
+  }
+  int64_t nrow = 0;
+  for (int64_t i = 0; i < BL; ++i)
+    if (slot[i] == 0) slot[i] = nrow++;
+  int64_t* row_flat = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrow ? nrow : 1));
+  double* dH = (double*)malloc(sizeof(double) * (size_t)((nrow ? nrow : 1) * HT * dv));
+  double* row_lse_v = (double*)malloc(sizeof(double) * (size_t)((nrow ? nrow : 1) * HT));
+  double* delta = (double*)malloc(sizeof(double) * (size_t)((nrow ? nrow : 1) * HT));
+  /* query-side output position of each needed row (-1: not an output row) */
+  int64_t* q_out = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrow ? nrow : 1));
+  if (!row_flat || !dH || !row_lse_v || !delta || !q_out) {
+    free(slot);
+    free(row_flat);
+    free(dH);
+    free(row_lse_v);
+    free(delta);
+    free(q_out);
+    return -8;
+  }
+  for (int64_t i = 0; i < BL; ++i)
+    if (slot[i] >= 0) row_flat[slot[i]] = i;
+  for (int64_t r = 0; r < nrow; ++r) q_out[r] = -1;
+  for (int64_t r = 0; r < nq; ++r) q_out[slot[q_rows ? q_rows[r] : r]] = r;
+
+  int failed = 0;
+  /* 1. Per needed row: every head's forward (lse, H), then the combine and gate
+   *    backward (dG, dlambda, dH), then delta = sum_s P_s dP_s for every head. */
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    double* H = (double*)malloc(sizeof(double) * (size_t)(HT * dv));
+    double* lam = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!z || !H || !lam) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < nrow; ++r) {
+        const int64_t flat = row_flat[r], b = flat / L, t = flat % L;
+        int64_t lo, hi;
+        visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, flat, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          const double ls = row_lse(q, q_off, &kv, b, kvh, lo, hi, scale, z);
+          row_lse_v[r * HT + h] = ls;
+          for (int64_t e = 0; e < dv; ++e) H[h * dv + e] = 0.0;
+          for (int64_t s2 = lo; s2 <= hi; ++s2) {
+            const double P = exp(z[s2 - lo] - ls);
+            for (int64_t e = 0; e < dv; ++e)
+              H[h * dv + e] += P * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
+          }
+        }
+        double* dHr = dH + r * HT * dv;
+        for (int64_t i = 0; i < S; ++i) {
+          const int64_t j = i / g;
+          double lm = rd(lambda, flat * S + i, dtype);
+          if (flags & GDA_REF_LAMBDA_LOGITS) lm = sigmoid(lm);
+          lam[i] = lm;
+          double dlam = 0.0;
+          for (int64_t e = 0; e < dv; ++e) {
+            const double D = H[i * dv + e] - lm * H[(S + j) * dv + e];
+            const double gi = rd(gate, (flat * S + i) * dv + e, dtype);
+            const double G = (flags & GDA_REF_GATE_LOGITS) ? sigmoid(gi) : gi;
+            const double dO = rd(d_out, (flat * S + i) * dv + e, dtype);
+            double dG = dO * D;
+            if ((flags & GDA_REF_GATE_LOGITS) && mutant != GDA_REF_MUT_BWD_GATE_DERIV)
+              dG *= G * (1.0 - G);
+            const double dD = dO * G;
+            dHr[i * dv + e] = dD;
+            dlam += (mutant == GDA_REF_MUT_BWD_LAMBDA_SIGN ? 1.0 : -1.0) * dD *
+                    H[(S + j) * dv + e];
+            if (q_out[r] >= 0) dgate[(q_out[r] * S + i) * dv + e] = dG;
+          }
+          if (flags & GDA_REF_LAMBDA_LOGITS) dlam *= lm * (1.0 - lm);
+          if (q_out[r] >= 0) dlambda[q_out[r] * S + i] = dlam;
+        }
+        for (int64_t j = 0; j < N; ++j)
+          for (int64_t e = 0; e < dv; ++e) {
+            double acc = 0.0;
+            for (int64_t i = g * j; i < g * j + g; ++i) acc -= lam[i] * dHr[i * dv + e];
+            dHr[(S + j) * dv + e] = acc;
+          }
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, flat, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          double dl = 0.0;
+          for (int64_t s2 = lo; s2 <= hi; ++s2) {
+            const double P = exp(score(q, q_off, &kv, b, kvh, s2, scale) - row_lse_v[r * HT + h]);
+            double dP = 0.0;
+            for (int64_t e = 0; e < dv; ++e)
+              dP += dHr[h * dv + e] * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
+            dl += P * dP;
+          }
+          delta[r * HT + h] = mutant == GDA_REF_MUT_BWD_NO_DELTA ? 0.0 : dl;
+        }
+      }
+    }
+    free(z);
+    free(H);
+    free(lam);
+  }
+
+  /* 2. Query side: dq_t = scale sum_s dz_s k_s for every head. */
+  if (!failed) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rq = 0; rq < nq; ++rq) {
+      const int64_t flat = q_rows ? q_rows[rq] : rq, b = flat / L, t = flat % L;
+      const int64_t r = slot[flat];
+      int64_t lo, hi;
+      visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+      for (int64_t h = 0; h < HT; ++h) {
+        const void* q;
+        int64_t q_off, kvh;
+        head_of(h, flat, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+        double* dq = h < S ? dq_sig + (rq * S + h) * dqk : dq_noise + (rq * N + h - S) * dqk;
+        for (int64_t d = 0; d < dqk; ++d) dq[d] = 0.0;
+        for (int64_t s2 = lo; s2 <= hi; ++s2) {
+          const double P = exp(score(q, q_off, &kv, b, kvh, s2, scale) - row_lse_v[r * HT + h]);
+          double dP = 0.0;
+          for (int64_t e = 0; e < dv; ++e)
+            dP += dH[(r * HT + h) * dv + e] * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
+          const double dz = P * (dP - delta[r * HT + h]);
+          for (int64_t d = 0; d < dqk; ++d)
+            dq[d] += scale * dz * rd(k, k_index(&kv, b, s2, kvh, d), dtype);
+        }
+      }
+    }
+
+    /* 3. Key side: dk_s = scale sum_t dz_ts q_t, dv_s = sum_t P_ts dH_t over every
+     *    query t that sees key s and every head on the KV head. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rk = 0; rk < nk; ++rk) {
+      const int64_t flat = k_rows ? k_rows[rk] : rk, b = flat / L, s2 = flat % L;
+      for (int64_t x = 0; x < Hkv * dqk; ++x) dk[rk * Hkv * dqk + x] = 0.0;
+      for (int64_t x = 0; x < Hkv * dv; ++x) dv_out[rk * Hkv * dv + x] = 0.0;
+      const int64_t t_hi = window ? (s2 + window - 1 < L - 1 ? s2 + window - 1 : L - 1) : L - 1;
+      for (int64_t t = s2; t <= t_hi; ++t) {
+        int64_t lo, hi;
+        visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+        if (s2 < lo || s2 > hi) continue;
+        const int64_t qflat = b * L + t, r = slot[qflat];
+        for (int64_t h = 0; h < HT; ++h) {
+          if (h >= S && mutant == GDA_REF_MUT_BWD_NOISE_KV) continue;
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, qflat, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          const double P = exp(score(q, q_off, &kv, b, kvh, s2, scale) - row_lse_v[r * HT + h]);
+          double dP = 0.0;
+          for (int64_t e = 0; e < dv; ++e)
+            dP += dH[(r * HT + h) * dv + e] * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
+          const double dz = P * (dP - delta[r * HT + h]);
+          const double ks = mutant == GDA_REF_MUT_BWD_DK_SCALE ? 1.0 : scale;
+          for (int64_t d = 0; d < dqk; ++d)
+            dk[(rk * Hkv + kvh) * dqk + d] += ks * dz * rd(q, q_off + d, dtype);
+          for (int64_t e = 0; e < dv; ++e)
+            dv_out[(rk * Hkv + kvh) * dv + e] += P * dH[(r * HT + h) * dv + e];
+        }
+      }
+    }
+  }
+  free(slot);
+  free(row_flat);
+  free(dH);
+  free(row_lse_v);
+  free(delta);
+  free(q_out);
+  return failed ? -8 : 0;
+}
+
 int gda_ref_threads(void) { return omp_get_max_threads(); }

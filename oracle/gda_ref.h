@@ -44,7 +44,12 @@ enum {
   GDA_REF_MUT_LATENT_W_T = 14,   /* latent: W^KV_b read as [Hkv, Dc, Dn+dv]   */
   GDA_REF_MUT_LATENT_NO_ROPE = 15, /* latent: rotary key term dropped         */
   GDA_REF_MUT_LATENT_V_ROWS = 16, /* latent: value from the key rows of W     */
-  GDA_REF_MUT_COUNT = 17
+  GDA_REF_MUT_BWD_NO_DELTA = 17,  /* backward: dz = P dP (row term dropped)    */
+  GDA_REF_MUT_BWD_LAMBDA_SIGN = 18, /* backward: dlambda with the wrong sign   */
+  GDA_REF_MUT_BWD_NOISE_KV = 19,  /* backward: noise path left out of dK, dV   */
+  GDA_REF_MUT_BWD_DK_SCALE = 20,  /* backward: dK without the softmax scale    */
+  GDA_REF_MUT_BWD_GATE_DERIV = 21, /* backward: gate logits without sigmoid'   */
+  GDA_REF_MUT_COUNT = 22
 };
 
 /* Prefill. Layouts (row-major, innermost contiguous):
@@ -114,6 +119,34 @@ int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_
                           int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
                           int64_t Dn, int64_t Dr, int64_t Dc, int64_t dv, int64_t window,
                           int dtype, double softmax_scale, int flags, int mutant);
+
+/* Training form of the forward: out as gda_ref_fwd_ex, plus what the backward
+ * takes from the forward:
+ *   h_sig [B,L,S,dv], h_noise [B,L,N,dv]: each path's normalised attention output;
+ *   lse [B,S+N,L]: log(sum_s exp(z_s)) of each attention row's scaled scores z
+ *   (natural log; heads 0..S-1 are the signal heads, S..S+N-1 the noise heads). */
+int gda_ref_fwd_train(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                      const void* lambda, const void* gate, double* out, double* h_sig,
+                      double* h_noise, double* lse,
+                      int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
+                      int64_t dqk, int64_t dv, int64_t window, int dtype,
+                      double softmax_scale, int flags);
+
+/* Backward of the prefill: the gradients of sum(d_out (.) out) with respect to
+ * q_sig, q_noise, k, v, lambda and gate (with the logit flags, with respect to the
+ * logits). d_out [B,L,S,dv] is of storage type dtype; every gradient is double.
+ * q_rows: NULL for every (b,t), else n_q_rows flat query rows b*L+t; the query-side
+ *   gradients are then dq_sig [n_q_rows,S,dqk], dq_noise [n_q_rows,N,dqk],
+ *   dlambda [n_q_rows,S], dgate [n_q_rows,S,dv] (else [B,L,...]).
+ * k_rows: likewise for the key side: dk [n_k_rows,Hkv,dqk], dv_out [n_k_rows,Hkv,dv]. */
+int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                const void* lambda, const void* gate, const void* d_out, double* dq_sig,
+                double* dq_noise, double* dk, double* dv_out, double* dlambda, double* dgate,
+                int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
+                int64_t dqk, int64_t dv, int64_t window, int dtype,
+                double softmax_scale, int flags,
+                const int64_t* q_rows, int64_t n_q_rows, const int64_t* k_rows,
+                int64_t n_k_rows, int mutant);
 
 /* Threads an OpenMP parallel region of this library starts with (for timing reports). */
 int gda_ref_threads(void);

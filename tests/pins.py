@@ -462,6 +462,127 @@ def pin_varlen(fwd_varlen):
     return msgs
 
 
+# ---------------------------------------------------------------------------------------
+# The backward and the training form of the forward.
+BWD_LAYOUTS = {
+    "A": LAYOUTS["A"], "B": LAYOUTS["B"],
+    # more noise heads than KV heads: S=4, N=2, Hkv=1, every head on KV 0, groups of 2
+    "D": dict(S=4, N=2, Hkv=1, kv_sig=lambda i: 0, kv_noise=lambda j: 0,
+              group=lambda i: i // 2),
+}
+
+
+def make_bwd(lay_name, *, B=2, L=7, dqk=6, dv=4, dtype="f32", case_id=1500, logits=False):
+    lay = BWD_LAYOUTS[lay_name]
+    x = gin.fwd_inputs(case_id, B=B, L=L, S=lay["S"], N=lay["N"], Hkv=lay["Hkv"], dqk=dqk,
+                       dv=dv, dtype=dtype)
+    if logits:  # logits: unbounded draws in place of the sigmoid values
+        x["lam"] = np.stack([gin.normal(case_id, 41, b, x["lam"].shape[1:], dtype)
+                             for b in range(B)])
+        x["gate"] = np.stack([gin.normal(case_id, 42, b, x["gate"].shape[1:], dtype)
+                              for b in range(B)])
+    x["d_out"] = np.stack([gin.normal(case_id, 50, b, x["gate"].shape[1:], dtype)
+                           for b in range(B)])
+    return x
+
+
+def torch_gda_grads(x, lay, window, scale=None, lambda_logits=False, gate_logits=False):
+    """Gradients of sum(d_out * out) by torch autograd in float64, with out composed from
+    torch's scaled_dot_product_attention per head as the workload descriptions state the
+    head maps (no step of the oracle)."""
+    t = {n: torch.from_numpy(f64(x[n])).requires_grad_(n != "d_out") for n in x}
+    L = t["q_sig"].shape[1]
+    mask = band_mask(L, window)
+    F = torch.nn.functional
+
+    def att(q, k, v):
+        return F.scaled_dot_product_attention(q[:, None], k[:, None], v[:, None],
+                                              attn_mask=mask, scale=scale)[:, 0]
+
+    HS = torch.stack([att(t["q_sig"][:, :, i], t["k"][:, :, lay["kv_sig"](i)],
+                          t["v"][:, :, lay["kv_sig"](i)]) for i in range(lay["S"])], dim=2)
+    HN = torch.stack([att(t["q_noise"][:, :, j], t["k"][:, :, lay["kv_noise"](j)],
+                          t["v"][:, :, lay["kv_noise"](j)]) for j in range(lay["N"])], dim=2)
+    lamv = torch.sigmoid(t["lam"]) if lambda_logits else t["lam"]
+    G = torch.sigmoid(t["gate"]) if gate_logits else t["gate"]
+    rep = HN[:, :, [lay["group"](i) for i in range(lay["S"])]]
+    out = G * (HS - lamv[..., None] * rep)
+    (out * t["d_out"]).sum().backward()
+    return dict(dq_sig=t["q_sig"].grad, dq_noise=t["q_noise"].grad, dk=t["k"].grad,
+                dv=t["v"].grad, dlam=t["lam"].grad, dgate=t["gate"].grad)
+
+
+BWD_CASES = [  # (layout, window, options)
+    ("A", 0, {}), ("A", 3, {}), ("B", 0, {}), ("B", 4, {}), ("D", 0, {}), ("D", 2, {}),
+    ("A", 0, dict(scale=0.3, lambda_logits=True, gate_logits=True)),
+    ("B", 3, dict(scale=0.45, gate_logits=True)),
+]
+
+
+def pin_backward(bwd, cases=BWD_CASES, dtype="f32"):
+    """Every gradient against torch autograd through the library attention."""
+    msgs = []
+    for lay_name, W, opts in cases:
+        x = make_bwd(lay_name, dtype=dtype, logits=bool(opts))
+        got = bwd(*(x[n] for n in ARGS), x["d_out"], window=W, **opts)
+        ref = torch_gda_grads(x, BWD_LAYOUTS[lay_name], W, **opts)
+        for name, r in ref.items():
+            r = r.numpy()
+            tol = 1e-11 * max(1.0, np.abs(r).max())
+            _fail(msgs, f"backward {name} layout {lay_name} W={W} {opts}",
+                  np.abs(got[name] - r).max(), tol)
+    return msgs
+
+
+def pin_fwd_train(fwd_train, fwd):
+    """Training-form outputs: out equals the plain forward, each path's output equals the
+    library attention, lse equals torch's logsumexp of the masked, scaled scores."""
+    msgs = []
+    for lay_name, W, opts in BWD_CASES:
+        lay = BWD_LAYOUTS[lay_name]
+        x = make_bwd(lay_name, logits=bool(opts))
+        out, hs, hn, lse = fwd_train(*(x[n] for n in ARGS), window=W, **opts)
+        _fail(msgs, f"train out {lay_name} W={W}",
+              np.abs(out - fwd(*(x[n] for n in ARGS), window=W, **opts)).max(), 1e-13)
+        qs, qn, k, v = (f64(x[n]) for n in ("q_sig", "q_noise", "k", "v"))
+        sc = opts.get("scale") or 1.0 / math.sqrt(qs.shape[-1])
+        mask = band_mask(qs.shape[1], W)
+        for h in range(lay["S"] + lay["N"]):
+            sig = h < lay["S"]
+            q = qs[:, :, h] if sig else qn[:, :, h - lay["S"]]
+            kv = lay["kv_sig"](h) if sig else lay["kv_noise"](h - lay["S"])
+            H = sdpa(q, k[:, :, kv], v[:, :, kv], W, scale=opts.get("scale"))
+            got_h = hs[:, :, h] if sig else hn[:, :, h - lay["S"]]
+            _fail(msgs, f"train H head {h} {lay_name} W={W}", np.abs(got_h - H).max(), 1e-12)
+            z = sc * torch.einsum("bld,bsd->bls", torch.from_numpy(q),
+                                  torch.from_numpy(k[:, :, kv]))
+            ref_lse = torch.logsumexp(z.masked_fill(~mask, -math.inf), dim=-1).numpy()
+            _fail(msgs, f"train lse head {h} {lay_name} W={W}",
+                  np.abs(lse[:, h] - ref_lse).max(), 1e-12)
+    return msgs
+
+
+def pin_backward_rows(bwd):
+    """Selected query and key rows equal the same rows of the full backward (the sampled
+    form the full-size checks use)."""
+    msgs = []
+    for W in (0, 3):
+        x = make_bwd("A", B=2, L=11)
+        full = bwd(*(x[n] for n in ARGS), x["d_out"], window=W)
+        q_rows, k_rows = [0, 5, 13, 21], [1, 10, 11, 20]
+        part = bwd(*(x[n] for n in ARGS), x["d_out"], window=W, q_rows=q_rows, k_rows=k_rows)
+        L = 11
+        for name in ("dq_sig", "dq_noise", "dlam", "dgate"):
+            f = full[name].reshape((2 * L,) + full[name].shape[2:])[q_rows]
+            if not np.array_equal(f, part[name]):
+                msgs.append(f"rows {name} W={W}")
+        for name in ("dk", "dv"):
+            f = full[name].reshape((2 * L,) + full[name].shape[2:])[k_rows]
+            if not np.array_equal(f, part[name]):
+                msgs.append(f"rows {name} W={W}")
+    return msgs
+
+
 def all_pins(fwd, decode):
     msgs = []
     for p in (pin_library_sdpa, pin_noise_one_hot, pin_identical_queries_zero,

@@ -136,3 +136,30 @@ def test_rejects_bad_arguments():
     with pytest.raises(TypeError):
         oracle.ref_fwd(x["q_sig"].astype(np.float64), x["q_noise"], x["k"], x["v"], x["lam"],
                        x["gate"], window=0)
+
+
+def _bwd(mutant=oracle.EXACT):
+    def f(*a, **kw):
+        return oracle.ref_bwd(*a, mutant=mutant, **kw)
+    return f
+
+
+def test_backward_pin():
+    assert pins.pin_backward(_bwd()) == []
+
+
+def test_backward_pin_bf16_inputs():
+    assert pins.pin_backward(_bwd(), cases=pins.BWD_CASES[:3], dtype="bf16") == []
+
+
+@pytest.mark.parametrize("name", sorted(oracle.BWD_MUTANTS))
+def test_backward_planted_mistake_is_caught(name):
+    assert pins.pin_backward(_bwd(oracle.BWD_MUTANTS[name])) != []
+
+
+def test_fwd_train_pin():
+    assert pins.pin_fwd_train(oracle.ref_fwd_train, oracle.ref_fwd) == []
+
+
+def test_backward_rows_subset():
+    assert pins.pin_backward_rows(_bwd()) == []
