@@ -1,7 +1,7 @@
 """PyTorch front end of libgda: tensors in, tensors out, same names as the C ABI.
 
 PyTorch only provides device memory and the stream. Every step of the
-computation runs in the HIP kernels behind ``gda_fwd`` / ``gda_decode``.
+computation runs in the HIP kernels behind the C entry points.
 """
 from __future__ import annotations
 
@@ -195,3 +195,82 @@ def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Te
 def latent_workspace_bytes(B: int, Lmax: int, S: int, N: int, window: int = 0) -> int:
     """Bytes of workspace gda_decode_latent needs for these sizes."""
     return _lib.latent_workspace_bytes(B, Lmax, S, N, int(window))
+
+
+def _prefill_shapes(name, q_sig, q_noise, k, v, lam, gate):
+    if q_sig.dim() != 4 or q_noise.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"{name}: q_sig, q_noise, k, v must be 4-D")
+    B, L, S, dqk = q_sig.shape
+    N, Hkv, dv = q_noise.shape[2], k.shape[2], v.shape[3]
+    dev, dt = q_sig.device, q_sig.dtype
+    _dtype_code(q_sig)
+    if dev.type != "cuda":
+        raise ValueError(f"{name}: tensors must be on a HIP (cuda) device")
+    _check("q_sig", q_sig, (B, L, S, dqk), dt, dev)
+    _check("q_noise", q_noise, (B, L, N, dqk), dt, dev)
+    _check("k", k, (B, L, Hkv, dqk), dt, dev)
+    _check("v", v, (B, L, Hkv, dv), dt, dev)
+    _check("lam", lam, (B, L, S), dt, dev)
+    _check("gate", gate, (B, L, S, dv), dt, dev)
+    return B, L, S, N, Hkv, dqk, dv, dev, dt
+
+
+def gda_fwd_train(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  lam: torch.Tensor, gate: torch.Tensor, window: int = 0,
+                  scale: float | None = None, lambda_logits: bool = False,
+                  gate_logits: bool = False):
+    """Training-form prefill (bf16): returns (out [B,L,S,dv], h_sig [B,L,S,dv],
+    h_noise [B,L,N,dv], lse float32 [B,S+N,L]) - the output, each path's normalised
+    attention output and each attention row's log-sum-exp (natural log)."""
+    B, L, S, N, Hkv, dqk, dv, dev, dt = _prefill_shapes("gda_fwd_train", q_sig, q_noise, k, v,
+                                                        lam, gate)
+    out = torch.empty((B, L, S, dv), dtype=dt, device=dev)
+    h_sig = torch.empty((B, L, S, dv), dtype=dt, device=dev)
+    h_noise = torch.empty((B, L, N, dv), dtype=dt, device=dev)
+    lse = torch.empty((B, S + N, L), dtype=torch.float32, device=dev)
+    _lib.check(_lib.fwd_train_raw(
+        q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), out.data_ptr(), h_sig.data_ptr(), h_noise.data_ptr(), lse.data_ptr(),
+        B, L, S, N, Hkv, dqk, dv, int(window), _dtype_code(q_sig),
+        _lib.options(scale, lambda_logits, gate_logits), _stream(dev)))
+    return out, h_sig, h_noise, lse
+
+
+def bwd_workspace_bytes(B: int, L: int, S: int, N: int, dv: int) -> int:
+    return _lib.bwd_workspace_bytes(B, L, S, N, dv)
+
+
+def gda_bwd(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            lam: torch.Tensor, gate: torch.Tensor, h_sig: torch.Tensor, h_noise: torch.Tensor,
+            lse: torch.Tensor, d_out: torch.Tensor, window: int = 0, scale: float | None = None,
+            lambda_logits: bool = False, gate_logits: bool = False,
+            workspace: torch.Tensor | None = None, grads: dict | None = None) -> dict:
+    """Backward (bf16) of the forward gda_fwd_train ran: gradients of sum(d_out * out).
+    Returns dict(dq_sig, dq_noise, dk, dv, dlam, dgate) shaped like the inputs.
+    ``workspace``: uint8 device tensor of at least bwd_workspace_bytes(...) bytes
+    (allocated here when None); ``grads``: preallocated outputs (same keys)."""
+    B, L, S, N, Hkv, dqk, dv, dev, dt = _prefill_shapes("gda_bwd", q_sig, q_noise, k, v, lam,
+                                                        gate)
+    _check("h_sig", h_sig, (B, L, S, dv), dt, dev)
+    _check("h_noise", h_noise, (B, L, N, dv), dt, dev)
+    _check("lse", lse, (B, S + N, L), torch.float32, dev)
+    _check("d_out", d_out, (B, L, S, dv), dt, dev)
+    shapes = dict(dq_sig=(B, L, S, dqk), dq_noise=(B, L, N, dqk), dk=(B, L, Hkv, dqk),
+                  dv=(B, L, Hkv, dv), dlam=(B, L, S), dgate=(B, L, S, dv))
+    if grads is None:
+        grads = {n: torch.empty(sh, dtype=dt, device=dev) for n, sh in shapes.items()}
+    for n, sh in shapes.items():
+        _check(n, grads[n], sh, dt, dev)
+    need = _lib.bwd_workspace_bytes(B, L, S, N, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("workspace", workspace, (workspace.numel(),), torch.uint8, dev)
+    _lib.check(_lib.bwd_raw(
+        q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), h_sig.data_ptr(), h_noise.data_ptr(), lse.data_ptr(), d_out.data_ptr(),
+        grads["dq_sig"].data_ptr(), grads["dq_noise"].data_ptr(), grads["dk"].data_ptr(),
+        grads["dv"].data_ptr(), grads["dlam"].data_ptr(), grads["dgate"].data_ptr(), B, L, S, N,
+        Hkv, dqk, dv, int(window), _dtype_code(q_sig),
+        _lib.options(scale, lambda_logits, gate_logits), workspace.data_ptr(), workspace.numel(),
+        _stream(dev)))
+    return grads

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgda.so")
 
 SOURCES = ["gda_api.cpp", "gda_fwd_bf16.hip", "gda_decode_bf16.hip", "gda_f32.hip",
-           "gda_latent_bf16.hip"]
+           "gda_latent_bf16.hip", "gda_bwd_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 

@@ -76,6 +76,20 @@ class Case:
         n = B * (S * dqk + N * dqk + S + 2 * S * dv) + keys * H * (dqk + dv)
         return n * e + (4 * B if lens is not None else 0)
 
+    def bwd_flops(self) -> int:
+        """Backward FLOPs per launch: per visible (query, key) pair and query head, the
+        score recompute (2 dqk), dP = dO V^T (2 dv), dV (2 dv), dQ (2 dqk), dK (2 dqk)."""
+        return 2 * (3 * self.dqk + 2 * self.dv) * self.visible_pairs() * (self.S + self.N)
+
+    def bwd_bytes(self) -> int:
+        """Backward bytes: every input read once (Q, K, V, lambda, gate, both paths'
+        outputs, the row log-sum-exps, d_out) and every gradient written once."""
+        e = self.elem_bytes()
+        B, L, S, N, H, dqk, dv = self.B, self.L, self.S, self.N, self.Hkv, self.dqk, self.dv
+        reads = (S * dqk + N * dqk + H * dqk + H * dv + S + S * dv + S * dv + N * dv + S * dv)
+        writes = S * dqk + N * dqk + H * dqk + H * dv + S + S * dv
+        return B * L * (reads + writes) * e + 4 * B * L * (S + N)
+
     def tokens(self) -> int:
         return self.B * self.L if self.kind == "fwd" else self.B
 

@@ -259,6 +259,110 @@ gda_status gda_fwd_varlen(const void* q_sig, const void* q_noise, const void* k,
   return from_hip(dtype == GDA_BF16 ? gda::launch_fwd_bf16(a, s) : gda::launch_fwd_f32(a, s));
 }
 
+gda_status gda_fwd_train(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                         const void* lambda, const void* gate, void* out, void* h_sig,
+                         void* h_noise, float* lse, int B, int L, int S, int N, int Hkv,
+                         int dqk, int dv, int window, gda_dtype dtype, const gda_options* opts,
+                         void* stream) {
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out || !h_sig || !h_noise || !lse)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
+  gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, out);
+  if (st != GDA_SUCCESS) return st;
+  if (!aligned(h_sig, 16) || !aligned(h_noise, 16) || !aligned(lse, 4))
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "tensors must be 16-byte aligned (lse 4-byte)");
+  st = validate_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "the training form is bf16 only");
+  if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+  gda::FwdArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.gate = gate;
+  a.out = out;
+  a.cu_q = nullptr;
+  a.cu_k = nullptr;
+  a.B = B;
+  a.L = L;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  a.plan = make_plan(S, N, Hkv);
+  a.h_sig = h_sig;
+  a.h_noise = h_noise;
+  a.lse = lse;
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
+  if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
+    return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  return from_hip(gda::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+size_t gda_bwd_workspace_bytes(int B, int L, int S, int N, int dv) {
+  if (B < 1 || L < 1 || S < 1 || N < 1 || dv < 1) return 0;
+  return gda::bwd_workspace_bytes(B, L, S, N, dv);
+}
+
+gda_status gda_bwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                   const void* lambda, const void* gate, const void* h_sig, const void* h_noise,
+                   const float* lse, const void* d_out, void* dq_sig, void* dq_noise, void* dk,
+                   void* dv_out, void* dlambda, void* dgate, int B, int L, int S, int N, int Hkv,
+                   int dqk, int dv, int window, gda_dtype dtype, const gda_options* opts,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !h_sig || !h_noise || !lse ||
+      !d_out || !dq_sig || !dq_noise || !dk || !dv_out || !dlambda || !dgate || !workspace)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null pointer");
+  gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, h_sig);
+  if (st != GDA_SUCCESS) return st;
+  if ((st = check_alignment(h_noise, d_out, dq_sig, dq_noise, dk, dv_out, dgate)) != GDA_SUCCESS)
+    return st;
+  if (!aligned(dlambda, 16) || !aligned(workspace, 256) || !aligned(lse, 4))
+    return fail(GDA_ERROR_INVALID_ARGUMENT,
+                "dlambda must be 16-byte, workspace 256-byte, lse 4-byte aligned");
+  st = validate_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  if (workspace_bytes < gda::bwd_workspace_bytes(B, L, S, N, dv))
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "workspace smaller than gda_bwd_workspace_bytes");
+  gda::BwdArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.gate = gate;
+  a.h_sig = h_sig;
+  a.h_noise = h_noise;
+  a.lse = lse;
+  a.d_out = d_out;
+  a.dq_sig = dq_sig;
+  a.dq_noise = dq_noise;
+  a.dk = dk;
+  a.dv_out = dv_out;
+  a.dlam = dlambda;
+  a.dgate = dgate;
+  a.workspace = workspace;
+  a.B = B;
+  a.L = L;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
+  if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "the backward is bf16 only");
+  if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  return from_hip(gda::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
 size_t gda_decode_latent_workspace_bytes(int B, int Lmax, int S, int N, int window) {
   if (B < 1 || Lmax < 1 || S < 1 || N < 1 || window < 0) return 0;
   return gda::latent_workspace_bytes(B, Lmax, S, N, window);

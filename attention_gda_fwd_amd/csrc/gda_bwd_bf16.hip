@@ -1,0 +1,557 @@
+// gda_bwd_bf16.hip - backward of the GDA/GDLA prefill, bf16 inputs, fp32 accumulation.
+//
+// The chain rule through out = G (.) (H_S - lambda Repeat_g(H_N)) (the combine
+// and gate of the Motif 3 walk-through's GDLA forward, equation D_t), then
+// through each path's softmax attention:
+//   dG = d_out (.) D,  dD = d_out (.) G,  dlambda_i = -dD_i . H_N,j(i)
+//   dO_S,i = dD_i,     dO_N,j = -sum over the group's signal heads lambda_i dD_i
+//   per attention row: P = exp(z - lse), dP = dO . v, delta = dO . H,
+//   dS = P (dP - delta), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO
+// Three kernels:
+//   bwd_prep_kernel  elementwise: dG, dlambda, each path's dO (bf16) and every
+//                    row's delta; one wave per (token, noise group);
+//   bwd_dq_kernel    one workgroup per (sequence, 64 queries, query head): the
+//                    head's K/V tiles stream through LDS while each wave keeps
+//                    its 16 queries' Q^T, dO^T and dQ^T in registers; scores
+//                    transposed (S^T = K Q^T) as in the forward;
+//   bwd_dkdv_kernel  one workgroup per (sequence, KV head, 64 keys): the Q and
+//                    dO tiles of every query head on that KV head stream through
+//                    LDS while each wave keeps its 16 keys' K, V and the dK^T,
+//                    dV^T accumulators in registers; scores S = Q K^T so that P
+//                    and dS are directly the B operands of dV^T = dO^T P and
+//                    dK^T = Q^T dS.
+// No atomics: every output row is written by exactly one workgroup.
+#include "gda_device.hpp"
+#include "gda_kernels.hpp"
+
+namespace gda {
+namespace {
+
+constexpr int kBwdThreads = 256;  // 4 waves
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Store 16-row accumulator tiles (lane (g, c) holds rows 16t + 4g + r of column c)
+// as one bf16 row per column: tile pairs are regrouped across lanes l and l^16
+// so each lane stores 8 consecutive values (16 bytes).
+template <int NTILE>
+__device__ __forceinline__ void store_col_row(uint16_t* row, int g4, const floatx4 (&acc)[NTILE],
+                                              float mul) {
+  static_assert(NTILE % 2 == 0, "tiles come in pairs");
+  uint16_t* dst = row + 16 * (g4 & 1) + 8 * (g4 >> 1);
+#pragma unroll
+  for (int p = 0; p < NTILE / 2; ++p) {
+    float e[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // vdst's odd rows trade places with vsrc's even rows.
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[2 * p][r] * mul),
+                                                       __float_as_uint(acc[2 * p + 1][r] * mul),
+                                                       false, false);
+      e[r] = __uint_as_float(sw[0]);
+      e[4 + r] = __uint_as_float(sw[1]);
+    }
+    u32x4 ow;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ow[w] = pack_bf16x2(e[2 * w], e[2 * w + 1]);
+    *(u32x4*)(dst + 32 * p) = ow;
+  }
+}
+
+// A operand [16 rows x 32] of an MFMA taken transposed from a row-major LDS tile
+// T[32][cols] (row stride in bytes): lane (g, i) receives T[16h + 4g + r][m0 + i]
+// in element 4h + r. Its K order matches a B operand built from two accumulator
+// tiles (element 4h + r = row 4g + r of tile h).
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int stride, int m0,
+                                             int g4, int col) {
+  shortx4 half[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const unsigned char* a =
+        tile + (16 * h + 4 * g4 + (col >> 2)) * stride + (m0 + 4 * (col & 3)) * 2;
+    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)a);
+  }
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
+  const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
+                      half[1][0], half[1][1], half[1][2], half[1][3]};
+  return __builtin_bit_cast(bf16x8, a8);
+}
+
+// Row operand: lane (g, c) reads T[r0 + c][32 ks + 8g .. +7].
+__device__ __forceinline__ bf16x8 row_operand(const unsigned char* tile, int stride, int r0,
+                                              int ks, int g4, int col) {
+  return *(const bf16x8*)(tile + (r0 + col) * stride + (32 * ks + 8 * g4) * 2);
+}
+
+// ---------------------------------------------------------------------------------
+// Elementwise part. One wave per (token row, noise group j); lanes own DV/64
+// channels each.
+template <int DV>
+__global__ void __launch_bounds__(kBwdThreads)
+bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__ gate,
+                const uint16_t* __restrict__ lam, const uint16_t* __restrict__ h_sig,
+                const uint16_t* __restrict__ h_noise, uint16_t* __restrict__ dgate,
+                uint16_t* __restrict__ dlam, uint16_t* __restrict__ do_sig,
+                uint16_t* __restrict__ do_noise, float* __restrict__ delta, int64_t items, int L,
+                int S, int N, int flags) {
+  constexpr int CPL = DV / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  if (item >= items) return;
+  const int64_t row = item / N;
+  const int j = (int)(item - row * N);
+  const int64_t b = row / L;
+  const int t = (int)(row - b * L);
+  const int g = S / N, HT = S + N;
+  float hn[CPL], dn[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    hn[c] = bf16_to_f32(h_noise[(row * N + j) * DV + lane * CPL + c]);
+    dn[c] = 0.f;
+  }
+  for (int ii = 0; ii < g; ++ii) {
+    const int i = j * g + ii;
+    float lm = bf16_to_f32(lam[row * S + i]);
+    if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
+    const int64_t base = (row * S + i) * DV + lane * CPL;
+    float pl = 0.f, pd = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float hs = bf16_to_f32(h_sig[base + c]);
+      float G = bf16_to_f32(gate[base + c]);
+      if (flags & kGateLogits) G = sigmoid_f32(G);
+      const float dO = bf16_to_f32(d_out[base + c]);
+      const float D = hs - lm * hn[c];
+      float dG = dO * D;
+      if (flags & kGateLogits) dG *= G * (1.f - G);
+      dgate[base + c] = f32_to_bf16(dG);
+      const float dD = dO * G;
+      const uint16_t dDb = f32_to_bf16(dD);
+      do_sig[base + c] = dDb;
+      pl += dD * hn[c];
+      pd += bf16_to_f32(dDb) * hs;  // delta from the dO the matrix kernels use
+      dn[c] -= lm * dD;
+    }
+    pl = wave_sum(pl);
+    pd = wave_sum(pd);
+    if (lane == 0) {
+      float dl = -pl;
+      if (flags & kLambdaLogits) dl *= lm * (1.f - lm);
+      dlam[row * S + i] = f32_to_bf16(dl);
+      delta[((int64_t)b * HT + i) * L + t] = pd;
+    }
+  }
+  float pn = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const uint16_t db = f32_to_bf16(dn[c]);
+    do_noise[(row * N + j) * DV + lane * CPL + c] = db;
+    pn += bf16_to_f32(db) * hn[c];
+  }
+  pn = wave_sum(pn);
+  if (lane == 0) delta[((int64_t)b * HT + S + j) * L + t] = pn;
+}
+
+// One query head's view: its Q and dO rows, and its KV head.
+struct HeadRef {
+  const uint16_t* q;   // row t at q + t * qstride
+  const uint16_t* dO;  // row t at dO + t * ostride
+  int64_t qstride, ostride;
+  int kvh;
+};
+
+__device__ __forceinline__ HeadRef head_ref(int hd, int64_t b, int L, int S, int N, int Hkv,
+                                            int DQK, int DV, const uint16_t* q_sig,
+                                            const uint16_t* q_noise, const uint16_t* do_sig,
+                                            const uint16_t* do_noise) {
+  HeadRef r;
+  if (hd < S) {
+    r.q = q_sig + ((int64_t)b * L * S + hd) * DQK;
+    r.dO = do_sig + ((int64_t)b * L * S + hd) * DV;
+    r.qstride = (int64_t)S * DQK;
+    r.ostride = (int64_t)S * DV;
+    r.kvh = (hd * Hkv) / S;
+  } else {
+    const int j = hd - S;
+    r.q = q_noise + ((int64_t)b * L * N + j) * DQK;
+    r.dO = do_noise + ((int64_t)b * L * N + j) * DV;
+    r.qstride = (int64_t)N * DQK;
+    r.ostride = (int64_t)N * DV;
+    r.kvh = (j * Hkv) / N;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------------
+// dQ. LDS tile of 32 keys: K rows then V rows, each row padded by 16 bytes.
+template <int DQK, int DV>
+struct DqShape {
+  static constexpr int KS = DQK / 32, VS = DV / 32, DT = DQK / 16;
+  static constexpr int KROW = DQK * 2 + 16, VROW = DV * 2 + 16;
+  static constexpr int V_OFF = 32 * KROW;
+  static constexpr int TILE = 32 * (KROW + VROW);
+  static constexpr int KP = 32 * DQK / 8, VP = 32 * DV / 8;  // 16-byte pieces
+  static constexpr int PPT = (KP + VP + kBwdThreads - 1) / kBwdThreads;
+};
+
+template <int DQK, int DV>
+__global__ void __launch_bounds__(kBwdThreads, 2)
+bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
+              const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+              const float* __restrict__ lse, const uint16_t* __restrict__ do_sig,
+              const uint16_t* __restrict__ do_noise, const float* __restrict__ delta,
+              uint16_t* __restrict__ dq_sig, uint16_t* __restrict__ dq_noise, int B, int L,
+              int S, int N, int Hkv, int window, int nqt, int heavy_first, float c2,
+              float scale) {
+  using C = DqShape<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];
+  const int HT = S + N;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per = B * HT;
+  const int slot = blockIdx.x / per;
+  const int qt = heavy_first ? nqt - 1 - slot : slot;
+  const int rem = blockIdx.x - slot * per;
+  const int b = rem / HT, hd = rem - (rem / HT) * HT;
+  const HeadRef hr = head_ref(hd, b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
+  const int q0 = qt * 64;
+  const int t0w = q0 + 16 * wave;
+  const int t = t0w + col;
+  const bool t_ok = t < L;
+  const int tq = min(t, L - 1);
+
+  bf16x8 qT[C::KS], doT[C::VS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+    qT[ks] = __builtin_bit_cast(bf16x8, ldg16(hr.q + tq * hr.qstride + 32 * ks + 8 * g4));
+#pragma unroll
+  for (int kv = 0; kv < C::VS; ++kv)
+    doT[kv] = __builtin_bit_cast(bf16x8, ldg16(hr.dO + tq * hr.ostride + 32 * kv + 8 * g4));
+  const float lse2 = lse[((int64_t)b * HT + hd) * L + tq] * kLog2e;
+  const float dl = delta[((int64_t)b * HT + hd) * L + tq];
+  floatx4 dqT[C::DT];
+#pragma unroll
+  for (int d = 0; d < C::DT; ++d) dqT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int k_lo = window ? max(0, q0 - window + 1) : 0;
+  const int k_hi = min(L - 1, q0 + 63);
+  const int kt0 = k_lo / 32, kt1 = k_hi / 32;
+  const uint16_t* kbase = kg + ((int64_t)b * L * Hkv + hr.kvh) * DQK;
+  const uint16_t* vbase = vg + ((int64_t)b * L * Hkv + hr.kvh) * DV;
+  const int64_t kstride = (int64_t)Hkv * DQK, vstride = (int64_t)Hkv * DV;
+
+  u32x4 stg[C::PPT];
+  auto stage_load = [&](int kt) {
+#pragma unroll
+    for (int p = 0; p < C::PPT; ++p) {
+      const int pc = tid + kBwdThreads * p;
+      if (pc < C::KP) {
+        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
+        const int key = min(kt * 32 + r, L - 1);
+        stg[p] = ldg16(kbase + key * kstride + 8 * cc);
+      } else if (pc < C::KP + C::VP) {
+        const int pv = pc - C::KP;
+        const int r = pv / (DV / 8), cc = pv - r * (DV / 8);
+        const int key = min(kt * 32 + r, L - 1);
+        stg[p] = ldg16(vbase + key * vstride + 8 * cc);
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+    unsigned char* base = smem + buf * C::TILE;
+#pragma unroll
+    for (int p = 0; p < C::PPT; ++p) {
+      const int pc = tid + kBwdThreads * p;
+      if (pc < C::KP) {
+        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
+        *(u32x4*)(base + r * C::KROW + 16 * cc) = stg[p];
+      } else if (pc < C::KP + C::VP) {
+        const int pv = pc - C::KP;
+        const int r = pv / (DV / 8), cc = pv - r * (DV / 8);
+        *(u32x4*)(base + C::V_OFF + r * C::VROW + 16 * cc) = stg[p];
+      }
+    }
+  };
+
+  stage_load(kt0);
+  stage_store(0);
+  __syncthreads();
+  if (kt0 + 1 <= kt1) stage_load(kt0 + 1);
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const unsigned char* Kl = smem + buf * C::TILE;
+    const unsigned char* Vl = Kl + C::V_OFF;
+    const int k0 = kt * 32;
+    // Is any key of this tile visible to a query of this wave? (wave-uniform)
+    const bool live = k0 <= t0w + 15 && (!window || k0 + 31 >= t0w - window + 1);
+    if (live) {
+      floatx4 sT[2], dpT[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sT[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dpT[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          sT[kb] = mfma_16x16x32(row_operand(Kl, C::KROW, 16 * kb, ks, g4, col), qT[ks], sT[kb]);
+#pragma unroll
+        for (int kv = 0; kv < C::VS; ++kv)
+          dpT[kb] = mfma_16x16x32(row_operand(Vl, C::VROW, 16 * kb, kv, g4, col), doT[kv],
+                                  dpT[kb]);
+      }
+      bf16x8 dsb;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * kb + 4 * g4 + r;
+          const bool vis = t_ok && key <= t && (!window || t - key < window);
+          const float p = vis ? fast_exp2(fmaf(sT[kb][r], c2, -lse2)) : 0.f;
+          dsb[4 * kb + r] = (__bf16)(p * (dpT[kb][r] - dl));
+        }
+#pragma unroll
+      for (int d = 0; d < C::DT; ++d)
+        dqT[d] = mfma_16x16x32(tr_operand(Kl, C::KROW, 16 * d, g4, col), dsb, dqT[d]);
+    }
+    if (kt + 1 <= kt1) stage_store(buf ^ 1);
+    __syncthreads();
+    if (kt + 2 <= kt1) stage_load(kt + 2);
+  }
+  if (t_ok) {
+    uint16_t* dst = hd < S ? dq_sig + (((int64_t)b * L + t) * S + hd) * DQK
+                           : dq_noise + (((int64_t)b * L + t) * N + hd - S) * DQK;
+    store_col_row<C::DT>(dst, g4, dqT, scale);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dK, dV. LDS tile of 32 queries of one head: Q rows, dO rows (each padded by 16
+// bytes), then the rows' lse (log2 units) and delta.
+template <int DQK, int DV>
+struct DkvShape {
+  static constexpr int KS = DQK / 32, VS = DV / 32, DT = DQK / 16, VT = DV / 16;
+  static constexpr int QROW = DQK * 2 + 16, OROW = DV * 2 + 16;
+  static constexpr int O_OFF = 32 * QROW;
+  static constexpr int L_OFF = O_OFF + 32 * OROW;
+  static constexpr int D_OFF = L_OFF + 32 * 4;
+  static constexpr int TILE = D_OFF + 32 * 4;
+  static constexpr int QP = 32 * DQK / 8, OP = 32 * DV / 8;
+  static constexpr int PPT = (QP + OP + kBwdThreads - 1) / kBwdThreads;
+};
+
+template <int DQK, int DV>
+__global__ void __launch_bounds__(kBwdThreads, 2)
+bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
+                const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
+                const float* __restrict__ lse, const uint16_t* __restrict__ do_sig,
+                const uint16_t* __restrict__ do_noise, const float* __restrict__ delta,
+                uint16_t* __restrict__ dk, uint16_t* __restrict__ dvo, int B, int L, int S,
+                int N, int Hkv, int window, float c2, float scale) {
+  using C = DkvShape<DQK, DV>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];
+  const int HT = S + N;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per = B * Hkv;
+  const int kt = blockIdx.x / per;  // key tiles in order: the first ones see the most queries
+  const int rem = blockIdx.x - kt * per;
+  const int b = rem / Hkv, h = rem - (rem / Hkv) * Hkv;
+  const int k0w = kt * 64 + 16 * wave;
+  const int s = k0w + col;  // this lane's key
+  const bool s_ok = s < L;
+  const int sk = min(s, L - 1);
+
+  bf16x8 kT[C::KS], vT[C::VS];
+  {
+    const uint16_t* kr = kg + (((int64_t)b * L + sk) * Hkv + h) * DQK;
+    const uint16_t* vr = vg + (((int64_t)b * L + sk) * Hkv + h) * DV;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      kT[ks] = __builtin_bit_cast(bf16x8, ldg16(kr + 32 * ks + 8 * g4));
+#pragma unroll
+    for (int kv = 0; kv < C::VS; ++kv)
+      vT[kv] = __builtin_bit_cast(bf16x8, ldg16(vr + 32 * kv + 8 * g4));
+  }
+  floatx4 dkT[C::DT], dvT[C::VT];
+#pragma unroll
+  for (int d = 0; d < C::DT; ++d) dkT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < C::VT; ++d) dvT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // The query heads on KV head h: signal heads h*S/Hkv ..; noise heads
+  // ceil(h*N/Hkv) .. ceil((h+1)*N/Hkv) - 1.
+  const int sig_lo = h * (S / Hkv), n_sig = S / Hkv;
+  const int j_lo = (h * N + Hkv - 1) / Hkv, j_hi = ((h + 1) * N + Hkv - 1) / Hkv;
+  const int nh = n_sig + (j_hi - j_lo);
+  const int q_lo = kt * 64;
+  const int q_hi = window ? min(L - 1, kt * 64 + 63 + window - 1) : L - 1;
+  const int qb0 = q_lo / 32, nqb = q_hi / 32 - qb0 + 1;
+  const int n_items = nh * nqb;
+
+  u32x4 stg[C::PPT];
+  float stg_s = 0.f;  // one lse or delta value (threads 0..63)
+  auto head_of_item = [&](int it) -> int {
+    const int hh = it / nqb;
+    return hh < n_sig ? sig_lo + hh : S + j_lo + (hh - n_sig);
+  };
+  auto stage_load = [&](int it) {
+    const int hd = head_of_item(it);
+    const int qb = qb0 + (it - (it / nqb) * nqb);
+    const HeadRef hr = head_ref(hd, b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
+#pragma unroll
+    for (int p = 0; p < C::PPT; ++p) {
+      const int pc = tid + kBwdThreads * p;
+      if (pc < C::QP) {
+        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
+        const int q = min(qb * 32 + r, L - 1);
+        stg[p] = ldg16(hr.q + q * hr.qstride + 8 * cc);
+      } else if (pc < C::QP + C::OP) {
+        const int po = pc - C::QP;
+        const int r = po / (DV / 8), cc = po - r * (DV / 8);
+        const int q = min(qb * 32 + r, L - 1);
+        stg[p] = ldg16(hr.dO + q * hr.ostride + 8 * cc);
+      }
+    }
+    if (tid < 64) {
+      const int q = min(qb * 32 + (tid & 31), L - 1);
+      const int64_t at = ((int64_t)b * HT + hd) * L + q;
+      stg_s = tid < 32 ? lse[at] * kLog2e : delta[at];
+    }
+  };
+  auto stage_store = [&](int buf) {
+    unsigned char* base = smem + buf * C::TILE;
+#pragma unroll
+    for (int p = 0; p < C::PPT; ++p) {
+      const int pc = tid + kBwdThreads * p;
+      if (pc < C::QP) {
+        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
+        *(u32x4*)(base + r * C::QROW + 16 * cc) = stg[p];
+      } else if (pc < C::QP + C::OP) {
+        const int po = pc - C::QP;
+        const int r = po / (DV / 8), cc = po - r * (DV / 8);
+        *(u32x4*)(base + C::O_OFF + r * C::OROW + 16 * cc) = stg[p];
+      }
+    }
+    if (tid < 64) *(float*)(base + C::L_OFF + 4 * tid) = stg_s;  // lse[32] then delta[32]
+  };
+
+  if (n_items > 0) {
+    stage_load(0);
+    stage_store(0);
+  }
+  __syncthreads();
+  if (1 < n_items) stage_load(1);
+  for (int it = 0; it < n_items; ++it) {
+    const int buf = it & 1;
+    const unsigned char* Ql = smem + buf * C::TILE;
+    const unsigned char* Ol = Ql + C::O_OFF;
+    const float* sL = (const float*)(Ql + C::L_OFF);
+    const float* sD = (const float*)(Ql + C::D_OFF);
+    const int q0 = (qb0 + (it - (it / nqb) * nqb)) * 32;
+    const bool live = k0w <= q0 + 31 && (!window || q0 <= k0w + 14 + window);
+    if (live) {
+      floatx4 sc[2], dp[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        sc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dp[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+          sc[qt] = mfma_16x16x32(row_operand(Ql, C::QROW, 16 * qt, ks, g4, col), kT[ks], sc[qt]);
+#pragma unroll
+        for (int kv = 0; kv < C::VS; ++kv)
+          dp[qt] = mfma_16x16x32(row_operand(Ol, C::OROW, 16 * qt, kv, g4, col), vT[kv], dp[qt]);
+      }
+      bf16x8 pb, dsb;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = 16 * qt + 4 * g4 + r;
+          const int q = q0 + qi;
+          const bool vis = s_ok && q < L && s <= q && (!window || q - s < window);
+          const float p = vis ? fast_exp2(fmaf(sc[qt][r], c2, -sL[qi])) : 0.f;
+          pb[4 * qt + r] = (__bf16)p;
+          dsb[4 * qt + r] = (__bf16)(p * (dp[qt][r] - sD[qi]));
+        }
+#pragma unroll
+      for (int d = 0; d < C::VT; ++d)
+        dvT[d] = mfma_16x16x32(tr_operand(Ol, C::OROW, 16 * d, g4, col), pb, dvT[d]);
+#pragma unroll
+      for (int d = 0; d < C::DT; ++d)
+        dkT[d] = mfma_16x16x32(tr_operand(Ql, C::QROW, 16 * d, g4, col), dsb, dkT[d]);
+    }
+    if (it + 1 < n_items) stage_store(buf ^ 1);
+    __syncthreads();
+    if (it + 2 < n_items) stage_load(it + 2);
+  }
+  if (s_ok) {
+    store_col_row<C::DT>(dk + (((int64_t)b * L + s) * Hkv + h) * DQK, g4, dkT, scale);
+    store_col_row<C::VT>(dvo + (((int64_t)b * L + s) * Hkv + h) * DV, g4, dvT, 1.f);
+  }
+}
+
+template <int DQK, int DV>
+hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
+  const int HT = a.S + a.N;
+  const int64_t items = (int64_t)a.B * a.L * a.N;
+  const int64_t prep_blocks = (items + 3) / 4;
+  const int nqt = (a.L + 63) / 64;
+  const int64_t dq_blocks = (int64_t)nqt * a.B * HT;
+  const int64_t dkv_blocks = (int64_t)nqt * a.B * a.Hkv;
+  if (prep_blocks > 0x7fffffff || dq_blocks > 0x7fffffff || dkv_blocks > 0x7fffffff)
+    return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_prep_kernel<DV>), dim3((unsigned)prep_blocks), dim3(kBwdThreads), 0,
+                     stream, (const uint16_t*)a.d_out, (const uint16_t*)a.gate,
+                     (const uint16_t*)a.lam, (const uint16_t*)a.h_sig,
+                     (const uint16_t*)a.h_noise, (uint16_t*)a.dgate, (uint16_t*)a.dlam,
+                     a.do_sig, a.do_noise, a.delta, items, a.L, a.S, a.N, a.flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int heavy_first = a.window == 0 ? 1 : 0;
+  hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV>), dim3((unsigned)dq_blocks), dim3(kBwdThreads), 0,
+                     stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
+                     a.delta, (uint16_t*)a.dq_sig, (uint16_t*)a.dq_noise, a.B, a.L, a.S, a.N,
+                     a.Hkv, a.window, nqt, heavy_first, a.scale_log2, a.scale);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV>), dim3((unsigned)dkv_blocks), dim3(kBwdThreads),
+                     0, stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
+                     a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv_out, a.B, a.L, a.S, a.N, a.Hkv,
+                     a.window, a.scale_log2, a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_bf16_supported(int dqk, int dv) {
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
+}
+
+size_t bwd_workspace_bytes(int B, int L, int S, int N, int dv) {
+  const size_t rows = (size_t)B * L;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return up(rows * S * dv * 2) + up(rows * N * dv * 2) + up(rows * (S + N) * 4);
+}
+
+hipError_t launch_bwd_bf16(BwdArgs a, hipStream_t stream) {
+  const size_t rows = (size_t)a.B * a.L;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  unsigned char* w = (unsigned char*)a.workspace;
+  a.do_sig = (uint16_t*)w;
+  w += up(rows * a.S * a.dv * 2);
+  a.do_noise = (uint16_t*)w;
+  w += up(rows * a.N * a.dv * 2);
+  a.delta = (float*)w;
+  if (a.dqk == 64 && a.dv == 64) return launch_bwd_dims<64, 64>(a, stream);
+  if (a.dqk == 128 && a.dv == 128) return launch_bwd_dims<128, 128>(a, stream);
+  if (a.dqk == 192 && a.dv == 128) return launch_bwd_dims<192, 128>(a, stream);
+  return (hipError_t)-1;
+}
+
+}  // namespace gda

@@ -25,6 +25,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ floatx4 mfma_16x16x32(const bf16x8& a, const bf16x8& b,
                                                   const floatx4& c) {

@@ -410,6 +410,35 @@ __device__ __forceinline__ void store_head(uint16_t* out, int64_t row, int S, in
   }
 }
 
+// Training form: one path's normalised output h * inv (bf16, regrouped like
+// store_head) and its row's log-sum-exp in natural-log units (-inf for a row
+// with no visible key). The four lane groups of a query column hold the same
+// value and all store it.
+template <int DV>
+__device__ __forceinline__ void store_train_head(uint16_t* h_out, float* lse_out, int g4,
+                                                 const floatx4 (&h)[DV / 16], float inv,
+                                                 float mref, float lsum) {
+  constexpr int NP = DV / 32;
+  uint16_t* dst = h_out + 16 * (g4 & 1) + 8 * (g4 >> 1);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    float e[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(h[2 * p][r] * inv),
+                                                       __float_as_uint(h[2 * p + 1][r] * inv),
+                                                       false, false);
+      e[r] = __uint_as_float(sw[0]);
+      e[4 + r] = __uint_as_float(sw[1]);
+    }
+    u32x4 ow;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ow[w] = pack_bf16x2(e[2 * w], e[2 * w + 1]);
+    *(u32x4*)(dst + 32 * p) = ow;
+  }
+  *lse_out = lsum > 0.f ? (mref + log2f(lsum)) * kLn2 : -INFINITY;
+}
+
 // The main loop of one wave group. Both groups run the same barrier sequence.
 template <class C, int NH, int PARITY>
 __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
@@ -455,14 +484,20 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
 
 // A 4-wave workgroup is meant to share its CU with a second one (2 waves per
 // SIMD, so at most 256 registers per wave).
-template <class C>
+// With TRAIN the kernel also writes what the backward takes from the forward
+// (batched calls only): each path's normalised output h_sig [B,L,S,dv] and
+// h_noise [B,L,N,dv], and each attention row's log-sum-exp lse [B,S+N,L].
+
+template <class C, bool TRAIN>
 __global__ void __launch_bounds__(C::NT, C::NW == 4 ? 2 : 1)
 fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
                 uint16_t* __restrict__ out, const int32_t* __restrict__ cu_q,
                 const int32_t* __restrict__ cu_k, int B, int L, int S, int N, int Hkv,
-                int window, int units, int R, int nqt, int heavy_first, float c, int flags) {
+                int window, int units, int R, int nqt, int heavy_first, float c, int flags,
+                uint16_t* __restrict__ h_sig, uint16_t* __restrict__ h_noise,
+                float* __restrict__ lse) {
   // K/V ring: two stages, each the tiles of the unit's KV heads.
   __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
   // Normalised noise output handed from the A waves to the B waves.
@@ -582,6 +617,18 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
       for (int s = 0; s < C::ASIG; ++s)
         store_head<C::DV>(out, row, S, sig0 + s, x.g4, st.o[s],
                           st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
+      if constexpr (TRAIN) {
+        const int64_t lrow = (int64_t)b * (S + N);
+        store_train_head<C::DV>(h_noise + (row * N + u) * C::DV,
+                                lse + (lrow + S + u) * L + tl, x.g4, st.o[NZ], inv_n,
+                                st.mref[NZ], st.lsum[NZ]);
+#pragma unroll
+        for (int s = 0; s < C::ASIG; ++s)
+          store_train_head<C::DV>(h_sig + (row * S + sig0 + s) * C::DV,
+                                  lse + (lrow + sig0 + s) * L + tl, x.g4, st.o[s],
+                                  st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, st.mref[s],
+                                  st.lsum[s]);
+      }
     }
     if constexpr (!C::kEarlyEpilogue) {
       if (C::NB > 0) __syncthreads();
@@ -615,6 +662,15 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
       for (int s = 0; s < C::BSIG; ++s)
         store_head<C::DV>(out, row, S, sig0 + b_first + s, x.g4, st.o[s],
                           st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
+      if constexpr (TRAIN) {
+        const int64_t lrow = (int64_t)b * (S + N);
+#pragma unroll
+        for (int s = 0; s < C::BSIG; ++s)
+          store_train_head<C::DV>(h_sig + (row * S + sig0 + b_first + s) * C::DV,
+                                  lse + (lrow + sig0 + b_first + s) * L + tl, x.g4, st.o[s],
+                                  st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, st.mref[s],
+                                  st.lsum[s]);
+      }
     }
   }
 }
@@ -626,12 +682,22 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)nqt * a.B * a.plan.units;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int heavy_first = a.window == 0 ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<C>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
-                     (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
-                     (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L, a.S,
-                     a.N, a.Hkv,
-                     a.window, a.plan.units, a.plan.R, nqt, heavy_first, a.scale_log2, a.flags);
+  if (a.h_sig)
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, true>), dim3((unsigned)grid), dim3(C::NT), 0, stream,
+                       (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
+                       (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L,
+                       a.S, a.N, a.Hkv, a.window, a.plan.units, a.plan.R, nqt, heavy_first,
+                       a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
+                       a.lse);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0,
+                       stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
+                       (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L,
+                       a.S, a.N, a.Hkv, a.window, a.plan.units, a.plan.R, nqt, heavy_first,
+                       a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
+                       a.lse);
   return hipGetLastError();
 }
 

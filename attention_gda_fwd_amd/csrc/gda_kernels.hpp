@@ -34,6 +34,11 @@ struct FwdArgs {
   float scale_log2;  // log2(e) * softmax scale
   float scale;       // softmax scale (1 / sqrt(dqk) unless the caller gives one)
   int flags;         // GDA_LAMBDA_LOGITS | GDA_GATE_LOGITS
+  // Training form (all NULL otherwise; batched calls only): per-path outputs
+  // h_sig [B,L,S,dv], h_noise [B,L,N,dv] and row log-sum-exps lse [B,S+N,L].
+  void* h_sig = nullptr;
+  void* h_noise = nullptr;
+  float* lse = nullptr;
 };
 
 struct DecodeArgs {
@@ -68,6 +73,36 @@ struct LatentArgs {
   int flags;
 };
 
+// Backward of the prefill (bf16): inputs, the training-form forward outputs,
+// d_out, the gradients, and a workspace of bwd_workspace_bytes.
+struct BwdArgs {
+  const void* q_sig;
+  const void* q_noise;
+  const void* k;
+  const void* v;
+  const void* lam;
+  const void* gate;
+  const void* h_sig;    // [B,L,S,dv]
+  const void* h_noise;  // [B,L,N,dv]
+  const float* lse;     // [B,S+N,L], natural log
+  const void* d_out;    // [B,L,S,dv]
+  void* dq_sig;
+  void* dq_noise;
+  void* dk;
+  void* dv_out;
+  void* dlam;
+  void* dgate;
+  void* workspace;
+  int B, L, S, N, Hkv, dqk, dv, window;
+  float scale_log2;
+  float scale;
+  int flags;
+  // carved from the workspace by the launcher
+  uint16_t* do_sig = nullptr;    // [B,L,S,dv]
+  uint16_t* do_noise = nullptr;  // [B,L,N,dv]
+  float* delta = nullptr;        // [B,S+N,L]
+};
+
 // Each returns hipSuccess or the launch error; -1 cast to hipError_t means no
 // compiled instance matches (the host API checks support first).
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
@@ -80,5 +115,8 @@ hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream);
 bool latent_supported(int Dn, int Dr, int Dc, int dv, int S, int N, int Hkv);
 size_t latent_workspace_bytes(int B, int Lmax, int S, int N, int window);
 bool decode_bf16_supported(int dqk, int dv, const UnitPlan& plan);
+bool bwd_bf16_supported(int dqk, int dv);
+size_t bwd_workspace_bytes(int B, int L, int S, int N, int dv);
+hipError_t launch_bwd_bf16(BwdArgs a, hipStream_t stream);
 
 }  // namespace gda

@@ -190,9 +190,48 @@ def event_times(torch, fn, reps, warmup, flush=None):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+BWD_SUFFIX = "_bwd"
+
+
+def bwd_setup(cfg, torch, gin):
+    """Inputs of a prefill workload, a seeded d_out, the training forward's outputs and
+    preallocated gradients; returns (fwd_train_fn, bwd_fn)."""
+    from attention_gda_fwd_amd import api
+    dev, _ = fill_fwd(cfg, torch, gin)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x6DA)
+    d_out = torch.randn(dev["gate"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    args = [dev[n] for n in ("q_sig", "q_noise", "k", "v", "lam", "gate")]
+    saved = api.gda_fwd_train(*args, window=cfg.window)
+    ws = torch.empty(api.bwd_workspace_bytes(cfg.B, cfg.L, cfg.S, cfg.N, cfg.dv),
+                     dtype=torch.uint8, device="cuda")
+    grads = api.gda_bwd(*args, *saved[1:], d_out, window=cfg.window, workspace=ws)
+
+    def fwd_train():
+        api.gda_fwd_train(*args, window=cfg.window)
+
+    def bwd():
+        api.gda_bwd(*args, *saved[1:], d_out, window=cfg.window, workspace=ws, grads=grads)
+    return fwd_train, bwd
+
+
 def run_only(args, torch, C, gin, gda_fwd, gda_decode):
     """One workload alone: a 1 GiB copy kernel (the byte counters' scale), then warmup
-    and timed launches. Prints a short JSON line."""
+    and timed launches. Prints a short JSON line. A prefill workload's name with the
+    suffix _bwd times its backward."""
+    if args.only.endswith(BWD_SUFFIX):
+        cfg = C.CONFIGS[args.only[:-len(BWD_SUFFIX)]]
+        _, fn = bwd_setup(cfg, torch, gin)
+        copy_kernel(torch)
+        ms = event_times(torch, fn, args.steps, args.warmup)
+        med = float(np.median(ms))
+        log(f"{args.only}: median {med:.4f} ms, min {min(ms):.4f} ms")
+        print(json.dumps({"mode": "only", "workload": args.only, "steps": args.steps,
+                          "warmup": args.warmup, "median_ms": round(med, 4),
+                          "min_ms": round(min(ms), 4), "avg_ms": round(sum(ms) / len(ms), 4),
+                          "tflops": round(cfg.bwd_flops() / (med * 1e-3) / 1e12, 2),
+                          "gbps": round(cfg.bwd_bytes() / (med * 1e-3) / 1e9, 1)}), flush=True)
+        return
     cfg = C.CONFIGS[args.only]
     if cfg.kind == "latent":
         from attention_gda_fwd_amd import api
@@ -380,6 +419,28 @@ def main():
             extra = {"flushed": flushed(event_times(torch, fn, reps, 10, flush))}
         record(cfg, event_times(torch, fn, reps, 10), extra)
         del dev, o
+        torch.cuda.empty_cache()
+    # the training pair: the forward that keeps what the backward needs, and the backward
+    for cfg in (C.MOTIF3_FULL, C.MOTIF3_SWA):
+        log(f"breakdown {cfg.name} training forward and backward")
+        fwd_train, bwd = bwd_setup(cfg, torch, gin)
+        n = 20 if cfg is C.MOTIF3_FULL else reps
+        ms = event_times(torch, fwd_train, n, 5)
+        med = float(np.median(ms))
+        breakdown[cfg.name + "_train_fwd"] = dict(
+            median_ms=round(med, 4), min_ms=round(min(ms), 4),
+            tflops=round(cfg.flops() / (med * 1e-3) / 1e12, 2),
+            mfma_frac=round(cfg.flops() / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4))
+        ms = event_times(torch, bwd, n, 5)
+        med = float(np.median(ms))
+        breakdown[cfg.name + BWD_SUFFIX] = dict(
+            median_ms=round(med, 4), min_ms=round(min(ms), 4),
+            tflops=round(cfg.bwd_flops() / (med * 1e-3) / 1e12, 2),
+            gbps=round(cfg.bwd_bytes() / (med * 1e-3) / 1e9, 1),
+            mfma_frac=round(cfg.bwd_flops() / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            hbm_frac=round(cfg.bwd_bytes() / (med * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            flops_per_launch=cfg.bwd_flops())
+        del fwd_train, bwd
         torch.cuda.empty_cache()
 
     result = {

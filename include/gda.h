@@ -176,6 +176,45 @@ gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void*
                              int dv, int window, gda_dtype dtype, const gda_options* opts,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training: the forward that also keeps what the backward needs, and the
+ * backward (the pages' setting is training: the Motif 3 walk-through trains the
+ * GDLA layers, steps 4 and 5). bf16 only.
+ *
+ * gda_fwd_train: gda_fwd_ex (same tensors, options, support) that also writes
+ *   h_sig   [B, L, S, dv] bf16   each signal head's normalised attention output H_S
+ *   h_noise [B, L, N, dv] bf16   each noise head's normalised attention output H_N
+ *   lse     [B, S+N, L]   float  each attention row's log-sum-exp of its scaled
+ *                                scores, natural log (heads 0..S-1 signal, then noise)
+ * h_sig and h_noise 16-byte aligned, lse 4-byte aligned. fp32 returns
+ * GDA_ERROR_UNSUPPORTED. */
+gda_status gda_fwd_train(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                         const void* lambda, const void* gate, void* out, void* h_sig,
+                         void* h_noise, float* lse, int B, int L, int S, int N, int Hkv,
+                         int dqk, int dv, int window, gda_dtype dtype, const gda_options* opts,
+                         void* stream);
+
+/* Workspace bytes gda_bwd needs (each path's dO and every row's delta), or 0 for
+ * sizes below 1. */
+size_t gda_bwd_workspace_bytes(int B, int L, int S, int N, int dv);
+
+/* gda_bwd: gradients of sum(d_out (.) out) for the forward gda_fwd_train ran, from
+ * the same inputs, options and window, and its h_sig, h_noise and lse.
+ *   d_out [B,L,S,dv]; outputs (all bf16, written, not accumulated):
+ *   dq_sig [B,L,S,dqk], dq_noise [B,L,N,dqk], dk [B,L,Hkv,dqk], dv_out [B,L,Hkv,dv],
+ *   dlambda [B,L,S], dgate [B,L,S,dv]; with GDA_LAMBDA_LOGITS / GDA_GATE_LOGITS the
+ *   gradients are with respect to the logits.
+ * workspace: device memory of at least gda_bwd_workspace_bytes(B, L, S, N, dv)
+ * bytes, 256-byte aligned, owned by the caller, not read across calls. Tensors
+ * 16-byte aligned (lse 4-byte). Supported as gda_fwd_train; fp32 returns
+ * GDA_ERROR_UNSUPPORTED. Outputs are written once each (no atomics), so results
+ * are deterministic. */
+gda_status gda_bwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                   const void* lambda, const void* gate, const void* h_sig, const void* h_noise,
+                   const float* lse, const void* d_out, void* dq_sig, void* dq_noise, void* dk,
+                   void* dv_out, void* dlambda, void* dgate, int B, int L, int S, int N, int Hkv,
+                   int dqk, int dv, int window, gda_dtype dtype, const gda_options* opts,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* gda_status_string(gda_status s);
 

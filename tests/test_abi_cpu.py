@@ -175,6 +175,57 @@ def test_varlen_unsupported_and_device_check():
         assert varlen(dtype=F32, dqk=40, dv=24) == HIPERR
 
 
+def train(**kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, out=FAKE, hs=FAKE, hn=FAKE,
+             lse=FAKE, B=1, L=64, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0, dtype=BF16)
+    a.update(kw)
+    return _lib.fwd_train_raw(a["q"], a["qn"], a["k"], a["v"], a["lam"], a["gate"], a["out"],
+                              a["hs"], a["hn"], a["lse"], a["B"], a["L"], a["S"], a["N"],
+                              a["Hkv"], a["dqk"], a["dv"], a["window"], a["dtype"], None, None)
+
+
+def bwd(ws=FAKE, ws_bytes=1 << 30, **kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, hs=FAKE, hn=FAKE, lse=FAKE,
+             do=FAKE, dqs=FAKE, dqn=FAKE, dk=FAKE, dvo=FAKE, dl=FAKE, dg=FAKE, B=1, L=64, S=8,
+             N=2, Hkv=2, dqk=64, dv=64, window=0, dtype=BF16)
+    a.update(kw)
+    return _lib.bwd_raw(*(a[n] for n in ("q", "qn", "k", "v", "lam", "gate", "hs", "hn", "lse",
+                                         "do", "dqs", "dqn", "dk", "dvo", "dl", "dg", "B", "L",
+                                         "S", "N", "Hkv", "dqk", "dv", "window", "dtype")),
+                        None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(hs=None), dict(lse=None), dict(hn=FAKE + 8),
+                                dict(lse=FAKE + 2), dict(B=0), dict(window=-1), dict(S=8, N=3)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_fwd_train_invalid_arguments(kw):
+    assert train(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(do=None), dict(dk=None), dict(ws=None), dict(ws=FAKE + 16),
+                                dict(ws_bytes=100), dict(dl=FAKE + 8), dict(lse=FAKE + 1),
+                                dict(L=0), dict(S=8, N=3)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_bwd_invalid_arguments(kw):
+    assert bwd(**kw) == INVALID
+
+
+def test_training_unsupported_and_device_check():
+    assert train(dtype=F32) == UNSUPPORTED
+    assert train(dqk=96, dv=96) == UNSUPPORTED
+    assert bwd(dtype=F32) == UNSUPPORTED
+    assert bwd(dqk=96, dv=96) == UNSUPPORTED
+    if not _gpu_visible():
+        assert train() == HIPERR
+        assert bwd() == HIPERR
+
+
+def test_bwd_workspace_size():
+    n = _lib.bwd_workspace_bytes(2, 8192, 64, 16, 128)
+    assert n >= 2 * 8192 * (64 + 16) * (128 * 2 + 4)
+    assert _lib.bwd_workspace_bytes(0, 1, 1, 1, 1) == 0
+
+
 def test_decode_misaligned_lengths():
     assert dec(lens=FAKE + 2) == INVALID
     assert b"aligned" in _lib.load().gda_last_error()
