@@ -10,10 +10,11 @@
 // Three kernels:
 //   bwd_prep_kernel  elementwise: dG, dlambda, each path's dO (bf16) and every
 //                    row's delta; one wave per (token, noise group);
-//   bwd_dq_kernel    one workgroup per (sequence, 64 queries, query head): the
-//                    head's K/V tiles stream through LDS while each wave keeps
-//                    its 16 queries' Q^T, dO^T and dQ^T in registers; scores
-//                    transposed (S^T = K Q^T) as in the forward;
+//   bwd_dq_kernel    one workgroup per (sequence, 64 queries, two query heads of
+//                    one KV head): that KV head's K/V tiles stream through LDS
+//                    while each wave keeps its 16 queries' Q^T, dO^T and dQ^T of
+//                    both heads in registers (every K/V fragment read serves two
+//                    heads); scores transposed (S^T = K Q^T) as in the forward;
 //   bwd_dkdv_kernel  one workgroup per (sequence, KV head, 64 keys): the Q and
 //                    dO tiles of every query head on that KV head stream through
 //                    LDS while each wave keeps its 16 keys' K, V and the dK^T,
@@ -187,143 +188,193 @@ __device__ __forceinline__ HeadRef head_ref(int hd, int64_t b, int L, int S, int
 }
 
 // ---------------------------------------------------------------------------------
-// dQ. LDS tile of 32 keys: K rows then V rows, each row padded by 16 bytes.
+// dQ. LDS tile of 32 keys: K rows then V rows, each row padded by 16 bytes,
+// each region rounded up to whole 1 KB copy blocks. The tiles arrive by direct
+// global -> LDS copies: copy block i of a region is the region's bytes
+// 1024 i .. 1024 i + 1023, and each lane fetches the row piece that lands at its
+// 16 bytes (pad and slack slots fetch row 0's first piece).
 template <int DQK, int DV>
 struct DqShape {
   static constexpr int KS = DQK / 32, VS = DV / 32, DT = DQK / 16;
   static constexpr int KROW = DQK * 2 + 16, VROW = DV * 2 + 16;
-  static constexpr int V_OFF = 32 * KROW;
-  static constexpr int TILE = 32 * (KROW + VROW);
-  static constexpr int KP = 32 * DQK / 8, VP = 32 * DV / 8;  // 16-byte pieces
-  static constexpr int PPT = (KP + VP + kBwdThreads - 1) / kBwdThreads;
+  static constexpr int KBLK = (32 * KROW + 1023) / 1024, VBLK = (32 * VROW + 1023) / 1024;
+  static constexpr int V_OFF = KBLK * 1024;
+  static constexpr int TILE = (KBLK + VBLK) * 1024;
 };
 
-template <int DQK, int DV>
+// Issue this wave's copy blocks (wave, wave + 4, ...) of a region of 32 rows:
+// source rows row0 + r (r clamped to rows_ok - 1), row r at src + r * gstride bytes.
+template <int ROWB, int STRIDE, int NBLK>
+__device__ __forceinline__ void copy_rows(const void* src, uint32_t gstride, int rows_ok,
+                                          uint32_t lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < (NBLK + 3) / 4; ++i) {
+    const int blk = wave + 4 * i;
+    if (blk < NBLK) {
+      const int o = blk * 1024 + 16 * lane;
+      int r = o / STRIDE, c = o - (o / STRIDE) * STRIDE;
+      if (c >= ROWB || r >= 32) r = 0, c = 0;
+      r = min(r, rows_ok - 1);
+      dma16_lds(src, (uint32_t)r * gstride + (uint32_t)c, lds + 1024u * blk);
+    }
+  }
+}
+
+// The query heads on KV head h: signal heads h*S/Hkv .. (S/Hkv of them), then
+// noise heads ceil(h*N/Hkv) .. ceil((h+1)*N/Hkv) - 1. Entry i of that list:
+__device__ __forceinline__ int kv_head_member(int h, int i, int S, int N, int Hkv) {
+  const int n_sig = S / Hkv;
+  return i < n_sig ? h * n_sig + i : S + (h * N + Hkv - 1) / Hkv + (i - n_sig);
+}
+
+__device__ __forceinline__ int kv_head_count(int h, int S, int N, int Hkv) {
+  return S / Hkv + ((h + 1) * N + Hkv - 1) / Hkv - (h * N + Hkv - 1) / Hkv;
+}
+
+// NH query heads of one KV head per wave (1 or 2): the K/V fragments read from
+// LDS serve every head of the wave. Workgroup: (query tile slot, sequence, KV
+// head, head group); with NH = 2 group p takes list entries 2p, 2p+1; with
+// NH = 1 the workgroup takes the last entry when the list is odd.
+template <int DQK, int DV, int NH>
 __global__ void __launch_bounds__(kBwdThreads, 2)
 bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
               const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
               const float* __restrict__ lse, const uint16_t* __restrict__ do_sig,
               const uint16_t* __restrict__ do_noise, const float* __restrict__ delta,
               uint16_t* __restrict__ dq_sig, uint16_t* __restrict__ dq_noise, int B, int L,
-              int S, int N, int Hkv, int window, int nqt, int heavy_first, float c2,
-              float scale) {
+              int S, int N, int Hkv, int window, int nqt, int groups, int heavy_first,
+              float c2, float scale) {
   using C = DqShape<DQK, DV>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];
   const int HT = S + N;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int per = B * HT;
+  const int per = B * Hkv * groups;
   const int slot = blockIdx.x / per;
   const int qt = heavy_first ? nqt - 1 - slot : slot;
-  const int rem = blockIdx.x - slot * per;
-  const int b = rem / HT, hd = rem - (rem / HT) * HT;
-  const HeadRef hr = head_ref(hd, b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
+  int rem = blockIdx.x - slot * per;
+  const int b = rem / (Hkv * groups);
+  rem -= b * (Hkv * groups);
+  const int h = rem / groups, grp = rem - (rem / groups) * groups;
+  const int nh_kv = kv_head_count(h, S, N, Hkv);
+  int first;
+  if (NH == 2) {
+    if (2 * grp + 1 >= nh_kv) return;  // whole workgroup, before any barrier
+    first = 2 * grp;
+  } else {
+    if ((nh_kv & 1) == 0) return;
+    first = nh_kv - 1;
+  }
+  int hd[NH];
+  HeadRef hr[NH];
+#pragma unroll
+  for (int u = 0; u < NH; ++u) {
+    hd[u] = kv_head_member(h, first + u, S, N, Hkv);
+    hr[u] = head_ref(hd[u], b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
+  }
   const int q0 = qt * 64;
   const int t0w = q0 + 16 * wave;
   const int t = t0w + col;
   const bool t_ok = t < L;
   const int tq = min(t, L - 1);
 
-  bf16x8 qT[C::KS], doT[C::VS];
+  bf16x8 qT[NH][C::KS], doT[NH][C::VS];
+  float lse2[NH], dl[NH];
+  floatx4 dqT[NH][C::DT];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks)
-    qT[ks] = __builtin_bit_cast(bf16x8, ldg16(hr.q + tq * hr.qstride + 32 * ks + 8 * g4));
+  for (int u = 0; u < NH; ++u) {
 #pragma unroll
-  for (int kv = 0; kv < C::VS; ++kv)
-    doT[kv] = __builtin_bit_cast(bf16x8, ldg16(hr.dO + tq * hr.ostride + 32 * kv + 8 * g4));
-  const float lse2 = lse[((int64_t)b * HT + hd) * L + tq] * kLog2e;
-  const float dl = delta[((int64_t)b * HT + hd) * L + tq];
-  floatx4 dqT[C::DT];
+    for (int ks = 0; ks < C::KS; ++ks)
+      qT[u][ks] =
+          __builtin_bit_cast(bf16x8, ldg16(hr[u].q + tq * hr[u].qstride + 32 * ks + 8 * g4));
 #pragma unroll
-  for (int d = 0; d < C::DT; ++d) dqT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int kv = 0; kv < C::VS; ++kv)
+      doT[u][kv] =
+          __builtin_bit_cast(bf16x8, ldg16(hr[u].dO + tq * hr[u].ostride + 32 * kv + 8 * g4));
+    lse2[u] = lse[((int64_t)b * HT + hd[u]) * L + tq] * kLog2e;
+    dl[u] = delta[((int64_t)b * HT + hd[u]) * L + tq];
+#pragma unroll
+    for (int d = 0; d < C::DT; ++d) dqT[u][d] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int k_lo = window ? max(0, q0 - window + 1) : 0;
   const int k_hi = min(L - 1, q0 + 63);
   const int kt0 = k_lo / 32, kt1 = k_hi / 32;
-  const uint16_t* kbase = kg + ((int64_t)b * L * Hkv + hr.kvh) * DQK;
-  const uint16_t* vbase = vg + ((int64_t)b * L * Hkv + hr.kvh) * DV;
+  const uint16_t* kbase = kg + ((int64_t)b * L * Hkv + h) * DQK;
+  const uint16_t* vbase = vg + ((int64_t)b * L * Hkv + h) * DV;
   const int64_t kstride = (int64_t)Hkv * DQK, vstride = (int64_t)Hkv * DV;
 
-  u32x4 stg[C::PPT];
-  auto stage_load = [&](int kt) {
-#pragma unroll
-    for (int p = 0; p < C::PPT; ++p) {
-      const int pc = tid + kBwdThreads * p;
-      if (pc < C::KP) {
-        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
-        const int key = min(kt * 32 + r, L - 1);
-        stg[p] = ldg16(kbase + key * kstride + 8 * cc);
-      } else if (pc < C::KP + C::VP) {
-        const int pv = pc - C::KP;
-        const int r = pv / (DV / 8), cc = pv - r * (DV / 8);
-        const int key = min(kt * 32 + r, L - 1);
-        stg[p] = ldg16(vbase + key * vstride + 8 * cc);
-      }
-    }
-  };
-  auto stage_store = [&](int buf) {
-    unsigned char* base = smem + buf * C::TILE;
-#pragma unroll
-    for (int p = 0; p < C::PPT; ++p) {
-      const int pc = tid + kBwdThreads * p;
-      if (pc < C::KP) {
-        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
-        *(u32x4*)(base + r * C::KROW + 16 * cc) = stg[p];
-      } else if (pc < C::KP + C::VP) {
-        const int pv = pc - C::KP;
-        const int r = pv / (DV / 8), cc = pv - r * (DV / 8);
-        *(u32x4*)(base + C::V_OFF + r * C::VROW + 16 * cc) = stg[p];
-      }
-    }
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(const lds_void*)smem;
+  auto issue = [&](int kt, int buf) {
+    const int rows_ok = min(32, L - kt * 32);
+    const uint32_t base = smem_lds + (uint32_t)(buf * C::TILE);
+    copy_rows<DQK * 2, C::KROW, C::KBLK>(kbase + (int64_t)kt * 32 * kstride,
+                                         (uint32_t)(kstride * 2), rows_ok, base, wave, lane);
+    copy_rows<DV * 2, C::VROW, C::VBLK>(vbase + (int64_t)kt * 32 * vstride,
+                                        (uint32_t)(vstride * 2), rows_ok, base + C::V_OFF, wave,
+                                        lane);
   };
 
-  stage_load(kt0);
-  stage_store(0);
-  __syncthreads();
-  if (kt0 + 1 <= kt1) stage_load(kt0 + 1);
+  issue(kt0, 0);
   for (int kt = kt0; kt <= kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile kt have landed
+    __syncthreads();                // ... and every wave's; tile kt-1 is consumed
+    if (kt + 1 <= kt1) issue(kt + 1, buf ^ 1);
     const unsigned char* Kl = smem + buf * C::TILE;
     const unsigned char* Vl = Kl + C::V_OFF;
     const int k0 = kt * 32;
     // Is any key of this tile visible to a query of this wave? (wave-uniform)
     const bool live = k0 <= t0w + 15 && (!window || k0 + 31 >= t0w - window + 1);
     if (live) {
-      floatx4 sT[2], dpT[2];
+      // One 16-key half at a time: its scores and dP are dead once its dS is packed.
+      bf16x8 dsb[NH];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sT[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        dpT[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 sT[NH], dpT[NH];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          sT[kb] = mfma_16x16x32(row_operand(Kl, C::KROW, 16 * kb, ks, g4, col), qT[ks], sT[kb]);
+        for (int u = 0; u < NH; ++u) {
+          sT[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dpT[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int kv = 0; kv < C::VS; ++kv)
-          dpT[kb] = mfma_16x16x32(row_operand(Vl, C::VROW, 16 * kb, kv, g4, col), doT[kv],
-                                  dpT[kb]);
-      }
-      bf16x8 dsb;
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 a = row_operand(Kl, C::KROW, 16 * kb, ks, g4, col);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int u = 0; u < NH; ++u) sT[u] = mfma_16x16x32(a, qT[u][ks], sT[u]);
+        }
+#pragma unroll
+        for (int kv = 0; kv < C::VS; ++kv) {
+          const bf16x8 a = row_operand(Vl, C::VROW, 16 * kb, kv, g4, col);
+#pragma unroll
+          for (int u = 0; u < NH; ++u) dpT[u] = mfma_16x16x32(a, doT[u][kv], dpT[u]);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + 16 * kb + 4 * g4 + r;
           const bool vis = t_ok && key <= t && (!window || t - key < window);
-          const float p = vis ? fast_exp2(fmaf(sT[kb][r], c2, -lse2)) : 0.f;
-          dsb[4 * kb + r] = (__bf16)(p * (dpT[kb][r] - dl));
-        }
 #pragma unroll
-      for (int d = 0; d < C::DT; ++d)
-        dqT[d] = mfma_16x16x32(tr_operand(Kl, C::KROW, 16 * d, g4, col), dsb, dqT[d]);
+          for (int u = 0; u < NH; ++u) {
+            const float p = vis ? fast_exp2(fmaf(sT[u][r], c2, -lse2[u])) : 0.f;
+            dsb[u][4 * kb + r] = (__bf16)(p * (dpT[u][r] - dl[u]));
+          }
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < C::DT; ++d) {
+        const bf16x8 a = tr_operand(Kl, C::KROW, 16 * d, g4, col);
+#pragma unroll
+        for (int u = 0; u < NH; ++u) dqT[u][d] = mfma_16x16x32(a, dsb[u], dqT[u][d]);
+      }
     }
-    if (kt + 1 <= kt1) stage_store(buf ^ 1);
-    __syncthreads();
-    if (kt + 2 <= kt1) stage_load(kt + 2);
   }
   if (t_ok) {
-    uint16_t* dst = hd < S ? dq_sig + (((int64_t)b * L + t) * S + hd) * DQK
-                           : dq_noise + (((int64_t)b * L + t) * N + hd - S) * DQK;
-    store_col_row<C::DT>(dst, g4, dqT, scale);
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+      uint16_t* dst = hd[u] < S ? dq_sig + (((int64_t)b * L + t) * S + hd[u]) * DQK
+                                : dq_noise + (((int64_t)b * L + t) * N + hd[u] - S) * DQK;
+      store_col_row<C::DT>(dst, g4, dqT[u], scale);
+    }
   }
 }
 
@@ -334,12 +385,11 @@ template <int DQK, int DV>
 struct DkvShape {
   static constexpr int KS = DQK / 32, VS = DV / 32, DT = DQK / 16, VT = DV / 16;
   static constexpr int QROW = DQK * 2 + 16, OROW = DV * 2 + 16;
-  static constexpr int O_OFF = 32 * QROW;
-  static constexpr int L_OFF = O_OFF + 32 * OROW;
+  static constexpr int QBLK = (32 * QROW + 1023) / 1024, OBLK = (32 * OROW + 1023) / 1024;
+  static constexpr int O_OFF = QBLK * 1024;
+  static constexpr int L_OFF = (QBLK + OBLK) * 1024;
   static constexpr int D_OFF = L_OFF + 32 * 4;
   static constexpr int TILE = D_OFF + 32 * 4;
-  static constexpr int QP = 32 * DQK / 8, OP = 32 * DV / 8;
-  static constexpr int PPT = (QP + OP + kBwdThreads - 1) / kBwdThreads;
 };
 
 template <int DQK, int DV>
@@ -381,71 +431,45 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
   for (int d = 0; d < C::VT; ++d) dvT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // The query heads on KV head h: signal heads h*S/Hkv ..; noise heads
-  // ceil(h*N/Hkv) .. ceil((h+1)*N/Hkv) - 1.
-  const int sig_lo = h * (S / Hkv), n_sig = S / Hkv;
-  const int j_lo = (h * N + Hkv - 1) / Hkv, j_hi = ((h + 1) * N + Hkv - 1) / Hkv;
-  const int nh = n_sig + (j_hi - j_lo);
+  const int nh = kv_head_count(h, S, N, Hkv);
   const int q_lo = kt * 64;
   const int q_hi = window ? min(L - 1, kt * 64 + 63 + window - 1) : L - 1;
   const int qb0 = q_lo / 32, nqb = q_hi / 32 - qb0 + 1;
   const int n_items = nh * nqb;
 
-  u32x4 stg[C::PPT];
-  float stg_s = 0.f;  // one lse or delta value (threads 0..63)
-  auto head_of_item = [&](int it) -> int {
-    const int hh = it / nqb;
-    return hh < n_sig ? sig_lo + hh : S + j_lo + (hh - n_sig);
-  };
-  auto stage_load = [&](int it) {
+  // Q and dO rows arrive by direct global -> LDS copies; the 32 rows' lse (log2
+  // units) and delta by plain loads of threads 0..63, written after the compute.
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(const lds_void*)smem;
+  float stg_s = 0.f;
+  auto head_of_item = [&](int it) -> int { return kv_head_member(h, it / nqb, S, N, Hkv); };
+  auto issue = [&](int it, int buf) {
     const int hd = head_of_item(it);
     const int qb = qb0 + (it - (it / nqb) * nqb);
     const HeadRef hr = head_ref(hd, b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
-#pragma unroll
-    for (int p = 0; p < C::PPT; ++p) {
-      const int pc = tid + kBwdThreads * p;
-      if (pc < C::QP) {
-        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
-        const int q = min(qb * 32 + r, L - 1);
-        stg[p] = ldg16(hr.q + q * hr.qstride + 8 * cc);
-      } else if (pc < C::QP + C::OP) {
-        const int po = pc - C::QP;
-        const int r = po / (DV / 8), cc = po - r * (DV / 8);
-        const int q = min(qb * 32 + r, L - 1);
-        stg[p] = ldg16(hr.dO + q * hr.ostride + 8 * cc);
-      }
-    }
+    const int rows_ok = min(32, L - qb * 32);
+    const uint32_t base = smem_lds + (uint32_t)(buf * C::TILE);
+    copy_rows<DQK * 2, C::QROW, C::QBLK>(hr.q + (int64_t)qb * 32 * hr.qstride,
+                                         (uint32_t)(hr.qstride * 2), rows_ok, base, wave, lane);
+    copy_rows<DV * 2, C::OROW, C::OBLK>(hr.dO + (int64_t)qb * 32 * hr.ostride,
+                                        (uint32_t)(hr.ostride * 2), rows_ok, base + C::O_OFF,
+                                        wave, lane);
     if (tid < 64) {
       const int q = min(qb * 32 + (tid & 31), L - 1);
       const int64_t at = ((int64_t)b * HT + hd) * L + q;
       stg_s = tid < 32 ? lse[at] * kLog2e : delta[at];
     }
   };
-  auto stage_store = [&](int buf) {
-    unsigned char* base = smem + buf * C::TILE;
-#pragma unroll
-    for (int p = 0; p < C::PPT; ++p) {
-      const int pc = tid + kBwdThreads * p;
-      if (pc < C::QP) {
-        const int r = pc / (DQK / 8), cc = pc - r * (DQK / 8);
-        *(u32x4*)(base + r * C::QROW + 16 * cc) = stg[p];
-      } else if (pc < C::QP + C::OP) {
-        const int po = pc - C::QP;
-        const int r = po / (DV / 8), cc = po - r * (DV / 8);
-        *(u32x4*)(base + C::O_OFF + r * C::OROW + 16 * cc) = stg[p];
-      }
-    }
-    if (tid < 64) *(float*)(base + C::L_OFF + 4 * tid) = stg_s;  // lse[32] then delta[32]
+  auto store_scalars = [&](int buf) {
+    if (tid < 64) *(float*)(smem + buf * C::TILE + C::L_OFF + 4 * tid) = stg_s;
   };
 
-  if (n_items > 0) {
-    stage_load(0);
-    stage_store(0);
-  }
-  __syncthreads();
-  if (1 < n_items) stage_load(1);
+  issue(0, 0);  // n_items >= 1: every KV head has a signal head and a query block
+  store_scalars(0);
   for (int it = 0; it < n_items; ++it) {
     const int buf = it & 1;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of item it have landed
+    __syncthreads();                // ... and every wave's; item it-1 is consumed
+    if (it + 1 < n_items) issue(it + 1, buf ^ 1);
     const unsigned char* Ql = smem + buf * C::TILE;
     const unsigned char* Ol = Ql + C::O_OFF;
     const float* sL = (const float*)(Ql + C::L_OFF);
@@ -484,9 +508,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
       for (int d = 0; d < C::DT; ++d)
         dkT[d] = mfma_16x16x32(tr_operand(Ql, C::QROW, 16 * d, g4, col), dsb, dkT[d]);
     }
-    if (it + 1 < n_items) stage_store(buf ^ 1);
-    __syncthreads();
-    if (it + 2 < n_items) stage_load(it + 2);
+    if (it + 1 < n_items) store_scalars(buf ^ 1);
   }
   if (s_ok) {
     store_col_row<C::DT>(dk + (((int64_t)b * L + s) * Hkv + h) * DQK, g4, dkT, scale);
@@ -500,9 +522,10 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.B * a.L * a.N;
   const int64_t prep_blocks = (items + 3) / 4;
   const int nqt = (a.L + 63) / 64;
-  const int64_t dq_blocks = (int64_t)nqt * a.B * HT;
+  const int64_t dq_blocks = (int64_t)nqt * a.B * a.Hkv;  // per head group
   const int64_t dkv_blocks = (int64_t)nqt * a.B * a.Hkv;
-  if (prep_blocks > 0x7fffffff || dq_blocks > 0x7fffffff || dkv_blocks > 0x7fffffff)
+  if (prep_blocks > 0x7fffffff || dq_blocks * (HT / a.Hkv + 2) > 0x7fffffff ||
+      dkv_blocks > 0x7fffffff)
     return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_prep_kernel<DV>), dim3((unsigned)prep_blocks), dim3(kBwdThreads), 0,
                      stream, (const uint16_t*)a.d_out, (const uint16_t*)a.gate,
@@ -512,13 +535,33 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int heavy_first = a.window == 0 ? 1 : 0;
-  hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV>), dim3((unsigned)dq_blocks), dim3(kBwdThreads), 0,
-                     stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
-                     a.delta, (uint16_t*)a.dq_sig, (uint16_t*)a.dq_noise, a.B, a.L, a.S, a.N,
-                     a.Hkv, a.window, nqt, heavy_first, a.scale_log2, a.scale);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // Heads per KV head: the most any KV head has (noise heads may sit on some only).
+  int nh_max = 0, any_odd = 0;
+  for (int h = 0; h < a.Hkv; ++h) {
+    const int n = a.S / a.Hkv + ((h + 1) * a.N + a.Hkv - 1) / a.Hkv - (h * a.N + a.Hkv - 1) / a.Hkv;
+    nh_max = n > nh_max ? n : nh_max;
+    any_odd |= n & 1;
+  }
+  const int pairs = nh_max / 2;
+  if (pairs > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, 2>), dim3((unsigned)(dq_blocks * pairs)),
+                       dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q_sig,
+                       (const uint16_t*)a.q_noise, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       a.lse, a.do_sig, a.do_noise, a.delta, (uint16_t*)a.dq_sig,
+                       (uint16_t*)a.dq_noise, a.B, a.L, a.S, a.N, a.Hkv, a.window, nqt, pairs,
+                       heavy_first, a.scale_log2, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (any_odd) {
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, 1>), dim3((unsigned)dq_blocks), dim3(kBwdThreads),
+                       0, stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
+                       a.delta, (uint16_t*)a.dq_sig, (uint16_t*)a.dq_noise, a.B, a.L, a.S, a.N,
+                       a.Hkv, a.window, nqt, 1, heavy_first, a.scale_log2, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV>), dim3((unsigned)dkv_blocks), dim3(kBwdThreads),
                      0, stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
