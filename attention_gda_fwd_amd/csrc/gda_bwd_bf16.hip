@@ -29,6 +29,10 @@ namespace gda {
 namespace {
 
 constexpr int kBwdThreads = 256;  // 4 waves
+// 16-key column tiles per dK/dV wave. Two tiles halve the LDS reads per matrix
+// instruction but need about 330 registers, so one wave per SIMD: measured
+// 22.0 ms against 15.1-15.5 ms for one tile on the Motif-3 full-layer backward.
+constexpr int kDkvTiles = 1;
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -392,8 +396,10 @@ struct DkvShape {
   static constexpr int TILE = D_OFF + 32 * 4;
 };
 
-template <int DQK, int DV>
-__global__ void __launch_bounds__(kBwdThreads, 2)
+// KT 16-key column tiles per wave (64*KT keys per workgroup): every Q/dO
+// fragment read from LDS serves KT tiles.
+template <int DQK, int DV, int KT>
+__global__ void __launch_bounds__(kBwdThreads, KT == 1 ? 2 : 1)
 bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const float* __restrict__ lse, const uint16_t* __restrict__ do_sig,
@@ -409,31 +415,31 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   const int kt = blockIdx.x / per;  // key tiles in order: the first ones see the most queries
   const int rem = blockIdx.x - kt * per;
   const int b = rem / Hkv, h = rem - (rem / Hkv) * Hkv;
-  const int k0w = kt * 64 + 16 * wave;
-  const int s = k0w + col;  // this lane's key
-  const bool s_ok = s < L;
-  const int sk = min(s, L - 1);
-
-  bf16x8 kT[C::KS], vT[C::VS];
-  {
+  const int k0w = kt * 64 * KT + 16 * KT * wave;  // this wave's first key
+  int s[KT];  // this lane's key in each column tile
+  bf16x8 kT[KT][C::KS], vT[KT][C::VS];
+  floatx4 dkT[KT][C::DT], dvT[KT][C::VT];
+#pragma unroll
+  for (int kc = 0; kc < KT; ++kc) {
+    s[kc] = k0w + 16 * kc + col;
+    const int sk = min(s[kc], L - 1);
     const uint16_t* kr = kg + (((int64_t)b * L + sk) * Hkv + h) * DQK;
     const uint16_t* vr = vg + (((int64_t)b * L + sk) * Hkv + h) * DV;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      kT[ks] = __builtin_bit_cast(bf16x8, ldg16(kr + 32 * ks + 8 * g4));
+      kT[kc][ks] = __builtin_bit_cast(bf16x8, ldg16(kr + 32 * ks + 8 * g4));
 #pragma unroll
     for (int kv = 0; kv < C::VS; ++kv)
-      vT[kv] = __builtin_bit_cast(bf16x8, ldg16(vr + 32 * kv + 8 * g4));
+      vT[kc][kv] = __builtin_bit_cast(bf16x8, ldg16(vr + 32 * kv + 8 * g4));
+#pragma unroll
+    for (int d = 0; d < C::DT; ++d) dkT[kc][d] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < C::VT; ++d) dvT[kc][d] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  floatx4 dkT[C::DT], dvT[C::VT];
-#pragma unroll
-  for (int d = 0; d < C::DT; ++d) dkT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int d = 0; d < C::VT; ++d) dvT[d] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int nh = kv_head_count(h, S, N, Hkv);
-  const int q_lo = kt * 64;
-  const int q_hi = window ? min(L - 1, kt * 64 + 63 + window - 1) : L - 1;
+  const int q_lo = kt * 64 * KT;
+  const int q_hi = window ? min(L - 1, q_lo + 64 * KT - 1 + window - 1) : L - 1;
   const int qb0 = q_lo / 32, nqb = q_hi / 32 - qb0 + 1;
   const int n_items = nh * nqb;
 
@@ -475,45 +481,66 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     const float* sL = (const float*)(Ql + C::L_OFF);
     const float* sD = (const float*)(Ql + C::D_OFF);
     const int q0 = (qb0 + (it - (it / nqb) * nqb)) * 32;
-    const bool live = k0w <= q0 + 31 && (!window || q0 <= k0w + 14 + window);
+    const bool live = k0w <= q0 + 31 && (!window || q0 <= k0w + 16 * KT - 2 + window);
     if (live) {
-      floatx4 sc[2], dp[2];
+      floatx4 sc[KT][2], dp[KT][2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        sc[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        dp[qt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          sc[qt] = mfma_16x16x32(row_operand(Ql, C::QROW, 16 * qt, ks, g4, col), kT[ks], sc[qt]);
+        for (int kc = 0; kc < KT; ++kc) {
+          sc[kc][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dp[kc][qt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int kv = 0; kv < C::VS; ++kv)
-          dp[qt] = mfma_16x16x32(row_operand(Ol, C::OROW, 16 * qt, kv, g4, col), vT[kv], dp[qt]);
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 a = row_operand(Ql, C::QROW, 16 * qt, ks, g4, col);
+#pragma unroll
+          for (int kc = 0; kc < KT; ++kc) sc[kc][qt] = mfma_16x16x32(a, kT[kc][ks], sc[kc][qt]);
+        }
+#pragma unroll
+        for (int kv = 0; kv < C::VS; ++kv) {
+          const bf16x8 a = row_operand(Ol, C::OROW, 16 * qt, kv, g4, col);
+#pragma unroll
+          for (int kc = 0; kc < KT; ++kc) dp[kc][qt] = mfma_16x16x32(a, vT[kc][kv], dp[kc][qt]);
+        }
       }
-      bf16x8 pb, dsb;
+      bf16x8 pb[KT], dsb[KT];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qi = 16 * qt + 4 * g4 + r;
           const int q = q0 + qi;
-          const bool vis = s_ok && q < L && s <= q && (!window || q - s < window);
-          const float p = vis ? fast_exp2(fmaf(sc[qt][r], c2, -sL[qi])) : 0.f;
-          pb[4 * qt + r] = (__bf16)p;
-          dsb[4 * qt + r] = (__bf16)(p * (dp[qt][r] - sD[qi]));
+          const float l2 = sL[qi], dl = sD[qi];
+#pragma unroll
+          for (int kc = 0; kc < KT; ++kc) {
+            const bool vis = s[kc] < L && q < L && s[kc] <= q && (!window || q - s[kc] < window);
+            const float p = vis ? fast_exp2(fmaf(sc[kc][qt][r], c2, -l2)) : 0.f;
+            pb[kc][4 * qt + r] = (__bf16)p;
+            dsb[kc][4 * qt + r] = (__bf16)(p * (dp[kc][qt][r] - dl));
+          }
         }
 #pragma unroll
-      for (int d = 0; d < C::VT; ++d)
-        dvT[d] = mfma_16x16x32(tr_operand(Ol, C::OROW, 16 * d, g4, col), pb, dvT[d]);
+      for (int d = 0; d < C::VT; ++d) {
+        const bf16x8 a = tr_operand(Ol, C::OROW, 16 * d, g4, col);
 #pragma unroll
-      for (int d = 0; d < C::DT; ++d)
-        dkT[d] = mfma_16x16x32(tr_operand(Ql, C::QROW, 16 * d, g4, col), dsb, dkT[d]);
+        for (int kc = 0; kc < KT; ++kc) dvT[kc][d] = mfma_16x16x32(a, pb[kc], dvT[kc][d]);
+      }
+#pragma unroll
+      for (int d = 0; d < C::DT; ++d) {
+        const bf16x8 a = tr_operand(Ql, C::QROW, 16 * d, g4, col);
+#pragma unroll
+        for (int kc = 0; kc < KT; ++kc) dkT[kc][d] = mfma_16x16x32(a, dsb[kc], dkT[kc][d]);
+      }
     }
     if (it + 1 < n_items) store_scalars(buf ^ 1);
   }
-  if (s_ok) {
-    store_col_row<C::DT>(dk + (((int64_t)b * L + s) * Hkv + h) * DQK, g4, dkT, scale);
-    store_col_row<C::VT>(dvo + (((int64_t)b * L + s) * Hkv + h) * DV, g4, dvT, 1.f);
-  }
+#pragma unroll
+  for (int kc = 0; kc < KT; ++kc)
+    if (s[kc] < L) {
+      store_col_row<C::DT>(dk + (((int64_t)b * L + s[kc]) * Hkv + h) * DQK, g4, dkT[kc], scale);
+      store_col_row<C::VT>(dvo + (((int64_t)b * L + s[kc]) * Hkv + h) * DV, g4, dvT[kc], 1.f);
+    }
 }
 
 template <int DQK, int DV>
@@ -523,7 +550,7 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
   const int64_t prep_blocks = (items + 3) / 4;
   const int nqt = (a.L + 63) / 64;
   const int64_t dq_blocks = (int64_t)nqt * a.B * a.Hkv;  // per head group
-  const int64_t dkv_blocks = (int64_t)nqt * a.B * a.Hkv;
+  const int64_t dkv_blocks = (int64_t)((a.L + 64 * kDkvTiles - 1) / (64 * kDkvTiles)) * a.B * a.Hkv;
   if (prep_blocks > 0x7fffffff || dq_blocks * (HT / a.Hkv + 2) > 0x7fffffff ||
       dkv_blocks > 0x7fffffff)
     return hipErrorInvalidConfiguration;
@@ -562,7 +589,8 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV>), dim3((unsigned)dkv_blocks), dim3(kBwdThreads),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, kDkvTiles>), dim3((unsigned)dkv_blocks),
+                     dim3(kBwdThreads),
                      0, stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
                      a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv_out, a.B, a.L, a.S, a.N, a.Hkv,
