@@ -12,7 +12,8 @@ against the fp64 oracle, through the C ABI.
 Tolerances. The forward's bf16 bar (max |err| <= 2e-2 and mean |err| <= 2e-3 on O(1)
 outputs) applied to each gradient tensor relative to its largest magnitude: the
 backward rounds P, dS and dO to bf16 before each matrix product (relative error
-2^-9 per operand) and accumulates in fp32, so errors scale with the gradient's size.
+2^-9 per operand) and accumulates in fp32, so errors scale with the gradient's size (with
+a floor of 0.05 for the magnitude, for gradients that vanish identically).
 """
 import numpy as np
 import pytest
@@ -32,7 +33,9 @@ ARGS = ("q_sig", "q_noise", "k", "v", "lam", "gate")
 
 
 def assert_grad_close(got, ref, what):
-    scale = float(np.abs(ref).max())
+    # A gradient that vanishes identically (a one-key window makes dS = P (dP - delta)
+    # zero) is held to the bound of an O(0.05) gradient: 1e-3 absolute.
+    scale = max(float(np.abs(ref).max()), 0.05)
     err = np.abs(got - ref)
     U.log(f"{what}: max|err| {err.max():.3e} mean|err| {err.mean():.3e} max|ref| {scale:.3e}")
     assert np.isfinite(got).all(), f"{what}: non-finite gradient"
@@ -71,6 +74,13 @@ SMALL = {
                             dict(scale=0.1, lambda_logits=True, gate_logits=True)),
     "tiny_L70_gate_logits": (618, dict(B=1, L=70, S=8, N=2, Hkv=2, dqk=64, dv=64), 0,
                              dict(gate_logits=True)),
+    # edges: one token; a window of one key (each query sees only itself); a window
+    # longer than the sequence (plain causal); a length just past a 32-row tile
+    "edge_tiny_B2_L1": (619, dict(B=2, L=1, S=8, N=2, Hkv=2, dqk=64, dv=64), 0, {}),
+    "edge_motif3_L40_w1": (620, dict(B=1, L=40, S=64, N=16, Hkv=16, dqk=192, dv=128,
+                                     rope_dims=64), 1, {}),
+    "edge_motif2_L33_w500": (621, dict(B=2, L=33, S=32, N=8, Hkv=16, dqk=128, dv=128), 500,
+                             {}),
 }
 
 
