@@ -86,6 +86,10 @@ def _load():
         lib.gda_ref_bwd.restype = ci
         lib.gda_ref_bwd.argtypes = ([vp] * 13 + [i64] * 8 + [ci, f64, ci, vp, i64, vp, i64,
                                                             ci])
+        lib.gda_ref_fwd_train_varlen.restype = ci
+        lib.gda_ref_fwd_train_varlen.argtypes = [vp] * 12 + [i64] * 7 + [ci, f64, ci]
+        lib.gda_ref_bwd_varlen.restype = ci
+        lib.gda_ref_bwd_varlen.argtypes = [vp] * 15 + [i64] * 7 + [ci, f64, ci]
         lib.gda_ref_threads.restype = ctypes.c_int
         lib.gda_ref_threads.argtypes = []
         _lib = lib
@@ -313,3 +317,54 @@ def ref_bwd(q_sig, q_noise, k, v, lam, gate, d_out, *, window: int, scale: float
         out["dk"] = dk.reshape(B, L, Hkv, dqk)
         out["dv"] = dvv.reshape(B, L, Hkv, dv)
     return out
+
+
+def _varlen_args(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k):
+    code = _dtype_code(q_sig)
+    q_sig, q_noise, k, v, lam, gate = (_c(x, code) for x in (q_sig, q_noise, k, v, lam, gate))
+    Tq, S, dqk = q_sig.shape
+    N, Tk, Hkv, dv = q_noise.shape[1], k.shape[0], k.shape[1], v.shape[2]
+    cu_q = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int32))
+    cu_k = np.ascontiguousarray(np.asarray(cu_k, dtype=np.int32))
+    assert cu_k.size == cu_q.size and cu_q[-1] == Tq and cu_k[-1] == Tk
+    return code, (q_sig, q_noise, k, v, lam, gate), cu_q, cu_k, Tq, Tk, S, N, Hkv, dqk, dv
+
+
+def ref_fwd_train_varlen(q_sig, q_noise, k, v, lam, gate, cu_q, cu_k, *, window: int,
+                         scale: float | None = None, lambda_logits: bool = False,
+                         gate_logits: bool = False):
+    """Packed-sequence training forward: (out [Tq,S,dv], h_sig [Tq,S,dv], h_noise [Tq,N,dv],
+    lse [S+N,Tq]) in float64 (shapes and positions as ref_fwd_varlen)."""
+    code, x, cu_q, cu_k, Tq, Tk, S, N, Hkv, dqk, dv = _varlen_args(q_sig, q_noise, k, v, lam,
+                                                                   gate, cu_q, cu_k)
+    out = np.empty((Tq, S, dv)); h_sig = np.empty((Tq, S, dv)); h_noise = np.empty((Tq, N, dv))
+    lse = np.empty((S + N, Tq))
+    rc = _load().gda_ref_fwd_train_varlen(*(_ptr(a) for a in x), _ptr(out), _ptr(h_sig),
+                                          _ptr(h_noise), _ptr(lse), _ptr(cu_q), _ptr(cu_k),
+                                          cu_q.size - 1, S, N, Hkv, dqk, dv, int(window), code,
+                                          float(scale or 0.0), _flags(lambda_logits, gate_logits))
+    if rc != 0:
+        raise ValueError(f"gda_ref_fwd_train_varlen rejected its arguments (code {rc})")
+    return out, h_sig, h_noise, lse
+
+
+def ref_bwd_varlen(q_sig, q_noise, k, v, lam, gate, d_out, cu_q, cu_k, *, window: int,
+                   scale: float | None = None, lambda_logits: bool = False,
+                   gate_logits: bool = False) -> dict:
+    """Packed-sequence backward oracle: gradients of sum(d_out * out), float64, shaped like
+    the packed inputs (dq_sig [Tq,S,dqk], dq_noise, dk [Tk,Hkv,dqk], dv, dlam, dgate)."""
+    code, x, cu_q, cu_k, Tq, Tk, S, N, Hkv, dqk, dv = _varlen_args(q_sig, q_noise, k, v, lam,
+                                                                   gate, cu_q, cu_k)
+    d_out = _c(d_out, code)
+    assert d_out.shape == (Tq, S, dv)
+    g = dict(dq_sig=np.empty((Tq, S, dqk)), dq_noise=np.empty((Tq, N, dqk)),
+             dk=np.empty((Tk, Hkv, dqk)), dv=np.empty((Tk, Hkv, dv)), dlam=np.empty((Tq, S)),
+             dgate=np.empty((Tq, S, dv)))
+    rc = _load().gda_ref_bwd_varlen(*(_ptr(a) for a in x), _ptr(d_out), _ptr(g["dq_sig"]),
+                                    _ptr(g["dq_noise"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                    _ptr(g["dlam"]), _ptr(g["dgate"]), _ptr(cu_q), _ptr(cu_k),
+                                    cu_q.size - 1, S, N, Hkv, dqk, dv, int(window), code,
+                                    float(scale or 0.0), _flags(lambda_logits, gate_logits))
+    if rc != 0:
+        raise ValueError(f"gda_ref_bwd_varlen rejected its arguments (code {rc})")
+    return g

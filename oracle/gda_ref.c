@@ -766,4 +766,261 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
   return failed ? -8 : 0;
 }
 
+/* ---- Packed sequences: training form of the forward, and the backward ------------
+ * The same steps over packed sequences with a query offset: sequence i owns query
+ * rows cu_q[i] .. cu_q[i+1]-1 and key rows cu_k[i] .. cu_k[i+1]-1; its local query t
+ * sits at key position Lk - Lq + t (a negative position sees no key). */
+
+static int check_cu(const int32_t* cu_q, const int32_t* cu_k, int64_t nseq, int64_t* maxk) {
+  if (nseq < 1 || !cu_q || !cu_k) return -1;
+  if (cu_q[0] != 0 || cu_k[0] != 0) return -10;
+  *maxk = 1;
+  for (int64_t i = 0; i < nseq; ++i) {
+    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i]) return -10;
+    if (cu_k[i + 1] - cu_k[i] > *maxk) *maxk = cu_k[i + 1] - cu_k[i];
+  }
+  return 0;
+}
+
+/* The sequence of packed row r under offsets cu (nseq+1 entries). */
+static int64_t seq_of(const int32_t* cu, int64_t r) {
+  int64_t i = 0;
+  while (cu[i + 1] <= r) ++i;
+  return i;
+}
+
+/* K/V view of sequence i: its key 0 at packed key row cu_k[i]. */
+static kv_view seq_view(const void* k, const void* v, const int32_t* cu_k, int64_t i,
+                        int64_t Hkv, int64_t dqk, int64_t dv, int dtype, int mutant,
+                        double softmax_scale, int flags) {
+  const kv_view kv = {offset_ptr(k, (int64_t)cu_k[i] * Hkv * dqk, dtype),
+                      offset_ptr(v, (int64_t)cu_k[i] * Hkv * dv, dtype),
+                      cu_k[i + 1] - cu_k[i], Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
+  return kv;
+}
+
+int gda_ref_fwd_train_varlen(const void* q_sig, const void* q_noise, const void* k,
+                             const void* v, const void* lambda, const void* gate, double* out,
+                             double* h_sig, double* h_noise, double* lse, const int32_t* cu_q,
+                             const int32_t* cu_k, int64_t nseq, int64_t S, int64_t N,
+                             int64_t Hkv, int64_t dqk, int64_t dv, int64_t window, int dtype,
+                             double softmax_scale, int flags) {
+  int rc = gda_ref_fwd_varlen(q_sig, q_noise, k, v, lambda, gate, out, cu_q, cu_k, nseq, S, N,
+                              Hkv, dqk, dv, window, dtype, softmax_scale, flags);
+  if (rc) return rc;
+  if (!h_sig || !h_noise || !lse) return -6;
+  int64_t maxk;
+  if ((rc = check_cu(cu_q, cu_k, nseq, &maxk))) return rc;
+  const int64_t Tq = cu_q[nseq], HT = S + N;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)maxk);
+    if (!z) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < Tq; ++r) {
+        const int64_t i = seq_of(cu_q, r);
+        const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
+                                    softmax_scale, flags);
+        const double scale = softmax_scale_of(&kv);
+        const int64_t pos = (kv.Lk - (cu_q[i + 1] - cu_q[i])) + (r - cu_q[i]);
+        int64_t lo, hi;
+        visible_range(pos, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, r, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          const double ls = row_lse(q, q_off, &kv, 0, kvh, lo, hi, scale, z);
+          lse[h * Tq + r] = ls;
+          double* H = h < S ? h_sig + (r * S + h) * dv : h_noise + (r * N + h - S) * dv;
+          for (int64_t e = 0; e < dv; ++e) H[e] = 0.0;
+          for (int64_t s2 = lo; s2 <= hi; ++s2) {
+            const double P = exp(z[s2 - lo] - ls);
+            for (int64_t e = 0; e < dv; ++e)
+              H[e] += P * rd(kv.v, v_index(&kv, 0, s2, kvh, e), dtype);
+          }
+        }
+      }
+    }
+    free(z);
+  }
+  return failed ? -8 : 0;
+}
+
+int gda_ref_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                       const void* lambda, const void* gate, const void* d_out, double* dq_sig,
+                       double* dq_noise, double* dk, double* dv_out, double* dlambda,
+                       double* dgate, const int32_t* cu_q, const int32_t* cu_k, int64_t nseq,
+                       int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv,
+                       int64_t window, int dtype, double softmax_scale, int flags) {
+  int rc = check_common(1, 1, S, N, Hkv, dqk, dv, window, dtype);
+  if (rc) return rc;
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !d_out || !dq_sig || !dq_noise ||
+      !dk || !dv_out || !dlambda || !dgate)
+    return -6;
+  if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
+    return -9;
+  int64_t maxk;
+  if ((rc = check_cu(cu_q, cu_k, nseq, &maxk))) return rc;
+  const int64_t Tq = cu_q[nseq], Tk = cu_k[nseq], HT = S + N, g = S / N;
+  const size_t n1 = (size_t)(Tq ? Tq : 1);
+  double* dH = (double*)malloc(sizeof(double) * n1 * (size_t)(HT * dv));
+  double* lse = (double*)malloc(sizeof(double) * n1 * (size_t)HT);
+  double* delta = (double*)malloc(sizeof(double) * n1 * (size_t)HT);
+  if (!dH || !lse || !delta) {
+    free(dH);
+    free(lse);
+    free(delta);
+    return -8;
+  }
+  int failed = 0;
+  /* 1. Per query row: every head's forward, the combine and gate backward, delta. */
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)maxk);
+    double* H = (double*)malloc(sizeof(double) * (size_t)(HT * dv));
+    double* lam = (double*)malloc(sizeof(double) * (size_t)S);
+    if (!z || !H || !lam) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < Tq; ++r) {
+        const int64_t i = seq_of(cu_q, r);
+        const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
+                                    softmax_scale, flags);
+        const double scale = softmax_scale_of(&kv);
+        const int64_t pos = (kv.Lk - (cu_q[i + 1] - cu_q[i])) + (r - cu_q[i]);
+        int64_t lo, hi;
+        visible_range(pos, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, r, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          const double ls = row_lse(q, q_off, &kv, 0, kvh, lo, hi, scale, z);
+          lse[r * HT + h] = ls;
+          for (int64_t e = 0; e < dv; ++e) H[h * dv + e] = 0.0;
+          for (int64_t s2 = lo; s2 <= hi; ++s2) {
+            const double P = exp(z[s2 - lo] - ls);
+            for (int64_t e = 0; e < dv; ++e)
+              H[h * dv + e] += P * rd(kv.v, v_index(&kv, 0, s2, kvh, e), dtype);
+          }
+        }
+        double* dHr = dH + r * HT * dv;
+        for (int64_t i2 = 0; i2 < S; ++i2) {
+          const int64_t j = i2 / g;
+          double lm = rd(lambda, r * S + i2, dtype);
+          if (flags & GDA_REF_LAMBDA_LOGITS) lm = sigmoid(lm);
+          lam[i2] = lm;
+          double dlam = 0.0;
+          for (int64_t e = 0; e < dv; ++e) {
+            const double D = H[i2 * dv + e] - lm * H[(S + j) * dv + e];
+            const double gi = rd(gate, (r * S + i2) * dv + e, dtype);
+            const double G = (flags & GDA_REF_GATE_LOGITS) ? sigmoid(gi) : gi;
+            const double dO = rd(d_out, (r * S + i2) * dv + e, dtype);
+            double dG = dO * D;
+            if (flags & GDA_REF_GATE_LOGITS) dG *= G * (1.0 - G);
+            const double dD = dO * G;
+            dHr[i2 * dv + e] = dD;
+            dlam -= dD * H[(S + j) * dv + e];
+            dgate[(r * S + i2) * dv + e] = dG;
+          }
+          if (flags & GDA_REF_LAMBDA_LOGITS) dlam *= lm * (1.0 - lm);
+          dlambda[r * S + i2] = dlam;
+        }
+        for (int64_t j = 0; j < N; ++j)
+          for (int64_t e = 0; e < dv; ++e) {
+            double acc = 0.0;
+            for (int64_t i2 = g * j; i2 < g * j + g; ++i2) acc -= lam[i2] * dHr[i2 * dv + e];
+            dHr[(S + j) * dv + e] = acc;
+          }
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, r, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          double dl = 0.0;
+          for (int64_t s2 = lo; s2 <= hi; ++s2) {
+            const double P = exp(score(q, q_off, &kv, 0, kvh, s2, scale) - lse[r * HT + h]);
+            double dP = 0.0;
+            for (int64_t e = 0; e < dv; ++e)
+              dP += dHr[h * dv + e] * rd(kv.v, v_index(&kv, 0, s2, kvh, e), dtype);
+            dl += P * dP;
+          }
+          delta[r * HT + h] = dl;
+        }
+      }
+    }
+    free(z);
+    free(H);
+    free(lam);
+  }
+  if (!failed) {
+    /* 2. Query side. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < Tq; ++r) {
+      const int64_t i = seq_of(cu_q, r);
+      const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
+                                  softmax_scale, flags);
+      const double scale = softmax_scale_of(&kv);
+      const int64_t pos = (kv.Lk - (cu_q[i + 1] - cu_q[i])) + (r - cu_q[i]);
+      int64_t lo, hi;
+      visible_range(pos, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+      for (int64_t h = 0; h < HT; ++h) {
+        const void* q;
+        int64_t q_off, kvh;
+        head_of(h, r, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+        double* dq = h < S ? dq_sig + (r * S + h) * dqk : dq_noise + (r * N + h - S) * dqk;
+        for (int64_t d = 0; d < dqk; ++d) dq[d] = 0.0;
+        for (int64_t s2 = lo; s2 <= hi; ++s2) {
+          const double P = exp(score(q, q_off, &kv, 0, kvh, s2, scale) - lse[r * HT + h]);
+          double dP = 0.0;
+          for (int64_t e = 0; e < dv; ++e)
+            dP += dH[(r * HT + h) * dv + e] * rd(kv.v, v_index(&kv, 0, s2, kvh, e), dtype);
+          const double dz = P * (dP - delta[r * HT + h]);
+          for (int64_t d = 0; d < dqk; ++d)
+            dq[d] += scale * dz * rd(kv.k, k_index(&kv, 0, s2, kvh, d), dtype);
+        }
+      }
+    }
+    /* 3. Key side: every query of the key's sequence that sees it. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t kr = 0; kr < Tk; ++kr) {
+      const int64_t i = seq_of(cu_k, kr);
+      const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
+                                  softmax_scale, flags);
+      const double scale = softmax_scale_of(&kv);
+      const int64_t s2 = kr - cu_k[i], Lq = cu_q[i + 1] - cu_q[i], qoff = kv.Lk - Lq;
+      for (int64_t x = 0; x < Hkv * dqk; ++x) dk[kr * Hkv * dqk + x] = 0.0;
+      for (int64_t x = 0; x < Hkv * dv; ++x) dv_out[kr * Hkv * dv + x] = 0.0;
+      for (int64_t t = 0; t < Lq; ++t) {
+        int64_t lo, hi;
+        visible_range(qoff + t, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+        if (s2 < lo || s2 > hi) continue;
+        const int64_t r = cu_q[i] + t;
+        for (int64_t h = 0; h < HT; ++h) {
+          const void* q;
+          int64_t q_off, kvh;
+          head_of(h, r, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
+          const double P = exp(score(q, q_off, &kv, 0, kvh, s2, scale) - lse[r * HT + h]);
+          double dP = 0.0;
+          for (int64_t e = 0; e < dv; ++e)
+            dP += dH[(r * HT + h) * dv + e] * rd(kv.v, v_index(&kv, 0, s2, kvh, e), dtype);
+          const double dz = P * (dP - delta[r * HT + h]);
+          for (int64_t d = 0; d < dqk; ++d)
+            dk[(kr * Hkv + kvh) * dqk + d] += scale * dz * rd(q, q_off + d, dtype);
+          for (int64_t e = 0; e < dv; ++e)
+            dv_out[(kr * Hkv + kvh) * dv + e] += P * dH[(r * HT + h) * dv + e];
+        }
+      }
+    }
+  }
+  free(dH);
+  free(lse);
+  free(delta);
+  return failed ? -8 : 0;
+}
+
 int gda_ref_threads(void) { return omp_get_max_threads(); }

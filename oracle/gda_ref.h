@@ -148,6 +148,27 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
                 const int64_t* q_rows, int64_t n_q_rows, const int64_t* k_rows,
                 int64_t n_k_rows, int mutant);
 
+/* Packed-sequence forms of the two above (sequences as in gda_ref_fwd_varlen):
+ * gda_ref_fwd_train_varlen: out [Tq,S,dv], h_sig [Tq,S,dv], h_noise [Tq,N,dv] and
+ *   lse [S+N, Tq]; gda_ref_bwd_varlen: d_out [Tq,S,dv] -> dq_sig [Tq,S,dqk],
+ *   dq_noise [Tq,N,dqk], dk [Tk,Hkv,dqk], dv_out [Tk,Hkv,dv], dlambda [Tq,S],
+ *   dgate [Tq,S,dv]. A query at a negative position has no visible key: its path
+ *   outputs are zero, its lse is -inf, and it contributes no gradient to K or V. */
+int gda_ref_fwd_train_varlen(const void* q_sig, const void* q_noise, const void* k,
+                             const void* v, const void* lambda, const void* gate, double* out,
+                             double* h_sig, double* h_noise, double* lse,
+                             const int32_t* cu_q, const int32_t* cu_k, int64_t nseq,
+                             int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv,
+                             int64_t window, int dtype, double softmax_scale, int flags);
+
+int gda_ref_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                       const void* lambda, const void* gate, const void* d_out,
+                       double* dq_sig, double* dq_noise, double* dk, double* dv_out,
+                       double* dlambda, double* dgate, const int32_t* cu_q,
+                       const int32_t* cu_k, int64_t nseq, int64_t S, int64_t N, int64_t Hkv,
+                       int64_t dqk, int64_t dv, int64_t window, int dtype,
+                       double softmax_scale, int flags);
+
 /* Threads an OpenMP parallel region of this library starts with (for timing reports). */
 int gda_ref_threads(void);
 

@@ -583,6 +583,81 @@ def pin_backward_rows(bwd):
     return msgs
 
 
+def pin_bwd_varlen(bwd_varlen, train_varlen):
+    """Packed-sequence backward against the batched backward, which is pinned above:
+    packed documents give each document's own gradients; a sequence cut into chunks whose
+    keys start with a W-1 halo gives the whole sequence's query-side gradients row for row,
+    and its K/V gradients once every chunk's contributions to a key are summed; queries at
+    negative positions get zero gradients and the rest are those of the shorter problem.
+    The training forward's outputs match the batched ones per document."""
+    msgs = []
+    Q = ("q_sig", "q_noise", "lam", "gate", "d_out")
+    for W in (0, 4):
+        x = make_bwd("A", B=3, L=17, case_id=1600)
+        # packed documents of lengths 17, 6, 11 taken from three batch rows
+        lens = (17, 6, 11)
+        pk = {n: np.concatenate([x[n][b, :lens[b]] for b in range(3)]) for n in x}
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        got = bwd_varlen(*(pk[n] for n in ARGS), pk["d_out"], cu, cu, window=W)
+        out, hs, hn, lse = train_varlen(*(pk[n] for n in ARGS), cu, cu, window=W)
+        for b in range(3):
+            one = {n: x[n][b:b + 1, :lens[b]] for n in x}
+            ref = oracle.ref_bwd(*(one[n] for n in ARGS), one["d_out"], window=W)
+            for name, r in ref.items():
+                if not np.array_equal(got[name][cu[b]:cu[b + 1]], r[0]):
+                    msgs.append(f"varlen bwd document {b} {name} W={W}")
+            r_out, r_hs, r_hn, r_lse = oracle.ref_fwd_train(*(one[n] for n in ARGS), window=W)
+            _fail(msgs, f"varlen train out doc {b} W={W}",
+                  np.abs(out[cu[b]:cu[b + 1]] - r_out[0]).max(), 1e-13)
+            _fail(msgs, f"varlen train h doc {b} W={W}",
+                  max(np.abs(hs[cu[b]:cu[b + 1]] - r_hs[0]).max(),
+                      np.abs(hn[cu[b]:cu[b + 1]] - r_hn[0]).max()), 1e-13)
+            _fail(msgs, f"varlen train lse doc {b} W={W}",
+                  np.abs(lse[:, cu[b]:cu[b + 1]] - r_lse[0]).max(), 1e-13)
+    # halo chunks: one sequence of 17 rows in chunks of 6, 6, 5; window W = 4 (halo 3)
+    W, L = 4, 17
+    x = make_bwd("B", B=1, L=L, case_id=1610)
+    one = {n: x[n][0] for n in x}
+    full = oracle.ref_bwd(*(x[n] for n in ARGS), x["d_out"], window=W)
+    starts, C = (0, 6, 12), 6
+    q_parts, k_parts, cu_q, cu_k = {n: [] for n in Q}, {"k": [], "v": []}, [0], [0]
+    for c0 in starts:
+        c1, h0 = min(c0 + C, L), max(0, c0 - (W - 1))
+        for n in Q:
+            q_parts[n].append(one[n][c0:c1])
+        for n in ("k", "v"):
+            k_parts[n].append(one[n][h0:c1])
+        cu_q.append(cu_q[-1] + c1 - c0)
+        cu_k.append(cu_k[-1] + c1 - h0)
+    pk = {n: np.concatenate(v) for n, v in {**q_parts, **k_parts}.items()}
+    got = bwd_varlen(*(pk[n] for n in ARGS), pk["d_out"], cu_q, cu_k, window=W)
+    for name in ("dq_sig", "dq_noise", "dlam", "dgate"):
+        if not np.array_equal(got[name], full[name][0]):
+            msgs.append(f"halo chunks {name}")
+    for name in ("dk", "dv"):
+        acc = np.zeros_like(full[name][0])
+        for ci, c0 in enumerate(starts):
+            c1, h0 = min(c0 + C, L), max(0, c0 - (W - 1))
+            acc[h0:c1] += got[name][cu_k[ci]:cu_k[ci + 1]]
+        _fail(msgs, f"halo chunks {name} summed", np.abs(acc - full[name][0]).max(), 1e-12)
+    # more queries than keys: 17 queries over the first 13 keys
+    x = make_bwd("D", B=1, L=17, case_id=1620)
+    one = {n: x[n][0] for n in x}
+    kk = {n: (one[n][:13] if n in ("k", "v") else one[n]) for n in one}
+    got = bwd_varlen(*(kk[n] for n in ARGS), kk["d_out"], [0, 17], [0, 13], window=0)
+    for name in ("dq_sig", "dq_noise", "dlam", "dgate"):
+        if np.any(got[name][:4] != 0.0):
+            msgs.append(f"negative positions: {name} not zero")
+    sh = {n: (one[n][4:] if n in Q else one[n][:13]) for n in one}
+    ref = oracle.ref_bwd(*(sh[n][None] for n in ARGS), sh["d_out"][None], window=0)
+    for name in ("dq_sig", "dq_noise", "dlam", "dgate"):
+        if not np.array_equal(got[name][4:], ref[name][0]):
+            msgs.append(f"shifted queries {name}")
+    for name in ("dk", "dv"):
+        _fail(msgs, f"shifted queries {name}", np.abs(got[name] - ref[name][0]).max(), 1e-13)
+    return msgs
+
+
 def all_pins(fwd, decode):
     msgs = []
     for p in (pin_library_sdpa, pin_noise_one_hot, pin_identical_queries_zero,

@@ -163,3 +163,36 @@ def test_fwd_train_pin():
 
 def test_backward_rows_subset():
     assert pins.pin_backward_rows(_bwd()) == []
+
+
+def test_backward_varlen_pin():
+    assert pins.pin_bwd_varlen(oracle.ref_bwd_varlen, oracle.ref_fwd_train_varlen) == []
+
+
+def test_backward_varlen_pin_catches_a_wrong_offset():
+    """An oracle that aligns a sequence's queries with its first keys (not its last)
+    fails the halo and fewer-keys checks."""
+    def top_left(q_sig, q_noise, k, v, lam, gate, d_out, cu_q, cu_k, *, window, **kw):
+        cu_q = np.asarray(cu_q)
+        cu_k = np.asarray(cu_k)
+        g = {n: [] for n in ("dq_sig", "dq_noise", "dlam", "dgate", "dk", "dv")}
+        for i in range(len(cu_q) - 1):
+            lq, lk = cu_q[i + 1] - cu_q[i], cu_k[i + 1] - cu_k[i]
+            q = slice(cu_q[i], cu_q[i + 1])
+            kk = slice(cu_k[i], cu_k[i + 1])
+            # queries at key positions 0..lq-1, keys padded or cut to lq rows
+            def fit(a):
+                out = np.zeros((lq,) + a.shape[1:], a.dtype)
+                n = min(lq, lk)
+                out[:n] = a[:n]
+                return out
+            r = oracle.ref_bwd(q_sig[q][None], q_noise[q][None], fit(k[kk])[None],
+                               fit(v[kk])[None], lam[q][None], gate[q][None], d_out[q][None],
+                               window=window, **kw)
+            for n in ("dq_sig", "dq_noise", "dlam", "dgate"):
+                g[n].append(r[n][0])
+            for n in ("dk", "dv"):
+                g[n].append(r[n][0][:lk] if lk <= lq else
+                            np.concatenate([r[n][0], np.zeros((lk - lq,) + r[n].shape[2:])]))
+        return {n: np.concatenate(v) for n, v in g.items()}
+    assert pins.pin_bwd_varlen(top_left, oracle.ref_fwd_train_varlen) != []
