@@ -16,7 +16,8 @@ GDA_BF16, GDA_F32 = 0, 1
 GDA_LAMBDA_LOGITS, GDA_GATE_LOGITS = 1, 2
 
 EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_fwd_varlen",
-            "gda_fwd_train", "gda_bwd", "gda_bwd_workspace_bytes", "gda_decode_latent",
+            "gda_fwd_train", "gda_bwd", "gda_bwd_workspace_bytes", "gda_fwd_train_varlen",
+            "gda_bwd_varlen", "gda_decode_latent",
             "gda_decode_latent_workspace_bytes", "gda_status_string", "gda_last_error")
 
 
@@ -63,6 +64,12 @@ def load() -> ctypes.CDLL:
     lib.gda_bwd.restype = i32
     lib.gda_bwd.argtypes = ([vp] * 16 + [i32] * 8 + [i32, ctypes.POINTER(Options), vp,
                                                      ctypes.c_size_t, vp])
+    lib.gda_fwd_train_varlen.restype = i32
+    lib.gda_fwd_train_varlen.argtypes = [vp] * 12 + [i32] * 9 + [i32, ctypes.POINTER(Options),
+                                                                 vp]
+    lib.gda_bwd_varlen.restype = i32
+    lib.gda_bwd_varlen.argtypes = ([vp] * 18 + [i32] * 10 + [i32, ctypes.POINTER(Options), vp,
+                                                             ctypes.c_size_t, vp])
     lib.gda_decode_latent_workspace_bytes.restype = ctypes.c_size_t
     lib.gda_decode_latent_workspace_bytes.argtypes = [i32] * 5
     lib.gda_decode_latent.restype = i32
@@ -164,3 +171,25 @@ def bwd_raw(q_sig, q_noise, k, v, lam, gate, h_sig, h_noise, lse, d_out, dq_sig,
                           dq_noise, dk, dv_out, dlam, dgate, B, L, S, N, Hkv, dqk, dv, window,
                           dtype, ctypes.byref(opts) if opts is not None else None, workspace,
                           workspace_bytes, stream)
+
+
+def fwd_train_varlen_raw(q_sig, q_noise, k, v, lam, gate, out, h_sig, h_noise, lse, cu_q, cu_k,
+                         nseq, max_seqlen_q, total_q, S, N, Hkv, dqk, dv, window, dtype, opts,
+                         stream) -> int:
+    """Direct call of gda_fwd_train_varlen (opts an Options or None)."""
+    return load().gda_fwd_train_varlen(q_sig, q_noise, k, v, lam, gate, out, h_sig, h_noise, lse,
+                                       cu_q, cu_k, nseq, max_seqlen_q, total_q, S, N, Hkv, dqk,
+                                       dv, window, dtype,
+                                       ctypes.byref(opts) if opts is not None else None, stream)
+
+
+def bwd_varlen_raw(q_sig, q_noise, k, v, lam, gate, h_sig, h_noise, lse, d_out, dq_sig, dq_noise,
+                   dk, dv_out, dlam, dgate, cu_q, cu_k, nseq, max_seqlen_q, max_seqlen_k, total_q,
+                   S, N, Hkv, dqk, dv, window, dtype, opts, workspace, workspace_bytes,
+                   stream) -> int:
+    """Direct call of gda_bwd_varlen (opts an Options or None)."""
+    return load().gda_bwd_varlen(q_sig, q_noise, k, v, lam, gate, h_sig, h_noise, lse, d_out,
+                                 dq_sig, dq_noise, dk, dv_out, dlam, dgate, cu_q, cu_k, nseq,
+                                 max_seqlen_q, max_seqlen_k, total_q, S, N, Hkv, dqk, dv, window,
+                                 dtype, ctypes.byref(opts) if opts is not None else None,
+                                 workspace, workspace_bytes, stream)

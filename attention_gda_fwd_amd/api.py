@@ -274,3 +274,75 @@ def gda_bwd(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor, v: torc
         _lib.options(scale, lambda_logits, gate_logits), workspace.data_ptr(), workspace.numel(),
         _stream(dev)))
     return grads
+
+
+def _packed_shapes(name, q_sig, q_noise, k, v, lam, gate, cu_seqlens_q, cu_seqlens_k):
+    if q_sig.dim() != 3 or q_noise.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError(f"{name}: q_sig, q_noise, k, v must be 3-D (packed rows)")
+    Tq, S, dqk = q_sig.shape
+    N, Tk, Hkv, dv = q_noise.shape[1], k.shape[0], k.shape[1], v.shape[2]
+    dev, dt = q_sig.device, q_sig.dtype
+    _dtype_code(q_sig)
+    if dev.type != "cuda":
+        raise ValueError(f"{name}: tensors must be on a HIP (cuda) device")
+    nseq = cu_seqlens_q.numel() - 1
+    _check("q_sig", q_sig, (Tq, S, dqk), dt, dev)
+    _check("q_noise", q_noise, (Tq, N, dqk), dt, dev)
+    _check("k", k, (Tk, Hkv, dqk), dt, dev)
+    _check("v", v, (Tk, Hkv, dv), dt, dev)
+    _check("lam", lam, (Tq, S), dt, dev)
+    _check("gate", gate, (Tq, S, dv), dt, dev)
+    _check("cu_seqlens_q", cu_seqlens_q, (nseq + 1,), torch.int32, dev)
+    _check("cu_seqlens_k", cu_seqlens_k, (nseq + 1,), torch.int32, dev)
+    return Tq, Tk, S, N, Hkv, dqk, dv, nseq, dev, dt
+
+
+def gda_fwd_train_varlen(q_sig, q_noise, k, v, lam, gate, cu_seqlens_q, cu_seqlens_k,
+                         max_seqlen_q: int, window: int = 0, scale: float | None = None,
+                         lambda_logits: bool = False, gate_logits: bool = False):
+    """Packed-sequence training forward (bf16): (out [Tq,S,dv], h_sig [Tq,S,dv],
+    h_noise [Tq,N,dv], lse float32 [S+N,Tq]); sequences as gda_fwd_varlen."""
+    Tq, Tk, S, N, Hkv, dqk, dv, nseq, dev, dt = _packed_shapes(
+        "gda_fwd_train_varlen", q_sig, q_noise, k, v, lam, gate, cu_seqlens_q, cu_seqlens_k)
+    out = torch.empty((Tq, S, dv), dtype=dt, device=dev)
+    h_sig = torch.empty((Tq, S, dv), dtype=dt, device=dev)
+    h_noise = torch.empty((Tq, N, dv), dtype=dt, device=dev)
+    lse = torch.empty((S + N, Tq), dtype=torch.float32, device=dev)
+    _lib.check(_lib.fwd_train_varlen_raw(
+        q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), out.data_ptr(), h_sig.data_ptr(), h_noise.data_ptr(), lse.data_ptr(),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), nseq, int(max_seqlen_q), Tq, S, N,
+        Hkv, dqk, dv, int(window), _dtype_code(q_sig),
+        _lib.options(scale, lambda_logits, gate_logits), _stream(dev)))
+    return out, h_sig, h_noise, lse
+
+
+def gda_bwd_varlen(q_sig, q_noise, k, v, lam, gate, h_sig, h_noise, lse, d_out, cu_seqlens_q,
+                   cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, window: int = 0,
+                   scale: float | None = None, lambda_logits: bool = False,
+                   gate_logits: bool = False, workspace: torch.Tensor | None = None) -> dict:
+    """Packed-sequence backward (bf16) of gda_fwd_train_varlen: dict(dq_sig, dq_noise, dk,
+    dv, dlam, dgate) shaped like the packed inputs."""
+    Tq, Tk, S, N, Hkv, dqk, dv, nseq, dev, dt = _packed_shapes(
+        "gda_bwd_varlen", q_sig, q_noise, k, v, lam, gate, cu_seqlens_q, cu_seqlens_k)
+    _check("h_sig", h_sig, (Tq, S, dv), dt, dev)
+    _check("h_noise", h_noise, (Tq, N, dv), dt, dev)
+    _check("lse", lse, (S + N, Tq), torch.float32, dev)
+    _check("d_out", d_out, (Tq, S, dv), dt, dev)
+    shapes = dict(dq_sig=(Tq, S, dqk), dq_noise=(Tq, N, dqk), dk=(Tk, Hkv, dqk),
+                  dv=(Tk, Hkv, dv), dlam=(Tq, S), dgate=(Tq, S, dv))
+    grads = {n: torch.empty(sh, dtype=dt, device=dev) for n, sh in shapes.items()}
+    need = _lib.bwd_workspace_bytes(1, Tq, S, N, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("workspace", workspace, (workspace.numel(),), torch.uint8, dev)
+    _lib.check(_lib.bwd_varlen_raw(
+        q_sig.data_ptr(), q_noise.data_ptr(), k.data_ptr(), v.data_ptr(), lam.data_ptr(),
+        gate.data_ptr(), h_sig.data_ptr(), h_noise.data_ptr(), lse.data_ptr(), d_out.data_ptr(),
+        grads["dq_sig"].data_ptr(), grads["dq_noise"].data_ptr(), grads["dk"].data_ptr(),
+        grads["dv"].data_ptr(), grads["dlam"].data_ptr(), grads["dgate"].data_ptr(),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), nseq, int(max_seqlen_q),
+        int(max_seqlen_k), Tq, S, N, Hkv, dqk, dv, int(window), _dtype_code(q_sig),
+        _lib.options(scale, lambda_logits, gate_logits), workspace.data_ptr(), workspace.numel(),
+        _stream(dev)))
+    return grads

@@ -296,6 +296,63 @@ gda_status gda_fwd_train(const void* q_sig, const void* q_noise, const void* k, 
   a.h_sig = h_sig;
   a.h_noise = h_noise;
   a.lse = lse;
+  a.lse_b = (int64_t)(S + N) * L;  // lse [B, S+N, L]
+  a.lse_q = 0;
+  a.lse_h = L;
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
+  if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
+    return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  return from_hip(gda::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+gda_status gda_fwd_train_varlen(const void* q_sig, const void* q_noise, const void* k,
+                                const void* v, const void* lambda, const void* gate, void* out,
+                                void* h_sig, void* h_noise, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int nseq, int max_seqlen_q, int total_q, int S, int N, int Hkv,
+                                int dqk, int dv, int window, gda_dtype dtype,
+                                const gda_options* opts, void* stream) {
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out || !h_sig || !h_noise ||
+      !lse || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null pointer");
+  gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, out);
+  if (st != GDA_SUCCESS) return st;
+  if (!aligned(h_sig, 16) || !aligned(h_noise, 16) || !aligned(lse, 4) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(GDA_ERROR_INVALID_ARGUMENT,
+                "h_sig, h_noise 16-byte, lse and cu_seqlens 4-byte aligned");
+  st = validate_common(nseq, max_seqlen_q, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  if (total_q < 1) return fail(GDA_ERROR_INVALID_ARGUMENT, "total_q must be >= 1");
+  if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "the training form is bf16 only");
+  if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+  gda::FwdArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.gate = gate;
+  a.out = out;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.B = nseq;
+  a.L = max_seqlen_q;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  a.plan = make_plan(S, N, Hkv);
+  a.h_sig = h_sig;
+  a.h_noise = h_noise;
+  a.lse = lse;
+  a.lse_b = 0;  // lse [S+N, total_q]
+  a.lse_q = 1;
+  a.lse_h = total_q;
   if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
     return st;
   if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
@@ -355,6 +412,80 @@ gda_status gda_bwd(const void* q_sig, const void* q_noise, const void* k, const 
   a.dqk = dqk;
   a.dv = dv;
   a.window = window;
+  a.Lk_max = L;
+  a.rows = (int64_t)B * L;
+  a.lse_b = (int64_t)(S + N) * L;  // lse and delta [B, S+N, L]
+  a.lse_q = 0;
+  a.lse_h = L;
+  if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+    return st;
+  if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "the backward is bf16 only");
+  if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  return from_hip(gda::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+gda_status gda_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                          const void* lambda, const void* gate, const void* h_sig,
+                          const void* h_noise, const float* lse, const void* d_out,
+                          void* dq_sig, void* dq_noise, void* dk, void* dv_out, void* dlambda,
+                          void* dgate, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int nseq, int max_seqlen_q, int max_seqlen_k, int total_q, int S,
+                          int N, int Hkv, int dqk, int dv, int window, gda_dtype dtype,
+                          const gda_options* opts, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !h_sig || !h_noise || !lse ||
+      !d_out || !dq_sig || !dq_noise || !dk || !dv_out || !dlambda || !dgate || !workspace ||
+      !cu_seqlens_q || !cu_seqlens_k)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "null pointer");
+  gda_status st = check_alignment(q_sig, q_noise, k, v, lambda, gate, h_sig);
+  if (st != GDA_SUCCESS) return st;
+  if ((st = check_alignment(h_noise, d_out, dq_sig, dq_noise, dk, dv_out, dgate)) != GDA_SUCCESS)
+    return st;
+  if (!aligned(dlambda, 16) || !aligned(workspace, 256) || !aligned(lse, 4) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(GDA_ERROR_INVALID_ARGUMENT,
+                "dlambda must be 16-byte, workspace 256-byte, lse and cu_seqlens 4-byte aligned");
+  st = validate_common(nseq, max_seqlen_q, S, N, Hkv, dqk, dv, window, dtype);
+  if (st != GDA_SUCCESS) return st;
+  if (max_seqlen_k < 1 || total_q < 1)
+    return fail(GDA_ERROR_INVALID_ARGUMENT, "max_seqlen_k and total_q must be >= 1");
+  if (workspace_bytes < gda::bwd_workspace_bytes(1, total_q, S, N, dv))
+    return fail(GDA_ERROR_INVALID_ARGUMENT,
+                "workspace smaller than gda_bwd_workspace_bytes(1, total_q, ...)");
+  gda::BwdArgs a;
+  a.q_sig = q_sig;
+  a.q_noise = q_noise;
+  a.k = k;
+  a.v = v;
+  a.lam = lambda;
+  a.gate = gate;
+  a.h_sig = h_sig;
+  a.h_noise = h_noise;
+  a.lse = lse;
+  a.d_out = d_out;
+  a.dq_sig = dq_sig;
+  a.dq_noise = dq_noise;
+  a.dk = dk;
+  a.dv_out = dv_out;
+  a.dlam = dlambda;
+  a.dgate = dgate;
+  a.workspace = workspace;
+  a.B = nseq;
+  a.L = max_seqlen_q;
+  a.S = S;
+  a.N = N;
+  a.Hkv = Hkv;
+  a.dqk = dqk;
+  a.dv = dv;
+  a.window = window;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.Lk_max = max_seqlen_k;
+  a.rows = total_q;
+  a.lse_b = 0;  // lse and delta [S+N, total_q]
+  a.lse_q = 1;
+  a.lse_h = total_q;
   if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
     return st;
   if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "the backward is bf16 only");

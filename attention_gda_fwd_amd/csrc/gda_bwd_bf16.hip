@@ -101,17 +101,20 @@ bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ h_sig,
                 const uint16_t* __restrict__ h_noise, uint16_t* __restrict__ dgate,
                 uint16_t* __restrict__ dlam, uint16_t* __restrict__ do_sig,
-                uint16_t* __restrict__ do_noise, float* __restrict__ delta, int64_t items, int L,
-                int S, int N, int flags) {
+                uint16_t* __restrict__ do_noise, float* __restrict__ delta, int64_t items,
+                int Lrow, int64_t dl_b, int64_t dl_h, int S, int N, int flags) {
   constexpr int CPL = DV / 64;
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
   if (item >= items) return;
   const int64_t row = item / N;
   const int j = (int)(item - row * N);
-  const int64_t b = row / L;
-  const int t = (int)(row - b * L);
-  const int g = S / N, HT = S + N;
+  // delta of head hd for token row at delta[b * dl_b + hd * dl_h + t], with b, t
+  // the row's (sequence, position) for a batch of Lrow-row sequences (packed
+  // sequences pass Lrow = all rows: b = 0, t = row).
+  const int64_t b = row / Lrow;
+  const int t = (int)(row - b * Lrow);
+  const int g = S / N;
   float hn[CPL], dn[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
@@ -147,7 +150,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__
       float dl = -pl;
       if (flags & kLambdaLogits) dl *= lm * (1.f - lm);
       dlam[row * S + i] = f32_to_bf16(dl);
-      delta[((int64_t)b * HT + i) * L + t] = pd;
+      delta[b * dl_b + i * dl_h + t] = pd;
     }
   }
   float pn = 0.f;
@@ -158,7 +161,7 @@ bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__
     pn += bf16_to_f32(db) * hn[c];
   }
   pn = wave_sum(pn);
-  if (lane == 0) delta[((int64_t)b * HT + S + j) * L + t] = pn;
+  if (lane == 0) delta[b * dl_b + (S + j) * dl_h + t] = pn;
 }
 
 // One query head's view: its Q and dO rows, and its KV head.
@@ -169,25 +172,52 @@ struct HeadRef {
   int kvh;
 };
 
-__device__ __forceinline__ HeadRef head_ref(int hd, int64_t b, int L, int S, int N, int Hkv,
+// qbase: the sequence's first query row.
+__device__ __forceinline__ HeadRef head_ref(int hd, int64_t qbase, int S, int N, int Hkv,
                                             int DQK, int DV, const uint16_t* q_sig,
                                             const uint16_t* q_noise, const uint16_t* do_sig,
                                             const uint16_t* do_noise) {
   HeadRef r;
   if (hd < S) {
-    r.q = q_sig + ((int64_t)b * L * S + hd) * DQK;
-    r.dO = do_sig + ((int64_t)b * L * S + hd) * DV;
+    r.q = q_sig + (qbase * S + hd) * DQK;
+    r.dO = do_sig + (qbase * S + hd) * DV;
     r.qstride = (int64_t)S * DQK;
     r.ostride = (int64_t)S * DV;
     r.kvh = (hd * Hkv) / S;
   } else {
     const int j = hd - S;
-    r.q = q_noise + ((int64_t)b * L * N + j) * DQK;
-    r.dO = do_noise + ((int64_t)b * L * N + j) * DV;
+    r.q = q_noise + (qbase * N + j) * DQK;
+    r.dO = do_noise + (qbase * N + j) * DV;
     r.qstride = (int64_t)N * DQK;
     r.ostride = (int64_t)N * DV;
     r.kvh = (j * Hkv) / N;
   }
+  return r;
+}
+
+// Sequence b: Lq queries from packed row qbase, Lk keys from packed row kbase, its
+// local query t at key position qoff + t (packed sequences), or rows b*L .. of both
+// (a batch). Its lse and delta entries for head hd and local query t sit at
+// lbase + hd * lh + t.
+struct SeqRef {
+  int64_t qbase, kbase, lbase;
+  int Lq, Lk, qoff;
+};
+
+__device__ __forceinline__ SeqRef seq_ref(const int32_t* cu_q, const int32_t* cu_k, int b,
+                                          int L, int64_t lse_b, int lse_q) {
+  SeqRef r;
+  if (cu_q) {
+    r.qbase = cu_q[b];
+    r.Lq = cu_q[b + 1] - cu_q[b];
+    r.kbase = cu_k[b];
+    r.Lk = cu_k[b + 1] - cu_k[b];
+  } else {
+    r.qbase = r.kbase = (int64_t)b * L;
+    r.Lq = r.Lk = L;
+  }
+  r.qoff = r.Lk - r.Lq;
+  r.lbase = lse_b * b + lse_q * r.qbase;
   return r;
 }
 
@@ -245,9 +275,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
               const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
               const float* __restrict__ lse, const uint16_t* __restrict__ do_sig,
               const uint16_t* __restrict__ do_noise, const float* __restrict__ delta,
-              uint16_t* __restrict__ dq_sig, uint16_t* __restrict__ dq_noise, int B, int L,
+              uint16_t* __restrict__ dq_sig, uint16_t* __restrict__ dq_noise,
+              const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int B, int L,
               int S, int N, int Hkv, int window, int nqt, int groups, int heavy_first,
-              float c2, float scale) {
+              int64_t lse_b, int lse_q, int64_t lse_h, float c2, float scale) {
   using C = DqShape<DQK, DV>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];
   const int HT = S + N;
@@ -260,6 +291,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
   const int b = rem / (Hkv * groups);
   rem -= b * (Hkv * groups);
   const int h = rem / groups, grp = rem - (rem / groups) * groups;
+  const SeqRef sq = seq_ref(cu_q, cu_k, b, L, lse_b, lse_q);
+  const int q0 = qt * 64;  // this tile's first query of the sequence
+  if (q0 >= sq.Lq) return;  // past the sequence (whole workgroup, before any barrier)
   const int nh_kv = kv_head_count(h, S, N, Hkv);
   int first;
   if (NH == 2) {
@@ -274,13 +308,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
 #pragma unroll
   for (int u = 0; u < NH; ++u) {
     hd[u] = kv_head_member(h, first + u, S, N, Hkv);
-    hr[u] = head_ref(hd[u], b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
+    hr[u] = head_ref(hd[u], sq.qbase, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
   }
-  const int q0 = qt * 64;
   const int t0w = q0 + 16 * wave;
-  const int t = t0w + col;
-  const bool t_ok = t < L;
-  const int tq = min(t, L - 1);
+  const int t = t0w + col;  // this lane's query (local)
+  const bool t_ok = t < sq.Lq;
+  const int tq = min(t, sq.Lq - 1);
+  const int pos = sq.qoff + t;  // its key position
 
   bf16x8 qT[NH][C::KS], doT[NH][C::VS];
   float lse2[NH], dl[NH];
@@ -295,22 +329,24 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
     for (int kv = 0; kv < C::VS; ++kv)
       doT[u][kv] =
           __builtin_bit_cast(bf16x8, ldg16(hr[u].dO + tq * hr[u].ostride + 32 * kv + 8 * g4));
-    lse2[u] = lse[((int64_t)b * HT + hd[u]) * L + tq] * kLog2e;
-    dl[u] = delta[((int64_t)b * HT + hd[u]) * L + tq];
+    lse2[u] = lse[sq.lbase + hd[u] * lse_h + tq] * kLog2e;
+    dl[u] = delta[sq.lbase + hd[u] * lse_h + tq];
 #pragma unroll
     for (int d = 0; d < C::DT; ++d) dqT[u][d] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int k_lo = window ? max(0, q0 - window + 1) : 0;
-  const int k_hi = min(L - 1, q0 + 63);
-  const int kt0 = k_lo / 32, kt1 = k_hi / 32;
-  const uint16_t* kbase = kg + ((int64_t)b * L * Hkv + h) * DQK;
-  const uint16_t* vbase = vg + ((int64_t)b * L * Hkv + h) * DV;
+  // Keys visible to the tile's queries (key positions qoff + q0 ..); none when every
+  // query sits at a negative position.
+  const int k_lo = window ? max(0, sq.qoff + q0 - window + 1) : 0;
+  const int k_hi = sq.qoff + min(q0 + 63, sq.Lq - 1);
+  const int kt0 = k_lo / 32, kt1 = k_hi >= 0 ? k_hi / 32 : kt0 - 1;
+  const uint16_t* kbase = kg + (sq.kbase * Hkv + h) * DQK;
+  const uint16_t* vbase = vg + (sq.kbase * Hkv + h) * DV;
   const int64_t kstride = (int64_t)Hkv * DQK, vstride = (int64_t)Hkv * DV;
 
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(const lds_void*)smem;
   auto issue = [&](int kt, int buf) {
-    const int rows_ok = min(32, L - kt * 32);
+    const int rows_ok = min(32, sq.Lk - kt * 32);  // >= 1: kt * 32 <= k_hi <= Lk - 1
     const uint32_t base = smem_lds + (uint32_t)(buf * C::TILE);
     copy_rows<DQK * 2, C::KROW, C::KBLK>(kbase + (int64_t)kt * 32 * kstride,
                                          (uint32_t)(kstride * 2), rows_ok, base, wave, lane);
@@ -319,7 +355,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
                                         lane);
   };
 
-  issue(kt0, 0);
+  if (kt0 <= kt1) issue(kt0, 0);
   for (int kt = kt0; kt <= kt1; ++kt) {
     const int buf = (kt - kt0) & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile kt have landed
@@ -329,7 +365,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
     const unsigned char* Vl = Kl + C::V_OFF;
     const int k0 = kt * 32;
     // Is any key of this tile visible to a query of this wave? (wave-uniform)
-    const bool live = k0 <= t0w + 15 && (!window || k0 + 31 >= t0w - window + 1);
+    const int p0 = sq.qoff + t0w;  // the wave's first query position
+    const bool live = k0 <= p0 + 15 && (!window || k0 + 31 >= p0 - window + 1);
     if (live) {
       // One 16-key half at a time: its scores and dP are dead once its dS is packed.
       bf16x8 dsb[NH];
@@ -356,7 +393,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = k0 + 16 * kb + 4 * g4 + r;
-          const bool vis = t_ok && key <= t && (!window || t - key < window);
+          const bool vis = t_ok && key <= pos && (!window || pos - key < window);
 #pragma unroll
           for (int u = 0; u < NH; ++u) {
             const float p = vis ? fast_exp2(fmaf(sT[u][r], c2, -lse2[u])) : 0.f;
@@ -375,8 +412,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q
   if (t_ok) {
 #pragma unroll
     for (int u = 0; u < NH; ++u) {
-      uint16_t* dst = hd[u] < S ? dq_sig + (((int64_t)b * L + t) * S + hd[u]) * DQK
-                                : dq_noise + (((int64_t)b * L + t) * N + hd[u] - S) * DQK;
+      uint16_t* dst = hd[u] < S ? dq_sig + ((sq.qbase + t) * S + hd[u]) * DQK
+                                : dq_noise + ((sq.qbase + t) * N + hd[u] - S) * DQK;
       store_col_row<C::DT>(dst, g4, dqT[u], scale);
     }
   }
@@ -404,27 +441,30 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                 const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                 const float* __restrict__ lse, const uint16_t* __restrict__ do_sig,
                 const uint16_t* __restrict__ do_noise, const float* __restrict__ delta,
-                uint16_t* __restrict__ dk, uint16_t* __restrict__ dvo, int B, int L, int S,
-                int N, int Hkv, int window, float c2, float scale) {
+                uint16_t* __restrict__ dk, uint16_t* __restrict__ dvo,
+                const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int B, int L,
+                int S, int N, int Hkv, int window, int64_t lse_b, int lse_q, int64_t lse_h,
+                float c2, float scale) {
   using C = DkvShape<DQK, DV>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::TILE];
-  const int HT = S + N;
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g4 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int per = B * Hkv;
   const int kt = blockIdx.x / per;  // key tiles in order: the first ones see the most queries
   const int rem = blockIdx.x - kt * per;
   const int b = rem / Hkv, h = rem - (rem / Hkv) * Hkv;
-  const int k0w = kt * 64 * KT + 16 * KT * wave;  // this wave's first key
+  const SeqRef sq = seq_ref(cu_q, cu_k, b, L, lse_b, lse_q);
+  if (kt * 64 * KT >= sq.Lk) return;  // past the sequence's keys (whole workgroup)
+  const int k0w = kt * 64 * KT + 16 * KT * wave;  // this wave's first key (local)
   int s[KT];  // this lane's key in each column tile
   bf16x8 kT[KT][C::KS], vT[KT][C::VS];
   floatx4 dkT[KT][C::DT], dvT[KT][C::VT];
 #pragma unroll
   for (int kc = 0; kc < KT; ++kc) {
     s[kc] = k0w + 16 * kc + col;
-    const int sk = min(s[kc], L - 1);
-    const uint16_t* kr = kg + (((int64_t)b * L + sk) * Hkv + h) * DQK;
-    const uint16_t* vr = vg + (((int64_t)b * L + sk) * Hkv + h) * DV;
+    const int sk = min(s[kc], sq.Lk - 1);
+    const uint16_t* kr = kg + ((sq.kbase + sk) * Hkv + h) * DQK;
+    const uint16_t* vr = vg + ((sq.kbase + sk) * Hkv + h) * DV;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
       kT[kc][ks] = __builtin_bit_cast(bf16x8, ldg16(kr + 32 * ks + 8 * g4));
@@ -438,9 +478,12 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   }
 
   const int nh = kv_head_count(h, S, N, Hkv);
-  const int q_lo = kt * 64 * KT;
-  const int q_hi = window ? min(L - 1, q_lo + 64 * KT - 1 + window - 1) : L - 1;
-  const int qb0 = q_lo / 32, nqb = q_hi / 32 - qb0 + 1;
+  // Local queries that see one of the tile's keys (query t sits at position qoff + t);
+  // none, and zero gradients, when that range is empty.
+  const int q_lo = max(0, kt * 64 * KT - sq.qoff);
+  const int q_hi = window ? min(sq.Lq - 1, kt * 64 * KT + 64 * KT - 1 + window - 1 - sq.qoff)
+                          : sq.Lq - 1;
+  const int qb0 = q_lo / 32, nqb = q_hi >= q_lo ? q_hi / 32 - qb0 + 1 : 0;
   const int n_items = nh * nqb;
 
   // Q and dO rows arrive by direct global -> LDS copies; the 32 rows' lse (log2
@@ -451,8 +494,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   auto issue = [&](int it, int buf) {
     const int hd = head_of_item(it);
     const int qb = qb0 + (it - (it / nqb) * nqb);
-    const HeadRef hr = head_ref(hd, b, L, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig, do_noise);
-    const int rows_ok = min(32, L - qb * 32);
+    const HeadRef hr = head_ref(hd, sq.qbase, S, N, Hkv, DQK, DV, q_sig, q_noise, do_sig,
+                                do_noise);
+    const int rows_ok = min(32, sq.Lq - qb * 32);  // >= 1: qb * 32 <= q_hi
     const uint32_t base = smem_lds + (uint32_t)(buf * C::TILE);
     copy_rows<DQK * 2, C::QROW, C::QBLK>(hr.q + (int64_t)qb * 32 * hr.qstride,
                                          (uint32_t)(hr.qstride * 2), rows_ok, base, wave, lane);
@@ -460,8 +504,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                                         (uint32_t)(hr.ostride * 2), rows_ok, base + C::O_OFF,
                                         wave, lane);
     if (tid < 64) {
-      const int q = min(qb * 32 + (tid & 31), L - 1);
-      const int64_t at = ((int64_t)b * HT + hd) * L + q;
+      const int q = min(qb * 32 + (tid & 31), sq.Lq - 1);
+      const int64_t at = sq.lbase + hd * lse_h + q;
       stg_s = tid < 32 ? lse[at] * kLog2e : delta[at];
     }
   };
@@ -469,8 +513,10 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     if (tid < 64) *(float*)(smem + buf * C::TILE + C::L_OFF + 4 * tid) = stg_s;
   };
 
-  issue(0, 0);  // n_items >= 1: every KV head has a signal head and a query block
-  store_scalars(0);
+  if (n_items > 0) {
+    issue(0, 0);
+    store_scalars(0);
+  }
   for (int it = 0; it < n_items; ++it) {
     const int buf = it & 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of item it have landed
@@ -481,7 +527,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     const float* sL = (const float*)(Ql + C::L_OFF);
     const float* sD = (const float*)(Ql + C::D_OFF);
     const int q0 = (qb0 + (it - (it / nqb) * nqb)) * 32;
-    const bool live = k0w <= q0 + 31 && (!window || q0 <= k0w + 16 * KT - 2 + window);
+    const int p0 = sq.qoff + q0;  // the block's first query position
+    const bool live = k0w <= p0 + 31 && (!window || p0 <= k0w + 16 * KT - 2 + window);
     if (live) {
       floatx4 sc[KT][2], dp[KT][2];
 #pragma unroll
@@ -514,7 +561,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
           const float l2 = sL[qi], dl = sD[qi];
 #pragma unroll
           for (int kc = 0; kc < KT; ++kc) {
-            const bool vis = s[kc] < L && q < L && s[kc] <= q && (!window || q - s[kc] < window);
+            const int qp = sq.qoff + q;  // the query's key position
+            const bool vis = s[kc] < sq.Lk && q < sq.Lq && s[kc] <= qp &&
+                             (!window || qp - s[kc] < window);
             const float p = vis ? fast_exp2(fmaf(sc[kc][qt][r], c2, -l2)) : 0.f;
             pb[kc][4 * qt + r] = (__bf16)p;
             dsb[kc][4 * qt + r] = (__bf16)(p * (dp[kc][qt][r] - dl));
@@ -537,20 +586,22 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   }
 #pragma unroll
   for (int kc = 0; kc < KT; ++kc)
-    if (s[kc] < L) {
-      store_col_row<C::DT>(dk + (((int64_t)b * L + s[kc]) * Hkv + h) * DQK, g4, dkT[kc], scale);
-      store_col_row<C::VT>(dvo + (((int64_t)b * L + s[kc]) * Hkv + h) * DV, g4, dvT[kc], 1.f);
+    if (s[kc] < sq.Lk) {
+      store_col_row<C::DT>(dk + ((sq.kbase + s[kc]) * Hkv + h) * DQK, g4, dkT[kc], scale);
+      store_col_row<C::VT>(dvo + ((sq.kbase + s[kc]) * Hkv + h) * DV, g4, dvT[kc], 1.f);
     }
 }
 
 template <int DQK, int DV>
 hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
-  const int HT = a.S + a.N;
-  const int64_t items = (int64_t)a.B * a.L * a.N;
+  // a.B sequences of at most a.L queries and a.Lk_max keys (a batch: a.Lk_max = a.L).
+  const int64_t items = (int64_t)a.rows * a.N;
   const int64_t prep_blocks = (items + 3) / 4;
   const int nqt = (a.L + 63) / 64;
   const int64_t dq_blocks = (int64_t)nqt * a.B * a.Hkv;  // per head group
-  const int64_t dkv_blocks = (int64_t)((a.L + 64 * kDkvTiles - 1) / (64 * kDkvTiles)) * a.B * a.Hkv;
+  const int64_t dkv_blocks =
+      (int64_t)((a.Lk_max + 64 * kDkvTiles - 1) / (64 * kDkvTiles)) * a.B * a.Hkv;
+  const int HT = a.S + a.N;
   if (prep_blocks > 0x7fffffff || dq_blocks * (HT / a.Hkv + 2) > 0x7fffffff ||
       dkv_blocks > 0x7fffffff)
     return hipErrorInvalidConfiguration;
@@ -558,7 +609,8 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
                      stream, (const uint16_t*)a.d_out, (const uint16_t*)a.gate,
                      (const uint16_t*)a.lam, (const uint16_t*)a.h_sig,
                      (const uint16_t*)a.h_noise, (uint16_t*)a.dgate, (uint16_t*)a.dlam,
-                     a.do_sig, a.do_noise, a.delta, items, a.L, a.S, a.N, a.flags);
+                     a.do_sig, a.do_noise, a.delta, items, a.cu_q ? a.rows : a.L,
+                     a.cu_q ? (int64_t)0 : (int64_t)HT * a.L, a.lse_h, a.S, a.N, a.flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int heavy_first = a.window == 0 ? 1 : 0;
@@ -575,8 +627,9 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
                        dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q_sig,
                        (const uint16_t*)a.q_noise, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        a.lse, a.do_sig, a.do_noise, a.delta, (uint16_t*)a.dq_sig,
-                       (uint16_t*)a.dq_noise, a.B, a.L, a.S, a.N, a.Hkv, a.window, nqt, pairs,
-                       heavy_first, a.scale_log2, a.scale);
+                       (uint16_t*)a.dq_noise, a.cu_q, a.cu_k, a.B, a.L, a.S, a.N, a.Hkv,
+                       a.window, nqt, pairs, heavy_first, a.lse_b, a.lse_q, a.lse_h,
+                       a.scale_log2, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -584,17 +637,18 @@ hipError_t launch_bwd_dims(const BwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dq_kernel<DQK, DV, 1>), dim3((unsigned)dq_blocks), dim3(kBwdThreads),
                        0, stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
-                       a.delta, (uint16_t*)a.dq_sig, (uint16_t*)a.dq_noise, a.B, a.L, a.S, a.N,
-                       a.Hkv, a.window, nqt, 1, heavy_first, a.scale_log2, a.scale);
+                       a.delta, (uint16_t*)a.dq_sig, (uint16_t*)a.dq_noise, a.cu_q, a.cu_k, a.B,
+                       a.L, a.S, a.N, a.Hkv, a.window, nqt, 1, heavy_first, a.lse_b, a.lse_q,
+                       a.lse_h, a.scale_log2, a.scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((bwd_dkdv_kernel<DQK, DV, kDkvTiles>), dim3((unsigned)dkv_blocks),
-                     dim3(kBwdThreads),
-                     0, stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.lse, a.do_sig, a.do_noise,
-                     a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv_out, a.B, a.L, a.S, a.N, a.Hkv,
-                     a.window, a.scale_log2, a.scale);
+                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q_sig,
+                     (const uint16_t*)a.q_noise, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     a.lse, a.do_sig, a.do_noise, a.delta, (uint16_t*)a.dk,
+                     (uint16_t*)a.dv_out, a.cu_q, a.cu_k, a.B, a.L, a.S, a.N, a.Hkv, a.window,
+                     a.lse_b, a.lse_q, a.lse_h, a.scale_log2, a.scale);
   return hipGetLastError();
 }
 
@@ -611,7 +665,7 @@ size_t bwd_workspace_bytes(int B, int L, int S, int N, int dv) {
 }
 
 hipError_t launch_bwd_bf16(BwdArgs a, hipStream_t stream) {
-  const size_t rows = (size_t)a.B * a.L;
+  const size_t rows = (size_t)a.rows;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   unsigned char* w = (unsigned char*)a.workspace;
   a.do_sig = (uint16_t*)w;

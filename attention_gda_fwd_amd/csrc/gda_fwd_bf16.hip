@@ -484,9 +484,11 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
 
 // A 4-wave workgroup is meant to share its CU with a second one (2 waves per
 // SIMD, so at most 256 registers per wave).
-// With TRAIN the kernel also writes what the backward takes from the forward
-// (batched calls only): each path's normalised output h_sig [B,L,S,dv] and
-// h_noise [B,L,N,dv], and each attention row's log-sum-exp lse [B,S+N,L].
+// With TRAIN the kernel also writes what the backward takes from the forward:
+// each path's normalised output h_sig [rows,S,dv] and h_noise [rows,N,dv], and
+// each attention row's log-sum-exp at lse[lse_b * b + lse_q * qbase + hd * lse_h + t]
+// for head hd and local query t: [B,S+N,L] for a batch (lse_b = (S+N) L, lse_q = 0,
+// lse_h = L), [S+N,Tq] for packed sequences (lse_b = 0, lse_q = 1, lse_h = Tq).
 
 template <class C, bool TRAIN>
 __global__ void __launch_bounds__(C::NT, C::NW == 4 ? 2 : 1)
@@ -497,7 +499,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                 const int32_t* __restrict__ cu_k, int B, int L, int S, int N, int Hkv,
                 int window, int units, int R, int nqt, int heavy_first, float c, int flags,
                 uint16_t* __restrict__ h_sig, uint16_t* __restrict__ h_noise,
-                float* __restrict__ lse) {
+                float* __restrict__ lse, int64_t lse_b, int lse_q, int64_t lse_h) {
   // K/V ring: two stages, each the tiles of the unit's KV heads.
   __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
   // Normalised noise output handed from the A waves to the B waves.
@@ -543,11 +545,25 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   x.kvB = C::TWO_KV ? u * R + 1 : u * R;
   x.q_lo = qoff + ql;
   x.q_hi = qoff + min(ql + C::BM, Lq) - 1;
+  const int64_t lbase = lse_b * b + lse_q * qbase;  // this sequence's lse origin
+  const int64_t lstride = lse_h;
   if (x.q_hi < 0) {  // every query before the first key (or no key): zeros
     const int nq = min(ql + C::BM, Lq) - ql;
     for (int idx = threadIdx.x; idx < nq * C::USIG * C::DV; idx += C::NT) {
       const int r = idx / (C::USIG * C::DV), rem = idx - r * (C::USIG * C::DV);
       out[((qbase + ql + r) * S + sig0) * C::DV + rem] = 0;
+      if constexpr (TRAIN) h_sig[((qbase + ql + r) * S + sig0) * C::DV + rem] = 0;
+    }
+    if constexpr (TRAIN) {
+      for (int idx = threadIdx.x; idx < nq * C::DV; idx += C::NT) {
+        const int r = idx / C::DV, e = idx - r * C::DV;
+        h_noise[((qbase + ql + r) * N + u) * C::DV + e] = 0;
+      }
+      for (int idx = threadIdx.x; idx < nq * (C::USIG + 1); idx += C::NT) {
+        const int r = idx / (C::USIG + 1), hh = idx - r * (C::USIG + 1);
+        const int hd = hh < C::USIG ? sig0 + hh : S + u;
+        lse[lbase + hd * lstride + ql + r] = -INFINITY;
+      }
     }
     return;
   }
@@ -618,14 +634,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
         store_head<C::DV>(out, row, S, sig0 + s, x.g4, st.o[s],
                           st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
       if constexpr (TRAIN) {
-        const int64_t lrow = (int64_t)b * (S + N);
         store_train_head<C::DV>(h_noise + (row * N + u) * C::DV,
-                                lse + (lrow + S + u) * L + tl, x.g4, st.o[NZ], inv_n,
-                                st.mref[NZ], st.lsum[NZ]);
+                                lse + lbase + (int64_t)(S + u) * lstride + tl, x.g4, st.o[NZ],
+                                inv_n, st.mref[NZ], st.lsum[NZ]);
 #pragma unroll
         for (int s = 0; s < C::ASIG; ++s)
           store_train_head<C::DV>(h_sig + (row * S + sig0 + s) * C::DV,
-                                  lse + (lrow + sig0 + s) * L + tl, x.g4, st.o[s],
+                                  lse + lbase + (int64_t)(sig0 + s) * lstride + tl, x.g4, st.o[s],
                                   st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, st.mref[s],
                                   st.lsum[s]);
       }
@@ -663,11 +678,11 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
         store_head<C::DV>(out, row, S, sig0 + b_first + s, x.g4, st.o[s],
                           st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
       if constexpr (TRAIN) {
-        const int64_t lrow = (int64_t)b * (S + N);
 #pragma unroll
         for (int s = 0; s < C::BSIG; ++s)
           store_train_head<C::DV>(h_sig + (row * S + sig0 + b_first + s) * C::DV,
-                                  lse + (lrow + sig0 + b_first + s) * L + tl, x.g4, st.o[s],
+                                  lse + lbase + (int64_t)(sig0 + b_first + s) * lstride + tl,
+                                  x.g4, st.o[s],
                                   st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, st.mref[s],
                                   st.lsum[s]);
       }
@@ -689,7 +704,7 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
                        (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L,
                        a.S, a.N, a.Hkv, a.window, a.plan.units, a.plan.R, nqt, heavy_first,
                        a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
-                       a.lse);
+                       a.lse, a.lse_b, a.lse_q, a.lse_h);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<C, false>), dim3((unsigned)grid), dim3(C::NT), 0,
                        stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
@@ -697,7 +712,7 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
                        (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L,
                        a.S, a.N, a.Hkv, a.window, a.plan.units, a.plan.R, nqt, heavy_first,
                        a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
-                       a.lse);
+                       a.lse, a.lse_b, a.lse_q, a.lse_h);
   return hipGetLastError();
 }
 

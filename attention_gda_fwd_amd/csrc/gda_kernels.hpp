@@ -34,11 +34,15 @@ struct FwdArgs {
   float scale_log2;  // log2(e) * softmax scale
   float scale;       // softmax scale (1 / sqrt(dqk) unless the caller gives one)
   int flags;         // GDA_LAMBDA_LOGITS | GDA_GATE_LOGITS
-  // Training form (all NULL otherwise; batched calls only): per-path outputs
-  // h_sig [B,L,S,dv], h_noise [B,L,N,dv] and row log-sum-exps lse [B,S+N,L].
+  // Training form (all NULL otherwise): per-path outputs h_sig [rows,S,dv],
+  // h_noise [rows,N,dv] and row log-sum-exps, head hd of local query t of
+  // sequence b at lse[lse_b * b + lse_q * (b's first query row) + hd * lse_h + t]:
+  // [B,S+N,L] for a batch, [S+N,Tq] for packed sequences.
   void* h_sig = nullptr;
   void* h_noise = nullptr;
   float* lse = nullptr;
+  int64_t lse_b = 0, lse_h = 0;
+  int lse_q = 0;
 };
 
 struct DecodeArgs {
@@ -97,6 +101,17 @@ struct BwdArgs {
   float scale_log2;
   float scale;
   int flags;
+  // Packed sequences (both NULL for a batch): B sequences, sequence i owning query
+  // rows cu_q[i] .. cu_q[i+1]-1 and key rows cu_k[i] .. cu_k[i+1]-1; L is then the
+  // longest query count and Lk_max the longest key count (a batch: Lk_max = L).
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int Lk_max = 0;
+  int64_t rows = 0;  // query rows in all (B * L for a batch)
+  // lse (and delta) of head hd, local query t of sequence b at
+  // lse_b * b + lse_q * (b's first query row) + hd * lse_h + t
+  int64_t lse_b = 0, lse_h = 0;
+  int lse_q = 0;
   // carved from the workspace by the launcher
   uint16_t* do_sig = nullptr;    // [B,L,S,dv]
   uint16_t* do_noise = nullptr;  // [B,L,N,dv]

@@ -215,6 +215,34 @@ gda_status gda_bwd(const void* q_sig, const void* q_noise, const void* k, const 
                    int dqk, int dv, int window, gda_dtype dtype, const gda_options* opts,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training over packed sequences (sequences and positions as gda_fwd_varlen; the
+ * chunk-with-halo form trains a sequence-sharded sliding-window layer).
+ * gda_fwd_train_varlen: gda_fwd_varlen plus h_sig [Tq,S,dv], h_noise [Tq,N,dv] and
+ *   lse [S+N, Tq] (total_q = Tq, the last cu_seqlens_q entry). A query at a
+ *   negative position gets zero path outputs and lse -inf.
+ * gda_bwd_varlen: gda_bwd over the packed tensors (gradients shaped like them:
+ *   dq_sig [Tq,S,dqk], dq_noise [Tq,N,dqk], dk [Tk,Hkv,dqk], dv_out [Tk,Hkv,dv],
+ *   dlambda [Tq,S], dgate [Tq,S,dv]); max_seqlen_k >= every sequence's key count.
+ *   Workspace: gda_bwd_workspace_bytes(1, total_q, S, N, dv) bytes. Keys no query
+ *   sees get zero gradients. Other rules as gda_bwd. */
+gda_status gda_fwd_train_varlen(const void* q_sig, const void* q_noise, const void* k,
+                                const void* v, const void* lambda, const void* gate, void* out,
+                                void* h_sig, void* h_noise, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int nseq, int max_seqlen_q, int total_q, int S, int N, int Hkv,
+                                int dqk, int dv, int window, gda_dtype dtype,
+                                const gda_options* opts, void* stream);
+
+gda_status gda_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, const void* v,
+                          const void* lambda, const void* gate, const void* h_sig,
+                          const void* h_noise, const float* lse, const void* d_out,
+                          void* dq_sig, void* dq_noise, void* dk, void* dv_out, void* dlambda,
+                          void* dgate, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int nseq, int max_seqlen_q, int max_seqlen_k, int total_q, int S,
+                          int N, int Hkv, int dqk, int dv, int window, gda_dtype dtype,
+                          const gda_options* opts, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Static, never-NULL description of a status code. */
 const char* gda_status_string(gda_status s);
 

@@ -226,6 +226,52 @@ def test_bwd_workspace_size():
     assert _lib.bwd_workspace_bytes(0, 1, 1, 1, 1) == 0
 
 
+def train_varlen(**kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, out=FAKE, hs=FAKE, hn=FAKE,
+             lse=FAKE, cq=FAKE, ck=FAKE, nseq=2, maxq=64, tq=100, S=8, N=2, Hkv=2, dqk=64,
+             dv=64, window=0, dtype=BF16)
+    a.update(kw)
+    return _lib.fwd_train_varlen_raw(*(a[n] for n in ("q", "qn", "k", "v", "lam", "gate", "out",
+                                                      "hs", "hn", "lse", "cq", "ck", "nseq",
+                                                      "maxq", "tq", "S", "N", "Hkv", "dqk", "dv",
+                                                      "window", "dtype")), None, None)
+
+
+def bwd_varlen(ws=FAKE, ws_bytes=1 << 30, **kw):
+    a = dict(q=FAKE, qn=FAKE, k=FAKE, v=FAKE, lam=FAKE, gate=FAKE, hs=FAKE, hn=FAKE, lse=FAKE,
+             do=FAKE, dqs=FAKE, dqn=FAKE, dk=FAKE, dvo=FAKE, dl=FAKE, dg=FAKE, cq=FAKE, ck=FAKE,
+             nseq=2, maxq=64, maxk=80, tq=100, S=8, N=2, Hkv=2, dqk=64, dv=64, window=0,
+             dtype=BF16)
+    a.update(kw)
+    return _lib.bwd_varlen_raw(*(a[n] for n in ("q", "qn", "k", "v", "lam", "gate", "hs", "hn",
+                                                "lse", "do", "dqs", "dqn", "dk", "dvo", "dl", "dg",
+                                                "cq", "ck", "nseq", "maxq", "maxk", "tq", "S", "N",
+                                                "Hkv", "dqk", "dv", "window", "dtype")),
+                               None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [dict(cq=None), dict(ck=FAKE + 2), dict(lse=None), dict(tq=0),
+                                dict(nseq=0), dict(maxq=0), dict(hs=FAKE + 8)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_fwd_train_varlen_invalid_arguments(kw):
+    assert train_varlen(**kw) == INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(cq=None), dict(ck=FAKE + 1), dict(maxk=0), dict(tq=0),
+                                dict(ws_bytes=100), dict(ws=FAKE + 16), dict(do=None)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_bwd_varlen_invalid_arguments(kw):
+    assert bwd_varlen(**kw) == INVALID
+
+
+def test_training_varlen_unsupported_and_device_check():
+    assert train_varlen(dtype=F32) == UNSUPPORTED
+    assert bwd_varlen(dqk=96, dv=96) == UNSUPPORTED
+    if not _gpu_visible():
+        assert train_varlen() == HIPERR
+        assert bwd_varlen() == HIPERR
+
+
 def test_decode_misaligned_lengths():
     assert dec(lens=FAKE + 2) == INVALID
     assert b"aligned" in _lib.load().gda_last_error()
