@@ -21,6 +21,8 @@
 //                    dV^T accumulators in registers; scores S = Q K^T so that P
 //                    and dS are directly the B operands of dV^T = dO^T P and
 //                    dK^T = Q^T dS.
+// A batch and packed sequences with a query offset (a sequence's queries are its
+// last Lq key positions) take the same kernels; keys no query sees get zeros.
 // No atomics: every output row is written by exactly one workgroup.
 #include "gda_device.hpp"
 #include "gda_kernels.hpp"

@@ -44,9 +44,9 @@ CSRC = os.path.join(ROOT, "attention_gda_fwd_amd", "csrc")
 # a 1 GiB elementwise copy in the same pass. A figure holds only for the kernel source it
 # was taken on (sha256 of the file below); once that file changes it is reported as null.
 MEASURED_TRAFFIC = {
-    "prefill": {"source": "gda_fwd_bf16.hip", "bytes": 2486893949,
-                "sha256": "b5685c7d2c186739944c2dfd0188ca90ec06b56ce98107d708ad99b8d344f316"},
-    "decode": {"source": "gda_decode_bf16.hip", "bytes": 21477996421,
+    "prefill": {"source": "gda_fwd_bf16.hip", "bytes": 2487100648,
+                "sha256": "ffe50f25eb82f9adc9d9e5403ad99a691d2febb9d0a85edc56bde40bc2154fd5"},
+    "decode": {"source": "gda_decode_bf16.hip", "bytes": 21478007003,
                "sha256": "c84bb16b28d53f926fb69ce8eeed59c281cb705a8de754fdd9e165d3b0765b14"},
 }
 
@@ -213,6 +213,43 @@ def bwd_setup(cfg, torch, gin):
     def bwd():
         api.gda_bwd(*args, *saved[1:], d_out, window=cfg.window, workspace=ws, grads=grads)
     return fwd_train, bwd
+
+
+def chunked_swa_setup(cfg, parts, torch, gin):
+    """A sliding-window workload cut into `parts` chunks, each chunk's keys starting with
+    the W-1 keys before it (packed sequences): returns (forward, training forward,
+    backward) launch functions over seeded device inputs."""
+    from attention_gda_fwd_amd import api
+    chunk, halo = cfg.L // parts, cfg.window - 1
+    lens_q = [chunk] * parts
+    lens_k = [chunk] + [chunk + halo] * (parts - 1)
+    x = gin.varlen_inputs(cfg.case_id, lens_q=lens_q, lens_k=lens_k, S=cfg.S, N=cfg.N,
+                          Hkv=cfg.Hkv, dqk=cfg.dqk, dv=cfg.dv, dtype=cfg.dtype,
+                          rope_dims=cfg.rope_dims)
+    d = {n: torch.from_numpy(a).view(torch.bfloat16).cuda() for n, a in x.items()
+         if n not in ("cu_q", "cu_k")}
+    cu_q = torch.from_numpy(x["cu_q"]).cuda()
+    cu_k = torch.from_numpy(x["cu_k"]).cuda()
+    mk = max(lens_k)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x6DA)
+    d_out = torch.randn(d["gate"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    args = [d[n] for n in ("q_sig", "q_noise", "k", "v", "lam", "gate")]
+    out = torch.empty_like(d["gate"])
+    saved = api.gda_fwd_train_varlen(*args, cu_q, cu_k, chunk, window=cfg.window)
+    ws = torch.empty(api.bwd_workspace_bytes(1, cfg.L, cfg.S, cfg.N, cfg.dv), dtype=torch.uint8,
+                     device="cuda")
+
+    def fwd():
+        api.gda_fwd_varlen(*args, cu_q, cu_k, chunk, window=cfg.window, out=out)
+
+    def train():
+        api.gda_fwd_train_varlen(*args, cu_q, cu_k, chunk, window=cfg.window)
+
+    def bwd():
+        api.gda_bwd_varlen(*args, *saved[1:], d_out, cu_q, cu_k, chunk, mk, window=cfg.window,
+                           workspace=ws)
+    return fwd, train, bwd
 
 
 def run_only(args, torch, C, gin, gda_fwd, gda_decode):
@@ -442,6 +479,17 @@ def main():
             flops_per_launch=cfg.bwd_flops())
         del fwd_train, bwd
         torch.cuda.empty_cache()
+    # the sliding-window layer as one rank of an 8-way sequence split would train it: 8
+    # chunks of 4096 queries, each with the previous 127 keys as a halo (packed sequences)
+    log("breakdown motif3_swa128_L32768 as 8 halo chunks: forward, training forward, backward")
+    fwd_c, train_c, bwd_c = chunked_swa_setup(C.MOTIF3_SWA, 8, torch, gin)
+    for tag, fn in (("", fwd_c), ("_train_fwd", train_c), (BWD_SUFFIX, bwd_c)):
+        ms = event_times(torch, fn, reps, 5)
+        med = float(np.median(ms))
+        breakdown["motif3_swa128_L32768_chunks8" + tag] = dict(
+            median_ms=round(med, 4), min_ms=round(min(ms), 4))
+    del fwd_c, train_c, bwd_c
+    torch.cuda.empty_cache()
 
     result = {
         "metric": "GDA fwd TFLOP/s (% bf16 MFMA peak) + decode HBM GB/s, 1xMI355X",
