@@ -223,7 +223,9 @@ __device__ __forceinline__ void chunk_qk(const Ctx& x, const State<C, NH>& st, c
   // Schedule: the first two K fragment reads, then each fragment's MFMAs
   // followed by the read of the fragment two steps ahead, so LDS latency hides
   // behind MFMAs instead of stalling them.
-  constexpr int AH = 2;  // K fragments in flight (more do not fit in registers)
+  // K fragments in flight: 2 for a three-head wave (more do not fit in its
+  // registers), 4 for a wave of two heads or fewer.
+  constexpr int AH = NACT <= 2 ? 4 : 2;
   __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
   for (int i = 0; i < 2 * C::KS; ++i) {
@@ -303,7 +305,7 @@ __device__ __forceinline__ void chunk_pv(const Ctx& x, State<C, NH>& st, const u
     for (int h = 0; h < NACT; ++h) st.o[h][db] = mfma_16x16x32(a, pb[h], st.o[h][db]);
   }
   // Schedule: V^T pairs for two channel blocks ahead of the MFMAs that use them.
-  constexpr int AV = 2;  // V^T channel blocks in flight
+  constexpr int AV = NACT <= 2 ? 3 : 2;  // V^T channel blocks in flight
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * AV, 1);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) {
@@ -319,7 +321,12 @@ __device__ __forceinline__ void consume_chunk(const Ctx& x, State<C, NH>& st, co
   if (!chunk_live(x, c0)) return;
   floatx4 s[NH][2];
   bf16x8 pb[NH];
+  // The score products run at raised wave priority: of the two waves sharing a
+  // SIMD, the one that reaches its matrix phase first keeps the matrix core while
+  // the other is in its softmax, which moves the two out of phase.
+  __builtin_amdgcn_s_setprio(1);
   chunk_qk<C, NH, NACT>(x, st, sK, cc, s);
+  __builtin_amdgcn_s_setprio(0);
   chunk_softmax<C, NH, NACT>(x, st, s, c0, pb);
   chunk_pv<C, NH, NACT>(x, st, sV, cc, pb);
 }
