@@ -220,11 +220,10 @@ __device__ __forceinline__ void chunk_qk(const Ctx& x, const State<C, NH>& st, c
       for (int h = 0; h < NACT; ++h) s[h][kb] = mfma_16x16x32(a, st.q[h][ks], s[h][kb]);
     }
   }
-  // Schedule: the first two K fragment reads, then each fragment's MFMAs
-  // followed by the read of the fragment two steps ahead, so LDS latency hides
-  // behind MFMAs instead of stalling them.
-  // K fragments in flight: 2 for a three-head wave (more do not fit in its
-  // registers), 4 for a wave of two heads or fewer.
+  // Schedule: the first AH K fragment reads, then each fragment's MFMAs followed
+  // by the read of the fragment AH steps ahead, so LDS latency hides behind MFMAs
+  // instead of stalling them. AH = 2 for a three-head wave (more do not fit in
+  // its registers), 4 for a wave of two heads or fewer.
   constexpr int AH = NACT <= 2 ? 4 : 2;
   __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll

@@ -45,7 +45,7 @@ CSRC = os.path.join(ROOT, "attention_gda_fwd_amd", "csrc")
 # was taken on (sha256 of the file below); once that file changes it is reported as null.
 MEASURED_TRAFFIC = {
     "prefill": {"source": "gda_fwd_bf16.hip", "bytes": 2486868918,
-                "sha256": "09780ad52824356be410e55d3a3a2751eb80eb1523613d73aaab03f5d46ec8ca"},
+                "sha256": "46ecd85b0c2dbdc5a7329652a05583534738150f71403bd240efbc0211ac8c57"},
     "decode": {"source": "gda_decode_bf16.hip", "bytes": 21478004315,
                "sha256": "c84bb16b28d53f926fb69ce8eeed59c281cb705a8de754fdd9e165d3b0765b14"},
 }
