@@ -314,7 +314,7 @@ def main():
     os.environ.setdefault("OMP_NUM_THREADS", str(host_threads()))
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by (batch, unit) with no exchange; see the design notes)",
+              "(the path would shard by (batch, unit) with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

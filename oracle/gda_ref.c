@@ -10,7 +10,7 @@
  *   2. the noise output is repeated g = S/N times by group;
  *   3. D_t = H_S,t - lambda_t (.) Repeat_g(H_N,t)      (equation D_t);
  *   4. the sigmoid gate G_t multiplies D_t elementwise (before W^O).
- * Readings taken where the pages are silent (each listed in the design notes):
+ * Readings taken where the pages are silent:
  *   - softmax scale 1/sqrt(dqk), dqk the contraction length;
  *   - signal head i reads KV head floor(i*Hkv/S), noise head j reads KV head
  *     floor(j*Hkv/N), and noise head j serves signal heads g*j .. g*j+g-1
