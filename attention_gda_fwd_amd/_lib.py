@@ -9,7 +9,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgda.so")
+# GDA_LIB names another build of the library to load (a host-sanitizer build).
+LIB_PATH = os.environ.get("GDA_LIB") or os.path.join(PKG, "libgda.so")
 
 GDA_SUCCESS, GDA_ERROR_INVALID_ARGUMENT, GDA_ERROR_UNSUPPORTED, GDA_ERROR_HIP = range(4)
 GDA_BF16, GDA_F32 = 0, 1

@@ -157,7 +157,7 @@ gda_status gda_fwd_ex(const void* q_sig, const void* q_noise, const void* k, con
   if (dtype == GDA_BF16) {
     if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
     if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
-      return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+      return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: (dqk, dv) not compiled");
   }
   if ((st = require_device()) != GDA_SUCCESS) return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -207,7 +207,7 @@ gda_status gda_decode_ex(const void* q_sig, const void* q_noise, const void* k_c
   if (dtype == GDA_BF16) {
     if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
     if (!gda::decode_bf16_supported(dqk, dv, a.plan))
-      return fail(GDA_ERROR_UNSUPPORTED, "bf16 decode: more than 16 query heads per unit");
+      return fail(GDA_ERROR_UNSUPPORTED, "bf16 decode: (dqk, dv) not compiled");
   }
   if ((st = require_device()) != GDA_SUCCESS) return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -252,7 +252,7 @@ gda_status gda_fwd_varlen(const void* q_sig, const void* q_noise, const void* k,
   if (dtype == GDA_BF16) {
     if ((st = check_bf16_dims(dqk, dv)) != GDA_SUCCESS) return st;
     if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
-      return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+      return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: (dqk, dv) not compiled");
   }
   if ((st = require_device()) != GDA_SUCCESS) return st;
   const hipStream_t s = (hipStream_t)stream;
@@ -302,7 +302,7 @@ gda_status gda_fwd_train(const void* q_sig, const void* q_noise, const void* k, 
   if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
     return st;
   if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
-    return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+    return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: (dqk, dv) not compiled");
   if ((st = require_device()) != GDA_SUCCESS) return st;
   return from_hip(gda::launch_fwd_bf16(a, (hipStream_t)stream));
 }
@@ -356,7 +356,7 @@ gda_status gda_fwd_train_varlen(const void* q_sig, const void* q_noise, const vo
   if ((st = apply_options(opts, dqk, &a.scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
     return st;
   if (!gda::fwd_bf16_supported(dqk, dv, a.plan))
-    return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: head layout not compiled");
+    return fail(GDA_ERROR_UNSUPPORTED, "bf16 prefill: (dqk, dv) not compiled");
   if ((st = require_device()) != GDA_SUCCESS) return st;
   return from_hip(gda::launch_fwd_bf16(a, (hipStream_t)stream));
 }

@@ -38,6 +38,55 @@ constexpr int NT = 64 * NW;
 constexpr int CK = 32;          // keys per chunk
 constexpr float kNoMax = -1e30f;
 
+// Which heads a decode workgroup computes. A unit (as the prefill groups heads:
+// with Hkv >= N, noise head u and the R = Hkv/N KV heads u*R .. of its signal
+// heads; with N > Hkv, KV head u with its NS = S/Hkv signal and NN = N/Hkv
+// noise heads) normally fits the 16 columns of one MFMA tile. When it does not,
+// it is split into K sub-units, each recomputing the noise head(s) it needs:
+//   mode 0: the whole unit (K = 1);
+//   mode 1: (R > 1) sub-unit k takes signal heads k*c .. of each phase's NS,
+//           with the unit's noise head;
+//   mode 2: (R = 1, g < 16) sub-unit k takes noise heads k*m .. k*m+m-1 of the
+//           unit with their m*g signal heads;
+//   mode 3: (R = 1, g >= 16) sub-unit k takes one noise head of the unit and a
+//           chunk of c of its g signal heads.
+// Phase p of a sub-unit attends KV head kv0 + p with signal heads
+// (kv0+p)*NS + off .. +ns-1 and, in phase 0, noise heads nb .. nb+nn-1.
+struct DecMap {
+  int nsub;  // sub-units per sequence
+  int K;     // sub-units per unit
+  int mode;
+  int c, m;  // chunk sizes of modes 1 and 3, and of mode 2
+  int g, NS, NN, R;
+};
+
+struct SubHeads {
+  int kv0, nb, nn, off, ns;
+};
+
+__device__ __forceinline__ SubHeads sub_heads(const DecMap& d, int v) {
+  const int u = v / d.K, k = v - (v / d.K) * d.K;
+  SubHeads h;
+  h.kv0 = u * d.R;
+  switch (d.mode) {
+    case 1:
+      h.nb = u; h.nn = 1; h.off = k * d.c; h.ns = min(d.c, d.NS - h.off);
+      break;
+    case 2:
+      h.nb = u * d.NN + k * d.m; h.nn = d.m; h.off = k * d.m * d.g; h.ns = d.m * d.g;
+      break;
+    case 3: {
+      const int kc_n = (d.g + d.c - 1) / d.c;
+      const int j = k / kc_n, kc = k - (k / kc_n) * kc_n;
+      h.nb = u * d.NN + j; h.nn = 1; h.off = j * d.g + kc * d.c; h.ns = min(d.c, d.g - kc * d.c);
+      break;
+    }
+    default:
+      h.nb = u * d.NN; h.nn = d.NN; h.off = 0; h.ns = d.NS;
+  }
+  return h;
+}
+
 template <int DQK, int DV>
 struct DecTile {
   static constexpr int KS = DQK / 32;
@@ -78,8 +127,7 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
                    const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                    const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
                    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int Lmax,
-                   int S, int N, int Hkv, int window, int units, int NS, int NN, int R, float c,
-                   int flags) {
+                   int S, int N, int Hkv, int window, DecMap dm, float c, int flags) {
   using T = DecTile<DQK, DV>;
   constexpr int DB = T::DB;
   __shared__ __attribute__((aligned(16))) unsigned char smem[T::SHARED_BYTES];
@@ -87,14 +135,17 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.x / units, u = blockIdx.x - (blockIdx.x / units) * units;
-  const int sig0 = u * R * NS;
+  const int b = blockIdx.x / dm.nsub, v = blockIdx.x - (blockIdx.x / dm.nsub) * dm.nsub;
+  const SubHeads sh = sub_heads(dm, v);
+  const int NS = dm.NS, R = dm.R, ns = sh.ns;
 
   int len = lens ? lens[b] : Lmax;
   if (len > Lmax) len = Lmax;
-  if (len < 1) {  // no visible key: the output row is zero
-    for (int idx = tid; idx < R * NS * DV; idx += NT)
-      out[((int64_t)b * S + sig0 + idx / DV) * DV + idx % DV] = 0;
+  if (len < 1) {  // no visible key: the output rows are zero
+    for (int idx = tid; idx < R * ns * DV; idx += NT) {
+      const int ph = idx / (ns * DV), rem = idx - ph * (ns * DV);
+      out[((int64_t)b * S + (sh.kv0 + ph) * NS + sh.off + rem / DV) * DV + rem % DV] = 0;
+    }
     return;
   }
   const int pos = len - 1;
@@ -108,16 +159,17 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
 
 #pragma unroll 1
   for (int ph = 0; ph < R; ++ph) {
-    const int nh = ph == 0 ? NS + NN : NS;  // query heads (MFMA columns) of this phase
-    const int kvh = u * R + ph;
+    const int nh = ph == 0 ? ns + sh.nn : ns;  // query heads (MFMA columns) of this phase
+    const int kvh = sh.kv0 + ph;
+    const int sig0 = kvh * NS + sh.off;       // this phase's first signal head
     // Q^T B operand: column col is head col of the phase (zero if unused).
     bf16x8 qf[T::KS];
     {
       const uint16_t* qp = nullptr;
-      if (col < NS)
-        qp = q_sig + ((int64_t)b * S + sig0 + ph * NS + col) * DQK;
+      if (col < ns)
+        qp = q_sig + ((int64_t)b * S + sig0 + col) * DQK;
       else if (col < nh)
-        qp = q_noise + ((int64_t)b * N + u * NN + (col - NS)) * DQK;
+        qp = q_noise + ((int64_t)b * N + sh.nb + (col - ns)) * DQK;
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         u32x4 w = {0u, 0u, 0u, 0u};
@@ -225,15 +277,15 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
     // out = gate * (H_S - lambda * Repeat_g(H_N)) for this phase's signal heads;
     // each thread merges the two columns it needs.
     const int g = S / N;
-    for (int idx = tid; idx < NS * DV; idx += NT) {
+    for (int idx = tid; idx < ns * DV; idx += NT) {
       const int sl = idx / DV, d = idx - (idx / DV) * DV;
-      const int i = sig0 + ph * NS + sl;
-      const int nl = i / g - u * NN;  // noise head of signal i, local to the unit
+      const int i = sig0 + sl;
+      const int nl = i / g - sh.nb;  // noise head of signal i, local to the sub-unit
       const float hs = merged(merge, sl, d);
       float hn;
       if (ph == 0) {
-        hn = merged(merge, NS + nl, d);
-        if (R > 1 && sl == 0) sHN[d] = hn;  // one noise head per unit when R > 1
+        hn = merged(merge, ns + nl, d);
+        if (R > 1 && sl == 0) sHN[d] = hn;  // one noise head per sub-unit when R > 1
       } else {
         hn = sHN[d];
       }
@@ -309,22 +361,24 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
                      const uint16_t* __restrict__ kg, const uint16_t* __restrict__ vg,
                      const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
                      const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int Lmax,
-                     int S, int N, int Hkv, int window, int units, int NS, int NN, int R,
-                     float c, int flags) {
+                     int S, int N, int Hkv, int window, DecMap dm, float c, int flags) {
   using T = StreamTile<DQK, DV>;
   constexpr int DB = T::DB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::SHARED_BYTES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.x / units, u = blockIdx.x - (blockIdx.x / units) * units;
-  const int sig0 = u * R * NS;
+  const int b = blockIdx.x / dm.nsub, v = blockIdx.x - (blockIdx.x / dm.nsub) * dm.nsub;
+  const SubHeads sh = sub_heads(dm, v);
+  const int NS = dm.NS, R = dm.R, ns = sh.ns;
 
   int len = lens ? lens[b] : Lmax;
   if (len > Lmax) len = Lmax;
-  if (len < 1) {  // no visible key: the output row is zero
-    for (int idx = tid; idx < R * NS * DV; idx += NT)
-      out[((int64_t)b * S + sig0 + idx / DV) * DV + idx % DV] = 0;
+  if (len < 1) {  // no visible key: the output rows are zero
+    for (int idx = tid; idx < R * ns * DV; idx += NT) {
+      const int ph = idx / (ns * DV), rem = idx - ph * (ns * DV);
+      out[((int64_t)b * S + (sh.kv0 + ph) * NS + sh.off + rem / DV) * DV + rem % DV] = 0;
+    }
     return;
   }
   const int pos = len - 1;
@@ -342,15 +396,16 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
 
 #pragma unroll 1
   for (int ph = 0; ph < R; ++ph) {
-    const int nh = ph == 0 ? NS + NN : NS;
-    const int kvh = u * R + ph;
+    const int nh = ph == 0 ? ns + sh.nn : ns;
+    const int kvh = sh.kv0 + ph;
+    const int sig0 = kvh * NS + sh.off;
     bf16x8 qf[T::KS];
     {
       const uint16_t* qp = nullptr;
-      if (col < NS)
-        qp = q_sig + ((int64_t)b * S + sig0 + ph * NS + col) * DQK;
+      if (col < ns)
+        qp = q_sig + ((int64_t)b * S + sig0 + col) * DQK;
       else if (col < nh)
-        qp = q_noise + ((int64_t)b * N + u * NN + (col - NS)) * DQK;
+        qp = q_noise + ((int64_t)b * N + sh.nb + (col - ns)) * DQK;
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         u32x4 w = {0u, 0u, 0u, 0u};
@@ -478,15 +533,15 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
       for (int r = 0; r < 4; ++r) mw[32 + (16 * db + 4 * g4 + r) * 16 + col] = o[db][r];
     __syncthreads();
     const int g = S / N;
-    for (int idx = tid; idx < NS * DV; idx += NT) {
+    for (int idx = tid; idx < ns * DV; idx += NT) {
       const int sl = idx / DV, d = idx - (idx / DV) * DV;
-      const int i = sig0 + ph * NS + sl;
-      const int nl = i / g - u * NN;
+      const int i = sig0 + sl;
+      const int nl = i / g - sh.nb;
       const float hs = merged_impl<T::MERGE_FLOATS>(merge, sl, d);
       float hn;
       if (ph == 0) {
-        hn = merged_impl<T::MERGE_FLOATS>(merge, NS + nl, d);
-        hn_keep = hn;  // R > 1 means one noise head per unit: the same for every sl
+        hn = merged_impl<T::MERGE_FLOATS>(merge, ns + nl, d);
+        hn_keep = hn;  // R > 1 means one noise head per sub-unit: the same for every sl
       } else {
         hn = hn_keep;  // this thread's d is the same in every phase (NT % DV == 0)
       }
@@ -504,38 +559,73 @@ decode_stream_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restr
 // Visible keys per sequence above which the streaming kernel is used.
 constexpr int kStreamMinSpan = 2048;
 
+// Sub-units of a head layout: the whole unit when its query heads fit the 16
+// MFMA columns, else the split described at DecMap.
+DecMap make_decmap(const DecodeArgs& a) {
+  const UnitPlan& p = a.plan;
+  DecMap d;
+  d.g = a.S / a.N;
+  d.NS = p.NS;
+  d.NN = p.NN;
+  d.R = p.R;
+  d.c = d.m = 1;
+  if (p.NS + p.NN <= 16) {
+    d.mode = 0;
+    d.K = 1;
+  } else if (p.R > 1) {  // one noise head per unit
+    d.mode = 1;
+    d.c = 15;
+    d.K = (p.NS + 14) / 15;
+  } else if (d.g < 16) {
+    d.mode = 2;
+    d.m = 1;
+    for (int m = p.NN; m > 1; --m)
+      if (p.NN % m == 0 && m * (d.g + 1) <= 16) {
+        d.m = m;
+        break;
+      }
+    d.K = p.NN / d.m;
+  } else {
+    d.mode = 3;
+    d.c = 15;
+    d.K = p.NN * ((d.g + 14) / 15);
+  }
+  d.nsub = p.units * d.K;
+  return d;
+}
+
 template <int DQK, int DV>
 hipError_t launch_stream(const DecodeArgs& a, hipStream_t stream) {
   static_assert(NT % DV == 0, "a thread keeps one output channel across phases");
-  const int64_t grid = (int64_t)a.B * a.plan.units;
+  const DecMap dm = make_decmap(a);
+  const int64_t grid = (int64_t)a.B * dm.nsub;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_stream_kernel<DQK, DV>), dim3((unsigned)grid), dim3(NT), 0, stream,
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.lens, (const uint16_t*)a.lam,
                      (const uint16_t*)a.gate, (uint16_t*)a.out, a.Lmax, a.S, a.N, a.Hkv,
-                     a.window, a.plan.units, a.plan.NS, a.plan.NN, a.plan.R, a.scale_log2,
-                     a.flags);
+                     a.window, dm, a.scale_log2, a.flags);
   return hipGetLastError();
 }
 
 template <int DQK, int DV>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.B * a.plan.units;
+  const DecMap dm = make_decmap(a);
+  const int64_t grid = (int64_t)a.B * dm.nsub;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_bf16_kernel<DQK, DV>), dim3((unsigned)grid), dim3(NT), 0, stream,
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.lens, (const uint16_t*)a.lam,
                      (const uint16_t*)a.gate, (uint16_t*)a.out, a.Lmax, a.S, a.N, a.Hkv,
-                     a.window, a.plan.units, a.plan.NS, a.plan.NN, a.plan.R, a.scale_log2,
-                     a.flags);
+                     a.window, dm, a.scale_log2, a.flags);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool decode_bf16_supported(int dqk, int dv, const UnitPlan& p) {
-  const bool dims = (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
-  return dims && p.NS + p.NN <= 16 && p.NN <= 16;
+bool decode_bf16_supported(int dqk, int dv, const UnitPlan&) {
+  // Every valid head layout maps onto sub-units (DecMap); only head sizes are compiled.
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {

@@ -7,9 +7,12 @@
 // D = H_S - lambda * Repeat_g(H_N), and the gate product G * D.
 //
 // Work decomposition (MI355X-first; the pages give no kernel design):
-//  * a workgroup owns (batch row b, unit u, tile of 64 queries); a unit is the
-//    set of KV heads, signal heads and noise heads that the fused epilogue
-//    needs together, so the noise output never goes to HBM;
+//  * a workgroup owns (batch row b, sub-unit v, tile of 64 queries); a sub-unit
+//    is one noise head with a chunk of the signal heads it serves (on the noise
+//    head's KV head and, in layouts with more KV heads than noise heads, one
+//    other KV head), so the noise output never goes to HBM. Layouts whose
+//    groups are too large for one workgroup split into several sub-units, each
+//    recomputing the noise head (SubMap below);
 //  * 8 waves: wave w owns the 16 queries of group w%4; waves 0-3 ("A") compute
 //    the noise head and the first signal heads, waves 4-7 ("B") the other
 //    signal heads. Each SIMD then runs one A and one B wave over the same
@@ -41,7 +44,8 @@ constexpr float kNoMax = -1e30f;    // finite "no key seen yet" reference
 
 
 // ASIG signal heads + the noise head run in the A waves, BSIG signal heads in the
-// B waves; with TWO_KV the B heads read the unit's second KV head.
+// B waves; with TWO_KV the B heads read a second KV head (ASIG may then be 0:
+// the A waves compute only the noise head the B heads need).
 //
 // NQG query groups of 16 make a workgroup's query tile (BM = 16*NQG); BN keys
 // make an LDS tile. (NQG, BN) = (4, 64) fills a CU with one workgroup; (2, 32)
@@ -81,6 +85,26 @@ struct Cfg {
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "runs of NW blocks never mix K and V");
 };
 
+// Which heads a workgroup computes. Noise head n serves signal heads
+// g*n .. g*n+g-1 and reads KV head kv_noise(n) = floor(n*Hkv/N); signal head i
+// reads KV head floor(i/NS) (NS = S/Hkv). Sub-unit v of a batch row (v < nsub):
+//   n = v / (PK*P), r = v % (PK*P), pk = first_p + r / P, q = r % P;
+//   one KV head (TWO_KV false): the A and B heads are chunk q (ASIG+BSIG heads)
+//     of the g signal heads, all on kv_noise(n);
+//   two KV heads: the A heads are chunk q (ASIG heads) of the signal heads on
+//     kv_noise(n), the B heads chunk q (BSIG heads) of those on kv_noise(n)+pk.
+// The noise head's training outputs are written by the sub-unit with r == 0 of
+// the launch that owns them (own_noise), so each is written exactly once.
+struct SubMap {
+  int nsub;       // sub-units per batch row
+  int P;          // signal-head chunks per (noise head, KV head)
+  int PK;         // other KV heads per noise head in this launch (1 with one KV head)
+  int first_p;    // offset of the first other KV head from kv_noise(n)
+  int g;          // S / N
+  int NS;         // S / Hkv
+  int own_noise;  // this launch writes the noise heads' training outputs
+};
+
 struct Ctx {
   const uint16_t* kg;  // this sequence's key 0
   const uint16_t* vg;  // this sequence's value 0
@@ -95,17 +119,16 @@ struct Ctx {
   float c;  // log2(e)/sqrt(dqk)
 };
 
-// Issue one 1 KB direct-to-LDS block of a tile (keys k0 .. k0+BN-1). Rows past
-// the sequence's last key read that key (finite data; those keys are masked).
+// Issue one 1 KB direct-to-LDS block of a tile (keys k0 .. k0+BN-1) into the
+// ring stage at LDS byte address stage_lds. Rows past the sequence's last key
+// read that key (finite data; those keys are masked).
 template <class C>
-__device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint16_t* sK0,
-                                           uint16_t* sV0, uint16_t* sK1, uint16_t* sV1) {
+__device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint32_t stage_lds) {
   constexpr int per = C::KBLK + C::VBLK;
   const int kvi = (C::TWO_KV && blk >= per) ? 1 : 0;
   const int bi = blk - kvi * per;
   const int kvh = kvi ? x.kvB : x.kvA;
-  uint16_t* sK = kvi ? sK1 : sK0;
-  uint16_t* sV = kvi ? sV1 : sV0;
+  const uint32_t kv_lds = stage_lds + 2u * (uint32_t)(kvi * C::KV_ELEMS);
   // The per-lane part of every address is a 32-bit byte offset from a
   // wave-uniform base row (clamped so the base never passes row L-1).
   if (bi < C::KBLK) {
@@ -115,7 +138,7 @@ __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint1
     const int rel = min(x.lane & 15, x.L - 1 - row0);
     const char* base = (const char*)x.kg +
                        (((int64_t)row0 * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
-    dma16(base, (uint32_t)rel * stride + 16u * (uint32_t)(x.lane >> 4), (lds_void*)(sK + bi * 512));
+    dma16_lds(base, (uint32_t)rel * stride + 16u * (uint32_t)(x.lane >> 4), kv_lds + 1024u * bi);
   } else {
     const int vi = bi - C::KBLK;
     const int lr = x.lane / C::VCH;            // row within the block
@@ -125,16 +148,17 @@ __device__ __forceinline__ void issue_block(const Ctx& x, int blk, int k0, uint1
     const int row0 = min(k0 + C::VRPB * vi, x.L - 1);
     const int rel = min(lr, x.L - 1 - row0);
     const char* base = (const char*)x.vg + ((int64_t)row0 * x.Hkv + kvh) * C::DV * 2;
-    dma16(base, (uint32_t)rel * stride + 16u * (uint32_t)cch, (lds_void*)(sV + vi * 512));
+    dma16_lds(base, (uint32_t)rel * stride + 16u * (uint32_t)cch,
+              kv_lds + 2u * C::K_ELEMS + 1024u * vi);
   }
 }
 
-// Every wave issues its share of the tile's 1 KB blocks.
+// Every wave issues its share of the tile's 1 KB blocks into ring stage DST.
 template <class C>
-__device__ __forceinline__ void issue_tile(const Ctx& x, int k0, uint16_t* sK0, uint16_t* sV0,
-                                           uint16_t* sK1, uint16_t* sV1) {
+__device__ __forceinline__ void issue_tile(const Ctx& x, int k0, uint32_t ring_lds, int dst) {
+  const uint32_t stage_lds = ring_lds + 2u * (uint32_t)(dst * C::STAGE_ELEMS);
 #pragma unroll
-  for (int i = 0; i < C::TBLK / C::NW; ++i) issue_block<C>(x, x.wave + i * C::NW, k0, sK0, sV0, sK1, sV1);
+  for (int i = 0; i < C::TBLK / C::NW; ++i) issue_block<C>(x, x.wave + i * C::NW, k0, stage_lds);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -471,10 +495,7 @@ __device__ __forceinline__ void run_tiles(const Ctx& x, State<C, NH>& st,
   auto next_job = [&](int knext, int dst) -> int {
     if (knext > kt1 * C::BN) return -1;
     if (knext + C::BN <= x.L) return knext;
-    if (dst == 0)
-      issue_tile<C>(x, knext, sk[0][0], sv[0][0], sk[0][1], sv[0][1]);
-    else
-      issue_tile<C>(x, knext, sk[1][0], sv[1][0], sk[1][1], sv[1][1]);
+    issue_tile<C>(x, knext, ring_lds, dst);
     return -1;
   };
   for (int kt = kt0; kt <= kt1; kt += 2) {
@@ -505,10 +526,10 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
                 const uint16_t* __restrict__ lam, const uint16_t* __restrict__ gate,
                 uint16_t* __restrict__ out, const int32_t* __restrict__ cu_q,
                 const int32_t* __restrict__ cu_k, int B, int L, int S, int N, int Hkv,
-                int window, int units, int R, int nqt, int heavy_first, float c, int flags,
+                int window, SubMap sm, int nqt, int heavy_first, float c, int flags,
                 uint16_t* __restrict__ h_sig, uint16_t* __restrict__ h_noise,
                 float* __restrict__ lse, int64_t lse_b, int lse_q, int64_t lse_h) {
-  // K/V ring: two stages, each the tiles of the unit's KV heads.
+  // K/V ring: two stages, each the tiles of the sub-unit's KV heads.
   __shared__ __attribute__((aligned(16))) uint16_t ring[2 * C::STAGE_ELEMS];
   // Normalised noise output handed from the A waves to the B waves.
   __shared__ __attribute__((aligned(16))) float sHN[C::NB > 0 ? C::NQG * C::DB * 4 * 64 : 4];
@@ -524,11 +545,20 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   x.c = c;
   const bool group_b = x.wave >= C::NQG;
   const int qg = x.wave % C::NQG;
-  const int per = B * units;
+  const int per = B * sm.nsub;
   const int slot = blockIdx.x / per;
   const int qt = heavy_first ? nqt - 1 - slot : slot;
   const int bu = blockIdx.x - slot * per;
-  const int b = bu / units, u = bu - (bu / units) * units;
+  const int b = bu / sm.nsub, v = bu - (bu / sm.nsub) * sm.nsub;
+  // This sub-unit's heads (SubMap): noise head n, the A signal heads from sigA,
+  // the B signal heads from sigB.
+  const int pp = sm.PK * sm.P;
+  const int n = v / pp, r_ = v - (v / pp) * pp;
+  const int pk = sm.first_p + r_ / sm.P, q_ = r_ - (r_ / sm.P) * sm.P;
+  const int kv_n = (int)(((int64_t)n * Hkv) / N);
+  const int sigA = C::TWO_KV ? n * sm.g + q_ * C::ASIG : n * sm.g + q_ * C::USIG;
+  const int sigB = C::TWO_KV ? n * sm.g + pk * sm.NS + q_ * C::BSIG : sigA + C::ASIG;
+  const bool noise_owner = sm.own_noise && r_ == 0;
   // Sequence b: Lq queries from packed row qbase, Lk keys from packed row kbase
   // (packed sequences), or rows b*L .. b*L+L-1 of both (a batch).
   int64_t qbase, kbase;
@@ -545,12 +575,11 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   const int ql = qt * C::BM;  // this tile's first query of the sequence
   if (ql >= Lq) return;        // past the sequence (the whole workgroup)
   const int qoff = Lk - Lq;
-  const int sig0 = u * C::USIG;  // first signal head of the unit
   x.L = Lk;
   x.kg = kg + kbase * Hkv * C::DQK;
   x.vg = vg + kbase * Hkv * C::DV;
-  x.kvA = u * R;
-  x.kvB = C::TWO_KV ? u * R + 1 : u * R;
+  x.kvA = kv_n;
+  x.kvB = C::TWO_KV ? kv_n + pk : kv_n;
   x.q_lo = qoff + ql;
   x.q_hi = qoff + min(ql + C::BM, Lq) - 1;
   const int64_t lbase = lse_b * b + lse_q * qbase;  // this sequence's lse origin
@@ -559,17 +588,21 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     const int nq = min(ql + C::BM, Lq) - ql;
     for (int idx = threadIdx.x; idx < nq * C::USIG * C::DV; idx += C::NT) {
       const int r = idx / (C::USIG * C::DV), rem = idx - r * (C::USIG * C::DV);
-      out[((qbase + ql + r) * S + sig0) * C::DV + rem] = 0;
-      if constexpr (TRAIN) h_sig[((qbase + ql + r) * S + sig0) * C::DV + rem] = 0;
+      const int hh = rem / C::DV, e = rem - hh * C::DV;
+      const int hd = hh < C::ASIG ? sigA + hh : sigB + (hh - C::ASIG);
+      out[((qbase + ql + r) * S + hd) * C::DV + e] = 0;
+      if constexpr (TRAIN) h_sig[((qbase + ql + r) * S + hd) * C::DV + e] = 0;
     }
     if constexpr (TRAIN) {
-      for (int idx = threadIdx.x; idx < nq * C::DV; idx += C::NT) {
-        const int r = idx / C::DV, e = idx - r * C::DV;
-        h_noise[((qbase + ql + r) * N + u) * C::DV + e] = 0;
-      }
+      if (noise_owner)
+        for (int idx = threadIdx.x; idx < nq * C::DV; idx += C::NT) {
+          const int r = idx / C::DV, e = idx - r * C::DV;
+          h_noise[((qbase + ql + r) * N + n) * C::DV + e] = 0;
+        }
       for (int idx = threadIdx.x; idx < nq * (C::USIG + 1); idx += C::NT) {
         const int r = idx / (C::USIG + 1), hh = idx - r * (C::USIG + 1);
-        const int hd = hh < C::USIG ? sig0 + hh : S + u;
+        if (hh == C::USIG && !noise_owner) continue;
+        const int hd = hh < C::ASIG ? sigA + hh : hh < C::USIG ? sigB + (hh - C::ASIG) : S + n;
         lse[lbase + hd * lstride + ql + r] = -INFINITY;
       }
     }
@@ -599,7 +632,7 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     if (kf + C::BN <= Lk)
       issue_tile_fast<C, 0>(x, ring_lds, kf, 0, C::TBLK / C::NW);
     else
-      issue_tile<C>(x, kf, sk[0][0], sv[0][0], sk[0][1], sv[0][1]);
+      issue_tile<C>(x, kf, ring_lds, 0);
   }
 
   if (!group_b) {
@@ -608,14 +641,14 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     State<C, NH> st;
     const uint16_t* qrow[NH];
 #pragma unroll
-    for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sig0 + s) * C::DQK;
-    qrow[NZ] = q_noise + (row * N + u) * C::DQK;
+    for (int s = 0; s < C::ASIG; ++s) qrow[s] = q_sig + (row * S + sigA + s) * C::DQK;
+    qrow[NZ] = q_noise + (row * N + n) * C::DQK;
     run_tiles<C, NH, 0>(x, st, qrow, ring_lds, sk, sv);
-    HeadIn<C::DV> in[C::ASIG];
+    HeadIn<C::DV> in[C::ASIG > 0 ? C::ASIG : 1];
     if constexpr (C::kEarlyEpilogue) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
-        load_head_in<C::DV>(lam, gate, row, S, sig0 + s, x.g4, in[s]);
+        load_head_in<C::DV>(lam, gate, row, S, sigA + s, x.g4, in[s]);
     }
     // A query at a negative position has no visible key: its sums stay 0 and it
     // gives zeros.
@@ -634,21 +667,22 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     if constexpr (!C::kEarlyEpilogue) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
-        load_head_in<C::DV>(lam, gate, row, S, sig0 + s, x.g4, in[s]);
+        load_head_in<C::DV>(lam, gate, row, S, sigA + s, x.g4, in[s]);
     }
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::ASIG; ++s)
-        store_head<C::DV>(out, row, S, sig0 + s, x.g4, st.o[s],
+        store_head<C::DV>(out, row, S, sigA + s, x.g4, st.o[s],
                           st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
       if constexpr (TRAIN) {
-        store_train_head<C::DV>(h_noise + (row * N + u) * C::DV,
-                                lse + lbase + (int64_t)(S + u) * lstride + tl, x.g4, st.o[NZ],
-                                inv_n, st.mref[NZ], st.lsum[NZ]);
+        if (noise_owner)
+          store_train_head<C::DV>(h_noise + (row * N + n) * C::DV,
+                                  lse + lbase + (int64_t)(S + n) * lstride + tl, x.g4,
+                                  st.o[NZ], inv_n, st.mref[NZ], st.lsum[NZ]);
 #pragma unroll
         for (int s = 0; s < C::ASIG; ++s)
-          store_train_head<C::DV>(h_sig + (row * S + sig0 + s) * C::DV,
-                                  lse + lbase + (int64_t)(sig0 + s) * lstride + tl, x.g4, st.o[s],
+          store_train_head<C::DV>(h_sig + (row * S + sigA + s) * C::DV,
+                                  lse + lbase + (int64_t)(sigA + s) * lstride + tl, x.g4, st.o[s],
                                   st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, st.mref[s],
                                   st.lsum[s]);
       }
@@ -658,17 +692,16 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     }
   } else if (C::NB > 0) {
     constexpr int NH = C::NB > 0 ? C::NB : 1;  // [B signal heads]
-    constexpr int b_first = C::ASIG;           // first B head, unit-relative
     State<C, NH> st;
     const uint16_t* qrow[NH];
 #pragma unroll
-    for (int s = 0; s < C::BSIG; ++s) qrow[s] = q_sig + (row * S + sig0 + b_first + s) * C::DQK;
+    for (int s = 0; s < C::BSIG; ++s) qrow[s] = q_sig + (row * S + sigB + s) * C::DQK;
     run_tiles<C, NH, 1>(x, st, qrow, ring_lds, sk, sv);
     HeadIn<C::DV> in[NH];
     if constexpr (C::kEarlyEpilogue) {  // in flight while waiting for the A waves
 #pragma unroll
       for (int s = 0; s < C::BSIG; ++s)
-        load_head_in<C::DV>(lam, gate, row, S, sig0 + b_first + s, x.g4, in[s]);
+        load_head_in<C::DV>(lam, gate, row, S, sigB + s, x.g4, in[s]);
     }
     __syncthreads();  // the A waves' noise output is in LDS
     floatx4 hn[C::DB];
@@ -678,18 +711,18 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
     if constexpr (!C::kEarlyEpilogue) {
 #pragma unroll
       for (int s = 0; s < C::BSIG; ++s)
-        load_head_in<C::DV>(lam, gate, row, S, sig0 + b_first + s, x.g4, in[s]);
+        load_head_in<C::DV>(lam, gate, row, S, sigB + s, x.g4, in[s]);
     }
     if (t_ok) {
 #pragma unroll
       for (int s = 0; s < C::BSIG; ++s)
-        store_head<C::DV>(out, row, S, sig0 + b_first + s, x.g4, st.o[s],
+        store_head<C::DV>(out, row, S, sigB + s, x.g4, st.o[s],
                           st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, hn, in[s], flags);
       if constexpr (TRAIN) {
 #pragma unroll
         for (int s = 0; s < C::BSIG; ++s)
-          store_train_head<C::DV>(h_sig + (row * S + sig0 + b_first + s) * C::DV,
-                                  lse + lbase + (int64_t)(sig0 + b_first + s) * lstride + tl,
+          store_train_head<C::DV>(h_sig + (row * S + sigB + s) * C::DV,
+                                  lse + lbase + (int64_t)(sigB + s) * lstride + tl,
                                   x.g4, st.o[s],
                                   st.lsum[s] > 0.f ? 1.f / st.lsum[s] : 0.f, st.mref[s],
                                   st.lsum[s]);
@@ -699,10 +732,10 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 }
 
 template <class C>
-hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_inst(const FwdArgs& a, const SubMap& sm, hipStream_t stream) {
   // Packed sequences: B sequences of at most L queries each.
   const int nqt = (a.L + C::BM - 1) / C::BM;
-  const int64_t grid = (int64_t)nqt * a.B * a.plan.units;
+  const int64_t grid = (int64_t)nqt * a.B * sm.nsub;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int heavy_first = a.window == 0 ? 1 : 0;
   if (a.h_sig)
@@ -710,7 +743,7 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
                        (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
                        (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L,
-                       a.S, a.N, a.Hkv, a.window, a.plan.units, a.plan.R, nqt, heavy_first,
+                       a.S, a.N, a.Hkv, a.window, sm, nqt, heavy_first,
                        a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
                        a.lse, a.lse_b, a.lse_q, a.lse_h);
   else
@@ -718,32 +751,56 @@ hipError_t launch_inst(const FwdArgs& a, hipStream_t stream) {
                        stream, (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.lam,
                        (const uint16_t*)a.gate, (uint16_t*)a.out, a.cu_q, a.cu_k, a.B, a.L,
-                       a.S, a.N, a.Hkv, a.window, a.plan.units, a.plan.R, nqt, heavy_first,
+                       a.S, a.N, a.Hkv, a.window, sm, nqt, heavy_first,
                        a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
                        a.lse, a.lse_b, a.lse_q, a.lse_h);
   return hipGetLastError();
 }
 
-// Head groups of each compiled layout (NS signal heads per KV head, R KV heads
-// per unit, one noise head per unit), for a (query groups, key tile) shape.
+// Largest chunk of signal heads (at most MAXC) that divides n.
+inline int chunk_of(int n, int maxc) {
+  for (int c = maxc; c > 1; --c)
+    if (n % c == 0) return c;
+  return 1;
+}
+
+// Sub-unit launches of a head layout (g = S/N, NS = S/Hkv), for a (query
+// groups, key tile) shape:
+//  * N >= Hkv: every signal head of noise head n reads kv_noise(n); one launch,
+//    each sub-unit the noise head and a chunk of c <= 4 of its g signal heads
+//    (c = g, one sub-unit per noise head, in the workloads' layouts);
+//  * N < Hkv (R = Hkv/N KV heads per noise head, NS signal heads on each): a
+//    launch of sub-units pairing a chunk of the signal heads on kv_noise(n)
+//    (with the noise head, A waves) with the same chunk of those on the next
+//    KV head (B waves); for R > 2 a second launch whose A waves compute only the
+//    noise head, the B waves a chunk of the signal heads on each further KV head.
 template <int DQK, int DV, int NQG, int BN>
 hipError_t dispatch_layout(const FwdArgs& a, hipStream_t stream) {
-  const UnitPlan& p = a.plan;
-  if (p.NN != 1) return (hipError_t)-1;
-  if (p.R == 1) {
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 0, false, NQG, BN>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 1, 1, false, NQG, BN>>(a, stream);
-    if (p.NS == 4) return launch_inst<Cfg<DQK, DV, 2, 2, false, NQG, BN>>(a, stream);
-  } else if (p.R == 2) {
-    // Two KV heads' tiles per stage. With dqk = 192 only 32-key tiles fit, and
-    // those split evenly over 4 waves, not 8. With dqk = 128, 32-key tiles too:
-    // the 64-key form needs all 256 registers and runs 8% slower.
-    constexpr int NQG2 = DQK > 128 ? 2 : NQG;
-    constexpr int BN2 = DQK >= 128 ? 32 : BN;
-    if (p.NS == 1) return launch_inst<Cfg<DQK, DV, 1, 1, true, NQG2, BN2>>(a, stream);
-    if (p.NS == 2) return launch_inst<Cfg<DQK, DV, 2, 2, true, NQG2, BN2>>(a, stream);
+  const int g = a.S / a.N, NS = a.S / a.Hkv;
+  if (a.N >= a.Hkv) {
+    const int c = chunk_of(g, 4);
+    const SubMap sm{a.N * (g / c), g / c, 1, 0, g, NS, 1};
+    switch (c) {
+      case 1: return launch_inst<Cfg<DQK, DV, 1, 0, false, NQG, BN>>(a, sm, stream);
+      case 2: return launch_inst<Cfg<DQK, DV, 1, 1, false, NQG, BN>>(a, sm, stream);
+      case 3: return launch_inst<Cfg<DQK, DV, 1, 2, false, NQG, BN>>(a, sm, stream);
+      default: return launch_inst<Cfg<DQK, DV, 2, 2, false, NQG, BN>>(a, sm, stream);
+    }
   }
-  return (hipError_t)-1;
+  // Two KV heads' tiles per stage. With dqk = 192 only 32-key tiles fit, and
+  // those split evenly over 4 waves, not 8. With dqk = 128, 32-key tiles too:
+  // the 64-key form needs all 256 registers and runs 8% slower.
+  constexpr int NQG2 = DQK > 128 ? 2 : NQG;
+  constexpr int BN2 = DQK >= 128 ? 32 : BN;
+  const int R = a.Hkv / a.N;
+  const int c = chunk_of(NS, 2);
+  const SubMap paired{a.N * (NS / c), NS / c, 1, 1, g, NS, 1};
+  hipError_t e = c == 2 ? launch_inst<Cfg<DQK, DV, 2, 2, true, NQG2, BN2>>(a, paired, stream)
+                        : launch_inst<Cfg<DQK, DV, 1, 1, true, NQG2, BN2>>(a, paired, stream);
+  if (e != hipSuccess || R <= 2) return e;
+  const SubMap extra{a.N * (R - 2) * (NS / c), NS / c, R - 2, 2, g, NS, 0};
+  return c == 2 ? launch_inst<Cfg<DQK, DV, 0, 2, true, NQG2, BN2>>(a, extra, stream)
+                : launch_inst<Cfg<DQK, DV, 0, 1, true, NQG2, BN2>>(a, extra, stream);
 }
 
 // Causal full attention: 64-query tiles over 64-key tiles, one workgroup per
@@ -758,12 +815,10 @@ hipError_t dispatch_shape(const FwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool fwd_bf16_supported(int dqk, int dv, const UnitPlan& p) {
-  const bool dims = (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
-  if (!dims || p.NN != 1) return false;
-  if (p.R == 1) return p.NS == 1 || p.NS == 2 || p.NS == 4;
-  if (p.R == 2) return p.NS == 1 || p.NS == 2;
-  return false;
+bool fwd_bf16_supported(int dqk, int dv, const UnitPlan&) {
+  // Every head layout the host accepts (S % N == 0, S % Hkv == 0, one of N, Hkv
+  // dividing the other) maps onto sub-units; only the head sizes are compiled.
+  return (dqk == 64 && dv == 64) || (dqk == 128 && dv == 128) || (dqk == 192 && dv == 128);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {

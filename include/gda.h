@@ -45,7 +45,8 @@ typedef enum {
   GDA_SUCCESS = 0,
   GDA_ERROR_INVALID_ARGUMENT = 1, /* null or misaligned pointer, size < 1, window < 0,
                                      head counts that do not divide, unknown dtype         */
-  GDA_ERROR_UNSUPPORTED = 2,      /* valid but not compiled: (dqk, dv) or head layout      */
+  GDA_ERROR_UNSUPPORTED = 2,      /* valid but not compiled: (dqk, dv) for bf16, or a form
+                                     offered for bf16 only (training, latent decode)        */
   GDA_ERROR_HIP = 3               /* a HIP runtime or launch failure                       */
 } gda_status;
 
@@ -61,9 +62,9 @@ typedef enum { GDA_BF16 = 0, GDA_F32 = 1 } gda_dtype;
  *   out     [B, L, S,   dv ]      written: gate * (H_S - lambda * Repeat_g(H_N))
  * Requirements: all sizes >= 1; S % N == 0; S % Hkv == 0; N % Hkv == 0 or
  * Hkv % N == 0; window >= 0 (0 = full causal, W >= 1 = keys t-W+1 .. t).
- * GDA_BF16 needs (dqk, dv) in {(64,64), (128,128), (192,128)} and a head layout
- * with N <= Hkv and (S/Hkv, Hkv/N) in {(1,1), (2,1), (4,1), (1,2), (2,2)}
- * (returns GDA_ERROR_UNSUPPORTED otherwise). GDA_F32 takes any sizes and layout.
+ * GDA_BF16 needs (dqk, dv) in {(64,64), (128,128), (192,128)} (returns
+ * GDA_ERROR_UNSUPPORTED otherwise) and takes every head layout the requirements
+ * allow. GDA_F32 takes any sizes and layout.
  * Accumulation is fp32 in both dtypes; bf16 outputs are rounded to nearest even. */
 gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
                    const void* lambda, const void* gate, void* out,
@@ -83,8 +84,7 @@ gda_status gda_fwd(const void* q_sig, const void* q_noise, const void* k, const 
  *   gate    [B, S, dv]
  *   out     [B, S, dv]
  * Same requirements as gda_fwd, plus Lmax >= 1. GDA_BF16 needs the same
- * (dqk, dv) set and at most 16 query heads per unit (S/Hkv signal heads plus
- * max(1, N/Hkv) noise heads). */
+ * (dqk, dv) set and takes every valid head layout. */
 gda_status gda_decode(const void* q_sig, const void* q_noise, const void* k_cache,
                       const void* v_cache, const int32_t* cache_lens, const void* lambda,
                       const void* gate, void* out,

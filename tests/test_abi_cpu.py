@@ -169,9 +169,9 @@ def test_varlen_invalid_arguments(kw):
 
 def test_varlen_unsupported_and_device_check():
     assert varlen(dqk=96, dv=96) == UNSUPPORTED
-    assert varlen(S=16, N=2, Hkv=2) == UNSUPPORTED
     if not _gpu_visible():
         assert varlen() == HIPERR
+        assert varlen(S=16, N=2, Hkv=2) == HIPERR  # any valid head layout
         assert varlen(dtype=F32, dqk=40, dv=24) == HIPERR
 
 
@@ -277,17 +277,39 @@ def test_decode_misaligned_lengths():
     assert b"aligned" in _lib.load().gda_last_error()
 
 
-@pytest.mark.parametrize("kw", [dict(dqk=96, dv=96), dict(dqk=192, dv=192), dict(dqk=128, dv=64),
-                                dict(S=16, N=2, Hkv=2),        # 8 signal heads per KV head
-                                dict(S=16, N=4, Hkv=2),        # N > Hkv
-                                dict(S=16, N=2, Hkv=8)])       # Hkv/N = 4
+# bf16 is compiled for three (dqk, dv) pairs; only other pairs are unsupported.
+@pytest.mark.parametrize("kw", [dict(dqk=96, dv=96), dict(dqk=192, dv=192), dict(dqk=128, dv=64)])
 def test_fwd_bf16_unsupported(kw):
     assert fwd(**kw) == UNSUPPORTED
 
 
 def test_decode_bf16_unsupported():
     assert dec(dqk=96, dv=96) == UNSUPPORTED
-    assert dec(S=64, N=2, Hkv=2) == UNSUPPORTED  # 32 signal + 1 noise heads per unit
+
+
+# Every head layout the validation accepts (S % N == 0, S % Hkv == 0, one of N and
+# Hkv dividing the other) is accepted by every bf16 entry point: without a device it
+# gets as far as the device check.
+VALID_LAYOUTS = [dict(S=16, N=2, Hkv=2),   # 8 signal heads per KV head (g = 8)
+                 dict(S=16, N=4, Hkv=2),   # N > Hkv
+                 dict(S=16, N=2, Hkv=8),   # Hkv/N = 4
+                 dict(S=12, N=4, Hkv=4),   # g = 3
+                 dict(S=10, N=2, Hkv=2),   # g = 5
+                 dict(S=64, N=2, Hkv=2),   # 32 signal + 1 noise heads per KV head
+                 dict(S=32, N=1, Hkv=8),   # a group over 8 KV heads
+                 dict(S=8, N=8, Hkv=2)]    # g = 1, 4 noise heads per KV head
+
+
+@pytest.mark.parametrize("kw", VALID_LAYOUTS, ids=lambda d: "S{S}_N{N}_Hkv{Hkv}".format(**d))
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (192, 128)], ids=lambda d: f"d{d[0]}")
+def test_every_valid_bf16_layout_reaches_the_device(kw, dims):
+    if _gpu_visible():
+        pytest.skip("a GPU is visible: a valid call would launch on the fake pointers")
+    dqk, dv = dims
+    assert fwd(dqk=dqk, dv=dv, **kw) == HIPERR
+    assert dec(dqk=dqk, dv=dv, **kw) == HIPERR
+    assert varlen(dqk=dqk, dv=dv, **kw) == HIPERR
+    assert train(dqk=dqk, dv=dv, **kw) == HIPERR
 
 
 def _gpu_visible():

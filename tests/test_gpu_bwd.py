@@ -13,7 +13,15 @@ Tolerances. The forward's bf16 bar (max |err| <= 2e-2 and mean |err| <= 2e-3 on 
 outputs) applied to each gradient tensor relative to its largest magnitude: the
 backward rounds P, dS and dO to bf16 before each matrix product (relative error
 2^-9 per operand) and accumulates in fp32, so errors scale with the gradient's size (with
-a floor of 0.05 for the magnitude, for gradients that vanish identically).
+a floor of 0.05 for the magnitude, for gradients that vanish identically). Beside it,
+a per-row bound: each row (one token's gradient vector for one head, or a token's
+dlambda over the signal heads) must be within 5% of that row's own largest magnitude
+plus 0.3% of the tensor's, so that small late-row gradients are not judged only
+against the tensor's largest row. The absolute part is needed because a row's error
+does not shrink with its gradient: dQ and dK come from dS = P (dP - delta), where dP
+is formed from the bf16-rounded dO and V, so the rounding error follows |dO| |V|
+rather than the (often much smaller) difference. Measured worst rows sit at 0.6 of
+this bound; an error of a few tens of percent on a row of 0.05 exceeds it.
 """
 import numpy as np
 import pytest
@@ -32,15 +40,29 @@ GRADS = ("dq_sig", "dq_noise", "dk", "dv", "dlam", "dgate")
 ARGS = ("q_sig", "q_noise", "k", "v", "lam", "gate")
 
 
+# Per-row bound: max |err| over a row <= ROW_REL * max |ref| over the row
+# + ROW_ABS * the tensor's largest magnitude.
+ROW_REL, ROW_ABS = 5e-2, 3e-3
+
+
 def assert_grad_close(got, ref, what):
     # A gradient that vanishes identically (a one-key window makes dS = P (dP - delta)
     # zero) is held to the bound of an O(0.05) gradient: 1e-3 absolute.
     scale = max(float(np.abs(ref).max()), 0.05)
     err = np.abs(got - ref)
-    U.log(f"{what}: max|err| {err.max():.3e} mean|err| {err.mean():.3e} max|ref| {scale:.3e}")
     assert np.isfinite(got).all(), f"{what}: non-finite gradient"
+    rows_err = err.reshape(-1, err.shape[-1]).max(axis=1)
+    rows_ref = np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=1)
+    row_ratio = rows_err / (ROW_REL * rows_ref + ROW_ABS * scale)
+    worst = int(np.argmax(row_ratio))
+    U.log(f"{what}: max|err| {err.max():.3e} mean|err| {err.mean():.3e} max|ref| {scale:.3e}; "
+          f"worst row {worst}: err {rows_err[worst]:.3e} / max|ref| {rows_ref[worst]:.3e} "
+          f"= {row_ratio[worst]:.3f} of the row bound")
     assert err.max() <= 2e-2 * scale, f"{what}: max {err.max():.3e} > 2e-2 * {scale:.3e}"
     assert err.mean() <= 2e-3 * scale, f"{what}: mean {err.mean():.3e} > 2e-3 * {scale:.3e}"
+    assert row_ratio[worst] <= 1.0, (
+        f"{what}: row {worst} error {rows_err[worst]:.3e} > {ROW_REL} * {rows_ref[worst]:.3e}"
+        f" + {ROW_ABS} * {scale:.3e}")
 
 
 def make(case_id, *, B, L, S, N, Hkv, dqk, dv, rope_dims=0, logits=False):
@@ -81,6 +103,11 @@ SMALL = {
                                      rope_dims=64), 1, {}),
     "edge_motif2_L33_w500": (621, dict(B=2, L=33, S=32, N=8, Hkv=16, dqk=128, dv=128), 500,
                              {}),
+    # head layouts whose noise heads' groups span several prefill sub-units: g = 8 on
+    # one KV head, a group over four KV heads, two noise heads on one KV head
+    "g8_ns8_L140": (622, dict(B=1, L=140, S=32, N=4, Hkv=4, dqk=128, dv=128), 0, {}),
+    "g8_r4_L130_w40": (623, dict(B=1, L=130, S=16, N=2, Hkv=8, dqk=192, dv=128), 40, {}),
+    "nn2_g2_L110": (624, dict(B=2, L=110, S=16, N=8, Hkv=4, dqk=64, dv=64), 0, {}),
 }
 
 
@@ -135,6 +162,25 @@ def test_backward_full_size_causal_sampled():
     L = cfg.L
     _sampled(cfg, [0, 1, 63, 64, 2047, 4095, 6000, L - 2, L - 1],
              list(range(L - 48, L)) + [8000], 631)
+
+
+def test_backward_full_size_causal_early_keys():
+    """Motif-3 full layer: dK/dV of early keys of batch row 0 (keys 0, 63, 64 and 4095),
+    which accumulate over thousands of queries across many query tiles of the dK/dV
+    kernel. The oracle needs every query row of that sequence (about a minute)."""
+    cfg = C.MOTIF3_FULL
+    shp = dict(B=cfg.B, L=cfg.L, S=cfg.S, N=cfg.N, Hkv=cfg.Hkv, dqk=cfg.dqk, dv=cfg.dv,
+               rope_dims=cfg.rope_dims)
+    x = make(633, **shp)
+    _, _, got = run_gpu(x, cfg.window)
+    torch.cuda.synchronize()
+    k_rows = [0, 63, 64, 4095]
+    U.log(f"oracle backward on key rows {k_rows} of batch row 0 ({U.host_cpu()})")
+    ref = oracle.ref_bwd(*(x[n] for n in ARGS), x["d_out"], window=cfg.window, q_rows=[0],
+                         k_rows=k_rows)
+    for n in ("dk", "dv"):
+        flat = got[n].reshape((cfg.B * cfg.L,) + got[n].shape[2:])
+        assert_grad_close(flat[k_rows], ref[n], f"{cfg.name} {n} early keys")
 
 
 def test_backward_full_size_sliding_window_sampled():

@@ -61,12 +61,20 @@ def test_small_full_output(name):
     U.assert_close(got, ref, kw["dtype"], name)
 
 
-# Every compiled bf16 prefill layout (signal heads per KV head NS, KV heads per
-# unit R) at every head size, causal and with a window: several key tiles and
-# a ragged tail, so every tile shape, the partial last tile and every wave
-# split run against the oracle.
+# bf16 prefill head layouts (S, N, Hkv) at every head size, causal and with a
+# window: several key tiles and a ragged tail, so every tile shape, the partial
+# last tile and every wave split run against the oracle. The names give
+# NS = S/Hkv signal heads per KV head, R = Hkv/N KV heads per noise head (or NN =
+# N/Hkv noise heads per KV head) and g = S/N signal heads per noise head. The
+# first five take one sub-unit per noise head; the rest split a noise head's
+# signal heads over several sub-units (g = 3, 5, 6, 8, 16), put several noise
+# heads on one KV head (NN = 2, 4) or spread a group over 4 or 8 KV heads.
 LAYOUTS = {"ns1_r1": (4, 4, 4), "ns2_r1": (8, 4, 4), "ns4_r1": (16, 4, 4),
-           "ns1_r2": (8, 4, 8), "ns2_r2": (16, 4, 8)}  # (S, N, Hkv)
+           "ns1_r2": (8, 4, 8), "ns2_r2": (16, 4, 8),
+           "ns8_r1_g8": (32, 4, 4), "ns3_r1_g3": (12, 4, 4), "ns5_r1_g5": (10, 2, 2),
+           "nn2_g2": (16, 8, 4), "nn2_g4": (16, 4, 2), "nn4_g1": (8, 8, 2),
+           "ns4_r2_g8": (32, 4, 8), "ns3_r2_g6": (24, 4, 8), "ns1_r4_g4": (8, 2, 8),
+           "ns2_r4_g8": (16, 2, 8), "ns2_r8_g16": (16, 1, 8)}
 DIMS = {"d64": (64, 64), "d128": (128, 128), "d192": (192, 128)}
 
 
@@ -174,6 +182,35 @@ def test_decode_stream_ragged(name, window):
                             host["lam"], host["gate"], lens, window=window)
     U.assert_close(got, ref, "bf16", f"decode stream {name} W={window}")
     assert np.all(got[5] == 0.0), "a sequence with no visible key must give zeros"
+
+
+# Decode head layouts whose units hold more than the 16 query heads of one MFMA
+# tile, so the workgroups split them (and recompute the noise heads they need):
+# a group over two KV heads with 16 signal heads on each; four noise heads on a
+# KV head with 16 signal heads; one noise head serving 32 signal heads on one KV
+# head; and a group over four KV heads (no split). (S, N, Hkv, dqk, dv), both
+# decode kernels (short spans and the streaming one), causal and windowed.
+DEC_LAYOUTS = {"ns16_r2_g32": (32, 1, 2, 64, 64), "ns16_nn4_g4": (64, 16, 4, 192, 128),
+               "ns32_r1_g32": (32, 1, 1, 128, 128), "ns2_r4_g8": (16, 2, 8, 192, 128)}
+
+
+@pytest.mark.parametrize("window", [0, 100])
+@pytest.mark.parametrize("lmax", [300, 2100], ids=["short", "stream"])
+@pytest.mark.parametrize("layout", sorted(DEC_LAYOUTS))
+def test_decode_layouts(layout, lmax, window):
+    S, N, Hkv, dqk, dv = DEC_LAYOUTS[layout]
+    cid = 250 + sorted(DEC_LAYOUTS).index(layout)
+    U.log(f"decode layout parity {layout} Lmax={lmax} window={window}")
+    host, dev = _decode_case(cid, B=4, Lmax=lmax, S=S, N=N, Hkv=Hkv, dqk=dqk, dv=dv,
+                             dtype="bf16")
+    lens = np.array([lmax, 1, lmax // 2 + 3, 0], dtype=np.int32)
+    out = gda_decode(dev["q_sig"], dev["q_noise"], dev["k_cache"], dev["v_cache"], dev["lam"],
+                     dev["gate"], cache_lens=torch.from_numpy(lens).cuda(), window=window)
+    got = U.to_f64(out)
+    ref = oracle.ref_decode(host["q_sig"], host["q_noise"], host["k_cache"], host["v_cache"],
+                            host["lam"], host["gate"], lens, window=window)
+    U.assert_close(got, ref, "bf16", f"decode {layout} Lmax={lmax} W={window}")
+    assert np.all(got[3] == 0.0), "a sequence with no visible key must give zeros"
 
 
 # Call options: an explicit softmax scale, and lambda/gate given as logits (the kernels
