@@ -16,7 +16,10 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgda_ref.so")
+# GDA_ORACLE_LIB names another build of gda_ref.c to load instead (the sanitizer
+# test runs the pins against an AddressSanitizer/UBSan build); it is never rebuilt.
+_OVERRIDE = os.environ.get("GDA_ORACLE_LIB")
+LIB_PATH = _OVERRIDE or os.path.join(_HERE, "libgda_ref.so")
 SRC = os.path.join(_HERE, "gda_ref.c")
 
 BF16, F32 = 0, 1
@@ -60,7 +63,8 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build()
+        if not _OVERRIDE:
+            build()
         lib = ctypes.CDLL(LIB_PATH)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         lib.gda_ref_fwd.restype = ctypes.c_int
