@@ -18,8 +18,10 @@ GDA_LAMBDA_LOGITS, GDA_GATE_LOGITS = 1, 2
 
 EXPORTED = ("gda_fwd", "gda_decode", "gda_fwd_ex", "gda_decode_ex", "gda_fwd_varlen",
             "gda_fwd_train", "gda_bwd", "gda_bwd_workspace_bytes", "gda_fwd_train_varlen",
-            "gda_bwd_varlen", "gda_decode_latent",
+            "gda_bwd_varlen", "gda_decode_latent", "gda_decode_latent_noalloc",
             "gda_decode_latent_workspace_bytes", "gda_status_string", "gda_last_error")
+# Size of the static scratch of gda_decode_latent_noalloc (GDA_DECODE_LATENT_SCRATCH_BYTES).
+DECODE_LATENT_SCRATCH_BYTES = 64 << 20
 
 
 class Options(ctypes.Structure):
@@ -76,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.gda_decode_latent.restype = i32
     lib.gda_decode_latent.argtypes = ([vp] * 9 + [i32] * 10 + [i32, ctypes.POINTER(Options), vp,
                                                                ctypes.c_size_t, vp])
+    lib.gda_decode_latent_noalloc.restype = i32
+    lib.gda_decode_latent_noalloc.argtypes = ([vp] * 9 + [i32] * 10 +
+                                              [i32, ctypes.POINTER(Options), vp])
     lib.gda_status_string.restype = ctypes.c_char_p
     lib.gda_status_string.argtypes = [i32]
     lib.gda_last_error.restype = ctypes.c_char_p
@@ -142,6 +147,17 @@ def decode_latent_raw(q_sig, q_noise, c_kv, k_rope, w_kv_b, lens, lam, gate, out
                                     B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window, dtype,
                                     ctypes.byref(opts) if opts is not None else None, workspace,
                                     workspace_bytes, stream)
+
+
+def decode_latent_noalloc_raw(q_sig, q_noise, c_kv, k_rope, w_kv_b, lens, lam, gate, out, B,
+                              Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window, dtype, opts,
+                              stream) -> int:
+    """Direct call of gda_decode_latent_noalloc (opts an Options or None)."""
+    return load().gda_decode_latent_noalloc(q_sig, q_noise, c_kv, k_rope, w_kv_b, lens, lam, gate,
+                                            out, B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window,
+                                            dtype,
+                                            ctypes.byref(opts) if opts is not None else None,
+                                            stream)
 
 
 def fwd_varlen_raw(q_sig, q_noise, k, v, lam, gate, out, cu_q, cu_k, nseq, max_seqlen_q, S, N,

@@ -142,18 +142,9 @@ def gda_fwd_varlen(q_sig: torch.Tensor, q_noise: torch.Tensor, k: torch.Tensor,
     return out
 
 
-def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Tensor,
-                      k_rope: torch.Tensor, w_kv_b: torch.Tensor, lam: torch.Tensor,
-                      gate: torch.Tensor, cache_lens: torch.Tensor | None = None,
-                      window: int = 0, out: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None, scale: float | None = None,
-                      lambda_logits: bool = False, gate_logits: bool = False) -> torch.Tensor:
-    """Decode over the latent cache. q_sig [B,S,Dn+Dr], q_noise [B,N,Dn+Dr], c_kv [B,Lmax,Dc],
-    k_rope [B,Lmax,Dr], w_kv_b [Hkv,Dn+dv,Dc], lam [B,S], gate [B,S,dv], cache_lens int32 [B]
-    or None -> out [B,S,dv]. ``workspace``: a uint8 device tensor of at least
-    ``latent_workspace_bytes(...)`` bytes (allocated here when None)."""
+def _latent_shapes(name, q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, cache_lens, out):
     if q_sig.dim() != 3 or c_kv.dim() != 3 or k_rope.dim() != 3 or w_kv_b.dim() != 3:
-        raise ValueError("gda_decode_latent: q/c_kv/k_rope/w_kv_b must be 3-D")
+        raise ValueError(f"{name}: q/c_kv/k_rope/w_kv_b must be 3-D")
     B, S, dqk = q_sig.shape
     N = q_noise.shape[1]
     Lmax, Dc = c_kv.shape[1], c_kv.shape[2]
@@ -162,9 +153,9 @@ def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Te
     Dn = dqk - Dr
     dv = rows - Dn
     dev, dt = q_sig.device, q_sig.dtype
-    code = _dtype_code(q_sig)
+    _dtype_code(q_sig)
     if dev.type != "cuda":
-        raise ValueError("gda_decode_latent: tensors must be on a HIP (cuda) device")
+        raise ValueError(f"{name}: tensors must be on a HIP (cuda) device")
     _check("q_sig", q_sig, (B, S, dqk), dt, dev)
     _check("q_noise", q_noise, (B, N, dqk), dt, dev)
     _check("c_kv", c_kv, (B, Lmax, Dc), dt, dev)
@@ -179,6 +170,21 @@ def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Te
     if out is None:
         out = torch.empty((B, S, dv), dtype=dt, device=dev)
     _check("out", out, (B, S, dv), dt, dev)
+    return B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, dev, lens_ptr, out
+
+
+def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Tensor,
+                      k_rope: torch.Tensor, w_kv_b: torch.Tensor, lam: torch.Tensor,
+                      gate: torch.Tensor, cache_lens: torch.Tensor | None = None,
+                      window: int = 0, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, scale: float | None = None,
+                      lambda_logits: bool = False, gate_logits: bool = False) -> torch.Tensor:
+    """Decode over the latent cache. q_sig [B,S,Dn+Dr], q_noise [B,N,Dn+Dr], c_kv [B,Lmax,Dc],
+    k_rope [B,Lmax,Dr], w_kv_b [Hkv,Dn+dv,Dc], lam [B,S], gate [B,S,dv], cache_lens int32 [B]
+    or None -> out [B,S,dv]. ``workspace``: a uint8 device tensor of at least
+    ``latent_workspace_bytes(...)`` bytes (allocated here when None)."""
+    B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, dev, lens_ptr, out = _latent_shapes(
+        "gda_decode_latent", q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, cache_lens, out)
     need = _lib.latent_workspace_bytes(B, Lmax, S, N, int(window))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -187,8 +193,31 @@ def gda_decode_latent(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Te
     _lib.check(_lib.decode_latent_raw(
         q_sig.data_ptr(), q_noise.data_ptr(), c_kv.data_ptr(), k_rope.data_ptr(),
         w_kv_b.data_ptr(), lens_ptr, lam.data_ptr(), gate.data_ptr(), out.data_ptr(), B, Lmax, S,
-        N, Hkv, Dn, Dr, Dc, dv, int(window), code, _lib.options(scale, lambda_logits, gate_logits),
-        workspace.data_ptr(), workspace.numel(), _stream(dev)))
+        N, Hkv, Dn, Dr, Dc, dv, int(window), _dtype_code(q_sig),
+        _lib.options(scale, lambda_logits, gate_logits), workspace.data_ptr(), workspace.numel(),
+        _stream(dev)))
+    return out
+
+
+def gda_decode_latent_noalloc(q_sig: torch.Tensor, q_noise: torch.Tensor, c_kv: torch.Tensor,
+                              k_rope: torch.Tensor, w_kv_b: torch.Tensor, lam: torch.Tensor,
+                              gate: torch.Tensor, out: torch.Tensor,
+                              cache_lens: torch.Tensor | None = None, window: int = 0,
+                              scale: float | None = None, lambda_logits: bool = False,
+                              gate_logits: bool = False) -> torch.Tensor:
+    """gda_decode_latent without a workspace: the library's static per-GPU scratch
+    (DECODE_LATENT_SCRATCH_BYTES) serves instead, and nothing is allocated, so ``out``
+    must be given. Calls that may overlap on one GPU must be serialised by the caller."""
+    if out is None:
+        raise ValueError("gda_decode_latent_noalloc: out must be preallocated")
+    B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, dev, lens_ptr, out = _latent_shapes(
+        "gda_decode_latent_noalloc", q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, cache_lens,
+        out)
+    _lib.check(_lib.decode_latent_noalloc_raw(
+        q_sig.data_ptr(), q_noise.data_ptr(), c_kv.data_ptr(), k_rope.data_ptr(),
+        w_kv_b.data_ptr(), lens_ptr, lam.data_ptr(), gate.data_ptr(), out.data_ptr(), B, Lmax, S,
+        N, Hkv, Dn, Dr, Dc, dv, int(window), _dtype_code(q_sig),
+        _lib.options(scale, lambda_logits, gate_logits), _stream(dev)))
     return out
 
 

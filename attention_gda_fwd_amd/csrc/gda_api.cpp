@@ -499,12 +499,16 @@ size_t gda_decode_latent_workspace_bytes(int B, int Lmax, int S, int N, int wind
   return gda::latent_workspace_bytes(B, Lmax, S, N, window);
 }
 
-gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void* c_kv,
-                             const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
-                             const void* lambda, const void* gate, void* out, int B, int Lmax,
-                             int S, int N, int Hkv, int Dn, int Dr, int Dc, int dv, int window,
-                             gda_dtype dtype, const gda_options* opts, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument packing shared by the two latent-decode entry points.
+gda_status latent_prepare(const void* q_sig, const void* q_noise, const void* c_kv,
+                          const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
+                          const void* lambda, const void* gate, void* out, int B, int Lmax,
+                          int S, int N, int Hkv, int Dn, int Dr, int Dc, int dv, int window,
+                          gda_dtype dtype, const gda_options* opts, gda::LatentArgs* a) {
   if (!q_sig || !q_noise || !c_kv || !k_rope || !w_kv_b || !lambda || !gate || !out)
     return fail(GDA_ERROR_INVALID_ARGUMENT, "null tensor pointer");
   gda_status st = check_alignment(q_sig, q_noise, c_kv, k_rope, w_kv_b, lambda, gate);
@@ -515,36 +519,75 @@ gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void*
     return fail(GDA_ERROR_INVALID_ARGUMENT, "every size must be >= 1 (Dr >= 0)");
   st = validate_common(B, Lmax, S, N, Hkv, Dn + Dr, dv, window, dtype);
   if (st != GDA_SUCCESS) return st;
-  gda::LatentArgs a;
-  a.q_sig = q_sig;
-  a.q_noise = q_noise;
-  a.c_kv = c_kv;
-  a.k_rope = k_rope;
-  a.w_kv_b = w_kv_b;
-  a.lens = cache_lens;
-  a.lam = lambda;
-  a.gate = gate;
-  a.out = out;
-  a.workspace = workspace;
-  a.B = B;
-  a.Lmax = Lmax;
-  a.S = S;
-  a.N = N;
-  a.Hkv = Hkv;
-  a.window = window;
+  a->q_sig = q_sig;
+  a->q_noise = q_noise;
+  a->c_kv = c_kv;
+  a->k_rope = k_rope;
+  a->w_kv_b = w_kv_b;
+  a->lens = cache_lens;
+  a->lam = lambda;
+  a->gate = gate;
+  a->out = out;
+  a->workspace = nullptr;
+  a->B = B;
+  a->Lmax = Lmax;
+  a->S = S;
+  a->N = N;
+  a->Hkv = Hkv;
+  a->window = window;
   float scale = 0.f;
-  if ((st = apply_options(opts, Dn + Dr, &scale, &a.scale_log2, &a.flags)) != GDA_SUCCESS)
+  if ((st = apply_options(opts, Dn + Dr, &scale, &a->scale_log2, &a->flags)) != GDA_SUCCESS)
     return st;
   if (dtype != GDA_BF16) return fail(GDA_ERROR_UNSUPPORTED, "latent decode: bf16 only");
   if (!gda::latent_supported(Dn, Dr, Dc, dv, S, N, Hkv))
     return fail(GDA_ERROR_UNSUPPORTED,
                 "latent decode: needs (Dn,Dr,Dc,dv) = (128,64,512,128), S+N <= 128, "
                 "g <= 15 and <= 16 query heads per KV head");
+  return GDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void* c_kv,
+                             const void* k_rope, const void* w_kv_b, const int32_t* cache_lens,
+                             const void* lambda, const void* gate, void* out, int B, int Lmax,
+                             int S, int N, int Hkv, int Dn, int Dr, int Dc, int dv, int window,
+                             gda_dtype dtype, const gda_options* opts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  gda::LatentArgs a;
+  gda_status st = latent_prepare(q_sig, q_noise, c_kv, k_rope, w_kv_b, cache_lens, lambda, gate,
+                                 out, B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window, dtype, opts, &a);
+  if (st != GDA_SUCCESS) return st;
   if (!workspace || !aligned(workspace, 16))
     return fail(GDA_ERROR_INVALID_ARGUMENT, "latent decode: workspace missing or misaligned");
   if (workspace_bytes < gda::latent_workspace_bytes(B, Lmax, S, N, window))
     return fail(GDA_ERROR_INVALID_ARGUMENT, "latent decode: workspace too small");
+  a.workspace = workspace;
   if ((st = require_device()) != GDA_SUCCESS) return st;
+  return from_hip(gda::launch_decode_latent(a, (hipStream_t)stream));
+}
+
+gda_status gda_decode_latent_noalloc(const void* q_sig, const void* q_noise, const void* c_kv,
+                                     const void* k_rope, const void* w_kv_b,
+                                     const int32_t* cache_lens, const void* lambda,
+                                     const void* gate, void* out, int B, int Lmax, int S, int N,
+                                     int Hkv, int Dn, int Dr, int Dc, int dv, int window,
+                                     gda_dtype dtype, const gda_options* opts, void* stream) {
+  gda::LatentArgs a;
+  gda_status st = latent_prepare(q_sig, q_noise, c_kv, k_rope, w_kv_b, cache_lens, lambda, gate,
+                                 out, B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, window, dtype, opts, &a);
+  if (st != GDA_SUCCESS) return st;
+  if (gda::latent_workspace_bytes(B, Lmax, S, N, window) > GDA_DECODE_LATENT_SCRATCH_BYTES)
+    return fail(GDA_ERROR_INVALID_ARGUMENT,
+                "latent decode (no allocation): these sizes need more scratch than the "
+                "static GDA_DECODE_LATENT_SCRATCH_BYTES; use gda_decode_latent with a workspace");
+  if ((st = require_device()) != GDA_SUCCESS) return st;
+  void* scratch = nullptr;
+  const hipError_t e = gda::latent_scratch(&scratch);
+  if (e != hipSuccess) return from_hip(e);
+  a.workspace = scratch;
   return from_hip(gda::launch_decode_latent(a, (hipStream_t)stream));
 }
 

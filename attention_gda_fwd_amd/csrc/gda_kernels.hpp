@@ -127,6 +127,9 @@ hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 
 bool fwd_bf16_supported(int dqk, int dv, const UnitPlan& plan);
 hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream);
+// Address of this GPU's static latent-decode scratch (looked up once per device,
+// with that device current), for the allocation-free entry point.
+hipError_t latent_scratch(void** ptr);
 bool latent_supported(int Dn, int Dr, int Dc, int dv, int S, int N, int Hkv);
 size_t latent_workspace_bytes(int B, int Lmax, int S, int N, int window);
 bool decode_bf16_supported(int dqk, int dv, const UnitPlan& plan);

@@ -19,8 +19,17 @@
 //  3. latent_merge_kernel: merges the splits, up-projects o with W_v[h] (fp32),
 //     and applies lambda and the gate.
 // Reading 1152 B per cached token instead of Hkv * (dqk + dv) * 2 = 10240 B.
+#include <mutex>
+
+#include "../../include/gda.h"
 #include "gda_device.hpp"
 #include "gda_kernels.hpp"
+
+// The workspace of the allocation-free entry point: a file-scope device array
+// (each GPU holds its own copy). Host code must never pass its name to a kernel
+// or a copy: the name is a host-side stand-in; latent_scratch() gives the
+// device address.
+static __device__ __align__(256) unsigned char scratch[GDA_DECODE_LATENT_SCRATCH_BYTES];
 
 namespace gda {
 namespace {
@@ -432,6 +441,29 @@ size_t latent_workspace_bytes(int B, int Lmax, int S, int N, int window) {
   const size_t qa = (size_t)B * XP * LQW * 2;
   const size_t qa_pad = (qa + 255) & ~(size_t)255;
   return qa_pad + (size_t)B * ns * XP * LPART * 4;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t latent_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream) {

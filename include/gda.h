@@ -20,8 +20,10 @@
  *   - All tensors are dense, row-major, innermost dimension contiguous, device
  *     memory, 16-byte aligned, of the element type `dtype` (all share it).
  *   - Ownership: the caller owns every buffer. The library allocates no device
- *     memory and keeps no mutable global state (only a thread-local diagnostic
- *     string); calls are thread-safe. `out` must not alias an input.
+ *     memory at run time and keeps no mutable global state beyond a thread-local
+ *     diagnostic string and, for gda_decode_latent_noalloc only, one static
+ *     device array per GPU (below) with its looked-up address; calls are
+ *     thread-safe. `out` must not alias an input.
  *   - Asynchrony: a call enqueues its kernels on `stream` (a hipStream_t; NULL
  *     is the default stream) and returns without synchronizing.
  *   - Errors: arguments are validated on the host before any HIP call; a
@@ -175,6 +177,27 @@ gda_status gda_decode_latent(const void* q_sig, const void* q_noise, const void*
                              int B, int Lmax, int S, int N, int Hkv, int Dn, int Dr, int Dc,
                              int dv, int window, gda_dtype dtype, const gda_options* opts,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free latent-cache decode, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): gda_decode_latent with the same arguments
+ * minus the workspace, which is a static device array of
+ * GDA_DECODE_LATENT_SCRATCH_BYTES bytes built into the library (each GPU the
+ * library runs on holds its own copy from load until the process ends). Calls
+ * whose gda_decode_latent_workspace_bytes(...) exceeds that size return
+ * GDA_ERROR_INVALID_ARGUMENT and launch nothing. The call allocates nothing and
+ * needs no zeroed memory (every scratch byte it reads it wrote earlier in the
+ * same call). Every call on one GPU uses that GPU's one array: calls that may
+ * overlap in time on one GPU (different streams, or threads without ordering)
+ * race and must be serialised by the caller; calls on one stream are ordered. */
+#define GDA_DECODE_LATENT_SCRATCH_BYTES ((size_t)64 << 20)
+
+gda_status gda_decode_latent_noalloc(const void* q_sig, const void* q_noise, const void* c_kv,
+                                     const void* k_rope, const void* w_kv_b,
+                                     const int32_t* cache_lens, const void* lambda,
+                                     const void* gate, void* out, int B, int Lmax, int S, int N,
+                                     int Hkv, int Dn, int Dr, int Dc, int dv, int window,
+                                     gda_dtype dtype, const gda_options* opts, void* stream);
 
 /* Training: the forward that also keeps what the backward needs, and the
  * backward (the pages' setting is training: the Motif 3 walk-through trains the

@@ -140,6 +140,43 @@ def test_latent_unsupported(kw):
     assert lat(**kw) == UNSUPPORTED
 
 
+def lat_noalloc(**kw):
+    a = dict(q=FAKE, qn=FAKE, c=FAKE, r=FAKE, w=FAKE, lens=None, lam=FAKE, gate=FAKE, out=FAKE,
+             B=2, Lmax=64, S=64, N=16, Hkv=16, Dn=128, Dr=64, Dc=512, dv=128, window=0,
+             dtype=BF16)
+    a.update(kw)
+    return _lib.decode_latent_noalloc_raw(a["q"], a["qn"], a["c"], a["r"], a["w"], a["lens"],
+                                          a["lam"], a["gate"], a["out"], a["B"], a["Lmax"],
+                                          a["S"], a["N"], a["Hkv"], a["Dn"], a["Dr"], a["Dc"],
+                                          a["dv"], a["window"], a["dtype"], None, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(out=None), dict(c=FAKE + 8), dict(B=0),
+                                dict(S=8, N=3), dict(window=-1)],
+                         ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_latent_noalloc_invalid_arguments(kw):
+    assert lat_noalloc(**kw) == INVALID
+
+
+def test_latent_noalloc_rejects_sizes_beyond_its_scratch():
+    # Sizes whose workspace exceeds the static scratch are refused on the host, before
+    # any HIP call, with the reason in gda_last_error.
+    big = dict(B=512, Lmax=1 << 20)
+    assert _lib.latent_workspace_bytes(512, 1 << 20, 64, 16, 0) > _lib.DECODE_LATENT_SCRATCH_BYTES
+    assert lat_noalloc(**big) == INVALID
+    assert b"scratch" in _lib.load().gda_last_error()
+    assert lat_noalloc(dtype=F32) == UNSUPPORTED
+    assert lat_noalloc(Dc=256) == UNSUPPORTED
+    if not _gpu_visible():
+        assert lat_noalloc() == HIPERR
+
+
+def test_latent_noalloc_scratch_size_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "gda.h")).read()
+    m = re.search(r"#define GDA_DECODE_LATENT_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DECODE_LATENT_SCRATCH_BYTES
+
+
 def test_latent_workspace_size():
     n = _lib.latent_workspace_bytes(64, 32768, 64, 16, 0)
     assert 0 < n < 512 << 20
