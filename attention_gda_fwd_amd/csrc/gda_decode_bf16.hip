@@ -91,9 +91,11 @@ template <int DQK, int DV>
 struct DecTile {
   static constexpr int KS = DQK / 32;
   static constexpr int DB = DV / 16;
-  static constexpr int VROW = DV + 16;   // padded row of the V staging tile
   static constexpr int VCH = DV / 8;     // 16-byte chunks per V row
-  static constexpr int STAGE = CK * VROW;            // elements per wave stage
+  static constexpr int VPAIR = VCH / 2;  // 32-byte chunk pairs per V row
+  static constexpr int VRPB = 512 / DV;  // V rows per 1 KB copy block
+  static constexpr int VB = DV / 16;     // 1 KB copy blocks per 32-row V chunk
+  static constexpr int STAGE = CK * DV;  // elements per wave stage (one V chunk)
   // merge area per wave: m[16], l[16], O^T[DV][16]
   static constexpr int MERGE_FLOATS = 32 + DV * 16;
   static constexpr int STAGE_BYTES = NW * STAGE * 2;
@@ -120,7 +122,9 @@ __device__ __forceinline__ float merged_impl(const float* merge, int h, int d) {
 }
 
 // 4 waves per SIMD (<= 128 VGPRs) so that 4 workgroups share a CU and a
-// B x units = 1024-workgroup grid is resident at once on 256 CUs.
+// B x units = 1024-workgroup grid is resident at once on 256 CUs. The V chunk
+// goes HBM -> LDS with direct copies (no registers), so the K fragments, the
+// queries and the accumulators fit the 128 registers without spilling.
 template <int DQK, int DV>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4, 4)))
 decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
@@ -153,27 +157,48 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
   const int nch = (pos - lo + CK) / CK;
   const int ch0 = (int)(((int64_t)wave * nch) / NW), ch1 = (int)(((int64_t)(wave + 1) * nch) / NW);
 
-  uint16_t* stage = (uint16_t*)smem + wave * T::STAGE;
+  const uint16_t* stage = (const uint16_t*)smem + wave * T::STAGE;
+  const uint32_t stage_lds = (uint32_t)(uintptr_t)(const lds_void*)stage;
   float* merge = (float*)smem;
   auto merged = [](const float* mg, int h, int d) { return merged_impl<T::MERGE_FLOATS>(mg, h, d); };
+
+  // The epilogue's first lambda and gate values (phase 0, two per thread), loaded
+  // now so that their latency hides behind the key loop: with short spans the
+  // loop is one chunk per wave, and a second round trip to memory after it would
+  // be a large part of the kernel.
+  // Packed two bf16 per register: value k in bits 16k .. 16k+15.
+  uint32_t lam_pre = 0, gate_pre = 0;
+  {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = tid + k * NT;
+      if (idx < ns * DV) {
+        const int i = sh.kv0 * NS + sh.off + idx / DV;
+        lam_pre |= (uint32_t)lam[(int64_t)b * S + i] << (16 * k);
+        gate_pre |= (uint32_t)gate[((int64_t)b * S + i) * DV + idx % DV] << (16 * k);
+      }
+    }
+  }
 
 #pragma unroll 1
   for (int ph = 0; ph < R; ++ph) {
     const int nh = ph == 0 ? ns + sh.nn : ns;  // query heads (MFMA columns) of this phase
     const int kvh = sh.kv0 + ph;
     const int sig0 = kvh * NS + sh.off;       // this phase's first signal head
-    // Q^T B operand: column col is head col of the phase (zero if unused).
+    // Q^T B operand: column col is head col of the phase (zero if unused). Each
+    // load takes a wave-uniform base and a 32-bit lane offset, so no 64-bit
+    // per-lane address stays live.
     bf16x8 qf[T::KS];
     {
-      const uint16_t* qp = nullptr;
-      if (col < ns)
-        qp = q_sig + ((int64_t)b * S + sig0 + col) * DQK;
-      else if (col < nh)
-        qp = q_noise + ((int64_t)b * N + sh.nb + (col - ns)) * DQK;
+      const uint16_t* qs_row = q_sig + ((int64_t)b * S + sig0) * DQK;
+      const uint16_t* qn_row = q_noise + ((int64_t)b * N + sh.nb) * DQK;
+      const bool is_sig = col < ns, is_noise = !is_sig && col < nh;
+      const uint32_t off = (uint32_t)((is_sig ? col : col - ns) * DQK + 8 * g4);
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks) {
         u32x4 w = {0u, 0u, 0u, 0u};
-        if (qp) w = ldg16(qp + ks * 32 + 8 * g4);
+        if (is_sig) w = ldg16(qs_row + off + ks * 32);
+        if (is_noise) w = ldg16(qn_row + off + ks * 32);
         qf[ks] = __builtin_bit_cast(bf16x8, w);
       }
     }
@@ -189,34 +214,35 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
 #pragma unroll 1
     for (int ch = ch0; ch < ch1; ++ch) {
       const int s0 = lo + ch * CK;
-      // V rows of the chunk -> wave-private LDS tile (rows past pos are zero).
-      u32x4 vv[(CK * T::VCH) / 64];
+      // V rows of the chunk -> this wave's LDS stage, direct copies in 1 KB blocks
+      // of VRPB rows with 32-byte chunk pairs XOR-swizzled by row (the prefill's V
+      // layout). Rows past pos read row pos: finite data whose weights are 0.
+      {
+        const int nrows = min(CK, pos - s0 + 1);
+        const char* vb = (const char*)(vg + vbase + (int64_t)s0 * vstride);
 #pragma unroll
-      for (int i = 0; i < (CK * T::VCH) / 64; ++i) {
-        const int cidx = lane + 64 * i;
-        const int key = cidx / T::VCH, cc = cidx % T::VCH;
-        const int ka = s0 + key;
-        vv[i] = u32x4{0u, 0u, 0u, 0u};
-        if (ka <= pos) vv[i] = ldg16(vg + vbase + ka * vstride + cc * 8);
+        for (int j = 0; j < T::VB; ++j) {
+          const int r = T::VRPB * j + lane / T::VCH;
+          const int cch = (lane % T::VCH) ^ ((r % T::VPAIR) << 1);
+          dma16_lds(vb, (uint32_t)min(r, nrows - 1) * (uint32_t)(vstride * 2) + 16u * (uint32_t)cch,
+                    stage_lds + 1024u * (uint32_t)j);
+        }
       }
-      // S^T = K . Q^T, K fragments straight from global memory.
+      // S^T = K . Q^T, K fragments straight from global memory (a wave-uniform
+      // chunk base plus a 32-bit lane offset).
       floatx4 s[2];
+      const uint16_t* kchunk = kg + kbase + (int64_t)s0 * kstride;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int key = min(s0 + 16 * kb + col, pos);
-        const uint16_t* kp = kg + kbase + key * kstride + 8 * g4;
+        const uint32_t kr = (uint32_t)min(16 * kb + col, pos - s0);
+        const uint32_t koff = kr * (uint32_t)kstride + 8u * (uint32_t)g4;
         bf16x8 a[T::KS];
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) a[ks] = __builtin_bit_cast(bf16x8, ldg16(kp + ks * 32));
+        for (int ks = 0; ks < T::KS; ++ks)
+          a[ks] = __builtin_bit_cast(bf16x8, ldg16(kchunk + koff + ks * 32));
         s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) s[kb] = mfma_16x16x32(a[ks], qf[ks], s[kb]);
-      }
-#pragma unroll
-      for (int i = 0; i < (CK * T::VCH) / 64; ++i) {
-        const int cidx = lane + 64 * i;
-        const int key = cidx / T::VCH, cc = cidx % T::VCH;
-        *(u32x4*)(stage + key * T::VROW + cc * 8) = vv[i];
       }
       if (s0 + CK - 1 > pos) {
 #pragma unroll
@@ -249,14 +275,23 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
           pb[4 * kb + r] = (__bf16)p;
         }
       lsum += ps;
-      // O^T += V^T . P^T
+      // O^T += V^T . P^T, V^T from transposed reads of the swizzled V rows, once
+      // this wave's copies of the chunk have landed.
+      wait_vmcnt<0>();
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint16_t* va = stage + (4 * g4 + (col >> 2)) * T::VROW + 16 * db + 4 * (col & 3);
-        const shortx4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
-        const shortx4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(va + 16 * T::VROW));
+        shortx4 half[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int r = 16 * hf + 4 * g4 + (col >> 2);
+          const int chunk = 2 * db + ((col & 3) >> 1);
+          const uint16_t* va =
+              stage + r * DV + ((chunk ^ ((r % T::VPAIR) << 1)) << 3) + 4 * (col & 1);
+          half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
+        }
         typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
-        const shortx8 a8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
+                            half[1][0], half[1][1], half[1][2], half[1][3]};
         o[db] = mfma_16x16x32(__builtin_bit_cast(bf16x8, a8), pb, o[db]);
       }
     }
@@ -290,8 +325,12 @@ decode_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restric
         hn = sHN[d];
       }
       const int64_t o_idx = ((int64_t)b * S + i) * DV + d;
-      float lm = bf16_to_f32(lam[(int64_t)b * S + i]);
-      float gv = bf16_to_f32(gate[o_idx]);
+      const int k = (idx - tid) / NT;  // this thread's k-th value of the phase
+      const bool pre = ph == 0 && k < 2;
+      float lm = pre ? (k == 0 ? bf16_lo(lam_pre) : bf16_hi(lam_pre))
+                     : bf16_to_f32(lam[(int64_t)b * S + i]);
+      float gv = pre ? (k == 0 ? bf16_lo(gate_pre) : bf16_hi(gate_pre))
+                     : bf16_to_f32(gate[o_idx]);
       if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
       if (flags & kGateLogits) gv = sigmoid_f32(gv);
       out[o_idx] = f32_to_bf16(gv * (hs - lm * hn));
