@@ -10,12 +10,13 @@
 //
 // Nothing is expanded. The key term q_nope . (W_k[h] c) is (W_k[h]^T q_nope) . c,
 // and the value sum sum_s p_s W_v[h] c_s is W_v[h] (sum_s p_s c_s), so:
-//  1. latent_absorb_kernel: q~ = [W_k[h]^T q_nope ; q_rope] (Dc + Dr values) for
-//     every query head, rounded to bf16, into the workspace;
-//  2. latent_attend_kernel: every query head of a sequence attends over the same
-//     latent keys [c ; k_rope] with the latent c as the value (a multi-query
-//     attention of all S + N heads); split-KV over workgroups, each writing
-//     partial (max, sum, o) per head to the workspace;
+//  1. latent_absorb2_kernel: q~ = [W_k[h]^T q_nope ; q_rope] (Dc + Dr values) for
+//     every query head, on the matrix cores, rounded to bf16, into the workspace;
+//  2. latent_attend2_kernel (up to 80 query heads; latent_attend_kernel above
+//     that): every query head of a sequence attends over the same latent keys
+//     [c ; k_rope] with the latent c as the value (a multi-query attention of all
+//     S + N heads); split-KV over workgroups, each writing partial (max, sum, o)
+//     per head to the workspace;
 //  3. latent_merge_kernel: merges the splits, up-projects o with W_v[h] (fp32),
 //     and applies lambda and the gate.
 // Reading 1152 B per cached token instead of Hkv * (dqk + dv) * 2 = 10240 B.
@@ -58,94 +59,100 @@ __device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
 // Heads of KV head h: signal i when floor(i*Hkv/S) == h, noise j when floor(j*Hkv/N) == h.
 // Column of a head in the workspace: signal i -> i, noise j -> S + j.
 
-// ---- 1. absorb ----------------------------------------------------------------
-constexpr int ABS_SEQ = 4;  // sequences per absorb workgroup (the weight slice is loaded once)
+// ---- 1. absorb on the matrix cores ---------------------------------------------
+// Per KV head h the absorbed queries are one small GEMM: Q~^T[c][col] =
+// sum_d W_k[h][d][c] q_nope[col][d] over the query columns col that read h. One
+// workgroup per (h, block of AB_COLS columns) stages W_k[h] (128 rows of 1 KB)
+// in LDS with direct copies, 32-byte chunk pairs XOR-swizzled by row (pair ^=
+// row % 8), so that the W_k^T operand (16 latent dims x 32 rows) comes from
+// conflict-free transposed reads; each wave takes 16 columns, holds their q_nope
+// as the B operand (4 k-steps) and walks the 32 tiles of 16 latent dims, rounding
+// each fp32 result to bf16 once. The rotary part of each query is copied, and
+// padding columns are cleared by the workgroups of h = 0.
+constexpr int AB_COLS = 64;  // query columns per workgroup (16 per wave)
 
-// One workgroup per (KV head h, ABS_SEQ sequences). Thread t owns latent columns
-// 8(t%64) .. +7 and key dims 32(t/64) .. +31 of W_k[h], loaded once with 32
-// independent 16-byte loads; for each sequence and group of 4 heads the four dim
-// quarters are summed through LDS.
 __global__ void __launch_bounds__(256)
-latent_absorb_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
-                     const uint16_t* __restrict__ w_kv_b, uint16_t* __restrict__ qa, int B,
-                     int S, int N, int Hkv, int XP) {
-  constexpr int MAXH = 16, HG = 4;
-  __shared__ float sq[MAXH][LDN];
-  __shared__ float sred[4][HG][LDC];
-  __shared__ int scol[MAXH];
-  __shared__ int snh;
-  const int h = blockIdx.x % Hkv, b0 = (blockIdx.x / Hkv) * ABS_SEQ;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    int n = 0;
-    for (int i = 0; i < S && n < MAXH; ++i)
-      if ((int)(((int64_t)i * Hkv) / S) == h) scol[n++] = i;
-    for (int j = 0; j < N && n < MAXH; ++j)
-      if ((int)(((int64_t)j * Hkv) / N) == h) scol[n++] = S + j;
-    snh = n;
+latent_absorb2_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__ q_noise,
+                      const uint16_t* __restrict__ w_kv_b, uint16_t* __restrict__ qa, int B,
+                      int S, int N, int Hkv, int XP) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sW[LDN * LDC];  // 128 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g4 = lane >> 4;
+  // Query heads of KV head h: signal heads h*NS .. +NS-1, then noise heads
+  // ceil(h*N/Hkv) .. ceil((h+1)*N/Hkv)-1.
+  const int NS = S / Hkv;
+  const int nblk = (int)(((int64_t)B * (NS + (N + Hkv - 1) / Hkv) + AB_COLS - 1) / AB_COLS);
+  const int h = blockIdx.x / nblk, blk = blockIdx.x - (blockIdx.x / nblk) * nblk;
+  const int n0 = (int)(((int64_t)h * N + Hkv - 1) / Hkv);
+  const int n1 = (int)(((int64_t)(h + 1) * N + Hkv - 1) / Hkv);
+  const int nkv = NS + (n1 - n0);          // query heads on h
+  const int ncols = B * nkv;               // (sequence, head) columns of h
+  if (blk * AB_COLS >= ncols) return;
+
+  // W_k[h] -> LDS: row d is 1 KB (64 pieces of 16 bytes), piece p stored at slot
+  // p ^ ((d & 7) << 1); wave w copies rows w, w+4, ...
+  {
+    const char* wk = (const char*)(w_kv_b + (int64_t)h * (LDN + LDV) * LDC);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const lds_void*)sW;
+    for (int d = wave; d < LDN; d += 4)
+      dma16_lds(wk + (int64_t)d * LDC * 2, 16u * (uint32_t)(lane ^ ((d & 7) << 1)),
+                lds0 + 1024u * (uint32_t)d);
   }
-  const int cg = tid & 63, dq = tid >> 6;
-  const uint16_t* w = w_kv_b + ((int64_t)h * (LDN + LDV) + 32 * dq) * LDC + 8 * cg;
-  u32x4 wr[32];
+  // This wave's 16 columns: q_nope as the B operand (k-step ks: dims 32ks + 8 g4 ..).
+  const int c0 = blk * AB_COLS + 16 * wave + col;  // this lane's column
+  const bool live = c0 < ncols;
+  const int cb = live ? c0 / nkv : 0, cx = live ? c0 - (c0 / nkv) * nkv : 0;
+  const int head = cx < NS ? h * NS + cx : S + n0 + (cx - NS);
+  const uint16_t* q = cx < NS ? q_sig + ((int64_t)cb * S + h * NS + cx) * (LDN + LDR)
+                              : q_noise + ((int64_t)cb * N + n0 + (cx - NS)) * (LDN + LDR);
+  bf16x8 qb[LDN / 32];
 #pragma unroll
-  for (int d = 0; d < 32; ++d) wr[d] = ldg16(w + (int64_t)d * LDC);
-  __syncthreads();
-  const int nh = snh;
-  for (int b = b0; b < min(B, b0 + ABS_SEQ); ++b) {
-    for (int idx = tid; idx < nh * LDN; idx += 256) {
-      const int x = idx / LDN, d = idx - (idx / LDN) * LDN;
-      const int col = scol[x];
-      const uint16_t* q = col < S ? q_sig + ((int64_t)b * S + col) * (LDN + LDR)
-                                  : q_noise + ((int64_t)b * N + (col - S)) * (LDN + LDR);
-      sq[x][d] = bf16_to_f32(q[d]);
-    }
-    __syncthreads();
-    for (int h0 = 0; h0 < nh; h0 += HG) {
-      float acc[HG][8];
-#pragma unroll
-      for (int x = 0; x < HG; ++x)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[x][u] = 0.f;
-#pragma unroll
-      for (int d = 0; d < 32; ++d) {
-#pragma unroll
-        for (int x = 0; x < HG; ++x) {
-          const float qv = sq[min(h0 + x, nh - 1)][32 * dq + d];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            acc[x][2 * u] = fmaf(qv, bf16_lo(wr[d][u]), acc[x][2 * u]);
-            acc[x][2 * u + 1] = fmaf(qv, bf16_hi(wr[d][u]), acc[x][2 * u + 1]);
-          }
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < HG; ++x)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) sred[dq][x][8 * cg + u] = acc[x][u];
-      __syncthreads();
-      for (int idx = tid; idx < HG * LDC; idx += 256) {
-        const int x = idx / LDC, cidx = idx - (idx / LDC) * LDC;
-        if (h0 + x < nh) {
-          const float v =
-              (sred[0][x][cidx] + sred[1][x][cidx]) + (sred[2][x][cidx] + sred[3][x][cidx]);
-          qa[((int64_t)b * XP + scol[h0 + x]) * LQW + cidx] = f32_to_bf16(v);
-        }
-      }
-      __syncthreads();
-    }
-    // The rotary part of each query is copied as it is.
-    for (int idx = tid; idx < nh * LDR; idx += 256) {
-      const int x = idx / LDR, r = idx - (idx / LDR) * LDR;
-      const int col = scol[x];
-      const uint16_t* q = col < S ? q_sig + ((int64_t)b * S + col) * (LDN + LDR)
-                                  : q_noise + ((int64_t)b * N + (col - S)) * (LDN + LDR);
-      qa[((int64_t)b * XP + col) * LQW + LDC + r] = q[LDN + r];
-    }
-    // Padding columns (S + N .. XP-1) are zero queries; the workgroups of KV head 0 clear them.
-    if (h == 0)
-      for (int idx = tid; idx < (XP - S - N) * LQW; idx += 256)
-        qa[((int64_t)b * XP + S + N) * LQW + idx] = 0;
+  for (int ks = 0; ks < LDN / 32; ++ks) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (live) w = ldg16(q + 32 * ks + 8 * g4);
+    qb[ks] = __builtin_bit_cast(bf16x8, w);
   }
+  // The rotary part: lanes with g4 < 2 copy 32 of their column's 64 values each.
+  if (live && g4 < 2) {
+    const uint16_t* src = q + LDN + 32 * g4;
+    uint16_t* dst = qa + ((int64_t)cb * XP + head) * LQW + LDC + 32 * g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(dst + 8 * i) = ldg16(src + 8 * i);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // W_k[h] is in LDS
+  uint16_t* dst = qa + ((int64_t)cb * XP + head) * LQW + 4 * g4;
+#pragma unroll 4
+  for (int ct = 0; ct < LDC / 16; ++ct) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < LDN / 32; ++ks) {
+      shortx4 half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        // rows 32 ks + 8 g4 + 4 hf .. +3: lane (col, g4) gets W_k^T[16 ct + col][k]
+        // for k = 8 g4 .. 8 g4 + 7 in order, the k order of the q_nope operand
+        const int r = 32 * ks + 8 * g4 + 4 * hf + (col >> 2);
+        const int chunk = 2 * ct + ((col & 3) >> 1);
+        const uint16_t* va = sW + r * LDC + ((chunk ^ ((r & 7) << 1)) << 3) + 4 * (col & 1);
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
+      }
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
+      const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
+                          half[1][0], half[1][1], half[1][2], half[1][3]};
+      acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, a8), qb[ks], acc);
+    }
+    // lane (col, g4) holds latent dims 16 ct + 4 g4 .. +3 of its column
+    if (live) *(u32x2*)(dst + 16 * ct) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+  }
+  // Padding columns S+N .. XP-1 are zero queries (cleared by the workgroups of h = 0).
+  if (h == 0 && XP > S + N)
+    for (int64_t idx = (int64_t)blk * 256 + tid; idx < (int64_t)B * (XP - S - N) * LQW;
+         idx += (int64_t)nblk * 256) {
+      const int64_t bb = idx / ((XP - S - N) * LQW), rem = idx - bb * ((XP - S - N) * LQW);
+      qa[(bb * XP + S + N) * LQW + rem] = 0;
+    }
 }
 
 // ---- 2. attend ----------------------------------------------------------------
@@ -334,11 +341,277 @@ latent_attend_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict
     *(floatx4*)(ph + 4 + 16 * db + 4 * g4) = o[db];
 }
 
+// ---- 2'. attend, work split over 8 waves (up to 5 head tiles) ---------------------
+// The kernel above gives each wave 16 heads over the whole chunk, so every wave
+// reads all 36 KB of the chunk from LDS (the LDS traffic, not the matrix work,
+// sets its pace) and 5 head tiles load one SIMD twice. Here the 8 waves split
+// the work so that each chunk byte is read from LDS about once:
+//  * scores: wave w computes partial S^T for key tile kh = w/4 (16 keys) over its
+//    quarter dq = w%4 of the 18 k-steps (k-step ks belongs to quarter ks%4), for
+//    every head tile, and writes the partial to LDS;
+//  * softmax: wave t < HT sums the four quarters of head tile t (both key tiles),
+//    keeps that tile's running max and sum, and writes the P^T operand (bf16) and
+//    whether it rescaled;
+//  * P.V: wave w owns latent dims 64w .. 64w+63 of O^T for every head tile
+//    (rescaled when a softmax wave raised its reference).
+// Three workgroup barriers per chunk: chunk landed, partials written, P written.
+constexpr int A2_WAVES = 8;
+constexpr int A2_KSTEPS = (LDC + LDR) / 32;       // 18 k-steps of the scores
+constexpr int A2_KQ = (A2_KSTEPS + 3) / 4;        // at most 5 per quarter
+constexpr int A2_DT = LDC / 16 / A2_WAVES;        // 16-dim tiles of O^T per wave (4)
+constexpr int A2_MAX_HT = 5;
+
+template <int HT>
+struct Attend2Smem {
+  unsigned char ring[LNSTAGE * LSTAGE];            // latent + rotary rows of 3 chunks
+  floatx4 part[2][4][HT][64];                       // partial S^T [kh][dq][tile][lane]
+  bf16x8 pt[HT][64];                                // P^T operands [tile][lane]
+  int rescaled[HT];                                 // tile t raised its reference
+  float alpha[HT][16];                              // its factors, per head column
+};
+
+template <int HT>
+__global__ void __launch_bounds__(64 * A2_WAVES, 1)
+latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict__ c_kv,
+                      const uint16_t* __restrict__ k_rope, const int32_t* __restrict__ lens,
+                      float* __restrict__ part, int Lmax, int window, int nsplit, float c) {
+  constexpr int XP = 16 * HT;
+  __shared__ __attribute__((aligned(1024))) Attend2Smem<HT> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g4 = lane >> 4;
+  const int dq = wave & 3, kh = wave >> 2;
+  const int b = blockIdx.x / nsplit, k = blockIdx.x - (blockIdx.x / nsplit) * nsplit;
+  float* pw = part + ((int64_t)b * nsplit + k) * XP * LPART;
+
+  int len = lens ? lens[b] : Lmax;
+  if (len > Lmax) len = Lmax;
+  const int pos = len - 1;
+  const int lo = window ? max(0, pos - window + 1) : 0;
+  const int nch = len >= 1 ? (pos - lo + LCK) / LCK : 0;
+  const int c0 = (int)(((int64_t)k * nch) / nsplit), c1 = (int)(((int64_t)(k + 1) * nch) / nsplit);
+
+  // Absorbed queries of this wave's k-steps (ks = dq + 4i), every head tile, as
+  // MFMA B operands (Q~^T: 32 dims x 16 heads).
+  bf16x8 qf[A2_KQ][HT];
+  {
+    const uint16_t* qp = qa + ((int64_t)b * XP + col) * LQW + 8 * g4;
+#pragma unroll
+    for (int i = 0; i < A2_KQ; ++i) {
+      const int ks = dq + 4 * i;
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (ks < A2_KSTEPS) w = ldg16(qp + (int64_t)(16 * t) * LQW + 32 * ks);
+        qf[i][t] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < A2_KQ; ++i)
+#pragma unroll
+      for (int t = 0; t < HT; ++t) settle(qf[i][t]);  // before any copy is issued
+  }
+  // O^T: dims 64*wave + 16*dt + (4 g4 .. +3), head 16 t + col.
+  floatx4 o[A2_DT][HT];
+#pragma unroll
+  for (int dt = 0; dt < A2_DT; ++dt)
+#pragma unroll
+    for (int t = 0; t < HT; ++t) o[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Softmax state of head tile `wave` (waves < HT): per column reference and sum.
+  float mref = kLNoMax, lsum = 0.f;
+
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(const lds_void*)sm.ring;
+  const char* cbase = (const char*)(c_kv + (int64_t)b * Lmax * LDC);
+  const char* rbase = (const char*)(k_rope + (int64_t)b * Lmax * LDR);
+  auto issue = [&](int j, int st) {
+    const int s0 = lo + j * LCK;
+    const int last = pos - s0;
+    const uint32_t dst = ring_lds + (uint32_t)(st * LSTAGE);
+    for (int blk = wave; blk < LBLK; blk += A2_WAVES) {
+      if (blk < LCK) {
+        const int r = min(blk, last);
+        const uint32_t voff = (uint32_t)r * (LDC * 2) + 16u * (uint32_t)(lane ^ lswz(blk));
+        dma16_lds_nt(cbase + (int64_t)s0 * (LDC * 2), voff, dst + 1024u * blk);
+      } else {
+        const int q = blk - LCK;
+        const int rr = 8 * q + (lane >> 3);
+        const int r = min(rr, last);
+        const uint32_t voff = (uint32_t)r * (LDR * 2) + 16u * (uint32_t)((lane & 7) ^ rswz(rr));
+        dma16_lds_nt(rbase + (int64_t)s0 * (LDR * 2), voff, dst + 1024u * blk);
+      }
+    }
+  };
+  const int nmine = (LBLK - wave + A2_WAVES - 1) / A2_WAVES;
+
+  // Per-lane parts of the fragment addresses (the layout of the kernel above):
+  // K fragment of key tile kh, k-step ks: row 16 kh + col.
+  int kbase, ktab[4], rtab[LDR / 32], vbase, vtab[8];
+  {
+    const int f = lswz(col);
+    kbase = col * (LDC * 2) + 16 * (g4 ^ (f & 3));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ktab[t] = 64 * (t ^ (f >> 2));
+#pragma unroll
+    for (int ks = 0; ks < LDR / 32; ++ks) rtab[ks] = col * (LDR * 2) + ((((4 * ks + g4) ^ rswz(col))) << 4);
+    const int rv = 4 * g4 + (col >> 2);
+    const int fv = lswz(rv);
+    vbase = rv * (LDC * 2) + 16 * (((col & 3) >> 1) ^ (fv & 1)) + 8 * (col & 1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vtab[t] = 32 * (t ^ (rv & 7));
+  }
+  auto stage_of = [&](int j) { return sm.ring + ((j - c0) % LNSTAGE) * LSTAGE; };
+
+  // Partial S^T of chunk j's key tile kh over this wave's k-steps, every head tile.
+  auto scores = [&](int j) {
+    const unsigned char* sC = stage_of(j);
+    const unsigned char* sR = sC + LC_BYTES;
+    floatx4 s[HT];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) s[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < A2_KQ; ++i) {
+      const int ks = dq + 4 * i;
+      if (ks >= A2_KSTEPS) break;  // wave-uniform
+      bf16x8 a;
+      if (ks < LDC / 32)
+        a = *(const bf16x8*)(sC + kbase + kh * (16 * LDC * 2) + 256 * (ks >> 2) + ktab[ks & 3]);
+      else
+        a = *(const bf16x8*)(sR + kh * (16 * LDR * 2) + rtab[ks - LDC / 32]);
+#pragma unroll
+      for (int t = 0; t < HT; ++t) s[t] = mfma_16x16x32(a, qf[i][t], s[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < HT; ++t) sm.part[kh][dq][t][lane] = s[t];
+  };
+
+  // Softmax of head tile `wave` over chunk j's 32 keys: running reference and
+  // sum, the P^T operand and the rescale flag and factors.
+  auto softmax = [&](int j) {
+    const int s0 = lo + j * LCK;
+    floatx4 sk[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const floatx4 p0 = sm.part[h][0][wave][lane], p1 = sm.part[h][1][wave][lane];
+      const floatx4 p2 = sm.part[h][2][wave][lane], p3 = sm.part[h][3][wave][lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sk[h][r] = (p0[r] + p1[r]) + (p2[r] + p3[r]);
+    }
+    if (s0 + LCK - 1 > pos) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (s0 + 16 * h + 4 * g4 + r > pos) sk[h][r] = -INFINITY;
+    }
+    const float mx = fmaxf(fmaxf(fmaxf(sk[0][0], sk[0][1]), fmaxf(sk[0][2], sk[0][3])),
+                           fmaxf(fmaxf(sk[1][0], sk[1][1]), fmaxf(sk[1][2], sk[1][3])));
+    int resc = 0;
+    if (__builtin_amdgcn_ballot_w64(mx * c > mref + 8.f)) {
+      const float mnew = fmaxf(mref, col_max4(mx) * c);
+      const float alpha = fast_exp2(mref - mnew);
+      mref = mnew;
+      lsum *= alpha;
+      if (g4 == 0) sm.alpha[wave][col] = alpha;
+      resc = 1;
+    }
+    if (lane == 0) sm.rescaled[wave] = resc;
+    bf16x8 pb;
+    float ps = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(sk[h][r], c, -mref));
+        ps += p;
+        pb[4 * h + r] = (__bf16)p;
+      }
+    lsum += ps;
+    sm.pt[wave][lane] = pb;
+  };
+
+  // O^T (this wave's 64 latent dims) += C^T . P^T of chunk j, every head tile,
+  // after the rescale its softmax asked for.
+  auto pv = [&](int j) {
+    const unsigned char* sC = stage_of(j);
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+      if (__builtin_amdgcn_readfirstlane(sm.rescaled[t])) {
+        const float al = sm.alpha[t][col];
+#pragma unroll
+        for (int dt = 0; dt < A2_DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[dt][t][r] *= al;
+      }
+    }
+    bf16x8 pbt[HT];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) pbt[t] = sm.pt[t][lane];
+#pragma unroll
+    for (int dt = 0; dt < A2_DT; ++dt) {
+      const int db = A2_DT * wave + dt;
+      shortx4 half[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const unsigned char* va = sC + vbase + hf * (16 * LDC * 2) + 256 * (db >> 3) + vtab[db & 7];
+        half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
+      }
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
+      const shortx8 a8 = {half[0][0], half[0][1], half[0][2], half[0][3],
+                          half[1][0], half[1][1], half[1][2], half[1][3]};
+      const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+      for (int t = 0; t < HT; ++t) o[dt][t] = mfma_16x16x32(a, pbt[t], o[dt][t]);
+    }
+  };
+
+  // Software pipeline, two barriers per chunk: interval A of step j holds the
+  // P.V products of chunk j-1 and the score products of chunk j (independent
+  // matrix work for the two waves of each SIMD), interval B the softmax of
+  // chunk j. Chunk j's stage is read in steps j and j+1, so chunk j+2 is copied
+  // into the stage of chunk j-1 once step j's interval A is over.
+  if (c0 < c1) issue(c0, 0);
+  if (c0 + 1 < c1) issue(c0 + 1, 1);
+#pragma unroll 1
+  for (int j = c0; j <= c1; ++j) {
+    if (j < c1) {  // chunk j landed (chunk j+1's copies may still be in flight)
+      if (j + 1 < c1)
+        wait_own_blocks(nmine);
+      else
+        wait_vmcnt<0>();
+    }
+    __syncthreads();  // chunk j landed; P^T of chunk j-1 written
+    if (j > c0) pv(j - 1);
+    if (j < c1) scores(j);
+    __syncthreads();  // partial scores of chunk j written; chunk j-1 and P^T no longer read
+    if (j + 2 < c1) issue(j + 2, (j + 2 - c0) % LNSTAGE);
+    if (j < c1 && wave < HT) softmax(j);
+  }
+  // Partials: m (log2 units) and l of each head from its softmax wave, o[Dc]
+  // (unnormalised) from every wave's dims.
+  if (wave < HT) {
+    lsum = col_sum4(lsum);
+    float* ph = pw + (16 * wave + col) * LPART;
+    if (g4 == 0) {
+      ph[0] = mref;
+      ph[1] = lsum;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < HT; ++t) {
+    float* ph = pw + (16 * t + col) * LPART + 4;
+#pragma unroll
+    for (int dt = 0; dt < A2_DT; ++dt)
+      *(floatx4*)(ph + 16 * (A2_DT * wave + dt) + 4 * g4) = o[dt][t];
+  }
+}
+
 // ---- 3. merge, up-project, epilogue ------------------------------------------------
 // One workgroup per (sequence b, noise head j): heads = noise j and its g signal
 // heads g*j .. g*j+g-1. Each head's o is merged over the splits (fp32, in LDS),
-// then H[e] = W_v[h] o (fp32, one dot product per thread), then
-// out = gate * (H_S - lambda * H_N).
+// then H[e] = W_v[h] o (fp32): thread (half, e) walks half of W_v row e of each
+// KV head the group uses, once, applying each piece to every head on that KV head
+// (so a row is read once per workgroup, not once per head), and the two halves'
+// partial sums are added through LDS; then out = gate * (H_S - lambda * H_N).
 __global__ void __launch_bounds__(256)
 latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__ w_kv_b,
                     const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
@@ -347,6 +620,9 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
   constexpr int MAXG = 15;
   __shared__ float so[MAXG + 1][LDC];   // merged o: [0] noise, [1 + t] signal g*j + t
   __shared__ float sH[MAXG + 1][LDV];   // up-projected outputs
+  __shared__ float sHp[MAXG + 1][LDV];  // the first half's partial sums
+  __shared__ float sml[(MAXG + 1) * 64][2];  // (m, l) of each (head, split), then (weight, l)
+  __shared__ float sinvl[MAXG + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = blockIdx.x / N, j = blockIdx.x - (blockIdx.x / N) * N;
   const int g = S / N;
@@ -358,43 +634,100 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
       out[((int64_t)b * S + g * j + idx / LDV) * LDV + idx % LDV] = 0;
     return;
   }
-  // Merge: thread t owns latent dims t and t+256 of every head.
-  for (int x = 0; x < nh; ++x) {
+  const int e = tid & (LDV - 1), half = tid >> 7;
+  auto kv_of = [&](int x) {
+    return x == 0 ? (int)(((int64_t)j * Hkv) / N) : (int)(((int64_t)(g * j + x - 1) * Hkv) / S);
+  };
+  // This thread's half of W_v row e of the first head's KV head, loaded first so
+  // that its latency overlaps the merge below.
+  constexpr int NPC = 256 / 8;  // 16-byte pieces per half row
+  u32x4 wpre[NPC];
+  {
+    const uint16_t* wv = w_kv_b + ((int64_t)kv_of(0) * (LDN + LDV) + LDN + e) * LDC + 256 * half;
+#pragma unroll
+    for (int c8 = 0; c8 < NPC; ++c8) wpre[c8] = ldg16(wv + 8 * c8);
+  }
+  // Merge. First every (head, split) reference and sum into LDS in one round
+  // trip, then each head's split weights 2^(m_k - max m) and 1/L, then thread t
+  // sums latent dims t and t+256 of every head over the splits (all loads
+  // independent of each other).
+  auto head_part = [&](int x) {
     const int col = x == 0 ? S + j : g * j + (x - 1);
-    const float* p0 = part + ((int64_t)b * nsplit * XP + col) * LPART;
-    float M = -INFINITY;
-    for (int k = 0; k < nsplit; ++k) M = fmaxf(M, p0[(int64_t)k * XP * LPART]);
-    float L = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int k = 0; k < nsplit; ++k) {
-      const float* pk = p0 + (int64_t)k * XP * LPART;
-      const float wk = fast_exp2(pk[0] - M);
-      L += wk * pk[1];
-      a0 += wk * pk[4 + tid];
-      a1 += wk * pk[4 + tid + 256];
-    }
-    so[x][tid] = a0 / L;
-    so[x][tid + 256] = a1 / L;
+    return part + ((int64_t)b * nsplit * XP + col) * LPART;
+  };
+  for (int idx = tid; idx < nh * nsplit; idx += 256) {
+    const int x = idx / nsplit, k = idx - (idx / nsplit) * nsplit;
+    const float* pk = head_part(x) + (int64_t)k * XP * LPART;
+    sml[idx][0] = pk[0];
+    sml[idx][1] = pk[1];
   }
   __syncthreads();
-  // Up-projection: thread-owned dot products H[x][e] = W_v[h(x)] row e . o_x (fp32),
-  // 16-byte weight loads, o from LDS (the same address across a wave: a broadcast).
+  if (tid < nh) {  // per head: the split weights (in place of m) and 1/L
+    float M = -INFINITY;
+    for (int k = 0; k < nsplit; ++k) M = fmaxf(M, sml[tid * nsplit + k][0]);
+    float L = 0.f;
+    for (int k = 0; k < nsplit; ++k) {
+      const float wk = fast_exp2(sml[tid * nsplit + k][0] - M);
+      sml[tid * nsplit + k][0] = wk;
+      L += wk * sml[tid * nsplit + k][1];
+    }
+    sinvl[tid] = 1.f / L;
+  }
+  __syncthreads();
+  for (int x = 0; x < nh; ++x) {
+    const float* p0 = head_part(x) + 4;
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < nsplit; ++k) {
+      const float* pk = p0 + (int64_t)k * XP * LPART;
+      const float wk = sml[x * nsplit + k][0];
+      a0 = fmaf(wk, pk[tid], a0);
+      a1 = fmaf(wk, pk[tid + 256], a1);
+    }
+    so[x][tid] = a0 * sinvl[x];
+    so[x][tid + 256] = a1 * sinvl[x];
+  }
+  __syncthreads();
+  // Up-projection. Thread (half, e) sums latent dims 256*half .. +255 of
+  // H[x][e] = W_v[h(x)] row e . o_x for every head x, heads in runs (of up to 4)
+  // on one KV head sharing each 16-byte weight piece; o comes from LDS (one
+  // address per wave: a broadcast). The first run uses the prefetched pieces.
+  {
+    const int h0 = kv_of(0);
+    for (int x0 = 0; x0 < nh;) {
+      const int h = kv_of(x0);
+      int x1 = x0 + 1;
+      while (x1 < nh && x1 - x0 < 4 && kv_of(x1) == h) ++x1;  // a run of <= 4 heads on h
+      const bool pre = h == h0;
+      const uint16_t* wv = w_kv_b + ((int64_t)h * (LDN + LDV) + LDN + e) * LDC + 256 * half;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c8 = 0; c8 < NPC; ++c8) {
+        const u32x4 w = pre ? wpre[c8] : ldg16(wv + 8 * c8);
+#pragma unroll
+        for (int xi = 0; xi < 4; ++xi) {
+          if (x0 + xi < x1) {  // wave-uniform
+            const float* ov = &so[x0 + xi][256 * half + 8 * c8];
+            float a = acc[xi];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              a = fmaf(bf16_lo(w[u]), ov[2 * u], a);
+              a = fmaf(bf16_hi(w[u]), ov[2 * u + 1], a);
+            }
+            acc[xi] = a;
+          }
+        }
+      }
+#pragma unroll
+      for (int xi = 0; xi < 4; ++xi)
+        if (x0 + xi < x1) (half ? sH : sHp)[x0 + xi][e] = acc[xi];
+      x0 = x1;
+    }
+  }
+  __syncthreads();
   for (int idx = tid; idx < nh * LDV; idx += 256) {
     const int x = idx / LDV, e = idx - (idx / LDV) * LDV;
-    const int col = x == 0 ? S + j : g * j + (x - 1);
-    const int h = x == 0 ? (int)(((int64_t)j * Hkv) / N) : (int)(((int64_t)col * Hkv) / S);
-    const uint16_t* wv = w_kv_b + ((int64_t)h * (LDN + LDV) + LDN + e) * LDC;
-    float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 16
-    for (int c8 = 0; c8 < LDC / 8; ++c8) {
-      const u32x4 w = ldg16(wv + 8 * c8);
-      const float* ov = &so[x][8 * c8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc0 = fmaf(bf16_lo(w[u]), ov[2 * u], acc0);
-        acc1 = fmaf(bf16_hi(w[u]), ov[2 * u + 1], acc1);
-      }
-    }
-    sH[x][e] = acc0 + acc1;
+    sH[x][e] += sHp[x][e];
   }
   __syncthreads();
   for (int idx = tid; idx < g * LDV; idx += 256) {
@@ -409,11 +742,14 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
   }
 }
 
-// Splits per sequence: enough workgroups for the CUs, at least 4 chunks each.
-int latent_nsplit(int B, int Lmax, int window) {
+// Splits per sequence: enough workgroups for the CUs (the eight-wave kernel
+// fills a CU with one workgroup, the other with one of up to 8 waves), at least
+// 4 chunks each.
+int latent_nsplit(int B, int Lmax, int window, int XP) {
   const int span = window > 0 && window < Lmax ? window : Lmax;
   const int nch = (span + LCK - 1) / LCK;
-  int ns = (512 + B - 1) / B;
+  const int target = XP / 16 <= A2_MAX_HT ? 256 : 512;
+  int ns = (target + B - 1) / B;
   ns = min(ns, max(1, nch / 4));
   return max(1, min(ns, 64));
 }
@@ -437,7 +773,7 @@ bool latent_supported(int Dn, int Dr, int Dc, int dv, int S, int N, int Hkv) {
 
 size_t latent_workspace_bytes(int B, int Lmax, int S, int N, int window) {
   const int XP = ((S + N + 15) / 16) * 16;
-  const int ns = latent_nsplit(B, Lmax, window);
+  const int ns = latent_nsplit(B, Lmax, window, XP);
   const size_t qa = (size_t)B * XP * LQW * 2;
   const size_t qa_pad = (qa + 255) & ~(size_t)255;
   return qa_pad + (size_t)B * ns * XP * LPART * 4;
@@ -468,21 +804,40 @@ hipError_t latent_scratch(void** ptr) {
 
 hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream) {
   const int XP = ((a.S + a.N + 15) / 16) * 16;
-  const int ns = latent_nsplit(a.B, a.Lmax, a.window);
+  const int ns = latent_nsplit(a.B, a.Lmax, a.window, XP);
   const size_t qa_bytes = ((size_t)a.B * XP * LQW * 2 + 255) & ~(size_t)255;
   uint16_t* qa = (uint16_t*)a.workspace;
   float* part = (float*)((char*)a.workspace + qa_bytes);
-  const int64_t g1 = (int64_t)((a.B + ABS_SEQ - 1) / ABS_SEQ) * a.Hkv;
   const int64_t g2 = (int64_t)a.B * ns, g3 = (int64_t)a.B * a.N;
-  if (g1 > 0x7fffffff || g2 > 0x7fffffff || g3 > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(latent_absorb_kernel, dim3((unsigned)g1), dim3(256), 0, stream,
+  if (g2 > 0x7fffffff || g3 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int nkv_max = a.S / a.Hkv + (a.N + a.Hkv - 1) / a.Hkv;
+  const int64_t g1b = (int64_t)a.Hkv * (((int64_t)a.B * nkv_max + AB_COLS - 1) / AB_COLS);
+  if (g1b > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(latent_absorb2_kernel, dim3((unsigned)g1b), dim3(256), 0, stream,
                      (const uint16_t*)a.q_sig, (const uint16_t*)a.q_noise,
                      (const uint16_t*)a.w_kv_b, qa, a.B, a.S, a.N, a.Hkv, XP);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(latent_attend_kernel, dim3((unsigned)g2), dim3(64 * (XP / 16)), 0, stream,
-                     (const uint16_t*)qa, (const uint16_t*)a.c_kv, (const uint16_t*)a.k_rope,
-                     a.lens, part, a.Lmax, a.window, ns, XP, a.scale_log2);
+  const uint16_t* ckv = (const uint16_t*)a.c_kv;
+  const uint16_t* kr = (const uint16_t*)a.k_rope;
+  switch (XP / 16) {
+#define GDA_ATTEND2(HT)                                                                          \
+  case HT:                                                                                       \
+    hipLaunchKernelGGL(latent_attend2_kernel<HT>, dim3((unsigned)g2), dim3(64 * A2_WAVES), 0,    \
+                       stream, (const uint16_t*)qa, ckv, kr, a.lens, part, a.Lmax, a.window, ns, \
+                       a.scale_log2);                                                            \
+    break;
+    GDA_ATTEND2(1)
+    GDA_ATTEND2(2)
+    GDA_ATTEND2(3)
+    GDA_ATTEND2(4)
+    GDA_ATTEND2(5)
+#undef GDA_ATTEND2
+    default:
+      hipLaunchKernelGGL(latent_attend_kernel, dim3((unsigned)g2), dim3(64 * (XP / 16)), 0,
+                         stream, (const uint16_t*)qa, ckv, kr, a.lens, part, a.Lmax, a.window, ns,
+                         XP, a.scale_log2);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(latent_merge_kernel, dim3((unsigned)g3), dim3(256), 0, stream,
