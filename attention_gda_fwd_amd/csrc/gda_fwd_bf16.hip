@@ -386,7 +386,9 @@ __device__ __forceinline__ void consume_tile(const Ctx& x, State<C, NH>& st, con
 template <int DV>
 struct HeadIn {
   u32x4 gate[DV / 32];  // this lane's 8-channel gate pieces
-  float lam;
+  // lambda's bf16 bits: widened where it is used, so that the load's wait sits there
+  // and not right after the load is issued.
+  uint32_t lam_bits;
 };
 
 __device__ __forceinline__ int64_t head_base(int64_t row, int S, int i, int g4, int DV) {
@@ -400,18 +402,19 @@ __device__ __forceinline__ void load_head_in(const uint16_t* lam, const uint16_t
   const int64_t base = head_base(row, S, i, g4, DV);
 #pragma unroll
   for (int p = 0; p < DV / 32; ++p) in.gate[p] = ldg16(gate + base + 32 * p);
-  in.lam = bf16_to_f32(lam[row * S + i]);
+  in.lam_bits = lam[row * S + i];
 }
 
+// The output values of one signal head, rounded to bf16 and regrouped for 16-byte
+// stores (pair p goes to out + head_base + 32 p).
 template <int DV>
-__device__ __forceinline__ void store_head(uint16_t* out, int64_t row, int S, int i, int g4,
-                                           const floatx4 (&hs)[DV / 16], float inv_s,
-                                           const floatx4 (&hn)[DV / 16], const HeadIn<DV>& in,
-                                           int flags) {
+__device__ __forceinline__ void pack_head(const floatx4 (&hs)[DV / 16], float inv_s,
+                                          const floatx4 (&hn)[DV / 16], const HeadIn<DV>& in,
+                                          int flags, u32x4 (&ow)[DV / 32]) {
   constexpr int NP = DV / 32;
   static_assert(DV % 32 == 0, "channel blocks come in pairs");
-  const int64_t base = head_base(row, S, i, g4, DV);
-  const float lm = (flags & kLambdaLogits) ? sigmoid_f32(in.lam) : in.lam;
+  const float lraw = __uint_as_float(in.lam_bits << 16);
+  const float lm = (flags & kLambdaLogits) ? sigmoid_f32(lraw) : lraw;
   float e[NP][8];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
@@ -427,8 +430,7 @@ __device__ __forceinline__ void store_head(uint16_t* out, int64_t row, int S, in
     }
   const bool logits = (flags & kGateLogits) != 0;
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    u32x4 ow;
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       float glo = bf16_lo(in.gate[p][w]), ghi = bf16_hi(in.gate[p][w]);
@@ -436,10 +438,20 @@ __device__ __forceinline__ void store_head(uint16_t* out, int64_t row, int S, in
         glo = sigmoid_f32(glo);
         ghi = sigmoid_f32(ghi);
       }
-      ow[w] = pack_bf16x2(glo * e[p][2 * w], ghi * e[p][2 * w + 1]);
+      ow[p][w] = pack_bf16x2(glo * e[p][2 * w], ghi * e[p][2 * w + 1]);
     }
-    *(u32x4*)(out + base + 32 * p) = ow;
-  }
+}
+
+template <int DV>
+__device__ __forceinline__ void store_head(uint16_t* out, int64_t row, int S, int i, int g4,
+                                           const floatx4 (&hs)[DV / 16], float inv_s,
+                                           const floatx4 (&hn)[DV / 16], const HeadIn<DV>& in,
+                                           int flags) {
+  u32x4 ow[DV / 32];
+  pack_head<DV>(hs, inv_s, hn, in, flags, ow);
+  const int64_t base = head_base(row, S, i, g4, DV);
+#pragma unroll
+  for (int p = 0; p < DV / 32; ++p) *(u32x4*)(out + base + 32 * p) = ow[p];
 }
 
 // Training form: one path's normalised output h * inv (bf16, regrouped like
@@ -731,6 +743,13 @@ fwd_bf16_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
   }
 }
 
+// Largest chunk of signal heads (at most MAXC) that divides n.
+inline int chunk_of(int n, int maxc) {
+  for (int c = maxc; c > 1; --c)
+    if (n % c == 0) return c;
+  return 1;
+}
+
 template <class C>
 hipError_t launch_inst(const FwdArgs& a, const SubMap& sm, hipStream_t stream) {
   // Packed sequences: B sequences of at most L queries each.
@@ -755,13 +774,6 @@ hipError_t launch_inst(const FwdArgs& a, const SubMap& sm, hipStream_t stream) {
                        a.scale_log2, a.flags, (uint16_t*)a.h_sig, (uint16_t*)a.h_noise,
                        a.lse, a.lse_b, a.lse_q, a.lse_h);
   return hipGetLastError();
-}
-
-// Largest chunk of signal heads (at most MAXC) that divides n.
-inline int chunk_of(int n, int maxc) {
-  for (int c = maxc; c > 1; --c)
-    if (n % c == 0) return c;
-  return 1;
 }
 
 // Sub-unit launches of a head layout (g = S/N, NS = S/Hkv), for a (query

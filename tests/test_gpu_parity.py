@@ -94,6 +94,38 @@ def test_layout_sweep(layout, dims, window):
     U.assert_close(got, ref, "bf16", f"{layout} {dims} window={window}")
 
 
+# Sliding windows over batches with many sub-units: ragged tails, windows from 1
+# key to 194, one to eight signal heads per noise head, two noise heads per KV
+# head, and every head size.
+SWA_CASES = {
+    "motif3_B4_L1000_w128": dict(B=4, L=1000, S=64, N=16, Hkv=16, dqk=192, dv=128, window=128),
+    "motif3_B4_L1000_w129": dict(B=4, L=1000, S=64, N=16, Hkv=16, dqk=192, dv=128, window=129),
+    "motif3_B4_L1000_w130": dict(B=4, L=1000, S=64, N=16, Hkv=16, dqk=192, dv=128, window=130),
+    "motif3_B4_L777_w1": dict(B=4, L=777, S=64, N=16, Hkv=16, dqk=192, dv=128, window=1),
+    "motif3_B4_L777_w33": dict(B=4, L=777, S=64, N=16, Hkv=16, dqk=192, dv=128, window=33),
+    "g8_B4_L900_w97": dict(B=4, L=900, S=64, N=8, Hkv=8, dqk=192, dv=128, window=97),
+    "g3_B8_L600_w64": dict(B=8, L=600, S=24, N=8, Hkv=8, dqk=192, dv=128, window=64),
+    "g1_B16_L300_w128": dict(B=16, L=300, S=16, N=16, Hkv=16, dqk=192, dv=128, window=128),
+    "nn2_B8_L500_w80": dict(B=8, L=500, S=32, N=16, Hkv=8, dqk=192, dv=128, window=80),
+    "d128_B4_L1000_w193": dict(B=4, L=1000, S=64, N=16, Hkv=16, dqk=128, dv=128, window=193),
+    "d128_B4_L1000_w194": dict(B=4, L=1000, S=64, N=16, Hkv=16, dqk=128, dv=128, window=194),
+    "d128_g2_B8_L700_w128": dict(B=8, L=700, S=32, N=16, Hkv=16, dqk=128, dv=128, window=128),
+    "d64_B8_L700_w100": dict(B=8, L=700, S=16, N=4, Hkv=4, dqk=64, dv=64, window=100),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWA_CASES))
+def test_sliding_window_batches(name):
+    kw = dict(SWA_CASES[name], dtype="bf16")
+    cid = 600 + sorted(SWA_CASES).index(name)
+    U.log(f"parity sliding window {name} {kw}")
+    case = U.FwdCase(cid, **kw)
+    got = U.to_f64(case.run_gpu())
+    torch.cuda.synchronize()
+    ref = case.run_oracle()
+    U.assert_close(got, ref, "bf16", name)
+
+
 @pytest.mark.parametrize("cfg", [C.MOTIF2, C.MOTIF3_SWA, C.MOTIF3_FULL_SHARD8, C.MOTIF3_FULL],
                          ids=lambda c: c.name)
 def test_full_size_full_output(cfg):
