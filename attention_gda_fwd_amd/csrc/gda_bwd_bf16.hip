@@ -478,6 +478,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ q_sig, const uint16_t* __restrict__
 #pragma unroll
     for (int d = 0; d < C::VT; ++d) dvT[kc][d] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
+  // Wait for K and V here, once (a first use inside the item loop would put the
+  // wait there, where it drains the copies in flight every item).
+#pragma unroll
+  for (int kc = 0; kc < KT; ++kc) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) settle(kT[kc][ks]);
+#pragma unroll
+    for (int kv = 0; kv < C::VS; ++kv) settle(vT[kc][kv]);
+  }
 
   const int nh = kv_head_count(h, S, N, Hkv);
   // Local queries that see one of the tile's keys (query t sits at position qoff + t);
