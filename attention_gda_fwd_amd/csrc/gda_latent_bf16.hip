@@ -608,22 +608,26 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
 // ---- 3. merge, up-project, epilogue ------------------------------------------------
 // One workgroup per (sequence b, noise head j): heads = noise j and its g signal
 // heads g*j .. g*j+g-1. Each head's o is merged over the splits (fp32, in LDS),
-// then H[e] = W_v[h] o (fp32): thread (half, e) walks half of W_v row e of each
-// KV head the group uses, once, applying each piece to every head on that KV head
-// (so a row is read once per workgroup, not once per head), and the two halves'
-// partial sums are added through LDS; then out = gate * (H_S - lambda * H_N).
+// then H = W_v[h] o on the matrix cores: for each KV head h the group uses,
+// H^T [128 x heads] += W_v[h] [128 x 512] . O [512 x heads] with O's columns of
+// the heads on h (the others zero), O split into bf16 high and low parts (two
+// products with fp32 accumulation, so the bf16 weights meet o at about fp32
+// precision). Wave w owns W_v rows 32 w .. 32 w + 31, read straight from global
+// memory as A operands (the group's first KV head prefetched before the merge).
+// Then out = gate * (H_S - lambda * H_N).
 __global__ void __launch_bounds__(256)
 latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__ w_kv_b,
                     const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
                     const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int Lmax,
                     int S, int N, int Hkv, int nsplit, int XP, int flags) {
   constexpr int MAXG = 15;
-  __shared__ float so[MAXG + 1][LDC];   // merged o: [0] noise, [1 + t] signal g*j + t
+  constexpr int KST = LDC / 32;  // k-steps of the up-projection
+  __shared__ __attribute__((aligned(16))) float so[MAXG + 1][LDC];  // merged o: [0] noise, [1 + t] signal g*j + t
   __shared__ float sH[MAXG + 1][LDV];   // up-projected outputs
-  __shared__ float sHp[MAXG + 1][LDV];  // the first half's partial sums
   __shared__ float sml[(MAXG + 1) * 64][2];  // (m, l) of each (head, split), then (weight, l)
   __shared__ float sinvl[MAXG + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, g4 = lane >> 4;
   const int b = blockIdx.x / N, j = blockIdx.x - (blockIdx.x / N) * N;
   const int g = S / N;
   const int nh = 1 + g;
@@ -634,26 +638,29 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
       out[((int64_t)b * S + g * j + idx / LDV) * LDV + idx % LDV] = 0;
     return;
   }
-  const int e = tid & (LDV - 1), half = tid >> 7;
   auto kv_of = [&](int x) {
     return x == 0 ? (int)(((int64_t)j * Hkv) / N) : (int)(((int64_t)(g * j + x - 1) * Hkv) / S);
   };
-  // This thread's half of W_v row e of the first head's KV head, loaded first so
-  // that its latency overlaps the merge below.
-  constexpr int NPC = 256 / 8;  // 16-byte pieces per half row
-  u32x4 wpre[NPC];
-  {
-    const uint16_t* wv = w_kv_b + ((int64_t)kv_of(0) * (LDN + LDV) + LDN + e) * LDC + 256 * half;
+  // This wave's W_v rows of KV head h as A operands: row 32 wave + 16 mt + col,
+  // latent dims 32 ks + 8 g4 .. +7.
+  auto w_frag = [&](int h, int mt, int ks) {
+    const int row = 32 * wave + 16 * mt + col;
+    return __builtin_bit_cast(
+        bf16x8, ldg16(w_kv_b + ((int64_t)h * (LDN + LDV) + LDN + row) * LDC + 32 * ks + 8 * g4));
+  };
+  const int h0 = kv_of(0);
+  bf16x8 wpre[2][KST];  // the first KV head's fragments, in flight during the merge
 #pragma unroll
-    for (int c8 = 0; c8 < NPC; ++c8) wpre[c8] = ldg16(wv + 8 * c8);
-  }
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks) wpre[mt][ks] = w_frag(h0, mt, ks);
   // Merge. First every (head, split) reference and sum into LDS in one round
   // trip, then each head's split weights 2^(m_k - max m) and 1/L, then thread t
   // sums latent dims t and t+256 of every head over the splits (all loads
   // independent of each other).
   auto head_part = [&](int x) {
-    const int col = x == 0 ? S + j : g * j + (x - 1);
-    return part + ((int64_t)b * nsplit * XP + col) * LPART;
+    const int hc = x == 0 ? S + j : g * j + (x - 1);
+    return part + ((int64_t)b * nsplit * XP + hc) * LPART;
   };
   for (int idx = tid; idx < nh * nsplit; idx += 256) {
     const int x = idx / nsplit, k = idx - (idx / nsplit) * nsplit;
@@ -688,46 +695,41 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
     so[x][tid + 256] = a1 * sinvl[x];
   }
   __syncthreads();
-  // Up-projection. Thread (half, e) sums latent dims 256*half .. +255 of
-  // H[x][e] = W_v[h(x)] row e . o_x for every head x, heads in runs (of up to 4)
-  // on one KV head sharing each 16-byte weight piece; o comes from LDS (one
-  // address per wave: a broadcast). The first run uses the prefetched pieces.
-  {
-    const int h0 = kv_of(0);
-    for (int x0 = 0; x0 < nh;) {
-      const int h = kv_of(x0);
-      int x1 = x0 + 1;
-      while (x1 < nh && x1 - x0 < 4 && kv_of(x1) == h) ++x1;  // a run of <= 4 heads on h
-      const bool pre = h == h0;
-      const uint16_t* wv = w_kv_b + ((int64_t)h * (LDN + LDV) + LDN + e) * LDC + 256 * half;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // Up-projection: column col of the B operand is head col (zero unless it is one
+  // of this group's heads on KV head h).
+  floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  for (int x = 0; x < nh; ++x) {
+    const int h = kv_of(x);
+    bool seen = false;  // each KV head once (wave-uniform)
+    for (int y = 0; y < x; ++y) seen |= kv_of(y) == h;
+    if (seen) continue;
+    const bool mine = col < nh && kv_of(col) == h;
+    const bool pre = h == h0;
 #pragma unroll
-      for (int c8 = 0; c8 < NPC; ++c8) {
-        const u32x4 w = pre ? wpre[c8] : ldg16(wv + 8 * c8);
+    for (int ks = 0; ks < KST; ++ks) {
+      const floatx4 v0 = *(const floatx4*)&so[col][32 * ks + 8 * g4];
+      const floatx4 v1 = *(const floatx4*)&so[col][32 * ks + 8 * g4 + 4];
+      bf16x8 bh, bl;
 #pragma unroll
-        for (int xi = 0; xi < 4; ++xi) {
-          if (x0 + xi < x1) {  // wave-uniform
-            const float* ov = &so[x0 + xi][256 * half + 8 * c8];
-            float a = acc[xi];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              a = fmaf(bf16_lo(w[u]), ov[2 * u], a);
-              a = fmaf(bf16_hi(w[u]), ov[2 * u + 1], a);
-            }
-            acc[xi] = a;
-          }
-        }
+      for (int i = 0; i < 8; ++i) {
+        const float v = mine ? (i < 4 ? v0[i] : v1[i - 4]) : 0.f;
+        const __bf16 hi = (__bf16)v;
+        bh[i] = hi;
+        bl[i] = (__bf16)(v - (float)hi);
       }
 #pragma unroll
-      for (int xi = 0; xi < 4; ++xi)
-        if (x0 + xi < x1) (half ? sH : sHp)[x0 + xi][e] = acc[xi];
-      x0 = x1;
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = pre ? wpre[mt][ks] : w_frag(h, mt, ks);
+        acc[mt] = mfma_16x16x32(a, bh, acc[mt]);
+        acc[mt] = mfma_16x16x32(a, bl, acc[mt]);
+      }
     }
   }
-  __syncthreads();
-  for (int idx = tid; idx < nh * LDV; idx += 256) {
-    const int x = idx / LDV, e = idx - (idx / LDV) * LDV;
-    sH[x][e] += sHp[x][e];
+  if (col < nh) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sH[col][32 * wave + 16 * mt + 4 * g4 + r] = acc[mt][r];
   }
   __syncthreads();
   for (int idx = tid; idx < g * LDV; idx += 256) {
@@ -743,14 +745,16 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
 }
 
 // Splits per sequence: enough workgroups for the CUs (the eight-wave kernel
-// fills a CU with one workgroup, the other with one of up to 8 waves), at least
-// 4 chunks each.
+// fills a CU with one workgroup, the other with one of up to 8 waves).
 int latent_nsplit(int B, int Lmax, int window, int XP) {
   const int span = window > 0 && window < Lmax ? window : Lmax;
   const int nch = (span + LCK - 1) / LCK;
   const int target = XP / 16 <= A2_MAX_HT ? 256 : 512;
   int ns = (target + B - 1) / B;
-  ns = min(ns, max(1, nch / 4));
+  // Long spans keep at least four chunks per split (the pipeline's fill and the
+  // partials amortise over them); short spans (a window) split down to one chunk,
+  // or a W = 128 decode of 64 sequences would run on 64 workgroups.
+  ns = min(ns, max(1, nch < 16 ? nch : nch / 4));
   return max(1, min(ns, 64));
 }
 
