@@ -9,6 +9,7 @@ Inputs are numpy arrays at their storage type: ``uint16`` bf16 bit patterns or
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -24,26 +25,6 @@ SRC = os.path.join(_HERE, "gda_ref.c")
 
 BF16, F32 = 0, 1
 LAMBDA_LOGITS, GATE_LOGITS = 1, 2
-(EXACT, MUT_DROP_LAMBDA, MUT_PLUS_LAMBDA, MUT_TILED_REPEAT, MUT_KV_INTERLEAVE, MUT_WINDOW_OBO,
- MUT_SCALE_DV, MUT_NO_GATE, MUT_NO_CAUSAL, MUT_K_TRANSPOSED, MUT_LAMBDA_BY_GROUP,
- MUT_NO_NORMALIZE, MUT_DECODE_POS, MUT_SKIP_FIRST_KEY, MUT_LATENT_W_T, MUT_LATENT_NO_ROPE,
- MUT_LATENT_V_ROWS, MUT_BWD_NO_DELTA, MUT_BWD_LAMBDA_SIGN, MUT_BWD_NOISE_KV, MUT_BWD_DK_SCALE,
- MUT_BWD_GATE_DERIV) = range(22)
-MUTANTS = {
-    "drop_lambda": MUT_DROP_LAMBDA, "plus_lambda": MUT_PLUS_LAMBDA,
-    "tiled_repeat": MUT_TILED_REPEAT, "kv_interleave": MUT_KV_INTERLEAVE,
-    "window_off_by_one": MUT_WINDOW_OBO, "scale_dv": MUT_SCALE_DV, "no_gate": MUT_NO_GATE,
-    "no_causal": MUT_NO_CAUSAL, "k_transposed": MUT_K_TRANSPOSED,
-    "lambda_by_group": MUT_LAMBDA_BY_GROUP, "no_normalize": MUT_NO_NORMALIZE,
-    "decode_position": MUT_DECODE_POS, "skip_first_key": MUT_SKIP_FIRST_KEY,
-}
-# Planted mistakes of the backward only.
-BWD_MUTANTS = {"no_delta": MUT_BWD_NO_DELTA, "lambda_sign": MUT_BWD_LAMBDA_SIGN,
-               "noise_not_in_dkv": MUT_BWD_NOISE_KV, "dk_without_scale": MUT_BWD_DK_SCALE,
-               "gate_logit_derivative": MUT_BWD_GATE_DERIV}
-# Planted mistakes of the latent-cache decode only.
-LATENT_MUTANTS = {"w_transposed": MUT_LATENT_W_T, "no_rope": MUT_LATENT_NO_ROPE,
-                  "value_from_key_rows": MUT_LATENT_V_ROWS}
 
 
 def build(force: bool = False) -> str:
@@ -60,44 +41,54 @@ def build(force: bool = False) -> str:
 _lib = None
 
 
+def _bind(lib):
+    """Declare the C signatures on a loaded build of gda_ref.c."""
+    i64, vp, ci, f64 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    lib.gda_ref_fwd.restype = ci
+    lib.gda_ref_fwd.argtypes = [vp] * 7 + [i64] * 8 + [ci, vp, i64]
+    lib.gda_ref_decode.restype = ci
+    lib.gda_ref_decode.argtypes = [vp] * 8 + [i64] * 8 + [ci]
+    lib.gda_ref_fwd_ex.restype = ci
+    lib.gda_ref_fwd_ex.argtypes = [vp] * 7 + [i64] * 8 + [ci, vp, i64, f64, ci]
+    lib.gda_ref_decode_ex.restype = ci
+    lib.gda_ref_decode_ex.argtypes = [vp] * 8 + [i64] * 8 + [ci, f64, ci]
+    lib.gda_ref_fwd_varlen.restype = ci
+    lib.gda_ref_fwd_varlen.argtypes = [vp] * 9 + [i64] * 7 + [ci, f64, ci]
+    lib.gda_ref_decode_latent.restype = ci
+    lib.gda_ref_decode_latent.argtypes = [vp] * 9 + [i64] * 10 + [ci, f64, ci]
+    lib.gda_ref_fwd_train.restype = ci
+    lib.gda_ref_fwd_train.argtypes = [vp] * 10 + [i64] * 8 + [ci, f64, ci]
+    lib.gda_ref_bwd.restype = ci
+    lib.gda_ref_bwd.argtypes = [vp] * 13 + [i64] * 8 + [ci, f64, ci, vp, i64, vp, i64]
+    lib.gda_ref_fwd_train_varlen.restype = ci
+    lib.gda_ref_fwd_train_varlen.argtypes = [vp] * 12 + [i64] * 7 + [ci, f64, ci]
+    lib.gda_ref_bwd_varlen.restype = ci
+    lib.gda_ref_bwd_varlen.argtypes = [vp] * 15 + [i64] * 7 + [ci, f64, ci]
+    lib.gda_ref_threads.restype = ci
+    lib.gda_ref_threads.argtypes = []
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not _OVERRIDE:
             build()
-        lib = ctypes.CDLL(LIB_PATH)
-        i64, vp = ctypes.c_int64, ctypes.c_void_p
-        lib.gda_ref_fwd.restype = ctypes.c_int
-        lib.gda_ref_fwd.argtypes = [vp] * 7 + [i64] * 8 + [ctypes.c_int, vp, i64, ctypes.c_int]
-        lib.gda_ref_decode.restype = ctypes.c_int
-        lib.gda_ref_decode.argtypes = [vp] * 8 + [i64] * 8 + [ctypes.c_int, ctypes.c_int]
-        f64 = ctypes.c_double
-        lib.gda_ref_fwd_ex.restype = ctypes.c_int
-        lib.gda_ref_fwd_ex.argtypes = ([vp] * 7 + [i64] * 8 + [ctypes.c_int, vp, i64, f64,
-                                                                ctypes.c_int, ctypes.c_int])
-        lib.gda_ref_decode_ex.restype = ctypes.c_int
-        lib.gda_ref_decode_ex.argtypes = ([vp] * 8 + [i64] * 8 + [ctypes.c_int, f64, ctypes.c_int,
-                                                                  ctypes.c_int])
-        lib.gda_ref_fwd_varlen.restype = ctypes.c_int
-        lib.gda_ref_fwd_varlen.argtypes = ([vp] * 9 + [i64] * 7 + [ctypes.c_int, f64,
-                                                                  ctypes.c_int])
-        lib.gda_ref_decode_latent.restype = ctypes.c_int
-        lib.gda_ref_decode_latent.argtypes = ([vp] * 9 + [i64] * 10 + [ctypes.c_int, f64,
-                                                                     ctypes.c_int, ctypes.c_int])
-        ci = ctypes.c_int
-        lib.gda_ref_fwd_train.restype = ci
-        lib.gda_ref_fwd_train.argtypes = [vp] * 10 + [i64] * 8 + [ci, f64, ci]
-        lib.gda_ref_bwd.restype = ci
-        lib.gda_ref_bwd.argtypes = ([vp] * 13 + [i64] * 8 + [ci, f64, ci, vp, i64, vp, i64,
-                                                            ci])
-        lib.gda_ref_fwd_train_varlen.restype = ci
-        lib.gda_ref_fwd_train_varlen.argtypes = [vp] * 12 + [i64] * 7 + [ci, f64, ci]
-        lib.gda_ref_bwd_varlen.restype = ci
-        lib.gda_ref_bwd_varlen.argtypes = [vp] * 15 + [i64] * 7 + [ci, f64, ci]
-        lib.gda_ref_threads.restype = ctypes.c_int
-        lib.gda_ref_threads.argtypes = []
-        _lib = lib
+        _lib = _bind(ctypes.CDLL(LIB_PATH))
     return _lib
+
+
+@contextlib.contextmanager
+def loaded_from(path: str):
+    """Run every oracle function on another build of gda_ref.c while the block runs (the
+    tests build copies with one mistake planted, to show that the pins catch it)."""
+    global _lib
+    saved = _load()
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
 
 
 def _dtype_code(a: np.ndarray) -> int:
@@ -129,7 +120,7 @@ def _flags(lambda_logits: bool, gate_logits: bool) -> int:
 
 
 def ref_fwd(q_sig, q_noise, k, v, lam, gate, *, window: int, rows=None,
-            mutant: int = EXACT, scale: float | None = None, lambda_logits: bool = False,
+            scale: float | None = None, lambda_logits: bool = False,
             gate_logits: bool = False) -> np.ndarray:
     """Prefill oracle. Shapes: q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk],
     v [B,L,Hkv,dv], lam [B,L,S], gate [B,L,S,dv]. ``rows`` selects flat (b*L + t) rows;
@@ -154,14 +145,14 @@ def ref_fwd(q_sig, q_noise, k, v, lam, gate, *, window: int, rows=None,
     rc = _load().gda_ref_fwd_ex(_ptr(q_sig), _ptr(q_noise), _ptr(k), _ptr(v), _ptr(lam),
                                 _ptr(gate), _ptr(out), B, L, S, N, Hkv, dqk, dv, int(window),
                                 code, rp, n_rows, float(scale or 0.0),
-                                _flags(lambda_logits, gate_logits), int(mutant))
+                                _flags(lambda_logits, gate_logits))
     if rc != 0:
         raise ValueError(f"gda_ref_fwd rejected its arguments (code {rc})")
     return out
 
 
 def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window: int,
-               mutant: int = EXACT, scale: float | None = None, lambda_logits: bool = False,
+               scale: float | None = None, lambda_logits: bool = False,
                gate_logits: bool = False) -> np.ndarray:
     """Decode oracle. Shapes: q_sig [B,S,dqk], q_noise [B,N,dqk], k_cache [B,Lmax,Hkv,dqk],
     v_cache [B,Lmax,Hkv,dv], lam [B,S], gate [B,S,dv], lens int32 [B] or None (= Lmax).
@@ -183,7 +174,7 @@ def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window
     rc = _load().gda_ref_decode_ex(_ptr(q_sig), _ptr(q_noise), _ptr(k_cache), _ptr(v_cache),
                                    lp, _ptr(lam), _ptr(gate), _ptr(out), B, Lmax, S, N, Hkv,
                                    dqk, dv, int(window), code, float(scale or 0.0),
-                                   _flags(lambda_logits, gate_logits), int(mutant))
+                                   _flags(lambda_logits, gate_logits))
     if rc != 0:
         raise ValueError(f"gda_ref_decode rejected its arguments (code {rc})")
     return out
@@ -191,7 +182,7 @@ def ref_decode(q_sig, q_noise, k_cache, v_cache, lam, gate, lens=None, *, window
 
 def ref_decode_latent(q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, lens=None, *,
                       window: int, scale: float | None = None, lambda_logits: bool = False,
-                      gate_logits: bool = False, mutant: int = EXACT) -> np.ndarray:
+                      gate_logits: bool = False) -> np.ndarray:
     """Latent-cache decode oracle. Shapes: q_sig [B,S,Dn+Dr], q_noise [B,N,Dn+Dr],
     c_kv [B,Lmax,Dc], k_rope [B,Lmax,Dr], w_kv_b [Hkv,Dn+dv,Dc], lam [B,S], gate [B,S,dv],
     lens int32 [B] or None. Dr is k_rope's last dim; dv = w_kv_b rows - Dn. Returns
@@ -218,7 +209,7 @@ def ref_decode_latent(q_sig, q_noise, c_kv, k_rope, w_kv_b, lam, gate, lens=None
     rc = _load().gda_ref_decode_latent(
         _ptr(q_sig), _ptr(q_noise), _ptr(c_kv), _ptr(k_rope), _ptr(w_kv_b), lp, _ptr(lam),
         _ptr(gate), _ptr(out), B, Lmax, S, N, Hkv, Dn, Dr, Dc, dv, int(window), code,
-        float(scale or 0.0), _flags(lambda_logits, gate_logits), int(mutant))
+        float(scale or 0.0), _flags(lambda_logits, gate_logits))
     if rc != 0:
         raise ValueError(f"gda_ref_decode_latent rejected its arguments (code {rc})")
     return out
@@ -279,8 +270,8 @@ def ref_fwd_train(q_sig, q_noise, k, v, lam, gate, *, window: int, scale: float 
 
 
 def ref_bwd(q_sig, q_noise, k, v, lam, gate, d_out, *, window: int, scale: float | None = None,
-            lambda_logits: bool = False, gate_logits: bool = False, q_rows=None, k_rows=None,
-            mutant: int = EXACT) -> dict:
+            lambda_logits: bool = False, gate_logits: bool = False, q_rows=None,
+            k_rows=None) -> dict:
     """Backward oracle: gradients of sum(d_out * out). d_out [B,L,S,dv] at the inputs'
     storage type. Returns float64 dq_sig, dq_noise, dk, dv, dlam, dgate with the inputs'
     shapes, or, with ``q_rows`` / ``k_rows`` (flat b*L+t rows), only those rows:
@@ -307,8 +298,7 @@ def ref_bwd(q_sig, q_noise, k, v, lam, gate, d_out, *, window: int, scale: float
                              _ptr(d_out), _ptr(dq_sig), _ptr(dq_noise), _ptr(dk), _ptr(dvv),
                              _ptr(dlam), _ptr(dgate), B, L, S, N, Hkv, dqk, dv, int(window), code,
                              float(scale or 0.0), _flags(lambda_logits, gate_logits), qp,
-                             nq if qa is not None else 0, kp, nk if ka is not None else 0,
-                             int(mutant))
+                             nq if qa is not None else 0, kp, nk if ka is not None else 0)
     if rc != 0:
         raise ValueError(f"gda_ref_bwd rejected its arguments (code {rc})")
     out = dict(dq_sig=dq_sig, dq_noise=dq_noise, dk=dk, dv=dvv, dlam=dlam, dgate=dgate)

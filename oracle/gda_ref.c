@@ -38,7 +38,6 @@ typedef struct {
   const void* v;
   int64_t Lk, Hkv, dqk, dv;
   int dtype;
-  int mutant;
   double scale;  /* softmax scale given by the caller, or 0 for 1/sqrt(dqk) */
   int flags;     /* GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS */
 } kv_view;
@@ -56,8 +55,6 @@ static double rd(const void* base, int64_t i, int dtype) {
 }
 
 static int64_t k_index(const kv_view* kv, int64_t b, int64_t s, int64_t h, int64_t d) {
-  if (kv->mutant == GDA_REF_MUT_K_TRANSPOSED)
-    return ((b * kv->Hkv + h) * kv->Lk + s) * kv->dqk + d;
   return ((b * kv->Lk + s) * kv->Hkv + h) * kv->dqk + d;
 }
 
@@ -66,20 +63,11 @@ static int64_t v_index(const kv_view* kv, int64_t b, int64_t s, int64_t h, int64
 }
 
 /* Visible keys of query position t: [lo, hi]. */
-static void visible_range(int64_t t, int64_t W, int64_t Lk, int mutant, int64_t* lo,
-                          int64_t* hi) {
-  int64_t h = t, l;
-  if (mutant == GDA_REF_MUT_NO_CAUSAL) h = Lk - 1;
-  if (W == 0)
-    l = 0;
-  else if (mutant == GDA_REF_MUT_WINDOW_OBO)
-    l = t - W;
-  else
-    l = t - W + 1;
+static void visible_range(int64_t t, int64_t W, int64_t* lo, int64_t* hi) {
+  int64_t l = W == 0 ? 0 : t - W + 1;
   if (l < 0) l = 0;
-  if (mutant == GDA_REF_MUT_SKIP_FIRST_KEY && l == 0) l = 1;
   *lo = l;
-  *hi = h;
+  *hi = t;
 }
 
 /* One path's attention for one query row over KV head h of batch row b:
@@ -107,8 +95,7 @@ static void attend(const void* q, int64_t q_off, const kv_view* kv, int64_t b, i
   for (int64_t s = lo; s <= hi; ++s)
     for (int64_t e = 0; e < kv->dv; ++e)
       H[e] += z[s - lo] * rd(kv->v, v_index(kv, b, s, h, e), kv->dtype);
-  if (kv->mutant != GDA_REF_MUT_NO_NORMALIZE)
-    for (int64_t e = 0; e < kv->dv; ++e) H[e] /= l;
+  for (int64_t e = 0; e < kv->dv; ++e) H[e] /= l;
 }
 
 /* Every output of one query row: out[i][e] for signal heads i, dv channels e. */
@@ -117,13 +104,10 @@ static void gda_row(const void* q_sig, int64_t qs_off, const void* q_noise, int6
                     const kv_view* kv, int64_t b, int64_t t, int64_t S, int64_t N,
                     int64_t window, double* z, double* Hn, double* Hs, double* out) {
   const int64_t Hkv = kv->Hkv, dqk = kv->dqk, dv = kv->dv;
-  const int mut = kv->mutant;
   const int64_t g = S / N;
-  const double scale = kv->scale > 0.0
-                           ? kv->scale
-                           : 1.0 / sqrt((double)(mut == GDA_REF_MUT_SCALE_DV ? dv : dqk));
+  const double scale = kv->scale > 0.0 ? kv->scale : 1.0 / sqrt((double)dqk);
   int64_t lo, hi;
-  visible_range(t, window, kv->Lk, mut, &lo, &hi);
+  visible_range(t, window, &lo, &hi);
 
   /* Noise path: noise head j on KV head floor(j*Hkv/N). */
   for (int64_t j = 0; j < N; ++j)
@@ -131,22 +115,16 @@ static void gda_row(const void* q_sig, int64_t qs_off, const void* q_noise, int6
 
   /* Signal path, then D = H_S - lambda * Repeat_g(H_N), then the gate. */
   for (int64_t i = 0; i < S; ++i) {
-    const int64_t kvs = (mut == GDA_REF_MUT_KV_INTERLEAVE) ? i % Hkv : (i * Hkv) / S;
+    const int64_t kvs = (i * Hkv) / S;
     attend(q_sig, qs_off + i * dqk, kv, b, kvs, lo, hi, scale, z, Hs);
-    const int64_t j = (mut == GDA_REF_MUT_TILED_REPEAT) ? i % N : i / g;
-    double lam = rd(lambda, lam_off + (mut == GDA_REF_MUT_LAMBDA_BY_GROUP ? j : i), kv->dtype);
+    const int64_t j = i / g;
+    double lam = rd(lambda, lam_off + i, kv->dtype);
     if (kv->flags & GDA_REF_LAMBDA_LOGITS) lam = sigmoid(lam);
     for (int64_t e = 0; e < dv; ++e) {
-      double D;
-      if (mut == GDA_REF_MUT_DROP_LAMBDA)
-        D = Hs[e];
-      else if (mut == GDA_REF_MUT_PLUS_LAMBDA)
-        D = Hs[e] + lam * Hn[j * dv + e];
-      else
-        D = Hs[e] - lam * Hn[j * dv + e];
+      const double D = Hs[e] - lam * Hn[j * dv + e];
       double G = rd(gate, gate_off + i * dv + e, kv->dtype);
       if (kv->flags & GDA_REF_GATE_LOGITS) G = sigmoid(G);
-      out[i * dv + e] = (mut == GDA_REF_MUT_NO_GATE) ? D : G * D;
+      out[i * dv + e] = G * D;
     }
   }
 }
@@ -164,22 +142,22 @@ static int check_common(int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
 int gda_ref_fwd(const void* q_sig, const void* q_noise, const void* k, const void* v,
                 const void* lambda, const void* gate, double* out, int64_t B, int64_t L,
                 int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
-                int dtype, const int64_t* rows, int64_t n_rows, int mutant) {
+                int dtype, const int64_t* rows, int64_t n_rows) {
   return gda_ref_fwd_ex(q_sig, q_noise, k, v, lambda, gate, out, B, L, S, N, Hkv, dqk, dv,
-                        window, dtype, rows, n_rows, 0.0, 0, mutant);
+                        window, dtype, rows, n_rows, 0.0, 0);
 }
 
 int gda_ref_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const void* v,
                    const void* lambda, const void* gate, double* out, int64_t B, int64_t L,
                    int64_t S, int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
                    int dtype, const int64_t* rows, int64_t n_rows, double softmax_scale,
-                   int flags, int mutant) {
+                   int flags) {
   int rc = check_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
   if (rc) return rc;
   if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !out) return -6;
   if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
     return -9;
-  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, softmax_scale, flags};
   const int64_t total = rows ? n_rows : B * L;
   for (int64_t r = 0; r < total; ++r) {
     const int64_t flat = rows ? rows[r] : r;
@@ -213,23 +191,23 @@ int gda_ref_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const 
 int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
                    const void* v_cache, const int32_t* cache_lens, const void* lambda,
                    const void* gate, double* out, int64_t B, int64_t Lmax, int64_t S,
-                   int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window, int dtype,
-                   int mutant) {
+                   int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
+                   int dtype) {
   return gda_ref_decode_ex(q_sig, q_noise, k_cache, v_cache, cache_lens, lambda, gate, out, B,
-                           Lmax, S, N, Hkv, dqk, dv, window, dtype, 0.0, 0, mutant);
+                           Lmax, S, N, Hkv, dqk, dv, window, dtype, 0.0, 0);
 }
 
 int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cache,
                       const void* v_cache, const int32_t* cache_lens, const void* lambda,
                       const void* gate, double* out, int64_t B, int64_t Lmax, int64_t S,
                       int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
-                      int dtype, double softmax_scale, int flags, int mutant) {
+                      int dtype, double softmax_scale, int flags) {
   int rc = check_common(B, Lmax, S, N, Hkv, dqk, dv, window, dtype);
   if (rc) return rc;
   if (!q_sig || !q_noise || !k_cache || !v_cache || !lambda || !gate || !out) return -6;
   if (!(softmax_scale >= 0.0) || (flags & ~(GDA_REF_LAMBDA_LOGITS | GDA_REF_GATE_LOGITS)))
     return -9;
-  const kv_view kv = {k_cache, v_cache, Lmax, Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
+  const kv_view kv = {k_cache, v_cache, Lmax, Hkv, dqk, dv, dtype, softmax_scale, flags};
   int failed = 0;
 #pragma omp parallel
   {
@@ -249,8 +227,7 @@ int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cach
           for (int64_t x = 0; x < S * dv; ++x) o[x] = 0.0;
           continue;
         }
-        int64_t p = len - 1;
-        if (mutant == GDA_REF_MUT_DECODE_POS) p = len < Lmax ? len : Lmax - 1;
+        const int64_t p = len - 1;
         gda_row(q_sig, b * S * dqk, q_noise, b * N * dqk, lambda, b * S, gate, b * S * dv, &kv,
                 b, p, S, N, window, z, Hn, Hs, o);
       }
@@ -310,7 +287,7 @@ int gda_ref_fwd_varlen(const void* q_sig, const void* q_noise, const void* k, co
         const int64_t pos = (Lk - Lq) + (r - cu_q[i]);
         const kv_view kv = {offset_ptr(k, (int64_t)cu_k[i] * Hkv * dqk, dtype),
                             offset_ptr(v, (int64_t)cu_k[i] * Hkv * dv, dtype),
-                            Lk, Hkv, dqk, dv, dtype, GDA_REF_EXACT, softmax_scale, flags};
+                            Lk, Hkv, dqk, dv, dtype, softmax_scale, flags};
         gda_row(q_sig, r * S * dqk, q_noise, r * N * dqk, lambda, r * S, gate, r * S * dv, &kv,
                 0, pos, S, N, window, z, Hn, Hs, out + r * S * dv);
       }
@@ -334,19 +311,14 @@ int gda_ref_fwd_varlen(const void* q_sig, const void* q_noise, const void* k, co
  * and values (same head maps, window, lambda, gate, options). */
 static void expand_head(const void* c_kv, const void* w, int64_t b, int64_t h, int64_t lo,
                         int64_t hi, int64_t Lmax, int64_t Dn, int64_t Dc, int64_t dv, int dtype,
-                        int mutant, double* Kh, double* Vh) {
+                        double* Kh, double* Vh) {
   const int64_t rows = Dn + dv;
   for (int64_t s = lo; s <= hi; ++s) {
     const int64_t c0 = (b * Lmax + s) * Dc;
     for (int64_t r = 0; r < rows; ++r) {
-      int64_t wr = r;
-      if (mutant == GDA_REF_MUT_LATENT_V_ROWS && r >= Dn) wr = r - Dn; /* value from key rows */
       double acc = 0.0;
-      for (int64_t c = 0; c < Dc; ++c) {
-        const int64_t wi = (mutant == GDA_REF_MUT_LATENT_W_T) ? (h * Dc + c) * rows + wr
-                                                               : (h * rows + wr) * Dc + c;
-        acc += rd(w, wi, dtype) * rd(c_kv, c0 + c, dtype);
-      }
+      for (int64_t c = 0; c < Dc; ++c)
+        acc += rd(w, (h * rows + r) * Dc + c, dtype) * rd(c_kv, c0 + c, dtype);
       if (r < Dn)
         Kh[(s - lo) * Dn + r] = acc;
       else
@@ -358,16 +330,15 @@ static void expand_head(const void* c_kv, const void* w, int64_t b, int64_t h, i
 /* Attention of one query head over the expanded keys/values of its KV head. */
 static void attend_latent(const void* q, int64_t q_off, const void* k_rope, int64_t b,
                           int64_t lo, int64_t hi, int64_t Lmax, int64_t Dn, int64_t Dr,
-                          int64_t dv, int dtype, int mutant, double scale, const double* Kh,
+                          int64_t dv, int dtype, double scale, const double* Kh,
                           const double* Vh, double* z, double* H) {
   for (int64_t e = 0; e < dv; ++e) H[e] = 0.0;
   double m = -INFINITY;
   for (int64_t s = lo; s <= hi; ++s) {
     double acc = 0.0;
     for (int64_t d = 0; d < Dn; ++d) acc += rd(q, q_off + d, dtype) * Kh[(s - lo) * Dn + d];
-    if (mutant != GDA_REF_MUT_LATENT_NO_ROPE)
-      for (int64_t r = 0; r < Dr; ++r)
-        acc += rd(q, q_off + Dn + r, dtype) * rd(k_rope, (b * Lmax + s) * Dr + r, dtype);
+    for (int64_t r = 0; r < Dr; ++r)
+      acc += rd(q, q_off + Dn + r, dtype) * rd(k_rope, (b * Lmax + s) * Dr + r, dtype);
     z[s - lo] = scale * acc;
     if (z[s - lo] > m) m = z[s - lo];
   }
@@ -386,7 +357,7 @@ int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_
                           const void* lambda, const void* gate, double* out, int64_t B,
                           int64_t Lmax, int64_t S, int64_t N, int64_t Hkv, int64_t Dn,
                           int64_t Dr, int64_t Dc, int64_t dv, int64_t window, int dtype,
-                          double softmax_scale, int flags, int mutant) {
+                          double softmax_scale, int flags) {
   int rc = check_common(B, Lmax, S, N, Hkv, Dn + Dr, dv, window, dtype);
   if (rc) return rc;
   if (Dn < 1 || Dr < 0 || Dc < 1) return -1;
@@ -422,15 +393,15 @@ int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_
         if (len < 1) continue;
         const int64_t pos = len - 1;
         const int64_t lo = window ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
-        expand_head(c_kv, w_kv_b, b, h, lo, pos, Lmax, Dn, Dc, dv, dtype, mutant, Kh, Vh);
+        expand_head(c_kv, w_kv_b, b, h, lo, pos, Lmax, Dn, Dc, dv, dtype, Kh, Vh);
         for (int64_t j = 0; j < N; ++j)
           if ((j * Hkv) / N == h)
             attend_latent(q_noise, (b * N + j) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
-                          dtype, mutant, scale, Kh, Vh, z, Hn + (b * N + j) * dv);
+                          dtype, scale, Kh, Vh, z, Hn + (b * N + j) * dv);
         for (int64_t i = 0; i < S; ++i)
           if ((i * Hkv) / S == h)
             attend_latent(q_sig, (b * S + i) * dqk, k_rope, b, lo, pos, Lmax, Dn, Dr, dv,
-                          dtype, mutant, scale, Kh, Vh, z, Hs + (b * S + i) * dv);
+                          dtype, scale, Kh, Vh, z, Hs + (b * S + i) * dv);
       }
     }
     free(Kh);
@@ -521,10 +492,10 @@ int gda_ref_fwd_train(const void* q_sig, const void* q_noise, const void* k, con
                       int64_t N, int64_t Hkv, int64_t dqk, int64_t dv, int64_t window,
                       int dtype, double softmax_scale, int flags) {
   int rc = gda_ref_fwd_ex(q_sig, q_noise, k, v, lambda, gate, out, B, L, S, N, Hkv, dqk, dv,
-                          window, dtype, NULL, 0, softmax_scale, flags, GDA_REF_EXACT);
+                          window, dtype, NULL, 0, softmax_scale, flags);
   if (rc) return rc;
   if (!h_sig || !h_noise || !lse) return -6;
-  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, GDA_REF_EXACT, softmax_scale, flags};
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, softmax_scale, flags};
   const double scale = softmax_scale_of(&kv);
   const int64_t HT = S + N;
   int failed = 0;
@@ -539,7 +510,7 @@ int gda_ref_fwd_train(const void* q_sig, const void* q_noise, const void* k, con
       for (int64_t flat = 0; flat < B * L; ++flat) {
         const int64_t b = flat / L, t = flat % L;
         int64_t lo, hi;
-        visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+        visible_range(t, window, &lo, &hi);
         for (int64_t h = 0; h < HT; ++h) {
           const void* q;
           int64_t q_off, kvh;
@@ -567,7 +538,7 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
                 int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv, int64_t dqk,
                 int64_t dv, int64_t window, int dtype, double softmax_scale, int flags,
                 const int64_t* q_rows, int64_t n_q_rows, const int64_t* k_rows,
-                int64_t n_k_rows, int mutant) {
+                int64_t n_k_rows) {
   int rc = check_common(B, L, S, N, Hkv, dqk, dv, window, dtype);
   if (rc) return rc;
   if (!q_sig || !q_noise || !k || !v || !lambda || !gate || !d_out || !dq_sig || !dq_noise ||
@@ -581,7 +552,7 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
     if (q_rows && (q_rows[r] < 0 || q_rows[r] >= BL)) return -7;
   for (int64_t r = 0; r < nk; ++r)
     if (k_rows && (k_rows[r] < 0 || k_rows[r] >= BL)) return -7;
-  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
+  const kv_view kv = {k, v, L, Hkv, dqk, dv, dtype, softmax_scale, flags};
   const double scale = softmax_scale_of(&kv);
 
   /* Query rows whose forward quantities are needed: the query-side outputs, and
@@ -634,7 +605,7 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
       for (int64_t r = 0; r < nrow; ++r) {
         const int64_t flat = row_flat[r], b = flat / L, t = flat % L;
         int64_t lo, hi;
-        visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+        visible_range(t, window, &lo, &hi);
         for (int64_t h = 0; h < HT; ++h) {
           const void* q;
           int64_t q_off, kvh;
@@ -661,12 +632,10 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
             const double G = (flags & GDA_REF_GATE_LOGITS) ? sigmoid(gi) : gi;
             const double dO = rd(d_out, (flat * S + i) * dv + e, dtype);
             double dG = dO * D;
-            if ((flags & GDA_REF_GATE_LOGITS) && mutant != GDA_REF_MUT_BWD_GATE_DERIV)
-              dG *= G * (1.0 - G);
+            if (flags & GDA_REF_GATE_LOGITS) dG *= G * (1.0 - G);
             const double dD = dO * G;
             dHr[i * dv + e] = dD;
-            dlam += (mutant == GDA_REF_MUT_BWD_LAMBDA_SIGN ? 1.0 : -1.0) * dD *
-                    H[(S + j) * dv + e];
+            dlam -= dD * H[(S + j) * dv + e];
             if (q_out[r] >= 0) dgate[(q_out[r] * S + i) * dv + e] = dG;
           }
           if (flags & GDA_REF_LAMBDA_LOGITS) dlam *= lm * (1.0 - lm);
@@ -690,7 +659,7 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
               dP += dHr[h * dv + e] * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
             dl += P * dP;
           }
-          delta[r * HT + h] = mutant == GDA_REF_MUT_BWD_NO_DELTA ? 0.0 : dl;
+          delta[r * HT + h] = dl;
         }
       }
     }
@@ -706,7 +675,7 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
       const int64_t flat = q_rows ? q_rows[rq] : rq, b = flat / L, t = flat % L;
       const int64_t r = slot[flat];
       int64_t lo, hi;
-      visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+      visible_range(t, window, &lo, &hi);
       for (int64_t h = 0; h < HT; ++h) {
         const void* q;
         int64_t q_off, kvh;
@@ -735,11 +704,10 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
       const int64_t t_hi = window ? (s2 + window - 1 < L - 1 ? s2 + window - 1 : L - 1) : L - 1;
       for (int64_t t = s2; t <= t_hi; ++t) {
         int64_t lo, hi;
-        visible_range(t, window, L, GDA_REF_EXACT, &lo, &hi);
+        visible_range(t, window, &lo, &hi);
         if (s2 < lo || s2 > hi) continue;
         const int64_t qflat = b * L + t, r = slot[qflat];
         for (int64_t h = 0; h < HT; ++h) {
-          if (h >= S && mutant == GDA_REF_MUT_BWD_NOISE_KV) continue;
           const void* q;
           int64_t q_off, kvh;
           head_of(h, qflat, S, N, Hkv, dqk, q_sig, q_noise, &q, &q_off, &kvh);
@@ -748,9 +716,8 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
           for (int64_t e = 0; e < dv; ++e)
             dP += dH[(r * HT + h) * dv + e] * rd(v, v_index(&kv, b, s2, kvh, e), dtype);
           const double dz = P * (dP - delta[r * HT + h]);
-          const double ks = mutant == GDA_REF_MUT_BWD_DK_SCALE ? 1.0 : scale;
           for (int64_t d = 0; d < dqk; ++d)
-            dk[(rk * Hkv + kvh) * dqk + d] += ks * dz * rd(q, q_off + d, dtype);
+            dk[(rk * Hkv + kvh) * dqk + d] += scale * dz * rd(q, q_off + d, dtype);
           for (int64_t e = 0; e < dv; ++e)
             dv_out[(rk * Hkv + kvh) * dv + e] += P * dH[(r * HT + h) * dv + e];
         }
@@ -791,11 +758,11 @@ static int64_t seq_of(const int32_t* cu, int64_t r) {
 
 /* K/V view of sequence i: its key 0 at packed key row cu_k[i]. */
 static kv_view seq_view(const void* k, const void* v, const int32_t* cu_k, int64_t i,
-                        int64_t Hkv, int64_t dqk, int64_t dv, int dtype, int mutant,
+                        int64_t Hkv, int64_t dqk, int64_t dv, int dtype,
                         double softmax_scale, int flags) {
   const kv_view kv = {offset_ptr(k, (int64_t)cu_k[i] * Hkv * dqk, dtype),
                       offset_ptr(v, (int64_t)cu_k[i] * Hkv * dv, dtype),
-                      cu_k[i + 1] - cu_k[i], Hkv, dqk, dv, dtype, mutant, softmax_scale, flags};
+                      cu_k[i + 1] - cu_k[i], Hkv, dqk, dv, dtype, softmax_scale, flags};
   return kv;
 }
 
@@ -823,12 +790,12 @@ int gda_ref_fwd_train_varlen(const void* q_sig, const void* q_noise, const void*
 #pragma omp for schedule(dynamic, 1)
       for (int64_t r = 0; r < Tq; ++r) {
         const int64_t i = seq_of(cu_q, r);
-        const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
-                                    softmax_scale, flags);
+        const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, softmax_scale,
+                                    flags);
         const double scale = softmax_scale_of(&kv);
         const int64_t pos = (kv.Lk - (cu_q[i + 1] - cu_q[i])) + (r - cu_q[i]);
         int64_t lo, hi;
-        visible_range(pos, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+        visible_range(pos, window, &lo, &hi);
         for (int64_t h = 0; h < HT; ++h) {
           const void* q;
           int64_t q_off, kvh;
@@ -890,12 +857,12 @@ int gda_ref_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, co
 #pragma omp for schedule(dynamic, 1)
       for (int64_t r = 0; r < Tq; ++r) {
         const int64_t i = seq_of(cu_q, r);
-        const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
-                                    softmax_scale, flags);
+        const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, softmax_scale,
+                                    flags);
         const double scale = softmax_scale_of(&kv);
         const int64_t pos = (kv.Lk - (cu_q[i + 1] - cu_q[i])) + (r - cu_q[i]);
         int64_t lo, hi;
-        visible_range(pos, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+        visible_range(pos, window, &lo, &hi);
         for (int64_t h = 0; h < HT; ++h) {
           const void* q;
           int64_t q_off, kvh;
@@ -962,12 +929,12 @@ int gda_ref_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, co
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < Tq; ++r) {
       const int64_t i = seq_of(cu_q, r);
-      const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
-                                  softmax_scale, flags);
+      const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, softmax_scale,
+                                  flags);
       const double scale = softmax_scale_of(&kv);
       const int64_t pos = (kv.Lk - (cu_q[i + 1] - cu_q[i])) + (r - cu_q[i]);
       int64_t lo, hi;
-      visible_range(pos, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+      visible_range(pos, window, &lo, &hi);
       for (int64_t h = 0; h < HT; ++h) {
         const void* q;
         int64_t q_off, kvh;
@@ -989,15 +956,15 @@ int gda_ref_bwd_varlen(const void* q_sig, const void* q_noise, const void* k, co
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t kr = 0; kr < Tk; ++kr) {
       const int64_t i = seq_of(cu_k, kr);
-      const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, GDA_REF_EXACT,
-                                  softmax_scale, flags);
+      const kv_view kv = seq_view(k, v, cu_k, i, Hkv, dqk, dv, dtype, softmax_scale,
+                                  flags);
       const double scale = softmax_scale_of(&kv);
       const int64_t s2 = kr - cu_k[i], Lq = cu_q[i + 1] - cu_q[i], qoff = kv.Lk - Lq;
       for (int64_t x = 0; x < Hkv * dqk; ++x) dk[kr * Hkv * dqk + x] = 0.0;
       for (int64_t x = 0; x < Hkv * dv; ++x) dv_out[kr * Hkv * dv + x] = 0.0;
       for (int64_t t = 0; t < Lq; ++t) {
         int64_t lo, hi;
-        visible_range(qoff + t, window, kv.Lk, GDA_REF_EXACT, &lo, &hi);
+        visible_range(qoff + t, window, &lo, &hi);
         if (s2 < lo || s2 > hi) continue;
         const int64_t r = cu_q[i] + t;
         for (int64_t h = 0; h < HT; ++h) {

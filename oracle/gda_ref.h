@@ -25,33 +25,6 @@ extern "C" {
 
 enum { GDA_REF_BF16 = 0, GDA_REF_F32 = 1 };
 
-/* Deliberate mistakes, used only by tests that show the pins catch them. */
-enum {
-  GDA_REF_EXACT = 0,
-  GDA_REF_MUT_DROP_LAMBDA = 1,   /* D = H_S                                  */
-  GDA_REF_MUT_PLUS_LAMBDA = 2,   /* D = H_S + lambda H_N                     */
-  GDA_REF_MUT_TILED_REPEAT = 3,  /* noise head of signal i taken as i mod N  */
-  GDA_REF_MUT_KV_INTERLEAVE = 4, /* signal i reads KV head i mod Hkv         */
-  GDA_REF_MUT_WINDOW_OBO = 5,    /* window keeps t-s <= W (W+1 keys)         */
-  GDA_REF_MUT_SCALE_DV = 6,      /* softmax scale 1/sqrt(dv)                 */
-  GDA_REF_MUT_NO_GATE = 7,       /* gate not applied                         */
-  GDA_REF_MUT_NO_CAUSAL = 8,     /* prefill keys up to L-1 visible           */
-  GDA_REF_MUT_K_TRANSPOSED = 9,  /* K read as [B, Hkv, L, dqk]               */
-  GDA_REF_MUT_LAMBDA_BY_GROUP = 10, /* lambda read at the noise index        */
-  GDA_REF_MUT_NO_NORMALIZE = 11, /* softmax weights not divided by their sum */
-  GDA_REF_MUT_DECODE_POS = 12,   /* decode query at position len, not len-1  */
-  GDA_REF_MUT_SKIP_FIRST_KEY = 13, /* key 0 never visible                    */
-  GDA_REF_MUT_LATENT_W_T = 14,   /* latent: W^KV_b read as [Hkv, Dc, Dn+dv]   */
-  GDA_REF_MUT_LATENT_NO_ROPE = 15, /* latent: rotary key term dropped         */
-  GDA_REF_MUT_LATENT_V_ROWS = 16, /* latent: value from the key rows of W     */
-  GDA_REF_MUT_BWD_NO_DELTA = 17,  /* backward: dz = P dP (row term dropped)    */
-  GDA_REF_MUT_BWD_LAMBDA_SIGN = 18, /* backward: dlambda with the wrong sign   */
-  GDA_REF_MUT_BWD_NOISE_KV = 19,  /* backward: noise path left out of dK, dV   */
-  GDA_REF_MUT_BWD_DK_SCALE = 20,  /* backward: dK without the softmax scale    */
-  GDA_REF_MUT_BWD_GATE_DERIV = 21, /* backward: gate logits without sigmoid'   */
-  GDA_REF_MUT_COUNT = 22
-};
-
 /* Prefill. Layouts (row-major, innermost contiguous):
  *   q_sig [B,L,S,dqk], q_noise [B,L,N,dqk], k [B,L,Hkv,dqk], v [B,L,Hkv,dv],
  *   lambda [B,L,S], gate [B,L,S,dv]; all of storage type `dtype`.
@@ -62,7 +35,7 @@ int gda_ref_fwd(const void* q_sig, const void* q_noise, const void* k, const voi
                 const void* lambda, const void* gate, double* out,
                 int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
                 int64_t dqk, int64_t dv, int64_t window, int dtype,
-                const int64_t* rows, int64_t n_rows, int mutant);
+                const int64_t* rows, int64_t n_rows);
 
 /* Decode: one query token per sequence at position len_b - 1 over a cache that
  * already holds that token's K/V.
@@ -74,7 +47,7 @@ int gda_ref_decode(const void* q_sig, const void* q_noise, const void* k_cache,
                    const void* v_cache, const int32_t* cache_lens, const void* lambda,
                    const void* gate, double* out,
                    int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
-                   int64_t dqk, int64_t dv, int64_t window, int dtype, int mutant);
+                   int64_t dqk, int64_t dv, int64_t window, int dtype);
 
 /* Options of the _ex forms (0 and 0 give the plain forms above):
  *   softmax_scale > 0 replaces 1/sqrt(dqk); 0 keeps it; negative or NaN is rejected;
@@ -85,15 +58,14 @@ int gda_ref_fwd_ex(const void* q_sig, const void* q_noise, const void* k, const 
                    const void* lambda, const void* gate, double* out,
                    int64_t B, int64_t L, int64_t S, int64_t N, int64_t Hkv,
                    int64_t dqk, int64_t dv, int64_t window, int dtype,
-                   const int64_t* rows, int64_t n_rows, double softmax_scale, int flags,
-                   int mutant);
+                   const int64_t* rows, int64_t n_rows, double softmax_scale, int flags);
 
 int gda_ref_decode_ex(const void* q_sig, const void* q_noise, const void* k_cache,
                       const void* v_cache, const int32_t* cache_lens, const void* lambda,
                       const void* gate, double* out,
                       int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
                       int64_t dqk, int64_t dv, int64_t window, int dtype,
-                      double softmax_scale, int flags, int mutant);
+                      double softmax_scale, int flags);
 
 /* Packed sequences with a query offset. Sequence i has query rows cu_q[i] ..
  * cu_q[i+1]-1 and key rows cu_k[i] .. cu_k[i+1]-1 of the packed tensors
@@ -118,7 +90,7 @@ int gda_ref_decode_latent(const void* q_sig, const void* q_noise, const void* c_
                           const void* lambda, const void* gate, double* out,
                           int64_t B, int64_t Lmax, int64_t S, int64_t N, int64_t Hkv,
                           int64_t Dn, int64_t Dr, int64_t Dc, int64_t dv, int64_t window,
-                          int dtype, double softmax_scale, int flags, int mutant);
+                          int dtype, double softmax_scale, int flags);
 
 /* Training form of the forward: out as gda_ref_fwd_ex, plus what the backward
  * takes from the forward:
@@ -146,7 +118,7 @@ int gda_ref_bwd(const void* q_sig, const void* q_noise, const void* k, const voi
                 int64_t dqk, int64_t dv, int64_t window, int dtype,
                 double softmax_scale, int flags,
                 const int64_t* q_rows, int64_t n_q_rows, const int64_t* k_rows,
-                int64_t n_k_rows, int mutant);
+                int64_t n_k_rows);
 
 /* Packed-sequence forms of the two above (sequences as in gda_ref_fwd_varlen):
  * gda_ref_fwd_train_varlen: out [Tq,S,dv], h_sig [Tq,S,dv], h_noise [Tq,N,dv] and

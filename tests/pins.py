@@ -667,11 +667,11 @@ def all_pins(fwd, decode):
     return msgs
 
 
-def oracle_entry_points(mutant=oracle.EXACT):
+def oracle_entry_points():
     def fwd(*a, window, rows=None):
-        return oracle.ref_fwd(*a, window=window, rows=rows, mutant=mutant)
+        return oracle.ref_fwd(*a, window=window, rows=rows)
 
     def decode(*a, window):
-        return oracle.ref_decode(*a, window=window, mutant=mutant)
+        return oracle.ref_decode(*a, window=window)
 
     return fwd, decode

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 
-from . import pins
+from . import pins, planted
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -32,10 +32,10 @@ def test_exact_oracle_decode_pin():
     assert pins.pin_decode_is_last_row(EXACT_FWD, EXACT_DEC) == []
 
 
-@pytest.mark.parametrize("name", sorted(oracle.MUTANTS))
+@pytest.mark.parametrize("name", sorted(planted.FWD))
 def test_planted_mistake_is_caught(name):
-    fwd, dec = pins.oracle_entry_points(oracle.MUTANTS[name])
-    assert pins.all_pins(fwd, dec), f"no pin catches the planted mistake {name!r}"
+    with oracle.loaded_from(planted.build(name)):
+        assert pins.all_pins(EXACT_FWD, EXACT_DEC), f"no pin catches the planted mistake {name!r}"
 
 
 def test_options_pin():
@@ -95,14 +95,11 @@ def test_latent_pin():
     assert pins.pin_latent(oracle.ref_decode_latent, oracle.ref_decode) == []
 
 
-@pytest.mark.parametrize("name", sorted(oracle.LATENT_MUTANTS))
+@pytest.mark.parametrize("name", sorted(planted.LATENT))
 def test_latent_planted_mistake_is_caught(name):
-    m = oracle.LATENT_MUTANTS[name]
-
-    def planted(*a, window, **kw):
-        return oracle.ref_decode_latent(*a, window=window, mutant=m, **kw)
-
-    assert pins.pin_latent(planted, oracle.ref_decode), f"no pin catches {name!r}"
+    with oracle.loaded_from(planted.build(name)):
+        assert pins.pin_latent(oracle.ref_decode_latent, oracle.ref_decode), \
+            f"no pin catches {name!r}"
 
 
 def test_hand_worked_example():
@@ -138,9 +135,9 @@ def test_rejects_bad_arguments():
                        x["gate"], window=0)
 
 
-def _bwd(mutant=oracle.EXACT):
+def _bwd():
     def f(*a, **kw):
-        return oracle.ref_bwd(*a, mutant=mutant, **kw)
+        return oracle.ref_bwd(*a, **kw)
     return f
 
 
@@ -152,9 +149,10 @@ def test_backward_pin_bf16_inputs():
     assert pins.pin_backward(_bwd(), cases=pins.BWD_CASES[:3], dtype="bf16") == []
 
 
-@pytest.mark.parametrize("name", sorted(oracle.BWD_MUTANTS))
+@pytest.mark.parametrize("name", sorted(planted.BWD))
 def test_backward_planted_mistake_is_caught(name):
-    assert pins.pin_backward(_bwd(oracle.BWD_MUTANTS[name])) != []
+    with oracle.loaded_from(planted.build(name)):
+        assert pins.pin_backward(_bwd()) != []
 
 
 def test_fwd_train_pin():
