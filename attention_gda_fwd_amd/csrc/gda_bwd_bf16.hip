@@ -36,12 +36,6 @@ constexpr int kBwdThreads = 256;  // 4 waves
 // 22.0 ms against 15.1-15.5 ms for one tile on the Motif-3 full-layer backward.
 constexpr int kDkvTiles = 1;
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 // Store 16-row accumulator tiles (lane (g, c) holds rows 16t + 4g + r of column c)
 // as one bf16 row per column: tile pairs are regrouped across lanes l and l^16
 // so each lane stores 8 consecutive values (16 bytes).
@@ -95,8 +89,18 @@ __device__ __forceinline__ bf16x8 row_operand(const unsigned char* tile, int str
 }
 
 // ---------------------------------------------------------------------------------
-// Elementwise part. One wave per (token row, noise group j); lanes own DV/64
-// channels each.
+// Elementwise part. One wave per (token row, noise group j). The wave takes the
+// group's g signal heads HP = 64 / (DV / 8) at a time: lane l works on head slot
+// l / (DV / 8) and the 8 channels 8 (l % (DV / 8)) .. +7 of it, so every load and
+// store moves 16 bytes per lane and whole rows per wave; a head's dot products
+// reduce over its DV / 8 lanes, and the noise head's dO sums the slots at the end.
+template <int DV>
+__device__ __forceinline__ float group_sum(float x) {  // over the DV / 8 lanes of a slot
+#pragma unroll
+  for (int o = DV / 16; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <int DV>
 __global__ void __launch_bounds__(kBwdThreads)
 bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__ gate,
@@ -105,7 +109,8 @@ bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__
                 uint16_t* __restrict__ dlam, uint16_t* __restrict__ do_sig,
                 uint16_t* __restrict__ do_noise, float* __restrict__ delta, int64_t items,
                 int Lrow, int64_t dl_b, int64_t dl_h, int S, int N, int flags) {
-  constexpr int CPL = DV / 64;
+  constexpr int LPH = DV / 8;    // lanes per head
+  constexpr int HP = 64 / LPH;   // head slots per wave
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
   if (item >= items) return;
@@ -117,53 +122,80 @@ bwd_prep_kernel(const uint16_t* __restrict__ d_out, const uint16_t* __restrict__
   const int64_t b = row / Lrow;
   const int t = (int)(row - b * Lrow);
   const int g = S / N;
-  float hn[CPL], dn[CPL];
+  const int slot = lane / LPH, c8 = lane - (lane / LPH) * LPH;
+  const u32x4 hnw = ldg16(h_noise + (row * N + j) * DV + 8 * c8);
+  float hn[8], dn[8];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    hn[c] = bf16_to_f32(h_noise[(row * N + j) * DV + lane * CPL + c]);
-    dn[c] = 0.f;
+  for (int w = 0; w < 4; ++w) {
+    hn[2 * w] = bf16_lo(hnw[w]);
+    hn[2 * w + 1] = bf16_hi(hnw[w]);
   }
-  for (int ii = 0; ii < g; ++ii) {
-    const int i = j * g + ii;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dn[c] = 0.f;
+  for (int p0 = 0; p0 < g; p0 += HP) {
+    const int ii = p0 + slot;
+    const bool on = ii < g;  // uniform over a slot's lanes
+    const int i = j * g + (on ? ii : 0);
+    const int64_t base = (row * S + i) * DV + 8 * c8;
     float lm = bf16_to_f32(lam[row * S + i]);
     if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
-    const int64_t base = (row * S + i) * DV + lane * CPL;
+    const u32x4 hsw = ldg16(h_sig + base), gw = ldg16(gate + base), ow = ldg16(d_out + base);
     float pl = 0.f, pd = 0.f;
+    u32x4 dgw, ddw;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const float hs = bf16_to_f32(h_sig[base + c]);
-      float G = bf16_to_f32(gate[base + c]);
-      if (flags & kGateLogits) G = sigmoid_f32(G);
-      const float dO = bf16_to_f32(d_out[base + c]);
-      const float D = hs - lm * hn[c];
-      float dG = dO * D;
-      if (flags & kGateLogits) dG *= G * (1.f - G);
-      dgate[base + c] = f32_to_bf16(dG);
-      const float dD = dO * G;
-      const uint16_t dDb = f32_to_bf16(dD);
-      do_sig[base + c] = dDb;
-      pl += dD * hn[c];
-      pd += bf16_to_f32(dDb) * hs;  // delta from the dO the matrix kernels use
-      dn[c] -= lm * dD;
+    for (int w = 0; w < 4; ++w) {
+      float dg2[2], dd2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 2 * w + h;
+        const float hs = h ? bf16_hi(hsw[w]) : bf16_lo(hsw[w]);
+        float G = h ? bf16_hi(gw[w]) : bf16_lo(gw[w]);
+        if (flags & kGateLogits) G = sigmoid_f32(G);
+        const float dO = h ? bf16_hi(ow[w]) : bf16_lo(ow[w]);
+        const float D = hs - lm * hn[c];
+        float dG = dO * D;
+        if (flags & kGateLogits) dG *= G * (1.f - G);
+        const float dD = dO * G;
+        dg2[h] = dG;
+        dd2[h] = dD;
+        const float dDb = bf16_to_f32(f32_to_bf16(dD));
+        pl += dD * hn[c];
+        pd += dDb * hs;  // delta from the dO the matrix kernels use
+        if (on) dn[c] -= lm * dD;
+      }
+      dgw[w] = pack_bf16x2(dg2[0], dg2[1]);
+      ddw[w] = pack_bf16x2(dd2[0], dd2[1]);
     }
-    pl = wave_sum(pl);
-    pd = wave_sum(pd);
-    if (lane == 0) {
-      float dl = -pl;
-      if (flags & kLambdaLogits) dl *= lm * (1.f - lm);
-      dlam[row * S + i] = f32_to_bf16(dl);
-      delta[b * dl_b + i * dl_h + t] = pd;
+    pl = group_sum<DV>(pl);
+    pd = group_sum<DV>(pd);
+    if (on) {
+      *(u32x4*)(dgate + base) = dgw;
+      *(u32x4*)(do_sig + base) = ddw;
+      if (c8 == 0) {
+        float dl = -pl;
+        if (flags & kLambdaLogits) dl *= lm * (1.f - lm);
+        dlam[row * S + i] = f32_to_bf16(dl);
+        delta[b * dl_b + i * dl_h + t] = pd;
+      }
     }
   }
-  float pn = 0.f;
+  // The noise head's dO: the sum over the slots (lanes c8, c8 + LPH, ...).
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const uint16_t db = f32_to_bf16(dn[c]);
-    do_noise[(row * N + j) * DV + lane * CPL + c] = db;
-    pn += bf16_to_f32(db) * hn[c];
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int o = LPH; o < 64; o <<= 1) dn[c] += __shfl_xor(dn[c], o);
+  if (slot == 0) {
+    u32x4 dnw;
+    float pn = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dnw[w] = pack_bf16x2(dn[2 * w], dn[2 * w + 1]);
+      pn += bf16_lo(dnw[w]) * hn[2 * w] + bf16_hi(dnw[w]) * hn[2 * w + 1];
+    }
+    *(u32x4*)(do_noise + (row * N + j) * DV + 8 * c8) = dnw;
+    pn = group_sum<DV>(pn);
+    if (lane == 0) delta[b * dl_b + (S + j) * dl_h + t] = pn;
   }
-  pn = wave_sum(pn);
-  if (lane == 0) delta[b * dl_b + (S + j) * dl_h + t] = pn;
 }
 
 // One query head's view: its Q and dO rows, and its KV head.
