@@ -17,8 +17,8 @@
 //     [c ; k_rope] with the latent c as the value (a multi-query attention of all
 //     S + N heads); split-KV over workgroups, each writing partial (max, sum, o)
 //     per head to the workspace;
-//  3. latent_merge_kernel: merges the splits, up-projects o with W_v[h] (fp32),
-//     and applies lambda and the gate.
+//  3. latent_merge_kernel: merges the splits, up-projects o with W_v[h] (matrix
+//     cores, several sequences per workgroup), and applies lambda and the gate.
 // Reading 1152 B per cached token instead of Hkv * (dqk + dv) * 2 = 10240 B.
 #include <mutex>
 
@@ -606,41 +606,48 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
 }
 
 // ---- 3. merge, up-project, epilogue ------------------------------------------------
-// One workgroup per (sequence b, noise head j): heads = noise j and its g signal
-// heads g*j .. g*j+g-1. Each head's o is merged over the splits (fp32, in LDS),
-// then H = W_v[h] o on the matrix cores: for each KV head h the group uses,
-// H^T [128 x heads] += W_v[h] [128 x 512] . O [512 x heads] with O's columns of
-// the heads on h (the others zero), O split into bf16 high and low parts (two
-// products with fp32 accumulation, so the bf16 weights meet o at about fp32
-// precision). Wave w owns W_v rows 32 w .. 32 w + 31, read straight from global
-// memory as A operands (the group's first KV head prefetched before the merge).
-// Then out = gate * (H_S - lambda * H_N).
+// One workgroup per (noise head j, SB = 16 / (1 + g) consecutive sequences): heads =
+// noise j and its g signal heads g*j .. g*j+g-1 of each of the SB sequences, at most
+// 16 (column x: sequence x / nh of the group, its head x % nh, 0 the noise head).
+// Each head's o is merged over the splits (fp32, in LDS), then H = W_v[h] o on the
+// matrix cores: for each KV head h the group's heads use, H^T [128 x 16] +=
+// W_v[h] [128 x 512] . O [512 x 16] with O's columns of the heads on h (the others
+// zero), O split into bf16 high and low parts (two products with fp32
+// accumulation, so the bf16 weights meet o at about fp32 precision). Wave w owns
+// W_v rows 32 w .. 32 w + 31, read straight from global memory as A operands (the
+// first KV head's fragments prefetched before the merge) and used for all SB
+// sequences. Then out = gate * (H_S - lambda * H_N).
 __global__ void __launch_bounds__(256)
 latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__ w_kv_b,
                     const int32_t* __restrict__ lens, const uint16_t* __restrict__ lam,
-                    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int Lmax,
-                    int S, int N, int Hkv, int nsplit, int XP, int flags) {
-  constexpr int MAXG = 15;
+                    const uint16_t* __restrict__ gate, uint16_t* __restrict__ out, int B,
+                    int Lmax, int S, int N, int Hkv, int nsplit, int XP, int flags) {
+  constexpr int MAXH = 16;  // heads of a workgroup (MFMA columns)
   constexpr int KST = LDC / 32;  // k-steps of the up-projection
-  __shared__ __attribute__((aligned(16))) float so[MAXG + 1][LDC];  // merged o: [0] noise, [1 + t] signal g*j + t
-  __shared__ float sH[MAXG + 1][LDV];   // up-projected outputs
-  __shared__ float sml[(MAXG + 1) * 64][2];  // (m, l) of each (head, split), then (weight, l)
-  __shared__ float sinvl[MAXG + 1];
+  __shared__ __attribute__((aligned(16))) float so[MAXH][LDC];  // merged o per column
+  __shared__ float sH[MAXH][LDV];                                // up-projected outputs
+  __shared__ float sml[MAXH * 64][2];  // (m, l) of each (column, split), then (weight, l)
+  __shared__ float sinvl[MAXH];
+  __shared__ int slen[MAXH];  // each column's sequence length (0: empty or past B)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g4 = lane >> 4;
-  const int b = blockIdx.x / N, j = blockIdx.x - (blockIdx.x / N) * N;
   const int g = S / N;
   const int nh = 1 + g;
-  int len = lens ? lens[b] : Lmax;
-  if (len > Lmax) len = Lmax;
-  if (len < 1) {
-    for (int idx = tid; idx < g * LDV; idx += 256)
-      out[((int64_t)b * S + g * j + idx / LDV) * LDV + idx % LDV] = 0;
-    return;
-  }
+  const int SB = MAXH / nh;  // sequences per workgroup
+  const int j = blockIdx.x % N, b0 = (blockIdx.x / N) * SB;
+  const int ncol = nh * SB;
   auto kv_of = [&](int x) {
     return x == 0 ? (int)(((int64_t)j * Hkv) / N) : (int)(((int64_t)(g * j + x - 1) * Hkv) / S);
   };
+  if (tid < MAXH) {
+    const int bb = b0 + tid / nh;
+    int len = 0;
+    if (tid < ncol && bb < B) {
+      len = lens ? lens[bb] : Lmax;
+      len = len > Lmax ? Lmax : len;
+    }
+    slen[tid] = len > 0 ? len : 0;
+  }
   // This wave's W_v rows of KV head h as A operands: row 32 wave + 16 mt + col,
   // latent dims 32 ks + 8 g4 .. +7.
   auto w_frag = [&](int h, int mt, int ks) {
@@ -654,56 +661,69 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) wpre[mt][ks] = w_frag(h0, mt, ks);
-  // Merge. First every (head, split) reference and sum into LDS in one round
-  // trip, then each head's split weights 2^(m_k - max m) and 1/L, then thread t
-  // sums latent dims t and t+256 of every head over the splits (all loads
-  // independent of each other).
-  auto head_part = [&](int x) {
-    const int hc = x == 0 ? S + j : g * j + (x - 1);
-    return part + ((int64_t)b * nsplit * XP + hc) * LPART;
+  __syncthreads();  // slen
+  // Merge. First every (column, split) reference and sum into LDS in one round
+  // trip, then each column's split weights 2^(m_k - max m) and 1/L, then thread t
+  // sums latent dims t and t+256 of every column over the splits (all loads
+  // independent of each other). Columns of empty sequences get o = 0.
+  auto col_part = [&](int x) {
+    const int hx = x % nh, bb = b0 + x / nh;
+    const int hc = hx == 0 ? S + j : g * j + (hx - 1);
+    return part + ((int64_t)bb * nsplit * XP + hc) * LPART;
   };
-  for (int idx = tid; idx < nh * nsplit; idx += 256) {
+  for (int idx = tid; idx < ncol * nsplit; idx += 256) {
     const int x = idx / nsplit, k = idx - (idx / nsplit) * nsplit;
-    const float* pk = head_part(x) + (int64_t)k * XP * LPART;
-    sml[idx][0] = pk[0];
-    sml[idx][1] = pk[1];
-  }
-  __syncthreads();
-  if (tid < nh) {  // per head: the split weights (in place of m) and 1/L
-    float M = -INFINITY;
-    for (int k = 0; k < nsplit; ++k) M = fmaxf(M, sml[tid * nsplit + k][0]);
-    float L = 0.f;
-    for (int k = 0; k < nsplit; ++k) {
-      const float wk = fast_exp2(sml[tid * nsplit + k][0] - M);
-      sml[tid * nsplit + k][0] = wk;
-      L += wk * sml[tid * nsplit + k][1];
+    float m = 0.f, l = 0.f;
+    if (slen[x] > 0) {
+      const float* pk = col_part(x) + (int64_t)k * XP * LPART;
+      m = pk[0];
+      l = pk[1];
     }
-    sinvl[tid] = 1.f / L;
+    sml[idx][0] = m;
+    sml[idx][1] = l;
   }
   __syncthreads();
-  for (int x = 0; x < nh; ++x) {
-    const float* p0 = head_part(x) + 4;
+  if (tid < ncol) {  // per column: the split weights (in place of m) and 1/L
+    if (slen[tid] > 0) {
+      float M = -INFINITY;
+      for (int k = 0; k < nsplit; ++k) M = fmaxf(M, sml[tid * nsplit + k][0]);
+      float L = 0.f;
+      for (int k = 0; k < nsplit; ++k) {
+        const float wk = fast_exp2(sml[tid * nsplit + k][0] - M);
+        sml[tid * nsplit + k][0] = wk;
+        L += wk * sml[tid * nsplit + k][1];
+      }
+      sinvl[tid] = 1.f / L;
+    } else {
+      sinvl[tid] = 0.f;
+    }
+  }
+  __syncthreads();
+  for (int x = 0; x < ncol; ++x) {
     float a0 = 0.f, a1 = 0.f;
+    if (slen[x] > 0) {  // uniform
+      const float* p0 = col_part(x) + 4;
 #pragma unroll 4
-    for (int k = 0; k < nsplit; ++k) {
-      const float* pk = p0 + (int64_t)k * XP * LPART;
-      const float wk = sml[x * nsplit + k][0];
-      a0 = fmaf(wk, pk[tid], a0);
-      a1 = fmaf(wk, pk[tid + 256], a1);
+      for (int k = 0; k < nsplit; ++k) {
+        const float* pk = p0 + (int64_t)k * XP * LPART;
+        const float wk = sml[x * nsplit + k][0];
+        a0 = fmaf(wk, pk[tid], a0);
+        a1 = fmaf(wk, pk[tid + 256], a1);
+      }
     }
     so[x][tid] = a0 * sinvl[x];
     so[x][tid + 256] = a1 * sinvl[x];
   }
   __syncthreads();
-  // Up-projection: column col of the B operand is head col (zero unless it is one
-  // of this group's heads on KV head h).
+  // Up-projection: column col of the B operand is column col of the group (zero
+  // unless it is one of the group's heads on KV head h).
   floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
   for (int x = 0; x < nh; ++x) {
     const int h = kv_of(x);
     bool seen = false;  // each KV head once (wave-uniform)
     for (int y = 0; y < x; ++y) seen |= kv_of(y) == h;
     if (seen) continue;
-    const bool mine = col < nh && kv_of(col) == h;
+    const bool mine = col < ncol && kv_of(col % nh) == h;
     const bool pre = h == h0;
 #pragma unroll
     for (int ks = 0; ks < KST; ++ks) {
@@ -725,22 +745,29 @@ latent_merge_kernel(const float* __restrict__ part, const uint16_t* __restrict__
       }
     }
   }
-  if (col < nh) {
+  if (col < ncol) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sH[col][32 * wave + 16 * mt + 4 * g4 + r] = acc[mt][r];
   }
   __syncthreads();
-  for (int idx = tid; idx < g * LDV; idx += 256) {
-    const int t = idx / LDV, e = idx - (idx / LDV) * LDV;
+  for (int idx = tid; idx < SB * g * LDV; idx += 256) {
+    const int sb = idx / (g * LDV), rem = idx - sb * (g * LDV);
+    const int t = rem / LDV, e = rem - (rem / LDV) * LDV;
+    const int bb = b0 + sb;
+    if (bb >= B) continue;
     const int i = g * j + t;
-    float lm = bf16_to_f32(lam[(int64_t)b * S + i]);
+    const int64_t o_idx = ((int64_t)bb * S + i) * LDV + e;
+    if (slen[sb * nh] == 0) {  // an empty cache gives zeros
+      out[o_idx] = 0;
+      continue;
+    }
+    float lm = bf16_to_f32(lam[(int64_t)bb * S + i]);
     if (flags & kLambdaLogits) lm = sigmoid_f32(lm);
-    const int64_t o_idx = ((int64_t)b * S + i) * LDV + e;
     float gv = bf16_to_f32(gate[o_idx]);
     if (flags & kGateLogits) gv = sigmoid_f32(gv);
-    out[o_idx] = f32_to_bf16(gv * (sH[1 + t][e] - lm * sH[0][e]));
+    out[o_idx] = f32_to_bf16(gv * (sH[sb * nh + 1 + t][e] - lm * sH[sb * nh][e]));
   }
 }
 
@@ -812,7 +839,8 @@ hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream) {
   const size_t qa_bytes = ((size_t)a.B * XP * LQW * 2 + 255) & ~(size_t)255;
   uint16_t* qa = (uint16_t*)a.workspace;
   float* part = (float*)((char*)a.workspace + qa_bytes);
-  const int64_t g2 = (int64_t)a.B * ns, g3 = (int64_t)a.B * a.N;
+  const int sb = 16 / (1 + a.S / a.N);  // sequences per merge workgroup
+  const int64_t g2 = (int64_t)a.B * ns, g3 = (int64_t)((a.B + sb - 1) / sb) * a.N;
   if (g2 > 0x7fffffff || g3 > 0x7fffffff) return hipErrorInvalidConfiguration;
   const int nkv_max = a.S / a.Hkv + (a.N + a.Hkv - 1) / a.Hkv;
   const int64_t g1b = (int64_t)a.Hkv * (((int64_t)a.B * nkv_max + AB_COLS - 1) / AB_COLS);
@@ -846,8 +874,8 @@ hipError_t launch_decode_latent(const LatentArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(latent_merge_kernel, dim3((unsigned)g3), dim3(256), 0, stream,
                      (const float*)part, (const uint16_t*)a.w_kv_b, a.lens,
-                     (const uint16_t*)a.lam, (const uint16_t*)a.gate, (uint16_t*)a.out, a.Lmax,
-                     a.S, a.N, a.Hkv, ns, XP, a.flags);
+                     (const uint16_t*)a.lam, (const uint16_t*)a.gate, (uint16_t*)a.out, a.B,
+                     a.Lmax, a.S, a.N, a.Hkv, ns, XP, a.flags);
   return hipGetLastError();
 }
 

@@ -356,6 +356,29 @@ def test_latent_small_ragged(name, window):
     assert np.all(got[3] == 0.0), "an empty cache must give zeros"
 
 
+# The merge takes 16 // (1 + g) sequences per workgroup: g = 1 puts 8 sequences in a
+# workgroup (9 sequences: a full group and a lone one), g = 8 one; empty caches among
+# them.
+LAT_GROUPS = {
+    "g1_B9": (dict(case_id=234, B=9, Lmax=300, S=16, N=16, Hkv=16),
+              [300, 0, 17, 1, 300, 255, 0, 64, 129]),
+    "g8_B3": (dict(case_id=235, B=3, Lmax=300, S=64, N=8, Hkv=8), [300, 0, 77]),
+}
+
+
+@pytest.mark.parametrize("window", [0, 100])
+@pytest.mark.parametrize("name", sorted(LAT_GROUPS))
+def test_latent_merge_groups(name, window):
+    kw, lens_l = LAT_GROUPS[name]
+    U.log(f"latent decode parity {name} window={window}")
+    host, dev = _latent_case(**kw)
+    lens = np.array(lens_l, dtype=np.int32)
+    got = U.to_f64(_run_latent(dev, torch.from_numpy(lens).cuda(), window))
+    ref = _ref_latent(host, lens, window)
+    U.assert_close(got, ref, "bf16", f"latent {name} W={window}")
+    assert np.all(got[lens == 0] == 0.0), "an empty cache must give zeros"
+
+
 def test_latent_options_and_null_lengths():
     kw = LAT_SMALL["motif3_heads"]
     host, dev = _latent_case(**kw)
