@@ -47,14 +47,21 @@ constexpr int LPART = 4 + LDC;    // floats per (split, head) partial: m, l, 2 p
 constexpr int LMAX_WAVES = 8;     // up to 128 query heads (16 per wave)
 constexpr float kLNoMax = -1e30f; // finite "no key seen yet" reference
 
-// Slot of 16-byte piece p of latent row r: p ^ lswz(r). For the 16 rows of an
-// MFMA fragment read (fixed p) the slots fall on 16 distinct bank groups, and
-// for the transposed V^T reads (4 consecutive rows, a 32-byte piece pair each)
-// the pairs stay adjacent and on distinct banks. The XOR stays inside the
-// piece's aligned group of 16, so a row's slots are a permutation of its pieces.
-__device__ __forceinline__ int lswz(int r) { return 2 * (r & 7) + ((r >> 3) & 1); }
-// Rotary rows (8 pieces of 16 bytes): the same rule as 128-byte K rows.
-__device__ __forceinline__ int rswz(int r) { return (r >> 1) & 7; }
+// Slot of 16-byte piece p of latent row r: p ^ lswz(r), a function of r % 16 (so
+// rows r and r + 16 of a chunk share it). Over the 16 rows of an MFMA fragment
+// read (fixed p) lswz takes all 16 values, and over each aligned run of 8 rows
+// its low three bits take all 8: the read is free of bank conflicts whether the
+// LDS serves 16 lanes of 16 bytes per cycle or 8. For the transposed V^T reads
+// (a 32-byte piece pair per row; pair index ^ lswz(r) / 2) lswz / 2 takes 8
+// distinct values over each aligned 8 rows and 4 over each aligned 4. The XOR
+// stays inside the piece's aligned group of 16, so a row's slots are a
+// permutation of its pieces and the piece pairs stay adjacent.
+__device__ __forceinline__ int lswz(int r) {
+  return 2 * (r & 3) + ((r >> 2) & 1) + 8 * (((r >> 2) ^ (r >> 3)) & 1);
+}
+// Rotary rows (8 pieces of 16 bytes, two rows per 256 bytes): slot p ^ rswz(r),
+// distinct over each aligned 8 rows and, with the row's half of 256 bytes, over 16.
+__device__ __forceinline__ int rswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Heads of KV head h: signal i when floor(i*Hkv/S) == h, noise j when floor(j*Hkv/N) == h.
 // Column of a head in the workspace: signal i -> i, noise j -> S + j.
@@ -246,7 +253,7 @@ latent_attend_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict
     const int fv = lswz(rv);
     vbase = rv * (LDC * 2) + 16 * (((col & 3) >> 1) ^ (fv & 1)) + 8 * (col & 1);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) vtab[t] = 32 * (t ^ (rv & 7));
+    for (int t = 0; t < 8; ++t) vtab[t] = 32 * (t ^ (fv >> 1));
   }
   if (c0 < c1) issue(c0, 0);
   if (c0 + 1 < c1) issue(c0 + 1, 1);
@@ -341,92 +348,79 @@ latent_attend_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict
     *(floatx4*)(ph + 4 + 16 * db + 4 * g4) = o[db];
 }
 
-// ---- 2'. attend, work split over 8 waves (up to 5 head tiles) ---------------------
+// ---- 2'. attend, 8 waves in two roles (up to 5 head tiles) -------------------------
 // The kernel above gives each wave 16 heads over the whole chunk, so every wave
-// reads all 36 KB of the chunk from LDS (the LDS traffic, not the matrix work,
-// sets its pace) and 5 head tiles load one SIMD twice. Here the 8 waves split
-// the work so that each chunk byte is read from LDS about once:
-//  * scores: wave w computes partial S^T for key tile kh = w/4 (16 keys) over its
-//    quarter dq = w%4 of the 18 k-steps (k-step ks belongs to quarter ks%4), for
-//    every head tile, and writes the partial to LDS;
-//  * softmax: wave t < HT sums the four quarters of head tile t (both key tiles),
-//    keeps that tile's running max and sum, and writes the P^T operand (bf16) and
-//    whether it rescaled;
-//  * P.V: wave w owns latent dims 64w .. 64w+63 of O^T for every head tile
-//    (rescaled when a softmax wave raised its reference).
-// Three workgroup barriers per chunk: chunk landed, partials written, P written.
+// reads all 36 KB of the chunk from LDS and 5 head tiles load one SIMD twice.
+// Here the work of a 32-key chunk is split by role:
+//  * score waves (wave t < HT): head tile t's absorbed queries for all 18 k-steps
+//    sit in registers; the wave computes the tile's complete S^T for both 16-key
+//    halves of the chunk, keeps its online softmax (running reference and sum) and
+//    writes the P^T operand and the rescale factors;
+//  * every wave accumulates O^T for its run of the 32 tiles of 16 latent dims and
+//    every head tile (more tiles for the waves that compute no scores, so the
+//    matrix work per SIMD is even).
+// One workgroup barrier per chunk: in step j the score waves take chunk j's
+// scores and softmax while every wave adds chunk j-1's P.V (P^T and the rescale
+// factors are double-buffered). The ring holds four chunks: j-1 and j are read in
+// step j, j+1 is in flight, and j+2 goes into the stage of chunk j-2 right after
+// the barrier, two steps before it is needed.
 constexpr int A2_WAVES = 8;
 constexpr int A2_KSTEPS = (LDC + LDR) / 32;       // 18 k-steps of the scores
-constexpr int A2_KQ = (A2_KSTEPS + 3) / 4;        // at most 5 per quarter
-constexpr int A2_DT = LDC / 16 / A2_WAVES;        // 16-dim tiles of O^T per wave (4)
+constexpr int A2_NSTAGE = 4;                      // chunk ring depth
+constexpr int A2_AH = 8;                          // K fragment reads in flight (score waves)
 constexpr int A2_MAX_HT = 5;
 
 template <int HT>
 struct Attend2Smem {
-  unsigned char ring[LNSTAGE * LSTAGE];            // latent + rotary rows of 3 chunks
-  floatx4 part[2][4][HT][64];                       // partial S^T [kh][dq][tile][lane]
-  bf16x8 pt[HT][64];                                // P^T operands [tile][lane]
-  int rescaled[HT];                                 // tile t raised its reference
-  float alpha[HT][16];                              // its factors, per head column
+  unsigned char ring[A2_NSTAGE * LSTAGE];          // latent + rotary rows of 4 chunks
+  bf16x8 pt[2][HT][64];                             // P^T operands [step parity][tile][lane]
+  float alpha[2][HT][16];                           // rescale factors, per head column
+  int rescaled[2][HT];                              // tile t raised its reference
 };
+static_assert(sizeof(Attend2Smem<A2_MAX_HT>) <= 160 * 1024, "LDS of one workgroup per CU");
 
+// The 16-dim O^T tiles of wave w: count and first. With five head tiles waves 0
+// and 4 (both score waves, on SIMD 0) take one, the other score waves two and the
+// three others eight, so each SIMD issues 82-86 matrix instructions per chunk;
+// with fewer head tiles every wave takes four.
 template <int HT>
-__global__ void __launch_bounds__(64 * A2_WAVES, 1)
-latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict__ c_kv,
-                      const uint16_t* __restrict__ k_rope, const int32_t* __restrict__ lens,
-                      float* __restrict__ part, int Lmax, int window, int nsplit, float c) {
+__device__ __forceinline__ int a2_first_dim_tile(int w) {
+  if constexpr (HT == A2_MAX_HT) return w == 0 ? 0 : w < 4 ? 2 * w - 1 : w == 4 ? 7 : 8 * (w - 4);
+  return 4 * w;
+}
+
+template <int HT, bool SCORE, int ND>
+__device__ __forceinline__ void attend2_wave(Attend2Smem<HT>& sm, const uint16_t* __restrict__ qa,
+                                             const char* cbase, const char* rbase,
+                                             float* __restrict__ pw, int b, int wave, int lane,
+                                             int lo, int pos, int c0, int c1, float c) {
   constexpr int XP = 16 * HT;
-  __shared__ __attribute__((aligned(1024))) Attend2Smem<HT> sm;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4;
-  const int dq = wave & 3, kh = wave >> 2;
-  const int b = blockIdx.x / nsplit, k = blockIdx.x - (blockIdx.x / nsplit) * nsplit;
-  float* pw = part + ((int64_t)b * nsplit + k) * XP * LPART;
+  const int d0 = a2_first_dim_tile<HT>(wave);
 
-  int len = lens ? lens[b] : Lmax;
-  if (len > Lmax) len = Lmax;
-  const int pos = len - 1;
-  const int lo = window ? max(0, pos - window + 1) : 0;
-  const int nch = len >= 1 ? (pos - lo + LCK) / LCK : 0;
-  const int c0 = (int)(((int64_t)k * nch) / nsplit), c1 = (int)(((int64_t)(k + 1) * nch) / nsplit);
-
-  // Absorbed queries of this wave's k-steps (ks = dq + 4i), every head tile, as
-  // MFMA B operands (Q~^T: 32 dims x 16 heads).
-  bf16x8 qf[A2_KQ][HT];
-  {
-    const uint16_t* qp = qa + ((int64_t)b * XP + col) * LQW + 8 * g4;
+  // Score waves: head tile `wave`'s absorbed queries, every k-step, as MFMA B
+  // operands (Q~^T: 32 dims x 16 heads).
+  bf16x8 qf[SCORE ? A2_KSTEPS : 1];
+  if constexpr (SCORE) {
+    const uint16_t* qp = qa + ((int64_t)b * XP + 16 * wave + col) * LQW + 8 * g4;
 #pragma unroll
-    for (int i = 0; i < A2_KQ; ++i) {
-      const int ks = dq + 4 * i;
+    for (int ks = 0; ks < A2_KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 32 * ks));
 #pragma unroll
-      for (int t = 0; t < HT; ++t) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (ks < A2_KSTEPS) w = ldg16(qp + (int64_t)(16 * t) * LQW + 32 * ks);
-        qf[i][t] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < A2_KQ; ++i)
-#pragma unroll
-      for (int t = 0; t < HT; ++t) settle(qf[i][t]);  // before any copy is issued
+    for (int ks = 0; ks < A2_KSTEPS; ++ks) settle(qf[ks]);  // before any copy is issued
   }
-  // O^T: dims 64*wave + 16*dt + (4 g4 .. +3), head 16 t + col.
-  floatx4 o[A2_DT][HT];
+  // O^T: dims 16 (d0 + dt) + (4 g4 .. +3), head 16 t + col.
+  floatx4 o[ND][HT];
 #pragma unroll
-  for (int dt = 0; dt < A2_DT; ++dt)
+  for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int t = 0; t < HT; ++t) o[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // Softmax state of head tile `wave` (waves < HT): per column reference and sum.
-  float mref = kLNoMax, lsum = 0.f;
+  float mref = kLNoMax, lsum = 0.f;  // head tile `wave`'s softmax state (score waves)
 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const lds_void*)sm.ring;
-  const char* cbase = (const char*)(c_kv + (int64_t)b * Lmax * LDC);
-  const char* rbase = (const char*)(k_rope + (int64_t)b * Lmax * LDR);
-  auto issue = [&](int j, int st) {
+  auto issue = [&](int j) {
     const int s0 = lo + j * LCK;
     const int last = pos - s0;
-    const uint32_t dst = ring_lds + (uint32_t)(st * LSTAGE);
+    const uint32_t dst = ring_lds + (uint32_t)(((j - c0) & (A2_NSTAGE - 1)) * LSTAGE);
     for (int blk = wave; blk < LBLK; blk += A2_WAVES) {
       if (blk < LCK) {
         const int r = min(blk, last);
@@ -444,8 +438,9 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
   const int nmine = (LBLK - wave + A2_WAVES - 1) / A2_WAVES;
 
   // Per-lane parts of the fragment addresses (the layout of the kernel above):
-  // K fragment of key tile kh, k-step ks: row 16 kh + col.
-  int kbase, ktab[4], rtab[LDR / 32], vbase, vtab[8];
+  // K fragment of key half kh, k-step ks: row 16 kh + col; V^T fragment of dim
+  // tile d0 + dt: vofs[dt] within each 16-row half of the chunk.
+  int kbase, ktab[4], rtab[LDR / 32], vofs[ND];
   {
     const int f = lswz(col);
     kbase = col * (LDC * 2) + 16 * (g4 ^ (f & 3));
@@ -455,47 +450,44 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
     for (int ks = 0; ks < LDR / 32; ++ks) rtab[ks] = col * (LDR * 2) + ((((4 * ks + g4) ^ rswz(col))) << 4);
     const int rv = 4 * g4 + (col >> 2);
     const int fv = lswz(rv);
-    vbase = rv * (LDC * 2) + 16 * (((col & 3) >> 1) ^ (fv & 1)) + 8 * (col & 1);
+    const int vbase = rv * (LDC * 2) + 16 * (((col & 3) >> 1) ^ (fv & 1)) + 8 * (col & 1);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) vtab[t] = 32 * (t ^ (rv & 7));
+    for (int dt = 0; dt < ND; ++dt) {
+      const int db = d0 + dt;
+      vofs[dt] = vbase + 256 * (db >> 3) + 32 * ((db & 7) ^ (fv >> 1));
+    }
   }
-  auto stage_of = [&](int j) { return sm.ring + ((j - c0) % LNSTAGE) * LSTAGE; };
+  auto stage_of = [&](int j) { return sm.ring + ((j - c0) & (A2_NSTAGE - 1)) * LSTAGE; };
 
-  // Partial S^T of chunk j's key tile kh over this wave's k-steps, every head tile.
-  auto scores = [&](int j) {
+  // Chunk j's scores of head tile `wave` (both key halves, all k-steps) and its
+  // softmax step: running reference and sum, the P^T operand and the rescale
+  // flag and factors, into the buffers of step parity j & 1.
+  auto scores_softmax = [&](int j) {
     const unsigned char* sC = stage_of(j);
     const unsigned char* sR = sC + LC_BYTES;
-    floatx4 s[HT];
+    floatx4 sk[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int t = 0; t < HT; ++t) s[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < A2_KSTEPS; ++ks) {
 #pragma unroll
-    for (int i = 0; i < A2_KQ; ++i) {
-      const int ks = dq + 4 * i;
-      if (ks >= A2_KSTEPS) break;  // wave-uniform
-      bf16x8 a;
-      if (ks < LDC / 32)
-        a = *(const bf16x8*)(sC + kbase + kh * (16 * LDC * 2) + 256 * (ks >> 2) + ktab[ks & 3]);
-      else
-        a = *(const bf16x8*)(sR + kh * (16 * LDR * 2) + rtab[ks - LDC / 32]);
-#pragma unroll
-      for (int t = 0; t < HT; ++t) s[t] = mfma_16x16x32(a, qf[i][t], s[t]);
+      for (int kh = 0; kh < 2; ++kh) {
+        bf16x8 a;
+        if (ks < LDC / 32)
+          a = *(const bf16x8*)(sC + kbase + kh * (16 * LDC * 2) + 256 * (ks >> 2) + ktab[ks & 3]);
+        else
+          a = *(const bf16x8*)(sR + kh * (16 * LDR * 2) + rtab[ks - LDC / 32]);
+        sk[kh] = mfma_16x16x32(a, qf[SCORE ? ks : 0], sk[kh]);
+      }
     }
+    // Schedule: the first A2_AH fragment reads, then each product followed by the
+    // read A2_AH fragments ahead, so the LDS latency hides behind the products
+    // (left to itself the compiler keeps one or two reads in flight).
+    __builtin_amdgcn_sched_group_barrier(0x100, A2_AH, 0);
 #pragma unroll
-    for (int t = 0; t < HT; ++t) sm.part[kh][dq][t][lane] = s[t];
-  };
-
-  // Softmax of head tile `wave` over chunk j's 32 keys: running reference and
-  // sum, the P^T operand and the rescale flag and factors.
-  auto softmax = [&](int j) {
+    for (int i = 0; i < 2 * A2_KSTEPS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + A2_AH < 2 * A2_KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
     const int s0 = lo + j * LCK;
-    floatx4 sk[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const floatx4 p0 = sm.part[h][0][wave][lane], p1 = sm.part[h][1][wave][lane];
-      const floatx4 p2 = sm.part[h][2][wave][lane], p3 = sm.part[h][3][wave][lane];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sk[h][r] = (p0[r] + p1[r]) + (p2[r] + p3[r]);
-    }
     if (s0 + LCK - 1 > pos) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -505,16 +497,17 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
     }
     const float mx = fmaxf(fmaxf(fmaxf(sk[0][0], sk[0][1]), fmaxf(sk[0][2], sk[0][3])),
                            fmaxf(fmaxf(sk[1][0], sk[1][1]), fmaxf(sk[1][2], sk[1][3])));
+    const int par = j & 1;
     int resc = 0;
     if (__builtin_amdgcn_ballot_w64(mx * c > mref + 8.f)) {
       const float mnew = fmaxf(mref, col_max4(mx) * c);
       const float alpha = fast_exp2(mref - mnew);
       mref = mnew;
       lsum *= alpha;
-      if (g4 == 0) sm.alpha[wave][col] = alpha;
+      if (g4 == 0) sm.alpha[par][wave][col] = alpha;
       resc = 1;
     }
-    if (lane == 0) sm.rescaled[wave] = resc;
+    if (lane == 0) sm.rescaled[par][wave] = resc;
     bf16x8 pb;
     float ps = 0.f;
 #pragma unroll
@@ -526,33 +519,33 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
         pb[4 * h + r] = (__bf16)p;
       }
     lsum += ps;
-    sm.pt[wave][lane] = pb;
+    sm.pt[par][wave][lane] = pb;
   };
 
-  // O^T (this wave's 64 latent dims) += C^T . P^T of chunk j, every head tile,
-  // after the rescale its softmax asked for.
+  // O^T (this wave's dim tiles) += C^T . P^T of chunk j, every head tile, after
+  // the rescale chunk j's softmax asked for.
   auto pv = [&](int j) {
     const unsigned char* sC = stage_of(j);
+    const int par = j & 1;
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
-      if (__builtin_amdgcn_readfirstlane(sm.rescaled[t])) {
-        const float al = sm.alpha[t][col];
+      if (__builtin_amdgcn_readfirstlane(sm.rescaled[par][t])) {
+        const float al = sm.alpha[par][t][col];
 #pragma unroll
-        for (int dt = 0; dt < A2_DT; ++dt)
+        for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[dt][t][r] *= al;
       }
     }
     bf16x8 pbt[HT];
 #pragma unroll
-    for (int t = 0; t < HT; ++t) pbt[t] = sm.pt[t][lane];
+    for (int t = 0; t < HT; ++t) pbt[t] = sm.pt[par][t][lane];
 #pragma unroll
-    for (int dt = 0; dt < A2_DT; ++dt) {
-      const int db = A2_DT * wave + dt;
+    for (int dt = 0; dt < ND; ++dt) {
       shortx4 half[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const unsigned char* va = sC + vbase + hf * (16 * LDC * 2) + 256 * (db >> 3) + vtab[db & 7];
+        const unsigned char* va = sC + vofs[dt] + hf * (16 * LDC * 2);
         half[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)va);
       }
       typedef __attribute__((__vector_size__(8 * sizeof(short)))) short shortx8;
@@ -564,13 +557,8 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
     }
   };
 
-  // Software pipeline, two barriers per chunk: interval A of step j holds the
-  // P.V products of chunk j-1 and the score products of chunk j (independent
-  // matrix work for the two waves of each SIMD), interval B the softmax of
-  // chunk j. Chunk j's stage is read in steps j and j+1, so chunk j+2 is copied
-  // into the stage of chunk j-1 once step j's interval A is over.
-  if (c0 < c1) issue(c0, 0);
-  if (c0 + 1 < c1) issue(c0 + 1, 1);
+  if (c0 < c1) issue(c0);
+  if (c0 + 1 < c1) issue(c0 + 1);
 #pragma unroll 1
   for (int j = c0; j <= c1; ++j) {
     if (j < c1) {  // chunk j landed (chunk j+1's copies may still be in flight)
@@ -579,16 +567,18 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
       else
         wait_vmcnt<0>();
     }
-    __syncthreads();  // chunk j landed; P^T of chunk j-1 written
+    // Chunk j landed; P^T of chunk j-1 written; chunk j-2's stage and the
+    // step-parity buffers of chunk j no longer read.
+    __syncthreads();
+    if (j + 2 < c1) issue(j + 2);
+    if constexpr (SCORE) {
+      if (j < c1) scores_softmax(j);
+    }
     if (j > c0) pv(j - 1);
-    if (j < c1) scores(j);
-    __syncthreads();  // partial scores of chunk j written; chunk j-1 and P^T no longer read
-    if (j + 2 < c1) issue(j + 2, (j + 2 - c0) % LNSTAGE);
-    if (j < c1 && wave < HT) softmax(j);
   }
-  // Partials: m (log2 units) and l of each head from its softmax wave, o[Dc]
-  // (unnormalised) from every wave's dims.
-  if (wave < HT) {
+  // Partials: m (log2 units) and l of each head from its score wave, o[Dc]
+  // (unnormalised) from every wave's dim tiles.
+  if constexpr (SCORE) {
     lsum = col_sum4(lsum);
     float* ph = pw + (16 * wave + col) * LPART;
     if (g4 == 0) {
@@ -600,8 +590,43 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
   for (int t = 0; t < HT; ++t) {
     float* ph = pw + (16 * t + col) * LPART + 4;
 #pragma unroll
-    for (int dt = 0; dt < A2_DT; ++dt)
-      *(floatx4*)(ph + 16 * (A2_DT * wave + dt) + 4 * g4) = o[dt][t];
+    for (int dt = 0; dt < ND; ++dt) *(floatx4*)(ph + 16 * (d0 + dt) + 4 * g4) = o[dt][t];
+  }
+}
+
+template <int HT>
+__global__ void __launch_bounds__(64 * A2_WAVES, 1)
+latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict__ c_kv,
+                      const uint16_t* __restrict__ k_rope, const int32_t* __restrict__ lens,
+                      float* __restrict__ part, int Lmax, int window, int nsplit, float c) {
+  constexpr int XP = 16 * HT;
+  __shared__ __attribute__((aligned(1024))) Attend2Smem<HT> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x / nsplit, k = blockIdx.x - (blockIdx.x / nsplit) * nsplit;
+  float* pw = part + ((int64_t)b * nsplit + k) * XP * LPART;
+
+  int len = lens ? lens[b] : Lmax;
+  if (len > Lmax) len = Lmax;
+  const int pos = len - 1;
+  const int lo = window ? max(0, pos - window + 1) : 0;
+  const int nch = len >= 1 ? (pos - lo + LCK) / LCK : 0;
+  const int c0 = (int)(((int64_t)k * nch) / nsplit), c1 = (int)(((int64_t)(k + 1) * nch) / nsplit);
+  const char* cbase = (const char*)(c_kv + (int64_t)b * Lmax * LDC);
+  const char* rbase = (const char*)(k_rope + (int64_t)b * Lmax * LDR);
+  // Wave-uniform role dispatch; every path runs the same barrier sequence.
+  if constexpr (HT == A2_MAX_HT) {
+    if (wave == 0 || wave == 4)
+      attend2_wave<HT, true, 1>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+    else if (wave < 4)
+      attend2_wave<HT, true, 2>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+    else
+      attend2_wave<HT, false, 8>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+  } else {
+    if (wave < HT)
+      attend2_wave<HT, true, 4>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+    else
+      attend2_wave<HT, false, 4>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
   }
 }
 
