@@ -352,18 +352,23 @@ latent_attend_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restrict
 // The kernel above gives each wave 16 heads over the whole chunk, so every wave
 // reads all 36 KB of the chunk from LDS and 5 head tiles load one SIMD twice.
 // Here the work of a 32-key chunk is split by role:
-//  * score waves (wave t < HT): head tile t's absorbed queries for all 18 k-steps
-//    sit in registers; the wave computes the tile's complete S^T for both 16-key
-//    halves of the chunk, keeps its online softmax (running reference and sum) and
-//    writes the P^T operand and the rescale factors;
-//  * every wave accumulates O^T for its run of the 32 tiles of 16 latent dims and
-//    every head tile (more tiles for the waves that compute no scores, so the
-//    matrix work per SIMD is even).
+//  * score waves (wave s < (HT+1)/2): head tiles 2s and 2s+1 (the last score wave
+//    of an odd HT takes one): their absorbed queries for all 18 k-steps sit in
+//    registers; the wave computes the tiles' complete S^T for both 16-key halves
+//    of the chunk, each K fragment read serving both tiles, keeps their online
+//    softmax (running reference and sum) and writes their P^T operands and
+//    rescale factors;
+//  * the other waves (and the one-tile score wave) accumulate O^T for runs of the
+//    32 tiles of 16 latent dims and every head tile, sized so that the matrix
+//    work per SIMD is even.
+// The K fragment reads (the largest LDS stream: 36 KB per score wave and chunk)
+// are what the score products wait on, so fewer score waves each serving two
+// tiles halve them.
 // One workgroup barrier per chunk: in step j the score waves take chunk j's
-// scores and softmax while every wave adds chunk j-1's P.V (P^T and the rescale
-// factors are double-buffered). The ring holds four chunks: j-1 and j are read in
-// step j, j+1 is in flight, and j+2 goes into the stage of chunk j-2 right after
-// the barrier, two steps before it is needed.
+// scores and softmax while the other waves add chunk j-1's P.V (P^T and the
+// rescale factors are double-buffered). The ring holds four chunks: j-1 and j are
+// read in step j, j+1 is in flight, and j+2 goes into the stage of chunk j-2 right
+// after the barrier, two steps before it is needed.
 constexpr int A2_WAVES = 8;
 constexpr int A2_KSTEPS = (LDC + LDR) / 32;       // 18 k-steps of the scores
 constexpr int A2_NSTAGE = 4;                      // chunk ring depth
@@ -379,42 +384,57 @@ struct Attend2Smem {
 };
 static_assert(sizeof(Attend2Smem<A2_MAX_HT>) <= 160 * 1024, "LDS of one workgroup per CU");
 
-// The 16-dim O^T tiles of wave w: count and first. With five head tiles waves 0
-// and 4 (both score waves, on SIMD 0) take one, the other score waves two and the
-// three others eight, so each SIMD issues 82-86 matrix instructions per chunk;
-// with fewer head tiles every wave takes four.
+// First 16-dim O^T tile of wave w (the counts are the ND of its role). Five
+// head tiles: waves 0 and 1 score two tiles each and take no dims, wave 2
+// scores one and takes 2 dims, waves 4 and 5 take 3 and waves 3, 6, 7 take 8:
+// 80-87 matrix instructions per SIMD and chunk (wave w runs on SIMD w % 4).
+// Fewer head tiles: waves 4-7 take 8 dims each, the others none.
 template <int HT>
 __device__ __forceinline__ int a2_first_dim_tile(int w) {
-  if constexpr (HT == A2_MAX_HT) return w == 0 ? 0 : w < 4 ? 2 * w - 1 : w == 4 ? 7 : 8 * (w - 4);
-  return 4 * w;
+  if constexpr (HT == A2_MAX_HT) return w == 3 ? 2 : w == 4 ? 10 : w == 5 ? 13 : w >= 6 ? 8 * (w - 4) : 0;
+  return w >= 4 ? 8 * (w - 4) : 0;
 }
 
-template <int HT, bool SCORE, int ND>
+// One wave's whole loop: NTS head tiles scored (0: none), ND dim tiles of O^T.
+template <int HT, int NTS, int ND>
 __device__ __forceinline__ void attend2_wave(Attend2Smem<HT>& sm, const uint16_t* __restrict__ qa,
                                              const char* cbase, const char* rbase,
                                              float* __restrict__ pw, int b, int wave, int lane,
                                              int lo, int pos, int c0, int c1, float c) {
   constexpr int XP = 16 * HT;
+  constexpr int NQ = NTS > 0 ? NTS : 1;
   const int col = lane & 15, g4 = lane >> 4;
   const int d0 = a2_first_dim_tile<HT>(wave);
+  const int t0 = 2 * wave;  // first head tile of a score wave
 
-  // Score waves: head tile `wave`'s absorbed queries, every k-step, as MFMA B
+  // Score waves: their head tiles' absorbed queries, every k-step, as MFMA B
   // operands (Q~^T: 32 dims x 16 heads).
-  bf16x8 qf[SCORE ? A2_KSTEPS : 1];
-  if constexpr (SCORE) {
-    const uint16_t* qp = qa + ((int64_t)b * XP + 16 * wave + col) * LQW + 8 * g4;
+  bf16x8 qf[NQ][A2_KSTEPS];
+  if constexpr (NTS > 0) {
 #pragma unroll
-    for (int ks = 0; ks < A2_KSTEPS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 32 * ks));
+    for (int u = 0; u < NTS; ++u) {
+      const uint16_t* qp = qa + ((int64_t)b * XP + 16 * (t0 + u) + col) * LQW + 8 * g4;
 #pragma unroll
-    for (int ks = 0; ks < A2_KSTEPS; ++ks) settle(qf[ks]);  // before any copy is issued
+      for (int ks = 0; ks < A2_KSTEPS; ++ks)
+        qf[u][ks] = __builtin_bit_cast(bf16x8, ldg16(qp + 32 * ks));
+    }
+#pragma unroll
+    for (int u = 0; u < NTS; ++u)
+#pragma unroll
+      for (int ks = 0; ks < A2_KSTEPS; ++ks) settle(qf[u][ks]);  // before any copy is issued
   }
   // O^T: dims 16 (d0 + dt) + (4 g4 .. +3), head 16 t + col.
-  floatx4 o[ND][HT];
+  floatx4 o[ND > 0 ? ND : 1][HT];
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int t = 0; t < HT; ++t) o[dt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float mref = kLNoMax, lsum = 0.f;  // head tile `wave`'s softmax state (score waves)
+  float mref[NQ], lsum[NQ];  // the scored tiles' softmax state
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    mref[u] = kLNoMax;
+    lsum[u] = 0.f;
+  }
 
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const lds_void*)sm.ring;
   auto issue = [&](int j) {
@@ -440,7 +460,7 @@ __device__ __forceinline__ void attend2_wave(Attend2Smem<HT>& sm, const uint16_t
   // Per-lane parts of the fragment addresses (the layout of the kernel above):
   // K fragment of key half kh, k-step ks: row 16 kh + col; V^T fragment of dim
   // tile d0 + dt: vofs[dt] within each 16-row half of the chunk.
-  int kbase, ktab[4], rtab[LDR / 32], vofs[ND];
+  int kbase, ktab[4], rtab[LDR / 32], vofs[ND > 0 ? ND : 1];
   {
     const int f = lswz(col);
     kbase = col * (LDC * 2) + 16 * (g4 ^ (f & 3));
@@ -459,13 +479,15 @@ __device__ __forceinline__ void attend2_wave(Attend2Smem<HT>& sm, const uint16_t
   }
   auto stage_of = [&](int j) { return sm.ring + ((j - c0) & (A2_NSTAGE - 1)) * LSTAGE; };
 
-  // Chunk j's scores of head tile `wave` (both key halves, all k-steps) and its
-  // softmax step: running reference and sum, the P^T operand and the rescale
-  // flag and factors, into the buffers of step parity j & 1.
+  // Chunk j's scores of the wave's head tiles (both key halves, all k-steps) and
+  // their softmax step: running reference and sum, the P^T operand and the
+  // rescale flag and factors, into the buffers of step parity j & 1.
   auto scores_softmax = [&](int j) {
     const unsigned char* sC = stage_of(j);
     const unsigned char* sR = sC + LC_BYTES;
-    floatx4 sk[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    floatx4 sk[NQ][2];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) sk[u][0] = sk[u][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < A2_KSTEPS; ++ks) {
 #pragma unroll
@@ -475,51 +497,57 @@ __device__ __forceinline__ void attend2_wave(Attend2Smem<HT>& sm, const uint16_t
           a = *(const bf16x8*)(sC + kbase + kh * (16 * LDC * 2) + 256 * (ks >> 2) + ktab[ks & 3]);
         else
           a = *(const bf16x8*)(sR + kh * (16 * LDR * 2) + rtab[ks - LDC / 32]);
-        sk[kh] = mfma_16x16x32(a, qf[SCORE ? ks : 0], sk[kh]);
+#pragma unroll
+        for (int u = 0; u < NTS; ++u) sk[u][kh] = mfma_16x16x32(a, qf[u][ks], sk[u][kh]);
       }
     }
-    // Schedule: the first A2_AH fragment reads, then each product followed by the
-    // read A2_AH fragments ahead, so the LDS latency hides behind the products
-    // (left to itself the compiler keeps one or two reads in flight).
+    // Schedule: the first A2_AH fragment reads, then each fragment's products
+    // followed by the read A2_AH fragments ahead, so the LDS latency hides behind
+    // the products (left to itself the compiler keeps one or two reads in flight).
     __builtin_amdgcn_sched_group_barrier(0x100, A2_AH, 0);
 #pragma unroll
     for (int i = 0; i < 2 * A2_KSTEPS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NTS, 0);
       if (i + A2_AH < 2 * A2_KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     const int s0 = lo + j * LCK;
-    if (s0 + LCK - 1 > pos) {
+    const int par = j & 1;
+#pragma unroll
+    for (int u = 0; u < NTS; ++u) {
+      floatx4 (&s)[2] = sk[u];
+      const int tt = t0 + u;
+      if (s0 + LCK - 1 > pos) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (s0 + 16 * h + 4 * g4 + r > pos) s[h][r] = -INFINITY;
+      }
+      const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                             fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      int resc = 0;
+      if (__builtin_amdgcn_ballot_w64(mx * c > mref[u] + 8.f)) {
+        const float mnew = fmaxf(mref[u], col_max4(mx) * c);
+        const float alpha = fast_exp2(mref[u] - mnew);
+        mref[u] = mnew;
+        lsum[u] *= alpha;
+        if (g4 == 0) sm.alpha[par][tt][col] = alpha;
+        resc = 1;
+      }
+      if (lane == 0) sm.rescaled[par][tt] = resc;
+      bf16x8 pb;
+      float ps = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (s0 + 16 * h + 4 * g4 + r > pos) sk[h][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(s[h][r], c, -mref[u]));
+          ps += p;
+          pb[4 * h + r] = (__bf16)p;
+        }
+      lsum[u] += ps;
+      sm.pt[par][tt][lane] = pb;
     }
-    const float mx = fmaxf(fmaxf(fmaxf(sk[0][0], sk[0][1]), fmaxf(sk[0][2], sk[0][3])),
-                           fmaxf(fmaxf(sk[1][0], sk[1][1]), fmaxf(sk[1][2], sk[1][3])));
-    const int par = j & 1;
-    int resc = 0;
-    if (__builtin_amdgcn_ballot_w64(mx * c > mref + 8.f)) {
-      const float mnew = fmaxf(mref, col_max4(mx) * c);
-      const float alpha = fast_exp2(mref - mnew);
-      mref = mnew;
-      lsum *= alpha;
-      if (g4 == 0) sm.alpha[par][wave][col] = alpha;
-      resc = 1;
-    }
-    if (lane == 0) sm.rescaled[par][wave] = resc;
-    bf16x8 pb;
-    float ps = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(sk[h][r], c, -mref));
-        ps += p;
-        pb[4 * h + r] = (__bf16)p;
-      }
-    lsum += ps;
-    sm.pt[par][wave][lane] = pb;
   };
 
   // O^T (this wave's dim tiles) += C^T . P^T of chunk j, every head tile, after
@@ -571,19 +599,22 @@ __device__ __forceinline__ void attend2_wave(Attend2Smem<HT>& sm, const uint16_t
     // step-parity buffers of chunk j no longer read.
     __syncthreads();
     if (j + 2 < c1) issue(j + 2);
-    if constexpr (SCORE) {
+    if constexpr (NTS > 0) {
       if (j < c1) scores_softmax(j);
     }
-    if (j > c0) pv(j - 1);
+    if constexpr (ND > 0) {
+      if (j > c0) pv(j - 1);
+    }
   }
   // Partials: m (log2 units) and l of each head from its score wave, o[Dc]
   // (unnormalised) from every wave's dim tiles.
-  if constexpr (SCORE) {
-    lsum = col_sum4(lsum);
-    float* ph = pw + (16 * wave + col) * LPART;
+#pragma unroll
+  for (int u = 0; u < NTS; ++u) {
+    const float l = col_sum4(lsum[u]);
+    float* ph = pw + (16 * (t0 + u) + col) * LPART;
     if (g4 == 0) {
-      ph[0] = mref;
-      ph[1] = lsum;
+      ph[0] = mref[u];
+      ph[1] = l;
     }
   }
 #pragma unroll
@@ -614,20 +645,30 @@ latent_attend2_kernel(const uint16_t* __restrict__ qa, const uint16_t* __restric
   const int c0 = (int)(((int64_t)k * nch) / nsplit), c1 = (int)(((int64_t)(k + 1) * nch) / nsplit);
   const char* cbase = (const char*)(c_kv + (int64_t)b * Lmax * LDC);
   const char* rbase = (const char*)(k_rope + (int64_t)b * Lmax * LDR);
-  // Wave-uniform role dispatch; every path runs the same barrier sequence.
+  // Wave-uniform role dispatch (a2_first_dim_tile gives the dims); every path
+  // runs the same barrier sequence.
+#define GDA_A2_WAVE(NTS, ND) \
+  attend2_wave<HT, NTS, ND>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c)
   if constexpr (HT == A2_MAX_HT) {
-    if (wave == 0 || wave == 4)
-      attend2_wave<HT, true, 1>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
-    else if (wave < 4)
-      attend2_wave<HT, true, 2>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+    if (wave < 2)
+      GDA_A2_WAVE(2, 0);
+    else if (wave == 2)
+      GDA_A2_WAVE(1, 2);
+    else if (wave == 4 || wave == 5)
+      GDA_A2_WAVE(0, 3);
     else
-      attend2_wave<HT, false, 8>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+      GDA_A2_WAVE(0, 8);
   } else {
-    if (wave < HT)
-      attend2_wave<HT, true, 4>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+    if (wave < HT / 2)
+      GDA_A2_WAVE(2, 0);
+    else if ((HT & 1) && wave == HT / 2)
+      GDA_A2_WAVE(1, 0);
+    else if (wave >= 4)
+      GDA_A2_WAVE(0, 8);
     else
-      attend2_wave<HT, false, 4>(sm, qa, cbase, rbase, pw, b, wave, lane, lo, pos, c0, c1, c);
+      GDA_A2_WAVE(0, 0);
   }
+#undef GDA_A2_WAVE
 }
 
 // ---- 3. merge, up-project, epilogue ------------------------------------------------
