@@ -13,8 +13,11 @@ decode's HBM GB/s is reported beside it. Inputs are resident in HBM before the
 timed region; times come from HIP events on the stream the kernels run on.
 A breakdown times every other workload (Motif-2 layer, sliding window W=128,
 W=128 decode, the decode over the latent cache (full and W=128), one GPU's share
-of the full layer split over 8 GPUs, the fp32 tiny case) outside the step: 10 warmup launches, 50 timed
-(median and min), and for the small ones a second run with a 1 GiB write between
+of the full layer split over 8 GPUs, the fp32 tiny case) outside the step. Every timed
+series, the step's included, starts after 0.3 s of untimed launches (the GPU's clocks
+reach their sustained level only after a few hundred milliseconds of load), then
+10 warmup launches; each workload is timed over 50 launches (median and min), and
+for the small ones a second run with a 1 GiB write between
 launches so that no input is left in L2 or the memory-side cache. The CPU baseline is the fp64 oracle
 timed on a bounded sample of the prefill rows. Prints ONE JSON line.
 
@@ -171,10 +174,32 @@ def latent_fn(torch, dev, cfg, out, api):
     return fn
 
 
+RAMP_S = 0.3
+
+
+def ramp(torch, fn, seconds):
+    """Untimed launches for at least ``seconds`` of wall time. The GPU's clocks reach
+    their sustained level only after a few hundred milliseconds under load; before
+    each timed series the inputs are generated on the host, during which the GPU
+    idles, so a series of a few dozen short launches would otherwise be timed at
+    ramping clocks (0.53 instead of 0.49 ms for the latent decode, measured)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return
+
+
 def event_times(torch, fn, reps, warmup, flush=None):
-    """Per-launch milliseconds, HIP events on the current stream around each launch.
+    """Per-launch milliseconds, HIP events on the current stream around each launch,
+    after a clock ramp and ``warmup`` untimed launches.
     With ``flush`` (a large device buffer) every launch is preceded, outside its
     events, by a write of the whole buffer, which evicts the inputs from the caches."""
+    ramp(torch, fn, RAMP_S)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -349,8 +374,13 @@ def main():
     if args.profile:
         copy_kernel(torch)
 
-    # ---- timed steps: warmup, barrier + sync, K steps, sync -------------------------
-    log(f"warmup {args.warmup} steps")
+    # ---- timed steps: clock ramp, warmup, barrier + sync, K steps, sync ---------------
+    def step():
+        run_fwd()
+        run_dec()
+
+    log(f"clock ramp ({RAMP_S} s of untimed steps), then warmup {args.warmup} steps")
+    ramp(torch, step, RAMP_S)
     for _ in range(args.warmup):
         run_fwd()
         run_dec()
@@ -503,6 +533,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_s": RAMP_S,
         "ms_per_step": round(wall * 1e3 / args.steps, 3),
         "higher_is_better": True,
         "scaling": "weak",
