@@ -265,15 +265,17 @@ __device__ __forceinline__ void chunk_softmax(const Ctx& x, State<C, NH>& st, fl
   const int W = x.window;
   const bool need_mask = (c0 + 31 > x.w_lo) || (W && c0 < x.w_hi - W + 1);
   if (need_mask) {
+    // Selects, not branches: a per-element branch here compiles to a divergent
+    // exec-mask sequence per score, on every chunk that crosses the diagonal or
+    // the window edge (two of the five chunks of a W = 128 window).
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = c0 + 16 * kb + 4 * x.g4 + r;
         const bool vis = key <= x.t && (!W || x.t - key < W);
-        if (!vis)
 #pragma unroll
-          for (int h = 0; h < NACT; ++h) s[h][kb][r] = -INFINITY;
+        for (int h = 0; h < NACT; ++h) s[h][kb][r] = vis ? s[h][kb][r] : -INFINITY;
       }
   }
 #pragma unroll
