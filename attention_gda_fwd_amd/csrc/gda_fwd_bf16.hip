@@ -80,6 +80,10 @@ struct Cfg {
   // key loop and release the B waves before the A waves' stores; long ones
   // (one per CU) run their measured-faster order: A stores, then B.
   static constexpr bool kEarlyEpilogue = NQG == 2;
+  // Per-tile copy bases (issue_block_fast) for the short one-KV-head workgroups,
+  // which issue a tile's copies on every tile of a short key range; in the other
+  // shapes the extra live values spill registers.
+  static constexpr bool kTileBase = !TWO_KV && NQG == 2;
   static_assert(BN == 32 || BN == 64, "an LDS tile is one or two 32-key chunks");
   static_assert(TBLK % NW == 0, "every wave issues the same number of tile blocks");
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "runs of NW blocks never mix K and V");
@@ -178,21 +182,40 @@ __device__ __forceinline__ void issue_block_fast(const Ctx& x, uint32_t ring_lds
   const int fb = first - kvi * per;
   const int kvh = kvi ? x.kvB : x.kvA;
   const uint32_t st_off = 2u * (uint32_t)((DST * C::NKV + kvi) * C::KV_ELEMS);
+  // With kTileBase: one 64-bit base per tile and kind (the tile's first key row,
+  // shared by every block of that kind, so it is computed once per tile), plus the
+  // block's offset from it, which depends only on the wave and the block (the same
+  // on every tile) and joins the lane's 32-bit offset; full 64-bit address
+  // arithmetic per block costs about 13 scalar instructions per copy.
   if (fb < C::KBLK) {
     const int bi = fb + x.wave;
     const int kb = bi / C::KS, ks = bi - (bi / C::KS) * C::KS;
-    const char* g = (const char*)x.kg +
-                    (((int64_t)(k0 + 16 * kb) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
-    dma16_lds(g, (uint32_t)(x.lane & 15) * (uint32_t)(x.Hkv * C::DQK * 2) + 16u * (uint32_t)(x.lane >> 4),
-              ring_lds + st_off + 1024u * (uint32_t)bi);
+    const uint32_t lane_off =
+        (uint32_t)(x.lane & 15) * (uint32_t)(x.Hkv * C::DQK * 2) + 16u * (uint32_t)(x.lane >> 4);
+    if constexpr (C::kTileBase) {
+      const char* g = (const char*)x.kg + (int64_t)k0 * (x.Hkv * C::DQK * 2);
+      const uint32_t boff = (uint32_t)(((16 * kb) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2u;
+      dma16_lds(g, boff + lane_off, ring_lds + st_off + 1024u * (uint32_t)bi);
+    } else {
+      const char* g = (const char*)x.kg +
+                      (((int64_t)(k0 + 16 * kb) * x.Hkv + kvh) * C::DQK + 32 * ks) * 2;
+      dma16_lds(g, lane_off, ring_lds + st_off + 1024u * (uint32_t)bi);
+    }
   } else {
     const int vi = fb - C::KBLK + x.wave;
     const int lr = x.lane / C::VCH;
     const int r = C::VRPB * vi + lr;
     const int cch = (x.lane % C::VCH) ^ ((r % C::VPAIR) << 1);
-    const char* g = (const char*)x.vg + ((int64_t)(k0 + C::VRPB * vi) * x.Hkv + kvh) * C::DV * 2;
-    dma16_lds(g, (uint32_t)lr * (uint32_t)(x.Hkv * C::DV * 2) + 16u * (uint32_t)cch,
-              ring_lds + st_off + 2u * C::K_ELEMS + 1024u * (uint32_t)vi);
+    const uint32_t lane_off = (uint32_t)lr * (uint32_t)(x.Hkv * C::DV * 2) + 16u * (uint32_t)cch;
+    if constexpr (C::kTileBase) {
+      const char* g = (const char*)x.vg + (int64_t)k0 * (x.Hkv * C::DV * 2);
+      const uint32_t boff = (uint32_t)((C::VRPB * vi) * x.Hkv + kvh) * (uint32_t)(C::DV * 2);
+      dma16_lds(g, boff + lane_off, ring_lds + st_off + 2u * C::K_ELEMS + 1024u * (uint32_t)vi);
+    } else {
+      const char* g =
+          (const char*)x.vg + ((int64_t)(k0 + C::VRPB * vi) * x.Hkv + kvh) * C::DV * 2;
+      dma16_lds(g, lane_off, ring_lds + st_off + 2u * C::K_ELEMS + 1024u * (uint32_t)vi);
+    }
   }
 }
 
