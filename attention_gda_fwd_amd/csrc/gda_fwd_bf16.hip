@@ -80,10 +80,11 @@ struct Cfg {
   // key loop and release the B waves before the A waves' stores; long ones
   // (one per CU) run their measured-faster order: A stores, then B.
   static constexpr bool kEarlyEpilogue = NQG == 2;
-  // Per-tile copy bases (issue_block_fast) for the short one-KV-head workgroups,
-  // which issue a tile's copies on every tile of a short key range; in the other
-  // shapes the extra live values spill registers.
-  static constexpr bool kTileBase = !TWO_KV && NQG == 2;
+  // Per-tile copy bases (issue_block_fast) where a tile is one 32-key chunk (its
+  // copies' scalar arithmetic is then a larger share of the tile): the short
+  // one-KV-head workgroups and the 64-query two-KV-head ones. In the short
+  // two-KV-head and the 64-key shapes the extra live values spill registers.
+  static constexpr bool kTileBase = NQG == 2 ? !TWO_KV : (TWO_KV && BN == 32);
   static_assert(BN == 32 || BN == 64, "an LDS tile is one or two 32-key chunks");
   static_assert(TBLK % NW == 0, "every wave issues the same number of tile blocks");
   static_assert(KBLK % NW == 0 && VBLK % NW == 0, "runs of NW blocks never mix K and V");
